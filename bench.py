@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Throughput of the pipelined persistent bf16 GEMM on one MI355X.
+
+A step is one C = A * B over the whole throughput workload (8192 x 8192 x 8192,
+B stored N x K, seeded uniform[-1, 1) bf16 inputs already resident in HBM).
+Each sync mode (barrier, flags, wave-specialised) is timed at its default
+stage count; ``value`` is the fastest mode and every mode is listed under
+``modes``.  Prints one JSON line.
+
+Also reports:
+  roofline      achieved matrix-core TFLOP/s of the GEMM kernel (2*M*N*K per
+                launch / mean launch time from HIP events on the launch
+                stream) against the dense bf16 peak, plus HBM traffic per
+                launch from the committed rocprofv3 counter summary when it
+                matches the current kernel source;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same product
+                (a few rows of C), on the host cores it actually uses.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sync all|barrier|flags|wavespec]
+                       [--stages S] [--workload NAME] [--no-cpu-baseline] [--copy-calibration]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm8192_nk.json")
+KERNEL_SOURCE = os.path.join(ROOT, "pipelined_tiled_dense_amd", "csrc", "gemm_bf16.hip")
+
+
+def kernel_sha():
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sync", default="all", choices=["all", "barrier", "flags", "wavespec"])
+    ap.add_argument("--stages", type=int, default=0)
+    ap.add_argument("--workload", default="gemm8192_nk")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a device-to-device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def time_mode(bd, dA, dB, C, w, sync, stages, steps, warmup, torch):
+    for _ in range(warmup):
+        bd.gemm(dA, dB, b_transposed=w.b_transposed, sync=sync, stages=stages, out=C)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        bd.gemm(dA, dB, b_transposed=w.b_transposed, sync=sync, stages=stages, out=C)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, per_launch_ms
+
+
+def cpu_baseline(w, A, B, target_s):
+    import numpy as np
+
+    import oracle
+    from pipelined_tiled_dense_amd.inputs import bits
+    o = oracle.load()
+    Ab, Bb = bits(A), bits(B)
+    threads = o.num_threads()
+    # calibrate on a few rows, then run a sample sized for ~target_s seconds
+    cal_rows = max(1, threads)
+    t0 = time.perf_counter()
+    o.gemm_bf16(np.ascontiguousarray(Ab[:cal_rows]), Bb, w.b_transposed)
+    t_cal = time.perf_counter() - t0
+    rows = int(max(cal_rows, min(w.M, cal_rows * target_s / max(t_cal, 1e-6))))
+    rows = max(threads, (rows // threads) * threads)
+    t0 = time.perf_counter()
+    o.gemm_bf16(np.ascontiguousarray(Ab[:rows]), Bb, w.b_transposed)
+    t = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "rows 0..%d of C (%d x %d x %d, %.3g GFLOP) in %.2f s; fp64 triple loop, "
+                      "one bf16 rounding" % (rows - 1, rows, w.N, w.K, flops / 1e9, t)}
+
+
+def traffic_per_launch():
+    try:
+        info = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if info.get("kernel_source_sha256") != kernel_sha():
+        return None
+    return info.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the GEMM has no multi-GPU path in this build "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from pipelined_tiled_dense_amd import binding as bd
+    from pipelined_tiled_dense_amd.inputs import WORKLOADS, workload_operands
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    bd.library()
+
+    if args.copy_calibration:
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes}))
+        return
+
+    w = WORKLOADS[args.workload]
+    A, B = workload_operands(w)
+    dA, dB = A.cuda(), B.cuda()
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    modes = ["barrier", "flags", "wavespec"] if args.sync == "all" else [args.sync]
+    flops = 2.0 * w.M * w.N * w.K
+    results = {}
+    for m in modes:
+        plan = bd.gemm_bf16_plan(w.M, w.N, w.K, w.b_transposed, args.stages, bd.SYNC_MODES[m])
+        wall, per = time_mode(bd, dA, dB, C, w, m, args.stages, args.steps, args.warmup, torch)
+        mean_ms = sum(per) / len(per)
+        results[m] = {"stages": plan["stages"], "tile": "%dx%dx%d" % (plan["bm"], plan["bn"], plan["bk"]),
+                      "grid": plan["grid"], "ms_per_step": wall * 1e3 / args.steps,
+                      "kernel_ms_mean": mean_ms, "kernel_ms_min": min(per),
+                      "tflops": flops / (wall / args.steps) / 1e12,
+                      "kernel_tflops": flops / (mean_ms * 1e-3) / 1e12}
+        print("# %s: %s" % (m, json.dumps(results[m])), file=sys.stderr, flush=True)
+    timeouts = bd.gemm_bf16_sync_timeouts()
+    best = max(results, key=lambda k: results[k]["tflops"])
+    r = results[best]
+    achieved = r["kernel_tflops"]
+    line = {
+        "metric": "bf16 GEMM TFLOP/s and % of MFMA peak at 1 GPU (8192^3, per sync mode)",
+        "value": round(r["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+                   "b_layout": "N x K (K contiguous)" if w.b_transposed else "K x N",
+                   "inputs": "seeded uniform[-1,1) rounded to bf16, seed %d" % w.seed,
+                   "sync_mode": best, "stages": r["stages"], "tile": r["tile"], "grid": r["grid"],
+                   "accumulate": "fp32", "output": "bf16 (RNE)"},
+        "pct_of_peak": round(100.0 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
+        "modes": {m: {"tflops": round(v["tflops"], 2), "pct_of_peak": round(100 * v["tflops"] / PEAK_BF16_TFLOPS, 2),
+                      "stages": v["stages"], "tile": v["tile"], "kernel_ms_mean": round(v["kernel_ms_mean"], 4)}
+                  for m, v in results.items()},
+        "sync_timeouts": timeouts,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_per_launch(),
+                     "kernel": "k_gemm (%s, %d stages)" % (best, r["stages"]) if best != "wavespec"
+                               else "k_gemm_ws (%d stages)" % r["stages"]},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

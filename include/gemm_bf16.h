@@ -1,0 +1,156 @@
+/*
+ * gemm_bf16.h -- C ABI of the MI355X (gfx950) pipelined, persistent bf16 GEMM.
+ *
+ * The operation is the matmul the reference pages build their pipelines
+ * around: C = A * B with bf16 operands, fp32 accumulation and the fp32
+ * results converted to bf16 in the epilogue ("Allow separate sub-DAG for load
+ * and compute warp groups with warp-specialized circular buffering", section
+ * "Pseudo-code").  Element by element:
+ *
+ *     C[i*ldc + j] = bf16_rne( sum_{k<K} A[i*lda + k] * B(k, j) )      (i<M, j<N)
+ *
+ * with B(k, j) = B[k*ldb + j] for gemm_bf16 (B stored K x N, row-major) and
+ * B(k, j) = B[j*ldb + k] for gemm_bf16_bt (B stored N x K, row-major).  The
+ * sum is accumulated in fp32 by the matrix cores; the order of the fp32
+ * additions is the library's, so results may differ from an exactly rounded
+ * product by the fp32 rounding of the partial sums (well under one bf16 ulp
+ * for K up to ~10^5 at unit-size inputs).  There is no alpha/beta: C is
+ * overwritten.
+ *
+ * How the work is done (none of this changes the result):
+ *   - a persistent grid walks the output tiles grid-stride ("Allow separate
+ *     sub-DAG ...", sections "Context" and "Scheduling Proposal");
+ *   - operand tiles stream through an S-stage LDS ring (circular buffer)
+ *     filled by direct global-to-LDS loads ("Use mbarrier for WAR for
+ *     circular buffering", both code listings);
+ *   - the ring is synchronised either by one workgroup barrier per k-step
+ *     (GEMM_SYNC_BARRIER, that page's first listing), or by separate per-stage
+ *     "loaded" (RAW) and "fully read" (WAR) counters (GEMM_SYNC_FLAGS, that
+ *     page's second listing), or by the same counters between dedicated
+ *     loader waves and MFMA waves (GEMM_SYNC_WAVESPEC, the producer/consumer
+ *     split of "Allow separate sub-DAG ...", section "Pseudo-code").
+ *
+ * Memory ownership: A, B and C are device pointers owned by the caller, on
+ * the HIP device that is current when the call is made.  The library never
+ * allocates, frees or retains them, and keeps no per-call allocation.  A and
+ * B are only read.  C must not overlap A or B.
+ *
+ * Asynchrony: a call validates its arguments on the host, enqueues its work
+ * on `stream` (a hipStream_t; NULL means the null stream) and returns.  A
+ * return of GEMM_OK means "enqueued"; faults during execution surface at the
+ * next synchronisation with the stream, as for any HIP kernel.
+ *
+ * Thread safety: calls may be made from several host threads.
+ */
+#ifndef GEMM_BF16_H
+#define GEMM_BF16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Ring synchronisation schemes. */
+enum {
+    GEMM_SYNC_BARRIER = 0,  /* one s_barrier per k-step covers RAW and WAR */
+    GEMM_SYNC_FLAGS = 1,    /* per-stage full/empty LDS counters, every wave loads and computes */
+    GEMM_SYNC_WAVESPEC = 2  /* per-stage counters between loader waves and MFMA waves */
+};
+
+/* Status codes.  Every entry point returns GEMM_OK (0) or one of these. */
+enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_VALUE = -1,     /* negative size, NULL pointer with a nonzero extent,
+                                        leading dimension too small, NULL output struct */
+    GEMM_ERR_MISALIGNED = -2,        /* a pointer not 16-byte aligned, or a leading
+                                        dimension not a multiple of 8 elements */
+    GEMM_ERR_UNSUPPORTED_SHAPE = -3, /* N or K not a multiple of 8, or a leading dimension
+                                        above 2^22 elements */
+    GEMM_ERR_STAGES = -4,            /* stages not 0 (default) or 2..4 */
+    GEMM_ERR_SYNC_MODE = -5,         /* sync_mode not one of GEMM_SYNC_* */
+    GEMM_ERR_DEVICE = -6,            /* no HIP device, or the current device is not gfx950 */
+    GEMM_ERR_LAUNCH = -7,            /* the kernel launch was rejected by the runtime */
+    GEMM_ERR_ALIAS = -8              /* C overlaps A or B */
+};
+
+/* The tiling and launch shape chosen for a problem (see gemm_bf16_plan). */
+typedef struct gemm_bf16_plan {
+    int32_t bm, bn, bk;       /* output tile BM x BN, k-step BK */
+    int32_t stages;           /* depth of the LDS ring */
+    int32_t sync_mode;        /* GEMM_SYNC_* */
+    int32_t b_transposed;     /* 1 for gemm_bf16_bt */
+    int32_t mfma_waves;       /* waves that run the matrix-core loop */
+    int32_t producer_waves;   /* dedicated loader waves (GEMM_SYNC_WAVESPEC), else 0 */
+    int32_t threads;          /* threads per workgroup */
+    int32_t lds_bytes;        /* LDS per workgroup */
+    int64_t tiles;            /* output tiles: ceil(M/bm) * ceil(N/bn) */
+    int64_t k_steps;          /* ceil(K/bk) */
+    int64_t grid;             /* persistent workgroups launched: min(tiles, compute units) */
+} gemm_bf16_plan_t;
+
+/*
+ * gemm_bf16: C[M,N] = A[M,K] * B[K,N]; A row-major (lda >= K), B row-major
+ * K x N (ldb >= N), C row-major (ldc >= N).  Sizes and leading dimensions are
+ * in elements.
+ *
+ * Requirements: M, N, K >= 0; N and K multiples of 8; lda, ldb, ldc
+ * multiples of 8 and at most 2^22; A, B, C 16-byte aligned (checked only for
+ * operands that are read or written).  M == 0 or N == 0 is a no-op.  K == 0
+ * writes +0 to every element of C.
+ *
+ * stages: 0 picks the default for the sync mode; otherwise 2, 3 or 4.
+ * sync_mode: GEMM_SYNC_BARRIER, GEMM_SYNC_FLAGS or GEMM_SYNC_WAVESPEC.
+ * stream: a hipStream_t (NULL for the null stream).
+ *
+ * Returns GEMM_OK once the work is enqueued, else a negative status; on a
+ * negative status nothing was enqueued.  Validation that does not need the
+ * device happens before any HIP call.
+ */
+int gemm_bf16(int64_t M, int64_t N, int64_t K,
+              const void* A, int64_t lda,
+              const void* B, int64_t ldb,
+              void* C, int64_t ldc,
+              int stages, int sync_mode, void* stream);
+
+/*
+ * gemm_bf16_bt: as gemm_bf16, but B is stored transposed: N x K row-major
+ * (ldb >= K), so that C[i][j] = sum_k A[i][k] * B[j*ldb + k].
+ */
+int gemm_bf16_bt(int64_t M, int64_t N, int64_t K,
+                 const void* A, int64_t lda,
+                 const void* B, int64_t ldb,
+                 void* C, int64_t ldc,
+                 int stages, int sync_mode, void* stream);
+
+/*
+ * gemm_bf16_plan: the plan gemm_bf16 (b_transposed == 0) or gemm_bf16_bt
+ * (b_transposed != 0) would use for this shape, stage count and sync mode.
+ * Writes *out and returns GEMM_OK, or returns a negative status (sizes,
+ * stages and sync mode are validated as in gemm_bf16; pointers and leading
+ * dimensions are not involved).  Queries the current device for its compute
+ * unit count.
+ */
+int gemm_bf16_plan(int64_t M, int64_t N, int64_t K, int b_transposed,
+                   int stages, int sync_mode, gemm_bf16_plan_t* out);
+
+/*
+ * gemm_bf16_strerror: a static, NUL-terminated description of a status code
+ * (never NULL; unknown codes give "unknown status").
+ */
+const char* gemm_bf16_strerror(int status);
+
+/*
+ * gemm_bf16_sync_timeouts: the number of bounded waits on ring counters that
+ * gave up since the library was loaded on the current device (a protocol
+ * failure: the kernel abandons the tile instead of hanging).  Zero in correct
+ * operation.  Synchronises the device.  If reset != 0 the counter is cleared
+ * after reading.  Returns the count (>= 0) or a negative status.
+ */
+int64_t gemm_bf16_sync_timeouts(int reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_BF16_H */

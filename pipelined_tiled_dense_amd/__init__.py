@@ -6,13 +6,12 @@ lazily so that ``inputs`` can be used without loading the HIP library.
 """
 from __future__ import annotations
 
-__all__ = ["binding", "inputs", "gemm", "GemmError"]
+import importlib
+
+__all__ = ["binding", "inputs", "gemm", "GemmError", "SYNC_MODES"]
 
 
 def __getattr__(name):
-    if name in ("gemm", "GemmError", "binding", "plan", "SYNC_MODES"):
-        from . import binding
-        if name == "binding":
-            return binding
-        return getattr(binding, name)
+    if name in ("gemm", "GemmError", "SYNC_MODES"):
+        return getattr(importlib.import_module(__name__ + ".binding"), name)
     raise AttributeError(name)

@@ -1,0 +1,1020 @@
+// Pipelined, persistent, tiled bf16 GEMM for MI355X (gfx950 / CDNA4).
+//
+//   C[M,N] = bf16_rne( A[M,K] * B )   with fp32 accumulation on the matrix cores,
+//   B stored K x N (gemm_bf16) or N x K (gemm_bf16_bt).
+//
+// The pages this follows describe the method for other hardware; what is kept
+// and how it maps onto gfx950:
+//
+// * Circular buffer ("Use mbarrier for WAR for circular buffering", both code
+//   listings).  Operand tiles stream through an S-stage ring in LDS.  A stage
+//   is filled by direct global-to-LDS loads (buffer_load_dwordx4 ... lds): each
+//   lane's 16 bytes land at a fixed slot of a 1 KiB LDS window, so the XOR
+//   swizzle that keeps the later fragment reads free of bank conflicts is
+//   applied on the global side (each lane fetches the chunk that belongs in its
+//   slot).  gfx950 has no bulk-copy engine or transaction-counting barrier:
+//   every loading wave issues its own share and learns that its data has
+//   landed from its vector-memory counter (s_waitcnt vmcnt).
+//
+// * Two ring synchronisation schemes.  GEMM_SYNC_BARRIER: one workgroup
+//   s_barrier per k-step, after each wave's own loads for the stage landed and
+//   its reads of the previous stage completed, covers both the read-after-write
+//   and the write-after-read hazard (the page's first listing, whose WAR guard
+//   is a block-wide barrier).  GEMM_SYNC_FLAGS: two monotonic counters per
+//   stage in LDS -- "full" (every loading wave's data for this use has landed)
+//   and "empty" (every reading wave has finished with it) -- the page's two
+//   signals per stage (the second listing).  The WAR wait is placed after the
+//   wave has issued its matrix-core work for the stage, so an MFMA never waits
+//   for a buffer it does not read (the page's motivation paragraph).
+//
+// * Wave specialisation ("Allow separate sub-DAG for load and compute warp
+//   groups with warp-specialized circular buffering", section "Pseudo-code").
+//   GEMM_SYNC_WAVESPEC runs loader waves over one flat stream of (tile, k-step)
+//   positions and MFMA waves over tile { k-step { ... } epilogue } loop nests,
+//   talking only through the full/empty counters.  The empty counters start at
+//   zero and are read as "free" for a stage's first use, which is what the
+//   consumer's initial arrive on every empty barrier achieves there.  gfx950
+//   cannot move registers between roles, so all waves get one register budget.
+//
+// * Persistent scheduling (same page, sections "Context" and "Scheduling
+//   Proposal").  A grid of min(tiles, CUs) workgroups walks the output tiles
+//   grid-stride; the load side sees the merged (tile, k-step) stream, so the
+//   ring keeps prefetching across tile boundaries while the compute side runs
+//   separate tile and k loops.  Tile ids are remapped so that the tiles the
+//   hardware places on one XCD at the same time are neighbours (shared L2).
+//
+// * Epilogue (same page, "Pseudo-code": convert fp32 to bf16, registers to
+//   shared memory, store).  Accumulators are converted with round-to-nearest-
+//   even, written to a wave-private LDS strip, read back as whole 128-byte row
+//   segments and stored with 16-byte buffer stores; being wave-private, the
+//   strip needs no block-wide sync.
+//
+// * Counter initialisation happens before any wave can arrive on a counter
+//   ("[Tutorial] Fix race condition in 2SM TMEM alloc ...", sections
+//   "Problem" and "Fix"): counters are zeroed, then one workgroup barrier,
+//   then the first arrive or poll.  Every counter wait is bounded; a wait that
+//   gives up is counted (gemm_bf16_sync_timeouts) and the wave leaves the
+//   kernel instead of hanging.
+//
+// Edges: buffer resources range-check every load and store.  Rows past M or
+// N, and the k tail of the last k-step, are read as zeros (the lane's offset is
+// pushed past the resource); stores past M or N are dropped the same way.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "gemm_bf16.h"
+
+namespace {
+
+#define LDS_AS __attribute__((address_space(3)))
+typedef LDS_AS char lds_char;
+typedef LDS_AS uint32_t lds_u32;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((ext_vector_type(8))) short i16x8_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+
+// A byte offset no resource covers: loads there return zeros, stores vanish.
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr uint32_t kMaxRecords = 0x7FFFFFF0u;
+// Raw buffer resource, 32-bit data format (third descriptor word for gfx9).
+constexpr int kRsrcWord3 = 0x00020000;
+// Bounded spin on ring counters: ~0.3 s at s_sleep(1) per poll.
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+__device__ unsigned long long g_sync_timeouts;
+
+// s_waitcnt immediates (gfx9 layout: vmcnt[3:0] + [15:14], expcnt[6:4],
+// lgkmcnt[11:8]); counters not named are left at their maximum.
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
+
+#define COMPILER_FENCE() asm volatile("" ::: "memory")
+
+// A value the optimiser must treat as unknown at this point.  Used inside
+// loops for per-lane address bases, so that the many addresses derived from
+// them are recomputed (a VALU op or two) instead of being hoisted out of the
+// tile loop and kept live next to 256 accumulator registers.
+__device__ __forceinline__ uint32_t opaque(uint32_t x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes)
+{
+    uint32_t n = bytes <= 0 ? 0u : (bytes > (int64_t)kMaxRecords ? kMaxRecords : (uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
+}
+
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)dst, 16, voff, 0, 0, 0);
+}
+
+enum { SYNC_BARRIER = GEMM_SYNC_BARRIER, SYNC_FLAGS = GEMM_SYNC_FLAGS, SYNC_WAVESPEC = GEMM_SYNC_WAVESPEC };
+
+// ---------------------------------------------------------------------------
+// Compile-time configuration of one kernel instance.
+// ---------------------------------------------------------------------------
+template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, int SYNC_, bool BT_, int NP_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_;
+    static constexpr int SYNC = SYNC_;
+    static constexpr bool BT = BT_;                 // B stored N x K
+    static constexpr int NCW = WM * WN;             // MFMA waves
+    static constexpr int NP = (SYNC == SYNC_WAVESPEC) ? NP_ : 0;   // dedicated loader waves
+    static constexpr int NLW = (SYNC == SYNC_WAVESPEC) ? NP : NCW; // waves that load
+    static constexpr int NW = NCW + NP;
+    static constexpr int THREADS = NW * 64;
+    static constexpr int TM = BM / WM, TN = BN / WN;                 // wave tile
+    static constexpr int FM = TM / 32, FN = TN / 32;                 // 32x32 MFMA blocks per wave
+    static constexpr int KK = BK / 16;                               // MFMA k-steps per stage
+    static constexpr int A_BYTES = BM * BK * 2;
+    static constexpr int B_BYTES = BN * BK * 2;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int A_LOADS = A_BYTES / 1024 / NLW;            // 1 KiB DMA instructions per loading wave
+    static constexpr int B_LOADS = B_BYTES / 1024 / NLW;
+    static constexpr int LOADS = A_LOADS + B_LOADS;
+    static constexpr int CPR_K = BK / 8;                             // 16-byte chunks per K-contiguous row
+    static constexpr int CPR_N = BN / 8;                             // chunks per row of a K x N B tile
+    static constexpr int RING_BYTES = S * STAGE_BYTES;
+    static constexpr int EPI_WAVE_BYTES = 32 * 64 * 2;               // 32 rows x 64 columns of bf16
+    static constexpr int EPI_OFFSET = RING_BYTES;
+    static constexpr int FLAG_OFFSET = EPI_OFFSET + NCW * EPI_WAVE_BYTES;
+    static constexpr int LDS_BYTES = FLAG_OFFSET + ((SYNC != SYNC_BARRIER) ? 2 * S * 4 : 0);
+
+    static_assert(BK == 32 || BK == 64, "BK");
+    static_assert(KK % 2 == 0, "fragment double buffering assumes an even number of MFMA k-steps");
+    static_assert(FM >= 1 && FN >= 2 && FN % 2 == 0, "wave tile");
+    static_assert(A_BYTES % (1024 * NLW) == 0 && B_BYTES % (1024 * NLW) == 0, "DMA split");
+    static_assert(64 % CPR_K == 0, "a DMA window covers whole K-contiguous rows");
+    static_assert(CPR_N == 16 || CPR_N == 32, "a DMA window covers whole K x N rows of B");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(S >= 2 && S <= 4, "stages");
+};
+
+struct Params {
+    const char* A;
+    const char* B;
+    char* C;
+    int64_t M, N, K, lda, ldb, ldc;   // elements
+    int32_t tiles_m, tiles_n, tiles, k_steps;
+    int32_t group_m;
+};
+
+// Swizzles.  K-contiguous tiles (A, and B stored N x K) hold rows of BK
+// elements; the 16-byte chunk index is XORed with a function of the row so
+// that the 8 lanes served together by one ds_read_b128 (8 consecutive rows,
+// one chunk) hit 8 different 16-byte bank groups.
+template <int BK>
+__device__ __forceinline__ int swz_k(int row)
+{
+    return BK == 64 ? (row & 7) : ((row >> 1) & 3);
+}
+// K x N tiles of B hold rows of BN elements; a transposing read touches 4
+// consecutive k-rows x 2 chunks per 16 lanes, spread by XOR with 2*(k mod 4).
+__device__ __forceinline__ int swz_n(int krow) { return (krow & 3) << 1; }
+
+// Output tile of the i-th tile id of this workgroup's grid-stride walk.
+__device__ __forceinline__ void tile_coords(const Params& p, int32_t t, int32_t G, int32_t& tm, int32_t& tn)
+{
+    int32_t L = t;
+    const int32_t round = t / G;
+    if ((G & 7) == 0 && (round + 1) * G <= p.tiles) {
+        // The hardware deals workgroups to the 8 XCDs round-robin; give XCD x
+        // a contiguous run of G/8 tile ids within each round.
+        const int32_t b = t - round * G;
+        L = round * G + (b & 7) * (G >> 3) + (b >> 3);
+    }
+    // Grouped raster: runs of group_m tile rows, walked column by column.
+    const int32_t per_group = p.group_m * p.tiles_n;
+    const int32_t grp = L / per_group;
+    const int32_t first_m = grp * p.group_m;
+    const int32_t gm = min(p.tiles_m - first_m, p.group_m);
+    const int32_t in = L - grp * per_group;
+    tm = first_m + in % gm;
+    tn = in / gm;
+}
+
+// Bounded wait until *ctr >= target.  Returns false (after counting the
+// timeout) if the counter does not get there.
+__device__ __forceinline__ bool wait_counter(lds_u32* ctr, uint32_t target)
+{
+    uint32_t spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+        if (++spins > kSpinLimit) {
+            if ((threadIdx.x & 63) == 0)
+                atomicAdd(&g_sync_timeouts, 1ull);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    COMPILER_FENCE();
+    return true;
+}
+
+__device__ __forceinline__ void arrive(lds_u32* ctr)
+{
+    COMPILER_FENCE();
+    if ((threadIdx.x & 63) == 0)
+        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    COMPILER_FENCE();
+}
+
+__device__ __forceinline__ void block_barrier()
+{
+    COMPILER_FENCE();
+    __builtin_amdgcn_s_barrier();
+    COMPILER_FENCE();
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    COMPILER_FENCE();
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(N));
+    COMPILER_FENCE();
+}
+
+__device__ __forceinline__ void wait_lgkm0()
+{
+    COMPILER_FENCE();
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    COMPILER_FENCE();
+}
+
+// ---------------------------------------------------------------------------
+// Load side: one loading wave's share of the (tile, k-step) stream.
+//
+// Slot s of an operand's stage region (16 bytes; s = (t*NLW + lw)*64 + lane
+// for the wave's t-th 1 KiB DMA instruction) holds row s / CPR and physical
+// chunk s % CPR; the lane fetches the logical chunk that the swizzle places
+// there.  These per-lane byte offsets do not depend on the tile, so they are
+// computed once.  Per position only the buffer resources move (scalar work):
+// their base is the tile origin at k0 and their byte count ends at the last
+// element of the operand, so rows past M (A), past N (B stored N x K) and
+// k-rows past K (B stored K x N) read as zeros by themselves.  The two edges
+// a byte count cannot express -- the k tail inside a row, and columns past N
+// of a K x N B tile -- are masked per lane in a uniform branch.
+// ---------------------------------------------------------------------------
+template <class C>
+struct Loader {
+    int32_t n_tiles, it, kt;      // position in this workgroup's stream
+    int32_t m0, n0;               // current load tile origin
+    uint32_t voffA[C::A_LOADS];
+    uint32_t voffB[C::B_LOADS];
+
+    __device__ __forceinline__ static int slot(int t, int lw, int lane) { return (t * C::NLW + lw) * 64 + lane; }
+    // Logical k offset (elements) of a K-contiguous slot.
+    __device__ __forceinline__ static int kofs_k(int s)
+    {
+        const int row = s / C::CPR_K;
+        return ((s % C::CPR_K) ^ swz_k<C::BK>(row)) * 8;
+    }
+    // Logical column offset (elements) of a slot in a K x N tile of B.
+    __device__ __forceinline__ static int nofs_n(int s)
+    {
+        const int row = s / C::CPR_N;
+        return ((s % C::CPR_N) ^ swz_n(row)) * 8;
+    }
+
+    __device__ __forceinline__ void init(const Params& p, int32_t ntiles, int lw, int lane)
+    {
+        const uint32_t lda2 = (uint32_t)p.lda * 2u, ldb2 = (uint32_t)p.ldb * 2u;
+#pragma unroll
+        for (int t = 0; t < C::A_LOADS; ++t) {
+            const int s = slot(t, lw, lane);
+            voffA[t] = (uint32_t)(s / C::CPR_K) * lda2 + (uint32_t)kofs_k(s) * 2u;
+        }
+#pragma unroll
+        for (int t = 0; t < C::B_LOADS; ++t) {
+            const int s = slot(t, lw, lane);
+            if constexpr (C::BT)
+                voffB[t] = (uint32_t)(s / C::CPR_K) * ldb2 + (uint32_t)kofs_k(s) * 2u;
+            else
+                voffB[t] = (uint32_t)(s / C::CPR_N) * ldb2 + (uint32_t)nofs_n(s) * 2u;
+        }
+        n_tiles = ntiles;
+        it = 0;
+        kt = 0;
+        set_tile(p);
+    }
+
+    __device__ __forceinline__ void set_tile(const Params& p)
+    {
+        int32_t tm = 0, tn = 0;
+        if (it < n_tiles)
+            tile_coords(p, (int32_t)blockIdx.x + it * (int32_t)gridDim.x, (int32_t)gridDim.x, tm, tn);
+        m0 = tm * C::BM;
+        n0 = tn * C::BN;
+    }
+
+    // Issue this wave's DMA for the current position into `stage`, then step.
+    __device__ __forceinline__ void issue_and_advance(const Params& p, lds_char* stage, int lw, int lane)
+    {
+        const int64_t k0 = (int64_t)kt * C::BK;
+        const int32_t krem = (int32_t)(p.K - k0);        // > 0
+        const __amdgpu_buffer_rsrc_t ra =
+            make_rsrc(p.A + ((int64_t)m0 * p.lda + k0) * 2, ((p.M - m0 - 1) * p.lda + krem) * 2);
+        __amdgpu_buffer_rsrc_t rb;
+        if constexpr (C::BT)
+            rb = make_rsrc(p.B + ((int64_t)n0 * p.ldb + k0) * 2, ((p.N - n0 - 1) * p.ldb + krem) * 2);
+        else
+            rb = make_rsrc(p.B + (k0 * p.ldb + n0) * 2, ((int64_t)(krem - 1) * p.ldb + (p.N - n0)) * 2);
+        const bool k_tail = krem < C::BK;
+        const bool n_edge = !C::BT && (p.N - n0 < C::BN);
+        if (!k_tail && !n_edge) {
+#pragma unroll
+            for (int t = 0; t < C::A_LOADS; ++t)
+                lds_dma16(ra, stage + (t * C::NLW + lw) * 1024, voffA[t]);
+#pragma unroll
+            for (int t = 0; t < C::B_LOADS; ++t)
+                lds_dma16(rb, stage + C::A_BYTES + (t * C::NLW + lw) * 1024, voffB[t]);
+        } else {
+            lane = (int)opaque((uint32_t)lane);
+            const int32_t nrem = (int32_t)(p.N - n0);
+#pragma unroll
+            for (int t = 0; t < C::A_LOADS; ++t) {
+                const bool ok = kofs_k(slot(t, lw, lane)) < krem;
+                lds_dma16(ra, stage + (t * C::NLW + lw) * 1024, ok ? voffA[t] : kOOB);
+            }
+#pragma unroll
+            for (int t = 0; t < C::B_LOADS; ++t) {
+                const int s = slot(t, lw, lane);
+                const bool ok = C::BT ? (kofs_k(s) < krem) : (nofs_n(s) < nrem);
+                lds_dma16(rb, stage + C::A_BYTES + (t * C::NLW + lw) * 1024, ok ? voffB[t] : kOOB);
+            }
+        }
+        if (++kt == p.k_steps) {
+            kt = 0;
+            ++it;
+            set_tile(p);
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Compute side: fragment reads and the MFMA chain of one MFMA wave.
+// ---------------------------------------------------------------------------
+template <class C>
+struct Frags {
+    bf16x8_t a[C::FM];
+    bf16x8_t b[C::FN];
+};
+
+// Fragments of MFMA k-step kk from a stage.  The MFMA runs with the B
+// fragment as its first operand, so accumulator block (i, j) holds
+// C^T: lane l owns column m = l%32 and rows n = 8*(r/4) + 4*(l/32) + r%4.
+//
+// K-contiguous tiles: lane l reads row (base + 32*i + l%32), logical chunk
+// 2*kk + l/32.  Every block starts on a multiple of 8 rows, so the swizzle
+// term depends on l only and the block index moves the address by a
+// constant.
+template <class C>
+__device__ __forceinline__ void read_frags(Frags<C>& f, const lds_char* stage, int wm, int wn, int lane, int kk)
+{
+    const int h = lane >> 5;
+    const int r32 = lane & 31;
+    const uint32_t xk = (uint32_t)(((2 * kk + h) ^ swz_k<C::BK>(r32)) << 4);
+    const uint32_t rowa = opaque((uint32_t)((wm * C::TM + r32) * (C::BK * 2)) + xk);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+        f.a[i] = *(const LDS_AS bf16x8_t*)(stage + rowa + i * (32 * C::BK * 2));
+    const lds_char* sb = stage + C::A_BYTES;
+    if constexpr (C::BT) {
+        const uint32_t rowb = opaque((uint32_t)((wn * C::TN + r32) * (C::BK * 2)) + xk);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+            f.b[j] = *(const LDS_AS bf16x8_t*)(sb + rowb + j * (32 * C::BK * 2));
+    } else {
+        // ds_read_b64_tr_b16: within each 16-lane group, lane 4r+q addresses
+        // k-row r, columns 4q..4q+3 of a 4 x 16 block; lane i receives column
+        // i for the 4 k-rows.  Two reads give the 8 k values of the operand.
+        // The k-row of lane (r, q) is 16*kk + 8*(l/32) + 4*hh + r, so its
+        // swizzle term is 2*r; the logical chunk of block j is
+        // 4*(wn*TN/32 + j) + 2*((l>>4)&1) + q/2, and XOR with 2*r splits into
+        // bit 2 (flips with r/2, i.e. +-4 chunks by the parity of j) and
+        // bits 0-1.
+        const int g = lane >> 4, i16 = lane & 15, r = i16 >> 2, q = i16 & 3;
+        const int low = (2 * (g & 1) + (q >> 1)) ^ (2 * (r & 1));
+        const uint32_t krow0 = (uint32_t)(16 * kk + 8 * (g >> 1) + r);
+        const uint32_t base = opaque(krow0 * (C::BN * 2) + (uint32_t)(low * 16 + (q & 1) * 8));
+        const int rh = r >> 1;
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            const int J = wn * (C::TN / 32) + j;
+            const int jchunk = 4 * (J ^ rh);
+            i16x4_t part[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const lds_char* addr = sb + base + (uint32_t)(4 * hh * (C::BN * 2)) + (uint32_t)(jchunk * 16);
+                part[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)addr);
+            }
+            const i16x8_t v = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+            f.b[j] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void mfma_step(f32x16_t (&acc)[C::FM][C::FN], const Frags<C>& f)
+{
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    const __bf16 l = (__bf16)lo, h = (__bf16)hi;
+    uint16_t ul, uh;
+    __builtin_memcpy(&ul, &l, 2);
+    __builtin_memcpy(&uh, &h, 2);
+    return (uint32_t)ul | ((uint32_t)uh << 16);
+}
+
+// fp32 accumulators -> bf16 (RNE) -> wave-private LDS strip -> 16-byte stores.
+// The strip is 32 rows (m) x 64 columns (n) with 128-byte rows whose 16-byte
+// chunks are XORed with (row % 8).  Writes: lane l holds row l%32 and, per
+// 4 accumulator registers, 4 consecutive columns (8 bytes).  Reads: 8 lanes
+// cover one 128-byte row segment of C, so each store instruction writes 8
+// full row segments.
+template <class C>
+__device__ __forceinline__ void epilogue(const Params& p, f32x16_t (&acc)[C::FM][C::FN], lds_char* strip,
+                                         int32_t m0, int32_t n0, int wm, int wn, int lane_in)
+{
+    const int lane = (int)opaque((uint32_t)lane_in);
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(p.C + ((int64_t)m0 * p.ldc + n0) * 2, ((p.M - m0 - 1) * p.ldc + (p.N - n0)) * 2);
+    const int row_w = lane & 31, half = lane >> 5;
+    const int32_t mrem = (int32_t)min(p.M - m0, (int64_t)C::BM);
+    const int32_t nrem = (int32_t)min(p.N - n0, (int64_t)C::BN);
+    const uint32_t ldc2 = (uint32_t)p.ldc * 2u;
+    const uint32_t wbase = opaque((uint32_t)(row_w * 128 + half * 8));
+    const int rrow = lane >> 3, rc8 = lane & 7;          // read slot u adds 8*u rows
+    const uint32_t rbase = opaque((uint32_t)(rrow * 128 + ((rc8 ^ (rrow & 7)) * 16)));
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+        for (int jp = 0; jp < C::FN / 2; ++jp) {
+            // Keep each pass's conversions next to its own stores.
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x16_t& a = acc[i][2 * jp + jj];
+                    u32x2_t v;
+                    v.x = pack_bf16x2(a[4 * g + 0], a[4 * g + 1]);
+                    v.y = pack_bf16x2(a[4 * g + 2], a[4 * g + 3]);
+                    const uint32_t chunk = (uint32_t)(((4 * jj + g) ^ (row_w & 7)) * 16);
+                    *(LDS_AS u32x2_t*)(strip + wbase + chunk - 0u) = v;
+                }
+            }
+            wait_lgkm0();
+            const int gr0 = wm * C::TM + 32 * i + rrow;            // tile row of read slot 0
+            const int gc = wn * C::TN + 64 * jp + 8 * rc8;         // tile column of this lane's chunk
+            const uint32_t obase = opaque((uint32_t)gr0 * ldc2 + (uint32_t)gc * 2u);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                // rows rrow + 8u keep (row % 8) == (rrow % 8), so the swizzle is unchanged
+                const u32x4_t v = *(const LDS_AS u32x4_t*)(strip + rbase + u * 8 * 128);
+                const bool ok = (gr0 + 8 * u < mrem) && (gc < nrem);
+                __builtin_amdgcn_raw_buffer_store_b128(v, rc, ok ? obase + (uint32_t)(8 * u) * ldc2 : kOOB, 0, 0);
+            }
+            wait_lgkm0();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel: every wave loads and computes (GEMM_SYNC_BARRIER, GEMM_SYNC_FLAGS).
+// ---------------------------------------------------------------------------
+template <class C>
+__global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
+{
+    static_assert(C::SYNC != SYNC_WAVESPEC, "wave-specialised configs use k_gemm_ws");
+    __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS_BYTES];
+    lds_char* smem = (lds_char*)smem_raw;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = w / C::WN, wn = w % C::WN;
+    lds_u32* full = (lds_u32*)(smem + C::FLAG_OFFSET);
+    lds_u32* empty = full + C::S;
+
+    if constexpr (C::SYNC == SYNC_FLAGS) {
+        if (threadIdx.x < 2 * C::S)
+            full[threadIdx.x] = 0u;
+    }
+    __syncthreads();   // counters are initialised before any wave can arrive
+
+    const int32_t G = gridDim.x, b = blockIdx.x;
+    const int32_t n_tiles = (b < p.tiles) ? (p.tiles - 1 - b) / G + 1 : 0;
+    const int32_t KT = p.k_steps;
+    const int32_t total = n_tiles * KT;
+
+    Loader<C> ld;
+    ld.init(p, n_tiles, w, lane);
+#pragma unroll
+    for (int q = 0; q < C::S - 1; ++q)
+        if (q < total)
+            ld.issue_and_advance(p, smem + q * C::STAGE_BYTES, w, lane);
+
+    Frags<C> fr[2];
+    lds_char* strip = smem + C::EPI_OFFSET + w * C::EPI_WAVE_BYTES;
+
+    // Make position c readable: RAW for every wave (and WAR for the stage the
+    // next load reuses, in BARRIER mode).  This wave's loads for positions
+    // c .. c+S-2 are outstanding (S-1 groups of LOADS), possibly followed by
+    // younger epilogue stores or spill traffic.  Waiting until at most
+    // LOADS*(S-2) vector-memory operations are outstanding leaves at most that
+    // many loads outstanding; loads complete in order, so group c has landed
+    // however the younger operations complete.  Near the end of the stream
+    // fewer groups are in flight and the wait drains everything.
+    auto sync_position = [&](int32_t c) -> bool {
+        if (c + C::S - 2 < total)
+            wait_vmcnt<C::LOADS * (C::S - 2)>();
+        else
+            wait_vmcnt<0>();
+        if constexpr (C::SYNC == SYNC_BARRIER) {
+            block_barrier();
+        } else {
+            const int s = c % C::S;
+            arrive(full + s);
+            if (!wait_counter(full + s, (uint32_t)(c / C::S + 1) * C::NW))
+                return false;
+        }
+        return true;
+    };
+    // Issue the load of position q = c + S - 1 (into the stage position c-1 used).
+    auto issue_next = [&](int32_t c) -> bool {
+        const int32_t q = c + C::S - 1;
+        if (q >= total)
+            return true;
+        const int s = q % C::S;
+        if constexpr (C::SYNC == SYNC_FLAGS) {
+            if (q >= C::S && !wait_counter(empty + s, (uint32_t)(q / C::S) * C::NW))
+                return false;
+        }
+        ld.issue_and_advance(p, smem + s * C::STAGE_BYTES, w, lane);
+        return true;
+    };
+
+    if (total == 0)
+        return;
+    if (!sync_position(0))
+        return;
+    if constexpr (C::SYNC == SYNC_BARRIER)
+        issue_next(0);
+    read_frags<C>(fr[0], smem, wm, wn, lane, 0);
+    if constexpr (C::SYNC == SYNC_FLAGS) {
+        if (!issue_next(0))
+            return;
+    }
+
+    int32_t c = 0;
+    for (int32_t it = 0; it < n_tiles; ++it) {
+        int32_t tm, tn;
+        tile_coords(p, b + it * G, G, tm, tn);
+        f32x16_t acc[C::FM][C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                acc[i][j] = f32x16_t{};
+
+        for (int32_t kt = 0; kt < KT; ++kt, ++c) {
+            const lds_char* stage = smem + (c % C::S) * C::STAGE_BYTES;
+            const bool more = c + 1 < total;
+#pragma unroll
+            for (int kk = 0; kk < C::KK; ++kk) {
+                if (kk + 1 < C::KK) {
+                    read_frags<C>(fr[(kk + 1) & 1], stage, wm, wn, lane, kk + 1);
+                } else if (more) {
+                    // Last MFMA k-step of this stage: hand the stage back and
+                    // make the next position readable, then read its first
+                    // fragments, so the MFMA pipe has work across the sync.
+                    wait_lgkm0();
+                    if constexpr (C::SYNC == SYNC_FLAGS)
+                        arrive(empty + c % C::S);
+                    if (!sync_position(c + 1))
+                        return;
+                    if constexpr (C::SYNC == SYNC_BARRIER)
+                        issue_next(c + 1);
+                    read_frags<C>(fr[0], smem + ((c + 1) % C::S) * C::STAGE_BYTES, wm, wn, lane, 0);
+                }
+                mfma_step<C>(acc, fr[kk & 1]);
+            }
+            if constexpr (C::SYNC == SYNC_FLAGS) {
+                // WAR wait for the stage the next load reuses, placed after
+                // this wave's MFMAs for the stage are issued.
+                if (more && !issue_next(c + 1))
+                    return;
+            }
+        }
+        epilogue<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel: dedicated loader waves and MFMA waves (GEMM_SYNC_WAVESPEC).
+// ---------------------------------------------------------------------------
+template <class C>
+__global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
+{
+    static_assert(C::SYNC == SYNC_WAVESPEC, "k_gemm_ws");
+    __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS_BYTES];
+    lds_char* smem = (lds_char*)smem_raw;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    lds_u32* full = (lds_u32*)(smem + C::FLAG_OFFSET);
+    lds_u32* empty = full + C::S;
+    if (threadIdx.x < 2 * C::S)
+        full[threadIdx.x] = 0u;
+    __syncthreads();   // counters are initialised before the roles split
+
+    const int32_t G = gridDim.x, b = blockIdx.x;
+    const int32_t n_tiles = (b < p.tiles) ? (p.tiles - 1 - b) / G + 1 : 0;
+    const int32_t KT = p.k_steps;
+    const int32_t total = n_tiles * KT;
+
+    if (w >= C::NCW) {
+        // Loader wave: one flat loop over (tile, k-step) positions.  The data
+        // of position q is announced on full[] once it has landed, D positions
+        // later (the wave keeps D + 1 positions of loads in flight).
+        const int lw = w - C::NCW;
+        constexpr int D = (C::S - 1 < 2) ? C::S - 1 : 2;
+        Loader<C> ld;
+        ld.init(p, n_tiles, lw, lane);
+        for (int32_t q = 0; q < total; ++q) {
+            const int s = q % C::S;
+            if (q >= C::S && !wait_counter(empty + s, (uint32_t)(q / C::S) * C::NCW))
+                return;
+            ld.issue_and_advance(p, smem + s * C::STAGE_BYTES, lw, lane);
+            if (q >= D) {
+                wait_vmcnt<C::LOADS * D>();
+                arrive(full + (q - D) % C::S);
+            }
+        }
+        wait_vmcnt<0>();
+        for (int32_t q = (total > D ? total - D : 0); q < total; ++q)
+            arrive(full + q % C::S);
+        return;
+    }
+
+    // MFMA wave: tile { k-step { wait full; read; release; MFMA } epilogue }.
+    const int wm = w / C::WN, wn = w % C::WN;
+    lds_char* strip = smem + C::EPI_OFFSET + w * C::EPI_WAVE_BYTES;
+    Frags<C> fr[2];
+    if (total == 0)
+        return;
+    if (!wait_counter(full, (uint32_t)C::NP))
+        return;
+    read_frags<C>(fr[0], smem, wm, wn, lane, 0);
+
+    int32_t c = 0;
+    for (int32_t it = 0; it < n_tiles; ++it) {
+        int32_t tm, tn;
+        tile_coords(p, b + it * G, G, tm, tn);
+        f32x16_t acc[C::FM][C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                acc[i][j] = f32x16_t{};
+        for (int32_t kt = 0; kt < KT; ++kt, ++c) {
+            const lds_char* stage = smem + (c % C::S) * C::STAGE_BYTES;
+#pragma unroll
+            for (int kk = 0; kk < C::KK; ++kk) {
+                if (kk + 1 < C::KK) {
+                    read_frags<C>(fr[(kk + 1) & 1], stage, wm, wn, lane, kk + 1);
+                } else {
+                    wait_lgkm0();
+                    arrive(empty + c % C::S);
+                    if (c + 1 < total) {
+                        const int s1 = (c + 1) % C::S;
+                        if (!wait_counter(full + s1, (uint32_t)((c + 1) / C::S + 1) * C::NP))
+                            return;
+                        read_frags<C>(fr[0], smem + s1 * C::STAGE_BYTES, wm, wn, lane, 0);
+                    }
+                }
+                mfma_step<C>(acc, fr[kk & 1]);
+            }
+        }
+        epilogue<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
+    }
+}
+
+// C = 0 for K == 0 (16-byte stores, range-checked like the epilogue).
+__global__ void __launch_bounds__(256) k_zero_fill(char* C, int64_t M, int64_t N, int64_t ldc)
+{
+    const int64_t chunks_per_row = N / 8;
+    const int64_t total = M * chunks_per_row;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = q / chunks_per_row, cch = q - r * chunks_per_row;
+        *(u32x4_t*)(C + (r * ldc + cch * 8) * 2) = u32x4_t{0u, 0u, 0u, 0u};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+using CfgB2N = Cfg<256, 256, 64, 2, 2, 2, SYNC_BARRIER, false, 0>;
+
+struct Variant {
+    int bm, bn, bk, waves_m, waves_n, producers;
+};
+
+Variant variant_for(int sync_mode, int stages)
+{
+    if (sync_mode == GEMM_SYNC_WAVESPEC)
+        return Variant{256, 128, stages == 2 ? 64 : 32, 2, 2, 4};
+    return Variant{256, 256, stages == 2 ? 64 : 32, 2, 2, 0};
+}
+
+int default_stages(int sync_mode)
+{
+    return sync_mode == GEMM_SYNC_WAVESPEC ? 4 : 2;
+}
+
+template <class C>
+int lds_bytes_of() { return C::LDS_BYTES; }
+
+struct DeviceInfo {
+    bool probed = false;
+    int status = GEMM_OK;
+    int cus = 0;
+};
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mutex;
+DeviceInfo g_dev[kMaxDevices];
+
+int device_info(int* cus)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return GEMM_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    DeviceInfo& d = g_dev[dev];
+    if (!d.probed) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            d.status = GEMM_ERR_DEVICE;
+        } else {
+            d.status = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? GEMM_OK : GEMM_ERR_DEVICE;
+            d.cus = prop.multiProcessorCount;
+        }
+        d.probed = true;
+    }
+    *cus = d.cus;
+    return d.status;
+}
+
+bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes)
+{
+    if (a_bytes <= 0 || b_bytes <= 0)
+        return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)b_bytes && b0 < a0 + (uintptr_t)a_bytes;
+}
+
+int64_t span_bytes(int64_t rows, int64_t cols, int64_t ld)
+{
+    return (rows <= 0 || cols <= 0) ? 0 : ((rows - 1) * ld + cols) * 2;
+}
+
+constexpr int64_t kMaxLd = (int64_t)1 << 22;
+
+int validate_shape(int64_t M, int64_t N, int64_t K, int stages, int sync_mode)
+{
+    if (sync_mode != GEMM_SYNC_BARRIER && sync_mode != GEMM_SYNC_FLAGS && sync_mode != GEMM_SYNC_WAVESPEC)
+        return GEMM_ERR_SYNC_MODE;
+    if (stages != 0 && (stages < 2 || stages > 4))
+        return GEMM_ERR_STAGES;
+    if (M < 0 || N < 0 || K < 0)
+        return GEMM_ERR_INVALID_VALUE;
+    if (N % 8 != 0 || K % 8 != 0)
+        return GEMM_ERR_UNSUPPORTED_SHAPE;
+    if (M > ((int64_t)1 << 31) - 1 || N > ((int64_t)1 << 31) - 1 || K > ((int64_t)1 << 31) - 1)
+        return GEMM_ERR_UNSUPPORTED_SHAPE;
+    return GEMM_OK;
+}
+
+int fill_plan(int64_t M, int64_t N, int64_t K, int b_transposed, int stages, int sync_mode, int cus,
+              gemm_bf16_plan_t* out);
+
+template <class C>
+int launch(const Params& p, int64_t grid, hipStream_t stream)
+{
+    if constexpr (C::SYNC == SYNC_WAVESPEC)
+        hipLaunchKernelGGL(k_gemm_ws<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+    else
+        hipLaunchKernelGGL(k_gemm<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+template <bool BT>
+int dispatch(const Params& p, int64_t grid, int stages, int sync_mode, hipStream_t stream)
+{
+    switch (sync_mode) {
+    case GEMM_SYNC_BARRIER:
+        if (stages == 2) return launch<Cfg<256, 256, 64, 2, 2, 2, SYNC_BARRIER, BT, 0>>(p, grid, stream);
+        if (stages == 3) return launch<Cfg<256, 256, 32, 3, 2, 2, SYNC_BARRIER, BT, 0>>(p, grid, stream);
+        return launch<Cfg<256, 256, 32, 4, 2, 2, SYNC_BARRIER, BT, 0>>(p, grid, stream);
+    case GEMM_SYNC_FLAGS:
+        if (stages == 2) return launch<Cfg<256, 256, 64, 2, 2, 2, SYNC_FLAGS, BT, 0>>(p, grid, stream);
+        if (stages == 3) return launch<Cfg<256, 256, 32, 3, 2, 2, SYNC_FLAGS, BT, 0>>(p, grid, stream);
+        return launch<Cfg<256, 256, 32, 4, 2, 2, SYNC_FLAGS, BT, 0>>(p, grid, stream);
+    default:
+        if (stages == 2) return launch<Cfg<256, 128, 64, 2, 2, 2, SYNC_WAVESPEC, BT, 4>>(p, grid, stream);
+        if (stages == 3) return launch<Cfg<256, 128, 32, 3, 2, 2, SYNC_WAVESPEC, BT, 4>>(p, grid, stream);
+        return launch<Cfg<256, 128, 32, 4, 2, 2, SYNC_WAVESPEC, BT, 4>>(p, grid, stream);
+    }
+}
+
+template <bool BT>
+int lds_of(int stages, int sync_mode)
+{
+    switch (sync_mode) {
+    case GEMM_SYNC_BARRIER:
+        if (stages == 2) return Cfg<256, 256, 64, 2, 2, 2, SYNC_BARRIER, BT, 0>::LDS_BYTES;
+        if (stages == 3) return Cfg<256, 256, 32, 3, 2, 2, SYNC_BARRIER, BT, 0>::LDS_BYTES;
+        return Cfg<256, 256, 32, 4, 2, 2, SYNC_BARRIER, BT, 0>::LDS_BYTES;
+    case GEMM_SYNC_FLAGS:
+        if (stages == 2) return Cfg<256, 256, 64, 2, 2, 2, SYNC_FLAGS, BT, 0>::LDS_BYTES;
+        if (stages == 3) return Cfg<256, 256, 32, 3, 2, 2, SYNC_FLAGS, BT, 0>::LDS_BYTES;
+        return Cfg<256, 256, 32, 4, 2, 2, SYNC_FLAGS, BT, 0>::LDS_BYTES;
+    default:
+        if (stages == 2) return Cfg<256, 128, 64, 2, 2, 2, SYNC_WAVESPEC, BT, 4>::LDS_BYTES;
+        if (stages == 3) return Cfg<256, 128, 32, 3, 2, 2, SYNC_WAVESPEC, BT, 4>::LDS_BYTES;
+        return Cfg<256, 128, 32, 4, 2, 2, SYNC_WAVESPEC, BT, 4>::LDS_BYTES;
+    }
+}
+
+int fill_plan(int64_t M, int64_t N, int64_t K, int b_transposed, int stages, int sync_mode, int cus,
+              gemm_bf16_plan_t* out)
+{
+    const int st = stages == 0 ? default_stages(sync_mode) : stages;
+    const Variant v = variant_for(sync_mode, st);
+    gemm_bf16_plan_t pl;
+    memset(&pl, 0, sizeof pl);
+    pl.bm = v.bm;
+    pl.bn = v.bn;
+    pl.bk = v.bk;
+    pl.stages = st;
+    pl.sync_mode = sync_mode;
+    pl.b_transposed = b_transposed ? 1 : 0;
+    pl.mfma_waves = v.waves_m * v.waves_n;
+    pl.producer_waves = v.producers;
+    pl.threads = 64 * (pl.mfma_waves + pl.producer_waves);
+    pl.lds_bytes = b_transposed ? lds_of<true>(st, sync_mode) : lds_of<false>(st, sync_mode);
+    const int64_t tm = (M + v.bm - 1) / v.bm, tn = (N + v.bn - 1) / v.bn;
+    pl.tiles = tm * tn;
+    pl.k_steps = (K + v.bk - 1) / v.bk;
+    pl.grid = pl.tiles < cus ? pl.tiles : cus;
+    if (pl.tiles > ((int64_t)1 << 30) || pl.tiles * pl.k_steps > ((int64_t)1 << 30))
+        return GEMM_ERR_UNSUPPORTED_SHAPE;
+    *out = pl;
+    return GEMM_OK;
+}
+
+int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                void* C, int64_t ldc, int stages, int sync_mode, void* stream, bool bt)
+{
+    int rc = validate_shape(M, N, K, stages, sync_mode);
+    if (rc != GEMM_OK)
+        return rc;
+    if (M == 0 || N == 0)
+        return GEMM_OK;
+    const bool reads = K > 0;
+    if (!C || (reads && (!A || !B)))
+        return GEMM_ERR_INVALID_VALUE;
+    if (ldc < N || (reads && (lda < K || ldb < (bt ? K : N))))
+        return GEMM_ERR_INVALID_VALUE;
+    if (ldc % 8 != 0 || ((uintptr_t)C & 15) != 0)
+        return GEMM_ERR_MISALIGNED;
+    if (reads && (lda % 8 != 0 || ldb % 8 != 0 || ((uintptr_t)A & 15) != 0 || ((uintptr_t)B & 15) != 0))
+        return GEMM_ERR_MISALIGNED;
+    if (ldc > kMaxLd || (reads && (lda > kMaxLd || ldb > kMaxLd)))
+        return GEMM_ERR_UNSUPPORTED_SHAPE;
+    const int64_t c_bytes = span_bytes(M, N, ldc);
+    if (reads && (overlaps(C, c_bytes, A, span_bytes(M, K, lda)) ||
+                  overlaps(C, c_bytes, B, bt ? span_bytes(N, K, ldb) : span_bytes(K, N, ldb))))
+        return GEMM_ERR_ALIAS;
+
+    int cus = 0;
+    rc = device_info(&cus);
+    if (rc != GEMM_OK)
+        return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if (!reads) {
+        const int64_t chunks = M * (N / 8);
+        int64_t blocks = (chunks + 255) / 256;
+        if (blocks > 65536)
+            blocks = 65536;
+        hipLaunchKernelGGL(k_zero_fill, dim3((unsigned)blocks), dim3(256), 0, s, (char*)C, M, N, ldc);
+        return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+    }
+    gemm_bf16_plan_t pl;
+    rc = fill_plan(M, N, K, bt, stages, sync_mode, cus, &pl);
+    if (rc != GEMM_OK)
+        return rc;
+    Params p;
+    p.A = (const char*)A;
+    p.B = (const char*)B;
+    p.C = (char*)C;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.tiles_m = (int32_t)((M + pl.bm - 1) / pl.bm);
+    p.tiles_n = (int32_t)((N + pl.bn - 1) / pl.bn);
+    p.tiles = (int32_t)pl.tiles;
+    p.k_steps = (int32_t)pl.k_steps;
+    p.group_m = 4;
+    return bt ? dispatch<true>(p, pl.grid, pl.stages, sync_mode, s)
+              : dispatch<false>(p, pl.grid, pl.stages, sync_mode, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+              void* C, int64_t ldc, int stages, int sync_mode, void* stream)
+{
+    return gemm_common(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, stream, false);
+}
+
+int gemm_bf16_bt(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                 void* C, int64_t ldc, int stages, int sync_mode, void* stream)
+{
+    return gemm_common(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, stream, true);
+}
+
+int gemm_bf16_plan(int64_t M, int64_t N, int64_t K, int b_transposed, int stages, int sync_mode,
+                   gemm_bf16_plan_t* out)
+{
+    if (!out)
+        return GEMM_ERR_INVALID_VALUE;
+    int rc = validate_shape(M, N, K, stages, sync_mode);
+    if (rc != GEMM_OK)
+        return rc;
+    int cus = 0;
+    rc = device_info(&cus);
+    if (rc != GEMM_OK)
+        return rc;
+    return fill_plan(M, N, K, b_transposed, stages, sync_mode, cus, out);
+}
+
+const char* gemm_bf16_strerror(int status)
+{
+    switch (status) {
+    case GEMM_OK: return "success";
+    case GEMM_ERR_INVALID_VALUE: return "invalid value (negative size, NULL pointer or leading dimension too small)";
+    case GEMM_ERR_MISALIGNED: return "misaligned operand (pointers need 16-byte alignment, leading dimensions a multiple of 8)";
+    case GEMM_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (N and K must be multiples of 8; leading dimensions at most 2^22)";
+    case GEMM_ERR_STAGES: return "stages must be 0 (default), 2, 3 or 4";
+    case GEMM_ERR_SYNC_MODE: return "sync_mode must be GEMM_SYNC_BARRIER, GEMM_SYNC_FLAGS or GEMM_SYNC_WAVESPEC";
+    case GEMM_ERR_DEVICE: return "no usable device (the current HIP device must be gfx950)";
+    case GEMM_ERR_LAUNCH: return "kernel launch failed";
+    case GEMM_ERR_ALIAS: return "C overlaps A or B";
+    default: return "unknown status";
+    }
+}
+
+int64_t gemm_bf16_sync_timeouts(int reset)
+{
+    int cus = 0;
+    int rc = device_info(&cus);
+    if (rc != GEMM_OK)
+        return rc;
+    if (hipDeviceSynchronize() != hipSuccess)
+        return GEMM_ERR_DEVICE;
+    unsigned long long v = 0;
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_sync_timeouts), sizeof v, 0, hipMemcpyDeviceToHost) != hipSuccess)
+        return GEMM_ERR_DEVICE;
+    if (reset) {
+        const unsigned long long zero = 0;
+        if (hipMemcpyToSymbol(HIP_SYMBOL(g_sync_timeouts), &zero, sizeof zero, 0, hipMemcpyHostToDevice) != hipSuccess)
+            return GEMM_ERR_DEVICE;
+    }
+    return (int64_t)v;
+}
+
+}  // extern "C"

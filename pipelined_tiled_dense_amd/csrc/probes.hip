@@ -1,0 +1,200 @@
+// Hardware-semantics probes for gfx950 (MI355X).
+//
+// The GEMM kernels rely on four instruction behaviours that the compiler
+// builtins do not document in full.  Each probe runs one 64-lane wave on
+// fixed-size buffers, records what the instruction produced, and returns it
+// to the host, where a test compares it with the layout the kernels assume:
+//   - global_load_lds_dwordx4: which LDS bytes each lane's 16-byte load lands
+//     in, and that s_waitcnt vmcnt(0) covers the LDS write;
+//   - v_mfma_f32_32x32x16_bf16: the operand and accumulator lane layouts;
+//   - ds_read_b64_tr_b16: which lane receives which 16-bit element;
+//   - the fp32 -> bf16 conversion used by the epilogue (rounding mode).
+// All accesses stay inside the buffers whose sizes are stated per entry
+// point; the host wrapper checks pointer arguments before launching.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define LDS_AS __attribute__((address_space(3)))
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+
+namespace {
+
+constexpr int kProbeLdsWords = 2048;   // 8 KiB of LDS per probe
+
+// Each lane l fetches the 16-byte chunk src[perm[l]] and the hardware writes
+// it into LDS at (lds_base_bytes + inst_offset + 16 * l) if the assumed layout
+// holds.  Two loads are issued: one with the instruction offset 0 and one
+// with 1024 bytes (which moves the global address by the same amount).  The whole 8 KiB window is then copied out.  src holds
+// 128 chunks; perm holds 64 entries, taken modulo 64.
+__global__ void __launch_bounds__(64) k_lds_dma(const uint4* __restrict__ src,
+                                                const int* __restrict__ perm,
+                                                int lds_base_bytes,
+                                                uint32_t* __restrict__ dump)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t lds[kProbeLdsWords];
+    const int l = threadIdx.x;
+    for (int i = l; i < kProbeLdsWords; i += 64)
+        lds[i] = 0xDEADBEEFu;
+    __syncthreads();
+    char LDS_AS* base = (char LDS_AS*)lds + lds_base_bytes;
+    const int p = perm[l] & 63;
+    __builtin_amdgcn_global_load_lds(src + p, (void LDS_AS*)base, 16, 0, 0);
+    // The instruction offset is added to the global address and to the LDS
+    // address alike: this load reads chunk 64 + p and lands 1 KiB further on.
+    __builtin_amdgcn_global_load_lds(src + p, (void LDS_AS*)base, 16, 1024, 0);
+    // vmcnt(0) with expcnt and lgkmcnt left at their maxima: only the vector
+    // memory counter is waited on before this single wave reads the LDS back.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    for (int i = l; i < kProbeLdsWords; i += 64)
+        dump[i] = lds[i];
+}
+
+// Buffer-resource loads into LDS and buffer stores, with hardware range
+// checking.  The source resource covers src_nrec bytes and the destination
+// resource dst_nrec bytes (raw buffers, stride 0).  Lane l loads 16 bytes at
+// byte offset voff[l] into LDS at 16*l, the LDS window is copied to dump, and
+// lane l then stores its 16 LDS bytes to dst at byte offset voff[l].  Offsets
+// are taken modulo 64 KiB and rounded down to 16 bytes; the caller provides
+// src and dst allocations of at least 64 KiB + 16 bytes, so every address
+// the hardware could form lies inside them whether or not the range check
+// suppresses it.
+__global__ void __launch_bounds__(64) k_buffer_oob(const void* __restrict__ src, int src_nrec,
+                                                   const uint32_t* __restrict__ voff,
+                                                   uint32_t* __restrict__ dump,
+                                                   void* __restrict__ dst, int dst_nrec)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t lds[kProbeLdsWords];
+    const int l = threadIdx.x;
+    for (int i = l; i < kProbeLdsWords; i += 64)
+        lds[i] = 0xDEADBEEFu;
+    __syncthreads();
+    const uint32_t off = voff[l] & 0xFFF0u;
+    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, src_nrec,
+                                                                  0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void LDS_AS*)lds, 16, off, 0, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    for (int i = l; i < kProbeLdsWords; i += 64)
+        dump[i] = lds[i];
+    typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+    u32x4_t v = *(u32x4_t LDS_AS*)((char LDS_AS*)lds + 16 * l);
+    __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, dst_nrec, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
+}
+
+// One MFMA with zero accumulator: lane l supplies a[8l..8l+7] and
+// b[8l..8l+7] as its operands and writes its 16 accumulator values to
+// d[16l..16l+15].
+__global__ void __launch_bounds__(64) k_mfma(const uint16_t* __restrict__ a,
+                                             const uint16_t* __restrict__ b,
+                                             float* __restrict__ d)
+{
+    const int l = threadIdx.x;
+    bf16x8_t va, vb;
+    __builtin_memcpy(&va, a + 8 * l, 16);
+    __builtin_memcpy(&vb, b + 8 * l, 16);
+    f32x16_t acc = {};
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, vb, acc, 0, 0, 0);
+    for (int r = 0; r < 16; ++r)
+        d[16 * l + r] = acc[r];
+}
+
+// LDS is filled with image[0..4095] (16-bit words); lane l then performs one
+// ds_read_b64_tr_b16 at byte address addr[l] and writes its four 16-bit
+// results to out[4l..4l+3].
+__global__ void __launch_bounds__(64) k_ds_read_tr(const uint16_t* __restrict__ image,
+                                                   const uint32_t* __restrict__ addr,
+                                                   uint16_t* __restrict__ out)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kProbeLdsWords];
+    const int l = threadIdx.x;
+    for (int i = l; i < 2 * kProbeLdsWords; i += 64)
+        lds[i] = image[i];
+    __syncthreads();
+    const uint32_t byte = addr[l] & (uint32_t)(4 * kProbeLdsWords - 8);   // in range, 8-byte aligned
+    i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (i16x4_t LDS_AS*)((char LDS_AS*)lds + byte));
+    for (int i = 0; i < 4; ++i)
+        out[4 * l + i] = (uint16_t)v[i];
+}
+
+// fp32 -> bf16 with the conversion the GEMM epilogue uses (a pair at a time).
+__global__ void __launch_bounds__(256) k_cvt(const float* __restrict__ in,
+                                             uint16_t* __restrict__ out, int n_pairs)
+{
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_pairs)
+        return;
+    __bf16 lo = (__bf16)in[2 * i];
+    __bf16 hi = (__bf16)in[2 * i + 1];
+    uint16_t ulo, uhi;
+    __builtin_memcpy(&ulo, &lo, 2);
+    __builtin_memcpy(&uhi, &hi, 2);
+    out[2 * i] = ulo;
+    out[2 * i + 1] = uhi;
+}
+
+int launch_status()
+{
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? 0 : -(int)e - 1000;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_probe_lds_dma(const void* src, const int* perm, int lds_base_bytes, uint32_t* dump,
+                       void* stream)
+{
+    if (!src || !perm || !dump)
+        return -1;
+    if (lds_base_bytes < 0 || lds_base_bytes % 16 != 0 || lds_base_bytes + 2048 > 4 * kProbeLdsWords)
+        return -1;
+    hipLaunchKernelGGL(k_lds_dma, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                       (const uint4*)src, perm, lds_base_bytes, dump);
+    return launch_status();
+}
+
+int gemm_probe_buffer_oob(const void* src, int src_nrec, const uint32_t* voff, uint32_t* dump,
+                          void* dst, int dst_nrec, void* stream)
+{
+    if (!src || !voff || !dump || !dst || src_nrec < 0 || dst_nrec < 0)
+        return -1;
+    hipLaunchKernelGGL(k_buffer_oob, dim3(1), dim3(64), 0, (hipStream_t)stream, src, src_nrec,
+                       voff, dump, dst, dst_nrec);
+    return launch_status();
+}
+
+int gemm_probe_mfma(const uint16_t* a, const uint16_t* b, float* d, void* stream)
+{
+    if (!a || !b || !d)
+        return -1;
+    hipLaunchKernelGGL(k_mfma, dim3(1), dim3(64), 0, (hipStream_t)stream, a, b, d);
+    return launch_status();
+}
+
+int gemm_probe_ds_read_tr(const uint16_t* image, const uint32_t* addr, uint16_t* out, void* stream)
+{
+    if (!image || !addr || !out)
+        return -1;
+    hipLaunchKernelGGL(k_ds_read_tr, dim3(1), dim3(64), 0, (hipStream_t)stream, image, addr, out);
+    return launch_status();
+}
+
+int gemm_probe_cvt_bf16(const float* in, uint16_t* out, int64_t n, void* stream)
+{
+    if (!in || !out || n < 0 || n % 2 != 0 || n > (int64_t)1 << 30)
+        return -1;
+    int pairs = (int)(n / 2);
+    if (pairs == 0)
+        return 0;
+    hipLaunchKernelGGL(k_cvt, dim3((pairs + 255) / 256), dim3(256), 0, (hipStream_t)stream,
+                       in, out, pairs);
+    return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,228 @@
+"""GPU parity: the HIP GEMM (through the C ABI) against the CPU oracle.
+
+Bar (the method's stated acceptance): |gpu - ref| <= 1e-2 * max(1, |ref|) for
+every element, computed in fp64 from the bf16 results.  Where fp32
+accumulation is exact (small-integer inputs) the bar is bit equality.  All
+sync modes, stage counts and both B layouts run the same MFMA chain per
+output element (k in increasing order), so their outputs must also be
+bit-identical to each other and from run to run.
+
+Small cases span several 256 x 256 tiles and ragged tails and are compared in
+full.  The five benchmark workloads run at their full sizes in the launch
+configuration the benchmark uses and are compared on sampled rows, which the
+oracle computes one by one, plus an all-ones case checked in full.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from pipelined_tiled_dense_amd import binding as bd
+from pipelined_tiled_dense_amd.inputs import WORKLOADS, bits, make_operands, workload_operands
+
+pytestmark = pytest.mark.gpu
+
+MODES = [("barrier", 2), ("barrier", 3), ("barrier", 4),
+         ("flags", 2), ("flags", 3), ("flags", 4),
+         ("wavespec", 2), ("wavespec", 3), ("wavespec", 4)]
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    bd.library()
+    bd.gemm_bf16_sync_timeouts(reset=True)
+    yield
+    assert bd.gemm_bf16_sync_timeouts() == 0, "a ring counter wait timed out"
+
+
+def run(A, B, bt, sync, stages, out=None):
+    print("  gemm M=%d K=%d B=%s bt=%s sync=%s stages=%d" % (A.shape[0], A.shape[1], tuple(B.shape),
+                                                          bt, sync, stages), flush=True)
+    C = bd.gemm(A, B, b_transposed=bt, sync=sync, stages=stages, out=out)
+    torch.cuda.synchronize()
+    return bits(C.cpu()).copy()
+
+
+def decode(b):
+    return oracle.bf16_bits_to_f64(b)
+
+
+def assert_within_tol(got, ref, what):
+    g, r = decode(got), decode(ref)
+    err = np.abs(g - r)
+    lim = TOL * np.maximum(1.0, np.abs(r))
+    bad = err > lim
+    if bad.any():
+        idx = np.argwhere(bad)[0]
+        raise AssertionError("%s: %d/%d elements outside tolerance; first %s got %r want %r" % (
+            what, int(bad.sum()), bad.size, tuple(idx), g[tuple(idx)], r[tuple(idx)]))
+    same = float(np.mean(got == ref))
+    print("  %s: max abs err %.3g, max rel err %.3g, bit-equal %.4f" % (
+        what, err.max() if err.size else 0.0,
+        (err / np.maximum(1.0, np.abs(r))).max() if err.size else 0.0, same), flush=True)
+    return same
+
+
+SMALL = [
+    (256, 256, 256, None),
+    (512, 512, 256, None),
+    (300, 264, 200, None),          # ragged in M, N and K
+    (777, 520, 1000, None),
+    (1, 8, 8, None),
+    (33, 8, 16, None),
+    (256, 256, 8, None),            # K shorter than one k-step
+    (513, 1032, 72, None),
+    (640, 384, 512, (520, 400)),    # padded leading dimensions for A and B
+]
+
+
+@pytest.fixture(scope="module")
+def small_refs():
+    cache = {}
+
+    def get(case, bt):
+        key = (case, bt)
+        if key not in cache:
+            M, N, K, lds = case
+            lda, ldb = (lds if lds else (None, None))
+            if bt and lds:
+                ldb = K + 16
+            A, B = make_operands(M, N, K, b_transposed=bt, seed=M * 7 + N * 3 + K, lda=lda, ldb=ldb)
+            ref = oracle.load().gemm_bf16(bits(A), bits(B), bt, K=K, N=N)
+            cache[key] = (A, B, ref)
+        return cache[key]
+    return get
+
+
+@pytest.mark.parametrize("bt", [False, True], ids=["kn", "nk"])
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "%dx%dx%d%s" % (c[0], c[1], c[2], "_ld" if c[3] else ""))
+def test_small_parity_all_modes(case, bt, small_refs):
+    A, B, ref = small_refs(case, bt)
+    dA, dB = A.cuda(), B.cuda()
+    first = None
+    for sync, stages in MODES:
+        got = run(dA, dB, bt, sync, stages)
+        assert_within_tol(got, ref, "%s/%d" % (sync, stages))
+        if first is None:
+            first = got
+        else:
+            np.testing.assert_array_equal(got, first, err_msg="modes disagree bitwise")
+
+
+def test_layouts_and_modes_bit_identical():
+    M, N, K = 520, 776, 392
+    A, B = make_operands(M, N, K, b_transposed=False, seed=99)
+    dA, dB, dBt = A.cuda(), B.cuda(), B.t().contiguous().cuda()
+    outs = []
+    for sync, stages in MODES:
+        outs.append(run(dA, dB, False, sync, stages))
+        outs.append(run(dA, dBt, True, sync, stages))
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+    again = run(dA, dB, False, "flags", 3)
+    np.testing.assert_array_equal(again, outs[0])
+
+
+@pytest.mark.parametrize("bt", [False, True], ids=["kn", "nk"])
+def test_exact_integer_inputs_bitwise(bt):
+    """Small integers: every fp32 partial sum is exact, so GPU == oracle bit for bit
+    (this pins tile placement and the epilogue's rounding)."""
+    rng = np.random.default_rng(7)
+    M, N, K = 600, 520, 1016
+    Av = rng.integers(-4, 5, size=(M, K)).astype(np.float32)
+    Bv = rng.integers(-4, 5, size=(N, K) if bt else (K, N)).astype(np.float32)
+    A = torch.from_numpy(Av).to(torch.bfloat16)
+    B = torch.from_numpy(Bv).to(torch.bfloat16)
+    ref = oracle.load().gemm_bf16(bits(A), bits(B), bt)
+    for sync, stages in MODES:
+        got = run(A.cuda(), B.cuda(), bt, sync, stages)
+        np.testing.assert_array_equal(got, ref, err_msg="%s/%d" % (sync, stages))
+
+
+def test_degenerate_sizes():
+    dev = "cuda"
+    A = torch.ones((4, 16), dtype=torch.bfloat16, device=dev)
+    B = torch.ones((16, 8), dtype=torch.bfloat16, device=dev)
+    # M == 0 and N == 0: no-ops
+    C = torch.full((0, 8), 7.0, dtype=torch.bfloat16, device=dev)
+    bd.gemm(A[:0], B, out=C)
+    C = torch.full((4, 0), 7.0, dtype=torch.bfloat16, device=dev)
+    bd.gemm(A, B[:, :0], out=C)
+    # K == 0: C is set to +0 everywhere
+    for sync in ("barrier", "flags", "wavespec"):
+        C = torch.full((300, 264), 7.0, dtype=torch.bfloat16, device=dev)
+        bd.gemm(A[:0].new_empty((300, 0)), B.new_empty((0, 264)), out=C, sync=sync)
+        torch.cuda.synchronize()
+        assert torch.all(bits(C.cpu()) == 0)
+    # C = A * B with K = 8 (a single partial k-step)
+    A8, B8 = make_operands(300, 264, 8, b_transposed=False, seed=5)
+    ref = oracle.load().gemm_bf16(bits(A8), bits(B8), False)
+    got = run(A8.cuda(), B8.cuda(), False, "barrier", 2)
+    assert_within_tol(got, ref, "K=8")
+
+
+def test_output_outside_the_matrix_untouched():
+    """Stores past M and N are dropped: a wider, taller C buffer keeps its
+    sentinel outside the M x N window."""
+    M, N, K = 300, 264, 200
+    A, B = make_operands(M, N, K, b_transposed=False, seed=3)
+    for sync, stages in MODES:
+        buf = torch.full((M + 40, N + 48), 3.0, dtype=torch.bfloat16, device="cuda")
+        view = buf[:M, :N]
+        bd.gemm(A.cuda(), B.cuda(), out=view, sync=sync, stages=stages)
+        torch.cuda.synchronize()
+        h = buf.cpu().float()
+        assert torch.all(h[M:, :] == 3.0) and torch.all(h[:, N:] == 3.0), (sync, stages)
+
+
+# --- the five workloads at full size ------------------------------------------
+FULL = {
+    "gemm256_kn": [("barrier", 2), ("flags", 2), ("wavespec", 4)],
+    "gemm4096_kn": [("barrier", 2), ("barrier", 3), ("barrier", 4), ("flags", 2), ("flags", 3), ("flags", 4)],
+    "gemm8192_nk": [("barrier", 2), ("barrier", 4), ("flags", 2), ("wavespec", 4)],
+    "longk1024_k32768_kn": [("barrier", 2), ("barrier", 3), ("barrier", 4), ("flags", 2), ("flags", 3), ("flags", 4)],
+    "tall32768x1024_k4096_kn": [("wavespec", 2), ("wavespec", 3), ("wavespec", 4), ("barrier", 2), ("flags", 2)],
+}
+
+
+def sample_rows(M, n=24, seed=0):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 31, 32, 255, 256, M // 2, M - 257, M - 256, M - 2, M - 1]
+    rows = sorted(set([r for r in fixed if 0 <= r < M] + list(rng.integers(0, M, size=n))))
+    return np.array(rows, dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", sorted(FULL))
+def test_workload_full_size_sampled(name):
+    w = WORKLOADS[name]
+    A, B = workload_operands(w)
+    rows = sample_rows(w.M) if w.M > 256 else np.arange(w.M)
+    Ab, Bb = bits(A), bits(B)
+    ref = oracle.load().gemm_bf16(np.ascontiguousarray(Ab[rows]), Bb, w.b_transposed)
+    dA, dB = A.cuda(), B.cuda()
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    first = None
+    for sync, stages in FULL[name]:
+        C.fill_(7.0)
+        got = run(dA, dB, w.b_transposed, sync, stages, out=C)
+        assert_within_tol(got[rows], ref, "%s %s/%d (sampled %d rows)" % (name, sync, stages, len(rows)))
+        if first is None:
+            first = got
+        else:
+            np.testing.assert_array_equal(got, first, err_msg="modes disagree bitwise")
+
+
+@pytest.mark.parametrize("name", ["gemm8192_nk", "tall32768x1024_k4096_kn", "longk1024_k32768_kn"])
+def test_workload_all_ones_exact(name):
+    """A = B = 1 at full size: every element is exactly K (a power of two, exact in
+    bf16 and in fp32 accumulation), checked for the whole output."""
+    w = WORKLOADS[name]
+    A = torch.ones((w.M, w.K), dtype=torch.bfloat16, device="cuda")
+    B = torch.ones((w.N, w.K) if w.b_transposed else (w.K, w.N), dtype=torch.bfloat16, device="cuda")
+    for sync, stages in FULL[name][:3]:
+        C = bd.gemm(A, B, b_transposed=w.b_transposed, sync=sync, stages=stages)
+        torch.cuda.synchronize()
+        assert torch.all(C == float(w.K)), (name, sync, stages)
