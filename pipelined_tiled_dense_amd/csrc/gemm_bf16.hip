@@ -204,21 +204,22 @@ __device__ __forceinline__ void tile_coords(const Params& p, int32_t t, int32_t 
     tn = in / gm;
 }
 
-// Bounded wait until *ctr >= target.  Returns false (after counting the
-// timeout) if the counter does not get there.
-__device__ __forceinline__ bool wait_counter(lds_u32* ctr, uint32_t target)
+// Bounded wait until *ctr >= target.  A wait that gives up is counted and
+// sets the wave's sticky `failed` flag; once set, later waits return at once,
+// so the wave runs its (finite) loops to the end without blocking and the
+// kernel always terminates.  Results of such a launch are not meaningful.
+__device__ __forceinline__ void wait_counter(lds_u32* ctr, uint32_t target, bool& failed)
 {
     uint32_t spins = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+    while (!failed && __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
         if (++spins > kSpinLimit) {
             if ((threadIdx.x & 63) == 0)
                 atomicAdd(&g_sync_timeouts, 1ull);
-            return false;
+            failed = true;
         }
         __builtin_amdgcn_s_sleep(1);
     }
     COMPILER_FENCE();
-    return true;
 }
 
 __device__ __forceinline__ void arrive(lds_u32* ctr)
@@ -435,13 +436,14 @@ __device__ __forceinline__ void mfma_step(f32x16_t (&acc)[C::FM][C::FN], const F
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// Two fp32 values -> two bf16 (round to nearest even) in one 32-bit word.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    const __bf16 l = (__bf16)lo, h = (__bf16)hi;
-    uint16_t ul, uh;
-    __builtin_memcpy(&ul, &l, 2);
-    __builtin_memcpy(&uh, &h, 2);
-    return (uint32_t)ul | ((uint32_t)uh << 16);
+    const bf16x2_t v = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // fp32 accumulators -> bf16 (RNE) -> wave-private LDS strip -> 16-byte stores.
@@ -472,6 +474,10 @@ __device__ __forceinline__ void epilogue(const Params& p, f32x16_t (&acc)[C::FM]
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
+                // Keep this block in AGPRs up to here, so its copy to VGPRs
+                // happens now rather than for all blocks at once.
+                if constexpr (C::FM * C::FN * 16 > 128)
+                    asm volatile("" : "+a"(acc[i][2 * jp + jj]));
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const f32x16_t& a = acc[i][2 * jp + jj];
@@ -542,7 +548,8 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
     // many loads outstanding; loads complete in order, so group c has landed
     // however the younger operations complete.  Near the end of the stream
     // fewer groups are in flight and the wait drains everything.
-    auto sync_position = [&](int32_t c) -> bool {
+    bool failed = false;
+    auto sync_position = [&](int32_t c) {
         if (c + C::S - 2 < total)
             wait_vmcnt<C::LOADS * (C::S - 2)>();
         else
@@ -552,36 +559,30 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
         } else {
             const int s = c % C::S;
             arrive(full + s);
-            if (!wait_counter(full + s, (uint32_t)(c / C::S + 1) * C::NW))
-                return false;
+            wait_counter(full + s, (uint32_t)(c / C::S + 1) * C::NW, failed);
         }
-        return true;
     };
     // Issue the load of position q = c + S - 1 (into the stage position c-1 used).
-    auto issue_next = [&](int32_t c) -> bool {
+    auto issue_next = [&](int32_t c) {
         const int32_t q = c + C::S - 1;
         if (q >= total)
-            return true;
+            return;
         const int s = q % C::S;
         if constexpr (C::SYNC == SYNC_FLAGS) {
-            if (q >= C::S && !wait_counter(empty + s, (uint32_t)(q / C::S) * C::NW))
-                return false;
+            if (q >= C::S)
+                wait_counter(empty + s, (uint32_t)(q / C::S) * C::NW, failed);
         }
         ld.issue_and_advance(p, smem + s * C::STAGE_BYTES, w, lane);
-        return true;
     };
 
     if (total == 0)
         return;
-    if (!sync_position(0))
-        return;
+    sync_position(0);
     if constexpr (C::SYNC == SYNC_BARRIER)
         issue_next(0);
     read_frags<C>(fr[0], smem, wm, wn, lane, 0);
-    if constexpr (C::SYNC == SYNC_FLAGS) {
-        if (!issue_next(0))
-            return;
-    }
+    if constexpr (C::SYNC == SYNC_FLAGS)
+        issue_next(0);
 
     int32_t c = 0;
     for (int32_t it = 0; it < n_tiles; ++it) {
@@ -608,8 +609,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
                     wait_lgkm0();
                     if constexpr (C::SYNC == SYNC_FLAGS)
                         arrive(empty + c % C::S);
-                    if (!sync_position(c + 1))
-                        return;
+                    sync_position(c + 1);
                     if constexpr (C::SYNC == SYNC_BARRIER)
                         issue_next(c + 1);
                     read_frags<C>(fr[0], smem + ((c + 1) % C::S) * C::STAGE_BYTES, wm, wn, lane, 0);
@@ -619,8 +619,8 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
             if constexpr (C::SYNC == SYNC_FLAGS) {
                 // WAR wait for the stage the next load reuses, placed after
                 // this wave's MFMAs for the stage are issued.
-                if (more && !issue_next(c + 1))
-                    return;
+                if (more)
+                    issue_next(c + 1);
             }
         }
         epilogue<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
@@ -657,10 +657,11 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
         constexpr int D = (C::S - 1 < 2) ? C::S - 1 : 2;
         Loader<C> ld;
         ld.init(p, n_tiles, lw, lane);
+        bool failed = false;
         for (int32_t q = 0; q < total; ++q) {
             const int s = q % C::S;
-            if (q >= C::S && !wait_counter(empty + s, (uint32_t)(q / C::S) * C::NCW))
-                return;
+            if (q >= C::S)
+                wait_counter(empty + s, (uint32_t)(q / C::S) * C::NCW, failed);
             ld.issue_and_advance(p, smem + s * C::STAGE_BYTES, lw, lane);
             if (q >= D) {
                 wait_vmcnt<C::LOADS * D>();
@@ -679,8 +680,8 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
     Frags<C> fr[2];
     if (total == 0)
         return;
-    if (!wait_counter(full, (uint32_t)C::NP))
-        return;
+    bool failed = false;
+    wait_counter(full, (uint32_t)C::NP, failed);
     read_frags<C>(fr[0], smem, wm, wn, lane, 0);
 
     int32_t c = 0;
@@ -704,8 +705,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
                     arrive(empty + c % C::S);
                     if (c + 1 < total) {
                         const int s1 = (c + 1) % C::S;
-                        if (!wait_counter(full + s1, (uint32_t)((c + 1) / C::S + 1) * C::NP))
-                            return;
+                        wait_counter(full + s1, (uint32_t)((c + 1) / C::S + 1) * C::NP, failed);
                         read_frags<C>(fr[0], smem + s1 * C::STAGE_BYTES, wm, wn, lane, 0);
                     }
                 }
