@@ -146,10 +146,14 @@ struct Cfg {
     static constexpr int CPR_K = BK / 8;                             // 16-byte chunks per K-contiguous row
     static constexpr int CPR_N = BN / 8;                             // chunks per row of a K x N B tile
     static constexpr int RING_BYTES = S * STAGE_BYTES;
-    static constexpr int EPI_WAVE_BYTES = 32 * 64 * 2;               // 32 rows x 64 columns of bf16
+    static constexpr int FLAG_BYTES = (SYNC != SYNC_BARRIER) ? 2 * S * 4 : 0;
+    // Epilogue strip per MFMA wave: 32 rows x 64 columns of bf16 when that
+    // fits next to the ring, else 32 rows x 32 columns.
+    static constexpr int EPI_W = (RING_BYTES + NCW * 32 * 64 * 2 + FLAG_BYTES <= 160 * 1024) ? 64 : 32;
+    static constexpr int EPI_WAVE_BYTES = 32 * EPI_W * 2;
     static constexpr int EPI_OFFSET = RING_BYTES;
     static constexpr int FLAG_OFFSET = EPI_OFFSET + NCW * EPI_WAVE_BYTES;
-    static constexpr int LDS_BYTES = FLAG_OFFSET + ((SYNC != SYNC_BARRIER) ? 2 * S * 4 : 0);
+    static constexpr int LDS_BYTES = FLAG_OFFSET + FLAG_BYTES;
 
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(KK % 2 == 0, "fragment double buffering assumes an even number of MFMA k-steps");
@@ -170,38 +174,45 @@ struct Params {
     int32_t group_m;
 };
 
-// Swizzles.  K-contiguous tiles (A, and B stored N x K) hold rows of BK
-// elements; the 16-byte chunk index is XORed with a function of the row so
-// that the 8 lanes served together by one ds_read_b128 (8 consecutive rows,
-// one chunk) hit 8 different 16-byte bank groups.
+// Swizzles.  The LDS has 64 four-byte banks (256 bytes per cycle); a 16-byte
+// read is served 16 lanes at a time, an 8-byte read 32 lanes at a time.
+//
+// K-contiguous tiles (A, and B stored N x K) hold rows of BK elements.  A
+// fragment read has lanes 0..15 on 16 consecutive rows at one logical chunk;
+// those rows span 8 (BK = 64, 128-byte rows) or 4 (BK = 32, 64-byte rows)
+// bank windows, so XORing the chunk with (row / 2) mod 8, respectively
+// (row / 4) mod 4, puts the 16 lanes on 16 different 16-byte bank groups.
 template <int BK>
 __device__ __forceinline__ int swz_k(int row)
 {
-    return BK == 64 ? (row & 7) : ((row >> 1) & 3);
+    return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
 }
-// K x N tiles of B hold rows of BN elements; a transposing read touches 4
-// consecutive k-rows x 2 chunks per 16 lanes, spread by XOR with 2*(k mod 4).
-__device__ __forceinline__ int swz_n(int krow) { return (krow & 3) << 1; }
+// K x N tiles of B hold rows of BN elements (512 or 256 bytes, so every row
+// starts on the same bank).  A transposing read has lanes 0..31 on 4
+// consecutive k-rows x 4 chunks; XORing chunk bits 2-3 with (k mod 4) spreads
+// the 16 (row, chunk) pairs over all 16 bank groups.
+__device__ __forceinline__ int swz_n(int krow) { return (krow & 3) << 2; }
 
-// Output tile of the i-th tile id of this workgroup's grid-stride walk.
+// Output tile (tm, tn) of tile id t, for a grid of G persistent workgroups
+// (workgroup b takes ids b, b + G, b + 2G, ...).  Branch-free scalar code.
 __device__ __forceinline__ void tile_coords(const Params& p, int32_t t, int32_t G, int32_t& tm, int32_t& tn)
 {
-    int32_t L = t;
+    // The hardware deals workgroups to the 8 XCDs round-robin; within every
+    // full round of G ids, give XCD x a contiguous run of G/8 ids.
     const int32_t round = t / G;
-    if ((G & 7) == 0 && (round + 1) * G <= p.tiles) {
-        // The hardware deals workgroups to the 8 XCDs round-robin; give XCD x
-        // a contiguous run of G/8 tile ids within each round.
-        const int32_t b = t - round * G;
-        L = round * G + (b & 7) * (G >> 3) + (b >> 3);
-    }
-    // Grouped raster: runs of group_m tile rows, walked column by column.
+    const int32_t b = t - round * G;
+    const int32_t remapped = round * G + (b & 7) * (G >> 3) + (b >> 3);
+    const int32_t L = ((G & 7) == 0 && (round + 1) * G <= p.tiles) ? remapped : t;
+    // Grouped raster: runs of group_m tile rows, walked column by column, so a
+    // run of consecutive ids covers a compact block of output tiles.
     const int32_t per_group = p.group_m * p.tiles_n;
     const int32_t grp = L / per_group;
     const int32_t first_m = grp * p.group_m;
     const int32_t gm = min(p.tiles_m - first_m, p.group_m);
     const int32_t in = L - grp * per_group;
-    tm = first_m + in % gm;
-    tn = in / gm;
+    const int32_t col = in / gm;
+    tm = first_m + (in - col * gm);
+    tn = col;
 }
 
 // Bounded wait until *ctr >= target.  A wait that gives up is counted and
@@ -263,14 +274,21 @@ __device__ __forceinline__ void wait_lgkm0()
 // computed once.  Per position only the buffer resources move (scalar work):
 // their base is the tile origin at k0 and their byte count ends at the last
 // element of the operand, so rows past M (A), past N (B stored N x K) and
-// k-rows past K (B stored K x N) read as zeros by themselves.  The two edges
-// a byte count cannot express -- the k tail inside a row, and columns past N
-// of a K x N B tile -- are masked per lane in a uniform branch.
+// k-rows past K (B stored K x N) read as zeros by themselves.  The two edges a
+// byte count cannot express -- the k tail inside a row, and columns past N of
+// a K x N B tile -- are masked per lane with a select.
+//
+// issue() derives everything from the stream position q (tile q / KT, k-step
+// q % KT) without branches, and a position past the end of the stream gets
+// resources of zero bytes, so it writes zeros and touches no memory.  Every
+// call therefore emits exactly LOADS DMA instructions, which keeps the
+// vector-memory counter arithmetic of the waits exact, and the code around it
+// stays one basic block that the scheduler can interleave with MFMAs.
 // ---------------------------------------------------------------------------
 template <class C>
 struct Loader {
-    int32_t n_tiles, it, kt;      // position in this workgroup's stream
-    int32_t m0, n0;               // current load tile origin
+    int32_t total;                // positions in this workgroup's stream
+    int32_t n_tiles;
     uint32_t voffA[C::A_LOADS];
     uint32_t voffB[C::B_LOADS];
 
@@ -305,61 +323,108 @@ struct Loader {
                 voffB[t] = (uint32_t)(s / C::CPR_N) * ldb2 + (uint32_t)nofs_n(s) * 2u;
         }
         n_tiles = ntiles;
-        it = 0;
-        kt = 0;
-        set_tile(p);
+        total = ntiles * p.k_steps;
+        start(p);
     }
 
-    __device__ __forceinline__ void set_tile(const Params& p)
+    // Scalar part of issuing one position: the two buffer resources and the
+    // remaining k / n extents used by the edge masks.
+    struct Prep {
+        __amdgpu_buffer_rsrc_t ra, rb;
+        int32_t krem, nrem;
+    };
+
+    // The load cursor: position q, its tile (index ti in this workgroup's
+    // list) and k-step kt, and the operand addresses and byte counts at that
+    // position.  Advancing by one k-step is a few scalar adds; only the step
+    // into a new tile recomputes the tile origin (a uniform branch taken once
+    // per tile).
+    int32_t q, ti, kt;
+    int32_t krem, nrem;
+    const char* pa;
+    const char* pb;
+    int64_t abytes, bbytes;
+
+    __device__ __forceinline__ void enter_tile(const Params& p)
     {
         int32_t tm = 0, tn = 0;
-        if (it < n_tiles)
-            tile_coords(p, (int32_t)blockIdx.x + it * (int32_t)gridDim.x, (int32_t)gridDim.x, tm, tn);
-        m0 = tm * C::BM;
-        n0 = tn * C::BN;
+        tile_coords(p, (int32_t)blockIdx.x + min(ti, n_tiles - 1) * (int32_t)gridDim.x, (int32_t)gridDim.x, tm, tn);
+        const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+        krem = (int32_t)p.K;
+        nrem = (int32_t)(p.N - n0);
+        pa = p.A + m0 * p.lda * 2;
+        abytes = ((p.M - m0 - 1) * p.lda + p.K) * 2;
+        if constexpr (C::BT) {
+            pb = p.B + n0 * p.ldb * 2;
+            bbytes = ((p.N - n0 - 1) * p.ldb + p.K) * 2;
+        } else {
+            pb = p.B + n0 * 2;
+            bbytes = ((p.K - 1) * p.ldb + nrem) * 2;
+        }
     }
 
-    // Issue this wave's DMA for the current position into `stage`, then step.
-    __device__ __forceinline__ void issue_and_advance(const Params& p, lds_char* stage, int lw, int lane)
+    __device__ __forceinline__ void start(const Params& p)
     {
-        const int64_t k0 = (int64_t)kt * C::BK;
-        const int32_t krem = (int32_t)(p.K - k0);        // > 0
-        const __amdgpu_buffer_rsrc_t ra =
-            make_rsrc(p.A + ((int64_t)m0 * p.lda + k0) * 2, ((p.M - m0 - 1) * p.lda + krem) * 2);
-        __amdgpu_buffer_rsrc_t rb;
-        if constexpr (C::BT)
-            rb = make_rsrc(p.B + ((int64_t)n0 * p.ldb + k0) * 2, ((p.N - n0 - 1) * p.ldb + krem) * 2);
-        else
-            rb = make_rsrc(p.B + (k0 * p.ldb + n0) * 2, ((int64_t)(krem - 1) * p.ldb + (p.N - n0)) * 2);
-        const bool k_tail = krem < C::BK;
-        const bool n_edge = !C::BT && (p.N - n0 < C::BN);
-        if (!k_tail && !n_edge) {
-#pragma unroll
-            for (int t = 0; t < C::A_LOADS; ++t)
-                lds_dma16(ra, stage + (t * C::NLW + lw) * 1024, voffA[t]);
-#pragma unroll
-            for (int t = 0; t < C::B_LOADS; ++t)
-                lds_dma16(rb, stage + C::A_BYTES + (t * C::NLW + lw) * 1024, voffB[t]);
-        } else {
-            lane = (int)opaque((uint32_t)lane);
-            const int32_t nrem = (int32_t)(p.N - n0);
-#pragma unroll
-            for (int t = 0; t < C::A_LOADS; ++t) {
-                const bool ok = kofs_k(slot(t, lw, lane)) < krem;
-                lds_dma16(ra, stage + (t * C::NLW + lw) * 1024, ok ? voffA[t] : kOOB);
-            }
-#pragma unroll
-            for (int t = 0; t < C::B_LOADS; ++t) {
-                const int s = slot(t, lw, lane);
-                const bool ok = C::BT ? (kofs_k(s) < krem) : (nofs_n(s) < nrem);
-                lds_dma16(rb, stage + C::A_BYTES + (t * C::NLW + lw) * 1024, ok ? voffB[t] : kOOB);
-            }
-        }
+        q = 0;
+        ti = 0;
+        kt = 0;
+        enter_tile(p);
+    }
+
+    // The cursor's position prepared for issue, then the cursor steps on.
+    // Positions at or past the end of the stream get empty resources.
+    __device__ __forceinline__ Prep prepare_and_advance(const Params& p)
+    {
+        const bool live = q < total;
+        Prep r;
+        r.krem = krem;
+        r.nrem = nrem;
+        r.ra = make_rsrc(pa, live ? abytes : 0);
+        r.rb = make_rsrc(pb, live ? bbytes : 0);
+        ++q;
         if (++kt == p.k_steps) {
             kt = 0;
-            ++it;
-            set_tile(p);
+            ++ti;
+            enter_tile(p);
+        } else {
+            constexpr int64_t kstep = (int64_t)C::BK * 2;
+            krem -= C::BK;
+            pa += kstep;
+            abytes -= kstep;
+            const int64_t bstep = C::BT ? kstep : kstep * p.ldb;
+            pb += bstep;
+            bbytes -= bstep;
         }
+        return r;
+    }
+
+    // Issue part `part` of NPARTS of this wave's DMA instructions for a
+    // prepared position (A and B instructions split evenly).
+    template <int NPARTS>
+    __device__ __forceinline__ void fire(const Prep& r, int part, lds_char* stage, int lw, int lane) const
+    {
+        static_assert(C::A_LOADS % NPARTS == 0 && C::B_LOADS % NPARTS == 0, "even split");
+        constexpr int NA = C::A_LOADS / NPARTS, NB = C::B_LOADS / NPARTS;
+#pragma unroll
+        for (int x = 0; x < NA; ++x) {
+            const int t = part * NA + x;
+            const bool ok = kofs_k(slot(t, lw, lane)) < r.krem;
+            lds_dma16(r.ra, stage + (t * C::NLW + lw) * 1024, ok ? voffA[t] : kOOB);
+        }
+#pragma unroll
+        for (int x = 0; x < NB; ++x) {
+            const int t = part * NB + x;
+            const int s = slot(t, lw, lane);
+            const bool ok = C::BT ? (kofs_k(s) < r.krem) : (nofs_n(s) < r.nrem);
+            lds_dma16(r.rb, stage + C::A_BYTES + (t * C::NLW + lw) * 1024, ok ? voffB[t] : kOOB);
+        }
+    }
+
+    // Issue all of this wave's DMA for the cursor's position into `stage`
+    // and step the cursor.
+    __device__ __forceinline__ void issue_next(const Params& p, lds_char* stage, int lw, int lane)
+    {
+        fire<1>(prepare_and_advance(p), 0, stage, lw, lane);
     }
 };
 
@@ -401,19 +466,17 @@ __device__ __forceinline__ void read_frags(Frags<C>& f, const lds_char* stage, i
         // k-row r, columns 4q..4q+3 of a 4 x 16 block; lane i receives column
         // i for the 4 k-rows.  Two reads give the 8 k values of the operand.
         // The k-row of lane (r, q) is 16*kk + 8*(l/32) + 4*hh + r, so its
-        // swizzle term is 2*r; the logical chunk of block j is
-        // 4*(wn*TN/32 + j) + 2*((l>>4)&1) + q/2, and XOR with 2*r splits into
-        // bit 2 (flips with r/2, i.e. +-4 chunks by the parity of j) and
-        // bits 0-1.
+        // swizzle term is 4*r; the logical chunk of block j is
+        // 4*(wn*TN/32 + j) + 2*((l>>4)&1) + q/2, and the XOR only touches the
+        // 4*(wn*TN/32 + j) part: it becomes 4*((wn*TN/32 + j) ^ r).
         const int g = lane >> 4, i16 = lane & 15, r = i16 >> 2, q = i16 & 3;
-        const int low = (2 * (g & 1) + (q >> 1)) ^ (2 * (r & 1));
+        const int low = 2 * (g & 1) + (q >> 1);
         const uint32_t krow0 = (uint32_t)(16 * kk + 8 * (g >> 1) + r);
         const uint32_t base = opaque(krow0 * (C::BN * 2) + (uint32_t)(low * 16 + (q & 1) * 8));
-        const int rh = r >> 1;
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
             const int J = wn * (C::TN / 32) + j;
-            const int jchunk = 4 * (J ^ rh);
+            const int jchunk = 4 * (J ^ r);
             i16x4_t part[2];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
@@ -425,6 +488,37 @@ __device__ __forceinline__ void read_frags(Frags<C>& f, const lds_char* stage, i
         }
     }
 }
+
+// Instruction order inside one MFMA k-step region: the scheduler is asked to
+// alternate one MFMA with one LDS fragment read (the reads are for the next
+// k-step, so they have the rest of this k-step's MFMAs to land), then pair
+// the remaining MFMAs with up to two global-to-LDS DMA issues.  With one wave
+// per SIMD this keeps the matrix pipe fed while the reads and loads go out.
+template <int M, int D, int V>
+__device__ __forceinline__ void sched_interleave()
+{
+    if constexpr (M > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+        if constexpr (D > 0) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // LDS read
+            sched_interleave<M - 1, D - 1, V>();
+        } else if constexpr (V > 0) {
+            constexpr int n = V >= 2 ? 2 : 1;
+            __builtin_amdgcn_sched_group_barrier(0x020, n, 0);      // VMEM read
+            sched_interleave<M - 1, 0, V - n>();
+        } else {
+            sched_interleave<M - 1, 0, 0>();
+        }
+    } else {
+        if constexpr (D > 0)
+            __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
+        if constexpr (V > 0)
+            __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
+    }
+}
+
+template <class C>
+constexpr int frag_reads() { return C::FM + (C::BT ? 1 : 2) * C::FN; }
 
 template <class C>
 __device__ __forceinline__ void mfma_step(f32x16_t (&acc)[C::FM][C::FN], const Frags<C>& f)
@@ -447,11 +541,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 }
 
 // fp32 accumulators -> bf16 (RNE) -> wave-private LDS strip -> 16-byte stores.
-// The strip is 32 rows (m) x 64 columns (n) with 128-byte rows whose 16-byte
-// chunks are XORed with (row % 8).  Writes: lane l holds row l%32 and, per
-// 4 accumulator registers, 4 consecutive columns (8 bytes).  Reads: 8 lanes
-// cover one 128-byte row segment of C, so each store instruction writes 8
-// full row segments.
+// The strip is 32 rows (m) x 64 columns (n) with 128-byte rows.  Writes: lane
+// l holds row l%32 and, per 4 accumulator registers, 4 consecutive columns
+// (8 bytes); the 32 lanes of one write cycle cover 32 rows at one column
+// position, so the chunk is XORed with (row / 2) mod 8 and the two 8-byte
+// halves of a chunk are swapped for rows 16..31, which gives 32 different
+// 8-byte bank slots.  Reads: 8 lanes cover one 128-byte row segment of C (16
+// lanes, two rows, per cycle), so each store instruction writes 8 full row
+// segments; reads of rows 16..31 swap the halves back.
 template <class C>
 __device__ __forceinline__ void epilogue(const Params& p, f32x16_t (&acc)[C::FM][C::FN], lds_char* strip,
                                          int32_t m0, int32_t n0, int wm, int wn, int lane_in)
@@ -463,9 +560,9 @@ __device__ __forceinline__ void epilogue(const Params& p, f32x16_t (&acc)[C::FM]
     const int32_t mrem = (int32_t)min(p.M - m0, (int64_t)C::BM);
     const int32_t nrem = (int32_t)min(p.N - n0, (int64_t)C::BN);
     const uint32_t ldc2 = (uint32_t)p.ldc * 2u;
-    const uint32_t wbase = opaque((uint32_t)(row_w * 128 + half * 8));
+    const uint32_t wbase = opaque((uint32_t)(row_w * 128 + (half ^ (row_w >> 4)) * 8));
     const int rrow = lane >> 3, rc8 = lane & 7;          // read slot u adds 8*u rows
-    const uint32_t rbase = opaque((uint32_t)(rrow * 128 + ((rc8 ^ (rrow & 7)) * 16)));
+    const uint32_t rbase = opaque((uint32_t)(rrow * 128 + ((rc8 ^ (rrow >> 1)) * 16)));
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
@@ -484,8 +581,8 @@ __device__ __forceinline__ void epilogue(const Params& p, f32x16_t (&acc)[C::FM]
                     u32x2_t v;
                     v.x = pack_bf16x2(a[4 * g + 0], a[4 * g + 1]);
                     v.y = pack_bf16x2(a[4 * g + 2], a[4 * g + 3]);
-                    const uint32_t chunk = (uint32_t)(((4 * jj + g) ^ (row_w & 7)) * 16);
-                    *(LDS_AS u32x2_t*)(strip + wbase + chunk - 0u) = v;
+                    const uint32_t chunk = (uint32_t)(((4 * jj + g) ^ ((row_w >> 1) & 7)) * 16);
+                    *(LDS_AS u32x2_t*)(strip + wbase + chunk) = v;
                 }
             }
             wait_lgkm0();
@@ -494,14 +591,80 @@ __device__ __forceinline__ void epilogue(const Params& p, f32x16_t (&acc)[C::FM]
             const uint32_t obase = opaque((uint32_t)gr0 * ldc2 + (uint32_t)gc * 2u);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                // rows rrow + 8u keep (row % 8) == (rrow % 8), so the swizzle is unchanged
-                const u32x4_t v = *(const LDS_AS u32x4_t*)(strip + rbase + u * 8 * 128);
+                // row rrow + 8u: (row / 2) mod 8 equals (rrow / 2) + 4u mod 8, i.e.
+                // the XOR term gains 4 for odd u; halves are swapped for u >= 2.
+                u32x4_t v = *(const LDS_AS u32x4_t*)(strip + ((rbase + u * 8 * 128) ^ ((u & 1) ? 64u : 0u)));
+                if (u >= 2)
+                    v = u32x4_t{v.z, v.w, v.x, v.y};
                 const bool ok = (gr0 + 8 * u < mrem) && (gc < nrem);
                 __builtin_amdgcn_raw_buffer_store_b128(v, rc, ok ? obase + (uint32_t)(8 * u) * ldc2 : kOOB, 0, 0);
             }
             wait_lgkm0();
         }
     }
+}
+
+// The same with a 32 x 32 strip (64-byte rows, one MFMA block per pass),
+// used when LDS is short.  Writes: the chunk (4 per row) is XORed with
+// (row / 4) mod 4 and halves are swapped for rows 16..31, so the 32 lanes of
+// a write cycle (32 rows, 4 rows per 256-byte bank window) hit 32 different
+// 8-byte slots.  Reads: 4 lanes cover one 64-byte row segment, 16 lanes (4
+// rows) per cycle on 16 different 16-byte slots.
+template <class C>
+__device__ __forceinline__ void epilogue_narrow(const Params& p, f32x16_t (&acc)[C::FM][C::FN], lds_char* strip,
+                                                int32_t m0, int32_t n0, int wm, int wn, int lane_in)
+{
+    const int lane = (int)opaque((uint32_t)lane_in);
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(p.C + ((int64_t)m0 * p.ldc + n0) * 2, ((p.M - m0 - 1) * p.ldc + (p.N - n0)) * 2);
+    const int row_w = lane & 31, half = lane >> 5;
+    const int32_t mrem = (int32_t)min(p.M - m0, (int64_t)C::BM);
+    const int32_t nrem = (int32_t)min(p.N - n0, (int64_t)C::BN);
+    const uint32_t ldc2 = (uint32_t)p.ldc * 2u;
+    const uint32_t wbase = opaque((uint32_t)(row_w * 64 + (half ^ (row_w >> 4)) * 8));
+    const int rrow = lane >> 2, rc4 = lane & 3;          // read slot u adds 16*u rows
+    const uint32_t rbase = opaque((uint32_t)(rrow * 64 + ((rc4 ^ ((rrow >> 2) & 3)) * 16)));
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (C::FM * C::FN * 16 > 128)
+                asm volatile("" : "+a"(acc[i][j]));
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x16_t& a = acc[i][j];
+                u32x2_t v;
+                v.x = pack_bf16x2(a[4 * g + 0], a[4 * g + 1]);
+                v.y = pack_bf16x2(a[4 * g + 2], a[4 * g + 3]);
+                const uint32_t chunk = (uint32_t)((g ^ ((row_w >> 2) & 3)) * 16);
+                *(LDS_AS u32x2_t*)(strip + wbase + chunk) = v;
+            }
+            wait_lgkm0();
+            const int gr0 = wm * C::TM + 32 * i + rrow;
+            const int gc = wn * C::TN + 32 * j + 8 * rc4;
+            const uint32_t obase = opaque((uint32_t)gr0 * ldc2 + (uint32_t)gc * 2u);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                u32x4_t v = *(const LDS_AS u32x4_t*)(strip + rbase + u * 16 * 64);
+                if (u == 1)
+                    v = u32x4_t{v.z, v.w, v.x, v.y};
+                const bool ok = (gr0 + 16 * u < mrem) && (gc < nrem);
+                __builtin_amdgcn_raw_buffer_store_b128(v, rc, ok ? obase + (uint32_t)(16 * u) * ldc2 : kOOB, 0, 0);
+            }
+            wait_lgkm0();
+        }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void store_tile(const Params& p, f32x16_t (&acc)[C::FM][C::FN], lds_char* strip,
+                                           int32_t m0, int32_t n0, int wm, int wn, int lane)
+{
+    if constexpr (C::EPI_W == 64)
+        epilogue<C>(p, acc, strip, m0, n0, wm, wn, lane);
+    else
+        epilogue_narrow<C>(p, acc, strip, m0, n0, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -530,61 +693,55 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
     const int32_t KT = p.k_steps;
     const int32_t total = n_tiles * KT;
 
+    if (total == 0)
+        return;
     Loader<C> ld;
     ld.init(p, n_tiles, w, lane);
 #pragma unroll
     for (int q = 0; q < C::S - 1; ++q)
-        if (q < total)
-            ld.issue_and_advance(p, smem + q * C::STAGE_BYTES, w, lane);
+        ld.issue_next(p, smem + q * C::STAGE_BYTES, w, lane);
 
     Frags<C> fr[2];
     lds_char* strip = smem + C::EPI_OFFSET + w * C::EPI_WAVE_BYTES;
+    auto stage_at = [&](int s) { return smem + s * C::STAGE_BYTES; };
 
-    // Make position c readable: RAW for every wave (and WAR for the stage the
-    // next load reuses, in BARRIER mode).  This wave's loads for positions
-    // c .. c+S-2 are outstanding (S-1 groups of LOADS), possibly followed by
-    // younger epilogue stores or spill traffic.  Waiting until at most
-    // LOADS*(S-2) vector-memory operations are outstanding leaves at most that
-    // many loads outstanding; loads complete in order, so group c has landed
-    // however the younger operations complete.  Near the end of the stream
-    // fewer groups are in flight and the wait drains everything.
+    // Ring bookkeeping for the position c being computed: its stage s_cur,
+    // the stage s_prev of position c - 1 (which the load of position
+    // c + S - 1 refills), and its generation gen = c / S.
+    int s_cur = 0, s_prev = C::S - 1;
+    uint32_t gen = 0;
     bool failed = false;
-    auto sync_position = [&](int32_t c) {
-        if (c + C::S - 2 < total)
-            wait_vmcnt<C::LOADS * (C::S - 2)>();
-        else
-            wait_vmcnt<0>();
+
+    // Make position c + 1 (stage s_nxt, generation g_nxt) readable.  This
+    // wave's DMA groups for positions c+1 .. c+S-1 are outstanding (S-1
+    // groups of LOADS; positions past the end of the stream are issued too, as
+    // empty loads), possibly followed by younger epilogue stores.  Waiting
+    // until at most LOADS*(S-2) vector-memory operations are outstanding
+    // leaves at most that many loads outstanding; loads complete in order, so
+    // the oldest group has landed however the younger operations complete.
+    // BARRIER: one s_barrier then covers the other waves' loads (RAW) and
+    // every wave's reads of the stage being refilled next (WAR).
+    auto sync_next = [&](int s_nxt, uint32_t g_nxt) {
+        wait_vmcnt<C::LOADS * (C::S - 2)>();
         if constexpr (C::SYNC == SYNC_BARRIER) {
             block_barrier();
         } else {
-            const int s = c % C::S;
-            arrive(full + s);
-            wait_counter(full + s, (uint32_t)(c / C::S + 1) * C::NW, failed);
+            arrive(full + s_nxt);
+            wait_counter(full + s_nxt, (g_nxt + 1) * C::NW, failed);
         }
-    };
-    // Issue the load of position q = c + S - 1 (into the stage position c-1 used).
-    auto issue_next = [&](int32_t c) {
-        const int32_t q = c + C::S - 1;
-        if (q >= total)
-            return;
-        const int s = q % C::S;
-        if constexpr (C::SYNC == SYNC_FLAGS) {
-            if (q >= C::S)
-                wait_counter(empty + s, (uint32_t)(q / C::S) * C::NW, failed);
-        }
-        ld.issue_and_advance(p, smem + s * C::STAGE_BYTES, w, lane);
     };
 
-    if (total == 0)
-        return;
-    sync_position(0);
-    if constexpr (C::SYNC == SYNC_BARRIER)
-        issue_next(0);
+    // A position's DMA is issued in KK parts, one per MFMA k-step region of
+    // the following stage, so the texture path never receives a burst of
+    // every wave's loads at once; its scalar preparation happens one position
+    // ahead, outside the MFMA regions.  Part 0 goes out right after the sync
+    // that frees its stage, parts 1..KK-1 with the next stage's MFMAs.
+    sync_next(0, 0);
+    typename Loader<C>::Prep fire_prep = ld.prepare_and_advance(p);      // position S - 1
+    ld.template fire<C::KK>(fire_prep, 0, stage_at(C::S - 1), w, lane);
+    typename Loader<C>::Prep next_prep = ld.prepare_and_advance(p);      // position S
     read_frags<C>(fr[0], smem, wm, wn, lane, 0);
-    if constexpr (C::SYNC == SYNC_FLAGS)
-        issue_next(0);
 
-    int32_t c = 0;
     for (int32_t it = 0; it < n_tiles; ++it) {
         int32_t tm, tn;
         tile_coords(p, b + it * G, G, tm, tn);
@@ -595,35 +752,53 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
             for (int j = 0; j < C::FN; ++j)
                 acc[i][j] = f32x16_t{};
 
-        for (int32_t kt = 0; kt < KT; ++kt, ++c) {
-            const lds_char* stage = smem + (c % C::S) * C::STAGE_BYTES;
-            const bool more = c + 1 < total;
+        for (int32_t kt = 0; kt < KT; ++kt) {
+            const lds_char* stage = stage_at(s_cur);
+            const int s_nxt = (s_cur + 1 == C::S) ? 0 : s_cur + 1;
+            const uint32_t g_nxt = gen + (s_nxt == 0 ? 1u : 0u);
 #pragma unroll
             for (int kk = 0; kk < C::KK; ++kk) {
                 if (kk + 1 < C::KK) {
                     read_frags<C>(fr[(kk + 1) & 1], stage, wm, wn, lane, kk + 1);
-                } else if (more) {
-                    // Last MFMA k-step of this stage: hand the stage back and
-                    // make the next position readable, then read its first
-                    // fragments, so the MFMA pipe has work across the sync.
+                    mfma_step<C>(acc, fr[kk & 1]);
+                    ld.template fire<C::KK>(fire_prep, kk + 1, stage_at(s_prev), w, lane);
+                    sched_interleave<C::FM * C::FN, frag_reads<C>(), C::LOADS / C::KK>();
+                } else if constexpr (C::SYNC == SYNC_BARRIER) {
+                    // Last MFMA k-step of this stage: one barrier hands the
+                    // stage back and makes the next position readable; then
+                    // the load of position c + S refills this stage and the
+                    // next stage's first fragments are read.  At the end of
+                    // the stream this runs once more on an empty position,
+                    // which keeps the block free of branches.
                     wait_lgkm0();
-                    if constexpr (C::SYNC == SYNC_FLAGS)
-                        arrive(empty + c % C::S);
-                    sync_position(c + 1);
-                    if constexpr (C::SYNC == SYNC_BARRIER)
-                        issue_next(c + 1);
-                    read_frags<C>(fr[0], smem + ((c + 1) % C::S) * C::STAGE_BYTES, wm, wn, lane, 0);
+                    sync_next(s_nxt, g_nxt);
+                    ld.template fire<C::KK>(next_prep, 0, stage_at(s_cur), w, lane);
+                    read_frags<C>(fr[0], stage_at(s_nxt), wm, wn, lane, 0);
+                    mfma_step<C>(acc, fr[kk & 1]);
+                    sched_interleave<C::FM * C::FN, frag_reads<C>(), C::LOADS / C::KK>();
+                } else {
+                    wait_lgkm0();
+                    arrive(empty + s_cur);
+                    sync_next(s_nxt, g_nxt);
+                    read_frags<C>(fr[0], stage_at(s_nxt), wm, wn, lane, 0);
+                    mfma_step<C>(acc, fr[kk & 1]);
+                    sched_interleave<C::FM * C::FN, frag_reads<C>(), 0>();
                 }
-                mfma_step<C>(acc, fr[kk & 1]);
+                __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (C::SYNC == SYNC_FLAGS) {
-                // WAR wait for the stage the next load reuses, placed after
-                // this wave's MFMAs for the stage are issued.
-                if (more)
-                    issue_next(c + 1);
+                // WAR: every wave has released this stage for position c;
+                // placed after this wave's MFMAs for the stage are issued.
+                wait_counter(empty + s_cur, (gen + 1) * C::NW, failed);
+                ld.template fire<C::KK>(next_prep, 0, stage_at(s_cur), w, lane);
             }
+            fire_prep = next_prep;
+            next_prep = ld.prepare_and_advance(p);
+            s_prev = s_cur;
+            s_cur = s_nxt;
+            gen = g_nxt;
         }
-        epilogue<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
+        store_tile<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
     }
 }
 
@@ -662,7 +837,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
             const int s = q % C::S;
             if (q >= C::S)
                 wait_counter(empty + s, (uint32_t)(q / C::S) * C::NCW, failed);
-            ld.issue_and_advance(p, smem + s * C::STAGE_BYTES, lw, lane);
+            ld.issue_next(p, smem + s * C::STAGE_BYTES, lw, lane);
             if (q >= D) {
                 wait_vmcnt<C::LOADS * D>();
                 arrive(full + (q - D) % C::S);
@@ -710,9 +885,12 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
                     }
                 }
                 mfma_step<C>(acc, fr[kk & 1]);
+                if (kk + 1 < C::KK)
+                    sched_interleave<C::FM * C::FN, frag_reads<C>(), 0>();
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        epilogue<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
+        store_tile<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
     }
 }
 
@@ -731,26 +909,59 @@ __global__ void __launch_bounds__(256) k_zero_fill(char* C, int64_t M, int64_t N
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
-using CfgB2N = Cfg<256, 256, 64, 2, 2, 2, SYNC_BARRIER, false, 0>;
-
-struct Variant {
-    int bm, bn, bk, waves_m, waves_n, producers;
+// The kernel instance used for each (sync mode, stage count).  All-wave modes
+// use a 256 x 256 tile over 8 waves (2 x 4, each 128 x 64, two waves per SIMD
+// so that one can issue MFMAs while the other waits on a load); the
+// wave-specialised mode uses 4 MFMA waves (2 x 2 over 256 x 128) and 4 loader
+// waves.  Two stages use BK = 64; three and four use BK = 32 (LDS budget).
+template <int SYNC, int S>
+struct Pick {
+    static constexpr int BK = (S == 2) ? 64 : 32;
+    template <bool BT>
+    using type = Cfg<256, (SYNC == SYNC_WAVESPEC) ? 128 : 256, BK, S, 2, (SYNC == SYNC_WAVESPEC) ? 2 : 4, SYNC, BT,
+                     (SYNC == SYNC_WAVESPEC) ? 4 : 0>;
 };
 
-Variant variant_for(int sync_mode, int stages)
+template <class C>
+int launch(const Params& p, int64_t grid, hipStream_t stream)
 {
-    if (sync_mode == GEMM_SYNC_WAVESPEC)
-        return Variant{256, 128, stages == 2 ? 64 : 32, 2, 2, 4};
-    return Variant{256, 256, stages == 2 ? 64 : 32, 2, 2, 0};
+    if constexpr (C::SYNC == SYNC_WAVESPEC)
+        hipLaunchKernelGGL(k_gemm_ws<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+    else
+        hipLaunchKernelGGL(k_gemm<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+struct Shape {
+    int bm, bn, bk, mfma_waves, producer_waves, threads, lds_bytes;
+};
+
+template <class C>
+Shape shape_of()
+{
+    return Shape{C::BM, C::BN, C::BK, C::NCW, C::NP, C::THREADS, C::LDS_BYTES};
+}
+
+// Calls f.template operator()<Cfg>() for the instance of (sync, stages, bt).
+template <class F>
+auto with_cfg(int sync_mode, int stages, bool bt, F&& f)
+{
+#define PTD_PICK(SY, ST)                                                            \
+    if (sync_mode == SY && stages == ST)                                            \
+        return bt ? f.template operator()<typename Pick<SY, ST>::template type<true>>() \
+                  : f.template operator()<typename Pick<SY, ST>::template type<false>>();
+    PTD_PICK(SYNC_BARRIER, 2) PTD_PICK(SYNC_BARRIER, 3) PTD_PICK(SYNC_BARRIER, 4)
+    PTD_PICK(SYNC_FLAGS, 2) PTD_PICK(SYNC_FLAGS, 3) PTD_PICK(SYNC_FLAGS, 4)
+    PTD_PICK(SYNC_WAVESPEC, 2) PTD_PICK(SYNC_WAVESPEC, 3)
+#undef PTD_PICK
+    return bt ? f.template operator()<typename Pick<SYNC_WAVESPEC, 4>::template type<true>>()
+              : f.template operator()<typename Pick<SYNC_WAVESPEC, 4>::template type<false>>();
 }
 
 int default_stages(int sync_mode)
 {
-    return sync_mode == GEMM_SYNC_WAVESPEC ? 4 : 2;
+    return sync_mode == GEMM_SYNC_FLAGS ? 2 : 4;
 }
-
-template <class C>
-int lds_bytes_of() { return C::LDS_BYTES; }
 
 struct DeviceInfo {
     bool probed = false;
@@ -814,61 +1025,10 @@ int validate_shape(int64_t M, int64_t N, int64_t K, int stages, int sync_mode)
 }
 
 int fill_plan(int64_t M, int64_t N, int64_t K, int b_transposed, int stages, int sync_mode, int cus,
-              gemm_bf16_plan_t* out);
-
-template <class C>
-int launch(const Params& p, int64_t grid, hipStream_t stream)
-{
-    if constexpr (C::SYNC == SYNC_WAVESPEC)
-        hipLaunchKernelGGL(k_gemm_ws<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
-    else
-        hipLaunchKernelGGL(k_gemm<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
-    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
-}
-
-template <bool BT>
-int dispatch(const Params& p, int64_t grid, int stages, int sync_mode, hipStream_t stream)
-{
-    switch (sync_mode) {
-    case GEMM_SYNC_BARRIER:
-        if (stages == 2) return launch<Cfg<256, 256, 64, 2, 2, 2, SYNC_BARRIER, BT, 0>>(p, grid, stream);
-        if (stages == 3) return launch<Cfg<256, 256, 32, 3, 2, 2, SYNC_BARRIER, BT, 0>>(p, grid, stream);
-        return launch<Cfg<256, 256, 32, 4, 2, 2, SYNC_BARRIER, BT, 0>>(p, grid, stream);
-    case GEMM_SYNC_FLAGS:
-        if (stages == 2) return launch<Cfg<256, 256, 64, 2, 2, 2, SYNC_FLAGS, BT, 0>>(p, grid, stream);
-        if (stages == 3) return launch<Cfg<256, 256, 32, 3, 2, 2, SYNC_FLAGS, BT, 0>>(p, grid, stream);
-        return launch<Cfg<256, 256, 32, 4, 2, 2, SYNC_FLAGS, BT, 0>>(p, grid, stream);
-    default:
-        if (stages == 2) return launch<Cfg<256, 128, 64, 2, 2, 2, SYNC_WAVESPEC, BT, 4>>(p, grid, stream);
-        if (stages == 3) return launch<Cfg<256, 128, 32, 3, 2, 2, SYNC_WAVESPEC, BT, 4>>(p, grid, stream);
-        return launch<Cfg<256, 128, 32, 4, 2, 2, SYNC_WAVESPEC, BT, 4>>(p, grid, stream);
-    }
-}
-
-template <bool BT>
-int lds_of(int stages, int sync_mode)
-{
-    switch (sync_mode) {
-    case GEMM_SYNC_BARRIER:
-        if (stages == 2) return Cfg<256, 256, 64, 2, 2, 2, SYNC_BARRIER, BT, 0>::LDS_BYTES;
-        if (stages == 3) return Cfg<256, 256, 32, 3, 2, 2, SYNC_BARRIER, BT, 0>::LDS_BYTES;
-        return Cfg<256, 256, 32, 4, 2, 2, SYNC_BARRIER, BT, 0>::LDS_BYTES;
-    case GEMM_SYNC_FLAGS:
-        if (stages == 2) return Cfg<256, 256, 64, 2, 2, 2, SYNC_FLAGS, BT, 0>::LDS_BYTES;
-        if (stages == 3) return Cfg<256, 256, 32, 3, 2, 2, SYNC_FLAGS, BT, 0>::LDS_BYTES;
-        return Cfg<256, 256, 32, 4, 2, 2, SYNC_FLAGS, BT, 0>::LDS_BYTES;
-    default:
-        if (stages == 2) return Cfg<256, 128, 64, 2, 2, 2, SYNC_WAVESPEC, BT, 4>::LDS_BYTES;
-        if (stages == 3) return Cfg<256, 128, 32, 3, 2, 2, SYNC_WAVESPEC, BT, 4>::LDS_BYTES;
-        return Cfg<256, 128, 32, 4, 2, 2, SYNC_WAVESPEC, BT, 4>::LDS_BYTES;
-    }
-}
-
-int fill_plan(int64_t M, int64_t N, int64_t K, int b_transposed, int stages, int sync_mode, int cus,
               gemm_bf16_plan_t* out)
 {
     const int st = stages == 0 ? default_stages(sync_mode) : stages;
-    const Variant v = variant_for(sync_mode, st);
+    const Shape v = with_cfg(sync_mode, st, b_transposed != 0, []<class C>() { return shape_of<C>(); });
     gemm_bf16_plan_t pl;
     memset(&pl, 0, sizeof pl);
     pl.bm = v.bm;
@@ -877,10 +1037,10 @@ int fill_plan(int64_t M, int64_t N, int64_t K, int b_transposed, int stages, int
     pl.stages = st;
     pl.sync_mode = sync_mode;
     pl.b_transposed = b_transposed ? 1 : 0;
-    pl.mfma_waves = v.waves_m * v.waves_n;
-    pl.producer_waves = v.producers;
-    pl.threads = 64 * (pl.mfma_waves + pl.producer_waves);
-    pl.lds_bytes = b_transposed ? lds_of<true>(st, sync_mode) : lds_of<false>(st, sync_mode);
+    pl.mfma_waves = v.mfma_waves;
+    pl.producer_waves = v.producer_waves;
+    pl.threads = v.threads;
+    pl.lds_bytes = v.lds_bytes;
     const int64_t tm = (M + v.bm - 1) / v.bm, tn = (N + v.bn - 1) / v.bn;
     pl.tiles = tm * tn;
     pl.k_steps = (K + v.bk - 1) / v.bk;
@@ -947,8 +1107,8 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
     p.tiles = (int32_t)pl.tiles;
     p.k_steps = (int32_t)pl.k_steps;
     p.group_m = 4;
-    return bt ? dispatch<true>(p, pl.grid, pl.stages, sync_mode, s)
-              : dispatch<false>(p, pl.grid, pl.stages, sync_mode, s);
+    const int64_t grid = pl.grid;
+    return with_cfg(sync_mode, pl.stages, bt, [&]<class C>() { return launch<C>(p, grid, s); });
 }
 
 }  // namespace
