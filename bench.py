@@ -52,7 +52,61 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device-to-device copy of known size (counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("GEMM_FETCH_CSV", "GEMM_WRITE_CSV",
+                                                            "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into the traffic "
+                         "summary read by the roofline line (no GPU needed)")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30
+
+
+def _counter_per_dispatch(path, counter, name_filter):
+    """Mean value of `counter` per dispatch of kernels whose name contains
+    name_filter, from a rocprofv3 counter_collection CSV (values summed over
+    counter instances within a dispatch)."""
+    import csv
+    per = {}
+    for row in csv.DictReader(open(path)):
+        if row["Counter_Name"] != counter or name_filter not in row["Kernel_Name"]:
+            continue
+        per[row["Dispatch_Id"]] = per.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise SystemExit("no %s samples for kernels matching %r in %s" % (counter, name_filter, path))
+    return sum(per.values()) / len(per), len(per)
+
+
+def summarize_traffic(paths):
+    """FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  Each is scaled by
+    the ratio of the known bytes a plain 1 GiB device copy moves to what the
+    same counter reads for that copy."""
+    gf, gw, cf, cw = paths
+    kname = "Cfg<256, 256, 32, 4, 2, 4, 0, true, 0>"     # barrier sync, 4 stages, B stored N x K
+    fetch_kib, n_f = _counter_per_dispatch(gf, "FETCH_SIZE", kname)
+    write_kib, n_w = _counter_per_dispatch(gw, "WRITE_SIZE", kname)
+    copy_f_kib, _ = _counter_per_dispatch(cf, "FETCH_SIZE", "copy")
+    copy_w_kib, _ = _counter_per_dispatch(cw, "WRITE_SIZE", "copy")
+    f_scale = COPY_BYTES / (copy_f_kib * 1024.0)
+    w_scale = COPY_BYTES / (copy_w_kib * 1024.0)
+    fetch = fetch_kib * 1024.0 * f_scale
+    write = write_kib * 1024.0 * w_scale
+    out = {
+        "kernel": "k_gemm %s" % kname,
+        "workload": "gemm8192_nk",
+        "kernel_source_sha256": kernel_sha(),
+        "fetch_bytes_per_launch": round(fetch),
+        "write_bytes_per_launch": round(write),
+        "hbm_bytes_per_launch": round(fetch + write),
+        "compulsory_bytes_per_launch": 2 * (3 * 8192 * 8192),
+        "raw_fetch_kib": fetch_kib, "raw_write_kib": write_kib,
+        "copy_fetch_kib": copy_f_kib, "copy_write_kib": copy_w_kib,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "dispatches": {"fetch": n_f, "write": n_w},
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def time_mode(bd, dA, dB, C, w, sync, stages, steps, warmup, torch):
@@ -109,6 +163,9 @@ def traffic_per_launch():
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the GEMM has no multi-GPU path in this build "
               "(run with --gpus 1)", file=sys.stderr)
@@ -126,7 +183,7 @@ def main():
     bd.library()
 
     if args.copy_calibration:
-        nbytes = 1 << 30
+        nbytes = COPY_BYTES
         src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(3):
