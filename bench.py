@@ -14,7 +14,10 @@ Also reports:
                 launch from the committed rocprofv3 counter summary when it
                 matches the current kernel source;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same product
-                (a few rows of C), on the host cores it actually uses.
+                (a few rows of C), on the host cores it actually uses;
+  reference     torch.matmul (hipBLASLt) on the same operands in the same
+                process, as context: under the board's power limit the
+                attainable clock varies from one GPU to the next.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sync all|barrier|flags|wavespec]
                        [--stages S] [--workload NAME] [--no-cpu-baseline] [--copy-calibration]
@@ -56,6 +59,10 @@ def parse():
                                                             "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into the traffic "
                          "summary read by the roofline line (no GPU needed)")
+    ap.add_argument("--traffic-kernel", default="Cfg<256, 256, 64, 2, 2, 4, 0, true, 0>",
+                    help="kernel configuration the counter CSVs were taken for (a substring of "
+                         "the kernel name: Cfg<BM, BN, BK, S, WM, WN, SYNC, B_NxK, loader waves>)")
+    ap.add_argument("--no-reference", action="store_true", help="skip the torch.matmul timing")
     return ap.parse_args()
 
 
@@ -77,12 +84,21 @@ def _counter_per_dispatch(path, counter, name_filter):
     return sum(per.values()) / len(per), len(per)
 
 
-def summarize_traffic(paths):
+SYNC_NAMES = {0: "barrier", 1: "flags", 2: "wavespec"}
+
+
+def cfg_fields(kname):
+    """(sync mode, stages) of a Cfg<BM, BN, BK, S, WM, WN, SYNC, ...> string."""
+    f = [x.strip() for x in kname[kname.index("<") + 1:].rstrip(">").split(",")]
+    return SYNC_NAMES[int(f[6])], int(f[3])
+
+
+def summarize_traffic(paths, kname):
     """FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  Each is scaled by
     the ratio of the known bytes a plain 1 GiB device copy moves to what the
     same counter reads for that copy."""
     gf, gw, cf, cw = paths
-    kname = "Cfg<256, 256, 32, 4, 2, 4, 0, true, 0>"     # barrier sync, 4 stages, B stored N x K
+    sync, stages = cfg_fields(kname)
     fetch_kib, n_f = _counter_per_dispatch(gf, "FETCH_SIZE", kname)
     write_kib, n_w = _counter_per_dispatch(gw, "WRITE_SIZE", kname)
     copy_f_kib, _ = _counter_per_dispatch(cf, "FETCH_SIZE", "copy")
@@ -93,6 +109,8 @@ def summarize_traffic(paths):
     write = write_kib * 1024.0 * w_scale
     out = {
         "kernel": "k_gemm %s" % kname,
+        "sync_mode": sync,
+        "stages": stages,
         "workload": "gemm8192_nk",
         "kernel_source_sha256": kernel_sha(),
         "fetch_bytes_per_launch": round(fetch),
@@ -151,20 +169,40 @@ def cpu_baseline(w, A, B, target_s):
                       "one bf16 rounding" % (rows - 1, rows, w.N, w.K, flops / 1e9, t)}
 
 
-def traffic_per_launch():
+def traffic_per_launch(workload, sync, stages):
+    """HBM bytes per launch from the committed counter summary, or None when
+    it was taken for another kernel configuration or an older kernel source."""
     try:
         info = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if info.get("kernel_source_sha256") != kernel_sha():
+    if (info.get("kernel_source_sha256") != kernel_sha() or info.get("workload") != workload
+            or info.get("sync_mode") != sync or info.get("stages") != stages):
         return None
     return info.get("hbm_bytes_per_launch")
+
+
+def reference_matmul(dA, dB, C, w, steps, warmup, torch):
+    """torch.matmul on the same operands (B^T as a view when B is stored N x K)."""
+    Bop = dB.t() if w.b_transposed else dB
+    for _ in range(warmup):
+        torch.matmul(dA, Bop, out=C)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        torch.matmul(dA, Bop, out=C)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"library": "torch.matmul (hipBLASLt)", "tflops": round(2.0 * w.M * w.N * w.K / ms / 1e9, 2),
+            "ms_per_step": round(ms, 4)}
 
 
 def main():
     args = parse()
     if args.summarize_traffic:
-        summarize_traffic(args.summarize_traffic)
+        summarize_traffic(args.summarize_traffic, args.traffic_kernel)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the GEMM has no multi-GPU path in this build "
@@ -238,10 +276,12 @@ def main():
         "sync_timeouts": timeouts,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_per_launch(),
+                     "traffic": traffic_per_launch(w.name, best, r["stages"]),
                      "kernel": "k_gemm (%s, %d stages)" % (best, r["stages"]) if best != "wavespec"
                                else "k_gemm_ws (%d stages)" % r["stages"]},
     }
+    if not args.no_reference:
+        line["reference"] = reference_matmul(dA, dB, C, w, args.steps, args.warmup, torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -65,6 +65,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <utility>
 
 #include "gemm_bf16.h"
 
@@ -215,14 +216,33 @@ __device__ __forceinline__ void tile_coords(const Params& p, int32_t t, int32_t 
     tn = col;
 }
 
+// The ring counters live in their own LDS words, apart from every stage.  Their
+// loads and atomic adds are written as inline assembly: issued as ordinary
+// LDS operations, the compiler's wait-count insertion cannot tell them apart
+// from the stages that in-flight global-to-LDS DMAs write, and waits for all
+// of the wave's outstanding loads before each one, which drains the ring.
+__device__ __forceinline__ uint32_t lds_addr(const lds_u32* p)
+{
+    return (uint32_t)(uintptr_t)p;
+}
+
+// The counter's current value (all lanes read the same word); the read is
+// complete when this returns.
+__device__ __forceinline__ uint32_t load_counter(const lds_u32* ctr)
+{
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(ctr)) : "memory");
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
 // Bounded wait until *ctr >= target.  A wait that gives up is counted and
 // sets the wave's sticky `failed` flag; once set, later waits return at once,
 // so the wave runs its (finite) loops to the end without blocking and the
 // kernel always terminates.  Results of such a launch are not meaningful.
-__device__ __forceinline__ void wait_counter(lds_u32* ctr, uint32_t target, bool& failed)
+__device__ __forceinline__ void wait_counter(const lds_u32* ctr, uint32_t target, bool& failed)
 {
     uint32_t spins = 0;
-    while (!failed && __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+    while (!failed && load_counter(ctr) < target) {
         if (++spins > kSpinLimit) {
             if ((threadIdx.x & 63) == 0)
                 atomicAdd(&g_sync_timeouts, 1ull);
@@ -233,11 +253,12 @@ __device__ __forceinline__ void wait_counter(lds_u32* ctr, uint32_t target, bool
     COMPILER_FENCE();
 }
 
+// One arrival (lane 0 adds 1).
 __device__ __forceinline__ void arrive(lds_u32* ctr)
 {
     COMPILER_FENCE();
     if ((threadIdx.x & 63) == 0)
-        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        asm volatile("ds_add_u32 %0, %1" ::"v"(lds_addr(ctr)), "v"(1u) : "memory");
     COMPILER_FENCE();
 }
 
@@ -278,19 +299,35 @@ __device__ __forceinline__ void wait_lgkm0()
 // byte count cannot express -- the k tail inside a row, and columns past N of
 // a K x N B tile -- are masked per lane with a select.
 //
-// issue() derives everything from the stream position q (tile q / KT, k-step
-// q % KT) without branches, and a position past the end of the stream gets
-// resources of zero bytes, so it writes zeros and touches no memory.  Every
-// call therefore emits exactly LOADS DMA instructions, which keeps the
-// vector-memory counter arithmetic of the waits exact, and the code around it
-// stays one basic block that the scheduler can interleave with MFMAs.
+// Every call emits exactly LOADS DMA instructions, also for a position past the
+// end of the stream (it gets resources of zero bytes, so it writes zeros and
+// touches no memory).  That keeps the vector-memory counter arithmetic of the
+// waits exact.
+//
+// The cursor steps from one position to the next with scalar adds.  Entering a
+// new tile needs its origin (tile_coords, a few integer divisions).  With
+// LONGK (at least S + 2 k-steps per tile) the origin of the cursor's next
+// tile is computed ahead, once per tile, by the compute loop
+// (prefetch_next_tile), so the step itself is a handful of selects and the
+// k-step loop body stays one basic block that the scheduler can interleave with
+// MFMAs.  Without LONGK the cursor can cross several tiles during one compute
+// tile, and the step enters the new tile itself (a uniform branch).
 // ---------------------------------------------------------------------------
-template <class C>
+// First DMA instruction of part `part` when a wave's `loads` instructions
+// for one position are cut into `nparts` contiguous runs.
+constexpr int part_begin(int part, int nparts, int loads) { return part * loads / nparts; }
+
+template <class C, bool LONGK>
 struct Loader {
     int32_t total;                // positions in this workgroup's stream
     int32_t n_tiles;
     uint32_t voffA[C::A_LOADS];
     uint32_t voffB[C::B_LOADS];
+    // One past the last byte of A and of B.  Each operand's resource runs from
+    // the position's origin to here, which excludes rows past M (A), rows past
+    // N (B stored N x K) and k-rows past K (B stored K x N).
+    const char* a_end;
+    const char* b_end;
 
     __device__ __forceinline__ static int slot(int t, int lw, int lane) { return (t * C::NLW + lw) * 64 + lane; }
     // Logical k offset (elements) of a K-contiguous slot.
@@ -322,9 +359,43 @@ struct Loader {
             else
                 voffB[t] = (uint32_t)(s / C::CPR_N) * ldb2 + (uint32_t)nofs_n(s) * 2u;
         }
+        a_end = p.A + ((p.M - 1) * p.lda + p.K) * 2;
+        b_end = C::BT ? p.B + ((p.N - 1) * p.ldb + p.K) * 2 : p.B + ((p.K - 1) * p.ldb + p.N) * 2;
         n_tiles = ntiles;
         total = ntiles * p.k_steps;
-        start(p);
+        q = 0;
+        kt = 0;
+        krem = (int32_t)p.K;
+        tile_origin(p, 0, pa, pb, nrem);
+        if constexpr (LONGK)
+            prefetch_next_tile(p, 1);
+        else
+            ti = 0;
+    }
+
+    // Origin of the workgroup's ti-th tile at k = 0 (ti is clamped to the last
+    // tile; positions past the end are never read).
+    __device__ __forceinline__ void tile_origin(const Params& p, int32_t t, const char*& a, const char*& b,
+                                                int32_t& n_left) const
+    {
+        int32_t tm = 0, tn = 0;
+        tile_coords(p, (int32_t)blockIdx.x + min(t, n_tiles - 1) * (int32_t)gridDim.x, (int32_t)gridDim.x, tm, tn);
+        const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+        a = p.A + m0 * p.lda * 2;
+        b = C::BT ? p.B + n0 * p.ldb * 2 : p.B + n0 * 2;
+        n_left = (int32_t)(p.N - n0);
+    }
+
+    // LONGK: the origin of the tile the cursor enters next.  Called at the
+    // start of compute tile t with t + 1.  The compute loop prepares position
+    // c + S + 1 at the end of k-step c, and preparing the last position of a
+    // tile is the step that moves the cursor onto the next tile's origin.  So
+    // the cursor enters tile t + 1 at the end of k-step (t + 1) * KT - S - 2,
+    // which lies inside compute tile t (after this call, before the next one)
+    // exactly when KT >= S + 2.
+    __device__ __forceinline__ void prefetch_next_tile(const Params& p, int32_t t)
+    {
+        tile_origin(p, t, pa_n, pb_n, nrem_n);
     }
 
     // Scalar part of issuing one position: the two buffer resources and the
@@ -334,42 +405,15 @@ struct Loader {
         int32_t krem, nrem;
     };
 
-    // The load cursor: position q, its tile (index ti in this workgroup's
-    // list) and k-step kt, and the operand addresses and byte counts at that
-    // position.  Advancing by one k-step is a few scalar adds; only the step
-    // into a new tile recomputes the tile origin (a uniform branch taken once
-    // per tile).
-    int32_t q, ti, kt;
+    // The cursor: position q, k-step kt within its tile, the operand origins
+    // at that position, and the k / n extents left for the edge masks.
+    int32_t q, kt, ti;
     int32_t krem, nrem;
     const char* pa;
     const char* pb;
-    int64_t abytes, bbytes;
-
-    __device__ __forceinline__ void enter_tile(const Params& p)
-    {
-        int32_t tm = 0, tn = 0;
-        tile_coords(p, (int32_t)blockIdx.x + min(ti, n_tiles - 1) * (int32_t)gridDim.x, (int32_t)gridDim.x, tm, tn);
-        const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
-        krem = (int32_t)p.K;
-        nrem = (int32_t)(p.N - n0);
-        pa = p.A + m0 * p.lda * 2;
-        abytes = ((p.M - m0 - 1) * p.lda + p.K) * 2;
-        if constexpr (C::BT) {
-            pb = p.B + n0 * p.ldb * 2;
-            bbytes = ((p.N - n0 - 1) * p.ldb + p.K) * 2;
-        } else {
-            pb = p.B + n0 * 2;
-            bbytes = ((p.K - 1) * p.ldb + nrem) * 2;
-        }
-    }
-
-    __device__ __forceinline__ void start(const Params& p)
-    {
-        q = 0;
-        ti = 0;
-        kt = 0;
-        enter_tile(p);
-    }
+    const char* pa_n;
+    const char* pb_n;
+    int32_t nrem_n;
 
     // The cursor's position prepared for issue, then the cursor steps on.
     // Positions at or past the end of the stream get empty resources.
@@ -379,45 +423,57 @@ struct Loader {
         Prep r;
         r.krem = krem;
         r.nrem = nrem;
-        r.ra = make_rsrc(pa, live ? abytes : 0);
-        r.rb = make_rsrc(pb, live ? bbytes : 0);
+        r.ra = make_rsrc(pa, live ? (int64_t)(a_end - pa) : 0);
+        r.rb = make_rsrc(pb, live ? (int64_t)(b_end - pb) : 0);
         ++q;
-        if (++kt == p.k_steps) {
-            kt = 0;
-            ++ti;
-            enter_tile(p);
+        constexpr int64_t kstep = (int64_t)C::BK * 2;
+        const int64_t bstep = C::BT ? kstep : kstep * p.ldb;
+        if constexpr (LONGK) {
+            const bool wrap = ++kt == p.k_steps;
+            kt = wrap ? 0 : kt;
+            krem = wrap ? (int32_t)p.K : krem - C::BK;
+            nrem = wrap ? nrem_n : nrem;
+            pa = wrap ? pa_n : pa + kstep;
+            pb = wrap ? pb_n : pb + bstep;
         } else {
-            constexpr int64_t kstep = (int64_t)C::BK * 2;
-            krem -= C::BK;
-            pa += kstep;
-            abytes -= kstep;
-            const int64_t bstep = C::BT ? kstep : kstep * p.ldb;
-            pb += bstep;
-            bbytes -= bstep;
+            if (++kt == p.k_steps) {
+                kt = 0;
+                krem = (int32_t)p.K;
+                tile_origin(p, ++ti, pa, pb, nrem);
+            } else {
+                krem -= C::BK;
+                pa += kstep;
+                pb += bstep;
+            }
         }
         return r;
     }
 
-    // Issue part `part` of NPARTS of this wave's DMA instructions for a
-    // prepared position (A and B instructions split evenly).
+    // DMA instruction t (0 <= t < LOADS; A first, then B) of this wave for a
+    // prepared position.
+    __device__ __forceinline__ void fire_one(const Prep& r, int t, lds_char* stage, int lw, int lane) const
+    {
+        if (t < C::A_LOADS) {
+            const bool ok = kofs_k(slot(t, lw, lane)) < r.krem;
+            lds_dma16(r.ra, stage + (t * C::NLW + lw) * 1024, ok ? voffA[t] : kOOB);
+        } else {
+            const int tb = t - C::A_LOADS;
+            const int s = slot(tb, lw, lane);
+            const bool ok = C::BT ? (kofs_k(s) < r.krem) : (nofs_n(s) < r.nrem);
+            lds_dma16(r.rb, stage + C::A_BYTES + (tb * C::NLW + lw) * 1024, ok ? voffB[tb] : kOOB);
+        }
+    }
+
+    // Part `part` of NPARTS of the wave's DMA instructions for a prepared
+    // position: the LOADS instructions cut into NPARTS contiguous runs.
     template <int NPARTS>
     __device__ __forceinline__ void fire(const Prep& r, int part, lds_char* stage, int lw, int lane) const
     {
-        static_assert(C::A_LOADS % NPARTS == 0 && C::B_LOADS % NPARTS == 0, "even split");
-        constexpr int NA = C::A_LOADS / NPARTS, NB = C::B_LOADS / NPARTS;
+        static_assert(NPARTS >= 1 && NPARTS <= C::LOADS, "parts");
 #pragma unroll
-        for (int x = 0; x < NA; ++x) {
-            const int t = part * NA + x;
-            const bool ok = kofs_k(slot(t, lw, lane)) < r.krem;
-            lds_dma16(r.ra, stage + (t * C::NLW + lw) * 1024, ok ? voffA[t] : kOOB);
-        }
-#pragma unroll
-        for (int x = 0; x < NB; ++x) {
-            const int t = part * NB + x;
-            const int s = slot(t, lw, lane);
-            const bool ok = C::BT ? (kofs_k(s) < r.krem) : (nofs_n(s) < r.nrem);
-            lds_dma16(r.rb, stage + C::A_BYTES + (t * C::NLW + lw) * 1024, ok ? voffB[t] : kOOB);
-        }
+        for (int t = 0; t < C::LOADS; ++t)
+            if (t >= part_begin(part, NPARTS, C::LOADS) && t < part_begin(part + 1, NPARTS, C::LOADS))
+                fire_one(r, t, stage, lw, lane);
     }
 
     // Issue all of this wave's DMA for the cursor's position into `stage`
@@ -434,91 +490,149 @@ struct Loader {
 template <class C>
 struct Frags {
     bf16x8_t a[C::FM];
-    bf16x8_t b[C::FN];
+    bf16x8_t b[C::FN];       // B stored N x K
+    i16x4_t bh[C::FN][2];    // B stored K x N: the two transposing reads per block
 };
 
-// Fragments of MFMA k-step kk from a stage.  The MFMA runs with the B
-// fragment as its first operand, so accumulator block (i, j) holds
-// C^T: lane l owns column m = l%32 and rows n = 8*(r/4) + 4*(l/32) + r%4.
+template <class C>
+constexpr int frag_reads() { return C::FM + (C::BT ? 1 : 2) * C::FN; }
+
+// The frag_reads<C>() LDS read instructions of MFMA k-step kk, one at a time.
+// The MFMA runs with the B fragment as its first operand, so accumulator
+// block (i, j) holds C^T: lane l owns column m = l%32 and rows
+// n = 8*(r/4) + 4*(l/32) + r%4.
 //
 // K-contiguous tiles: lane l reads row (base + 32*i + l%32), logical chunk
 // 2*kk + l/32.  Every block starts on a multiple of 8 rows, so the swizzle
 // term depends on l only and the block index moves the address by a
 // constant.
+//
+// B stored K x N, ds_read_b64_tr_b16: within each 16-lane group, lane 4r+q
+// addresses k-row r, columns 4q..4q+3 of a 4 x 16 block; lane i receives
+// column i for the 4 k-rows.  Two reads give the 8 k values of the operand.
+// The k-row of lane (r, q) is 16*kk + 8*(l/32) + 4*hh + r, so its swizzle
+// term is 4*r; the logical chunk of block j is 4*(wn*TN/32 + j) +
+// 2*((l>>4)&1) + q/2, and the XOR only touches the 4*(wn*TN/32 + j) part:
+// it becomes 4*((wn*TN/32 + j) ^ r).
+template <class C>
+struct FragReader {
+    uint32_t a_off, b_off;
+    int r;
+
+    __device__ __forceinline__ FragReader(int wm, int wn, int lane, int kk)
+    {
+        const int h = lane >> 5;
+        const int r32 = lane & 31;
+        const uint32_t xk = (uint32_t)(((2 * kk + h) ^ swz_k<C::BK>(r32)) << 4);
+        a_off = opaque((uint32_t)((wm * C::TM + r32) * (C::BK * 2)) + xk);
+        if constexpr (C::BT) {
+            b_off = opaque((uint32_t)((wn * C::TN + r32) * (C::BK * 2)) + xk) + C::A_BYTES;
+            r = 0;
+        } else {
+            const int g = lane >> 4, i16 = lane & 15, q = i16 & 3;
+            r = i16 >> 2;
+            const int low = 2 * (g & 1) + (q >> 1);
+            const uint32_t krow0 = (uint32_t)(16 * kk + 8 * (g >> 1) + r);
+            b_off = opaque(krow0 * (C::BN * 2) + (uint32_t)(low * 16 + (q & 1) * 8)) + C::A_BYTES;
+        }
+    }
+
+    // Read instruction d: A blocks first, then B.
+    __device__ __forceinline__ void read(Frags<C>& f, const lds_char* stage, int wn, int d) const
+    {
+        if (d < C::FM) {
+            f.a[d] = *(const LDS_AS bf16x8_t*)(stage + a_off + d * (32 * C::BK * 2));
+        } else if constexpr (C::BT) {
+            const int j = d - C::FM;
+            f.b[j] = *(const LDS_AS bf16x8_t*)(stage + b_off + j * (32 * C::BK * 2));
+        } else {
+            const int j = (d - C::FM) >> 1, hh = (d - C::FM) & 1;
+            const int J = wn * (C::TN / 32) + j;
+            const uint32_t jchunk = (uint32_t)(4 * (J ^ r)) * 16u;
+            const lds_char* addr = stage + b_off + (uint32_t)(4 * hh * (C::BN * 2)) + jchunk;
+            f.bh[j][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)addr);
+        }
+    }
+};
+
 template <class C>
 __device__ __forceinline__ void read_frags(Frags<C>& f, const lds_char* stage, int wm, int wn, int lane, int kk)
 {
-    const int h = lane >> 5;
-    const int r32 = lane & 31;
-    const uint32_t xk = (uint32_t)(((2 * kk + h) ^ swz_k<C::BK>(r32)) << 4);
-    const uint32_t rowa = opaque((uint32_t)((wm * C::TM + r32) * (C::BK * 2)) + xk);
+    const FragReader<C> rd(wm, wn, lane, kk);
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-        f.a[i] = *(const LDS_AS bf16x8_t*)(stage + rowa + i * (32 * C::BK * 2));
-    const lds_char* sb = stage + C::A_BYTES;
-    if constexpr (C::BT) {
-        const uint32_t rowb = opaque((uint32_t)((wn * C::TN + r32) * (C::BK * 2)) + xk);
+    for (int d = 0; d < frag_reads<C>(); ++d)
+        rd.read(f, stage, wn, d);
+}
+
+// Slots of one MFMA k-step region of M MFMAs, D LDS fragment reads and V
+// global-to-LDS DMA issues.  Slot i holds MFMA i, LDS read i while reads
+// remain (they are for the next k-step, so they have the rest of this
+// k-step's MFMAs to land), and the DMA issues that fall on it, V spread
+// evenly from the first slot on.  The texture path of a CU drains one 1 KiB
+// DMA issue in tens of cycles; bunching the issues of all waves (they leave
+// the barrier together) fills its queue and stalls every wave's instruction
+// issue, MFMAs included.
+//
+// DMA writes to and reads from LDS keep their program order (the compiler
+// cannot tell the ring stages apart), so emit_memops issues them in slot
+// order, and sched_slots then only has to place the MFMAs between them.
+template <int M, int V, int I>
+constexpr int slot_dma_begin() { return (I * V + M - 1) / M; }
+
+template <int M, int D, int V, int I = 0, class RD, class FR>
+__device__ __forceinline__ void emit_memops(RD&& rd, FR&& fr)
+{
+    if constexpr (I < M || I < D) {
+        if constexpr (I < D)
+            rd(I);
+        if constexpr (I < M) {
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-            f.b[j] = *(const LDS_AS bf16x8_t*)(sb + rowb + j * (32 * C::BK * 2));
-    } else {
-        // ds_read_b64_tr_b16: within each 16-lane group, lane 4r+q addresses
-        // k-row r, columns 4q..4q+3 of a 4 x 16 block; lane i receives column
-        // i for the 4 k-rows.  Two reads give the 8 k values of the operand.
-        // The k-row of lane (r, q) is 16*kk + 8*(l/32) + 4*hh + r, so its
-        // swizzle term is 4*r; the logical chunk of block j is
-        // 4*(wn*TN/32 + j) + 2*((l>>4)&1) + q/2, and the XOR only touches the
-        // 4*(wn*TN/32 + j) part: it becomes 4*((wn*TN/32 + j) ^ r).
-        const int g = lane >> 4, i16 = lane & 15, r = i16 >> 2, q = i16 & 3;
-        const int low = 2 * (g & 1) + (q >> 1);
-        const uint32_t krow0 = (uint32_t)(16 * kk + 8 * (g >> 1) + r);
-        const uint32_t base = opaque(krow0 * (C::BN * 2) + (uint32_t)(low * 16 + (q & 1) * 8));
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-            const int J = wn * (C::TN / 32) + j;
-            const int jchunk = 4 * (J ^ r);
-            i16x4_t part[2];
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const lds_char* addr = sb + base + (uint32_t)(4 * hh * (C::BN * 2)) + (uint32_t)(jchunk * 16);
-                part[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)addr);
-            }
-            const i16x8_t v = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-            f.b[j] = __builtin_bit_cast(bf16x8_t, v);
+            for (int v = slot_dma_begin<M, V, I>(); v < slot_dma_begin<M, V, I + 1>(); ++v)
+                fr(v);
         }
+        emit_memops<M, D, V, I + 1>(rd, fr);
     }
 }
 
-// Instruction order inside one MFMA k-step region: the scheduler is asked to
-// alternate one MFMA with one LDS fragment read (the reads are for the next
-// k-step, so they have the rest of this k-step's MFMAs to land), then pair
-// the remaining MFMAs with up to two global-to-LDS DMA issues.  With one wave
-// per SIMD this keeps the matrix pipe fed while the reads and loads go out.
-template <int M, int D, int V>
-__device__ __forceinline__ void sched_interleave()
+// The memory operations of one region: D fragment reads from stage `src`
+// and DMA instructions t0 .. t0 + V - 1 of a prepared position into stage
+// `dst`.  The two stages always differ, and saying so (restrict) lets the
+// compiler keep the reads apart from the in-flight DMA writes: without it,
+// every read that follows a DMA in program order waits for all of the wave's
+// outstanding loads.
+template <int M, int D, int V, class C, class LD>
+__device__ __forceinline__ void region_memops(const FragReader<C>& rdr, Frags<C>& f, const lds_char* __restrict__ src,
+                                              int wn, const LD& ld, const typename LD::Prep& prep, int t0,
+                                              lds_char* __restrict__ dst, int w, int lane)
 {
-    if constexpr (M > 0) {
+    emit_memops<M, D, V>([&](int d) { rdr.read(f, src, wn, d); },
+                         [&](int v) { ld.fire_one(prep, t0 + v, dst, w, lane); });
+}
+
+template <int M, int D, int V, int I = 0>
+__device__ __forceinline__ void sched_slots()
+{
+    if constexpr (I < M) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
-        if constexpr (D > 0) {
+        if constexpr (I < D)
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // LDS read
-            sched_interleave<M - 1, D - 1, V>();
-        } else if constexpr (V > 0) {
-            constexpr int n = V >= 2 ? 2 : 1;
-            __builtin_amdgcn_sched_group_barrier(0x020, n, 0);      // VMEM read
-            sched_interleave<M - 1, 0, V - n>();
-        } else {
-            sched_interleave<M - 1, 0, 0>();
-        }
-    } else {
-        if constexpr (D > 0)
-            __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
-        if constexpr (V > 0)
-            __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
+        constexpr int nv = slot_dma_begin<M, V, I + 1>() - slot_dma_begin<M, V, I>();
+        if constexpr (nv > 0)
+            __builtin_amdgcn_sched_group_barrier(0x020, nv, 0);     // VMEM read
+        sched_slots<M, D, V, I + 1>();
+    } else if constexpr (D > M) {
+        __builtin_amdgcn_sched_group_barrier(0x100, D - M, 0);
     }
 }
 
 template <class C>
-constexpr int frag_reads() { return C::FM + (C::BT ? 1 : 2) * C::FN; }
+__device__ __forceinline__ bf16x8_t b_frag(const Frags<C>& f, int j)
+{
+    if constexpr (C::BT)
+        return f.b[j];
+    const i16x8_t v = __builtin_shufflevector(f.bh[j][0], f.bh[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
+}
 
 template <class C>
 __device__ __forceinline__ void mfma_step(f32x16_t (&acc)[C::FM][C::FN], const Frags<C>& f)
@@ -527,7 +641,7 @@ __device__ __forceinline__ void mfma_step(f32x16_t (&acc)[C::FM][C::FN], const F
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b_frag<C>(f, j), f.a[i], acc[i][j], 0, 0, 0);
 }
 
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
@@ -670,7 +784,7 @@ __device__ __forceinline__ void store_tile(const Params& p, f32x16_t (&acc)[C::F
 // ---------------------------------------------------------------------------
 // Kernel: every wave loads and computes (GEMM_SYNC_BARRIER, GEMM_SYNC_FLAGS).
 // ---------------------------------------------------------------------------
-template <class C>
+template <class C, bool LONGK>
 __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
 {
     static_assert(C::SYNC != SYNC_WAVESPEC, "wave-specialised configs use k_gemm_ws");
@@ -695,7 +809,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
 
     if (total == 0)
         return;
-    Loader<C> ld;
+    Loader<C, LONGK> ld;
     ld.init(p, n_tiles, w, lane);
 #pragma unroll
     for (int q = 0; q < C::S - 1; ++q)
@@ -731,20 +845,33 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
         }
     };
 
-    // A position's DMA is issued in KK parts, one per MFMA k-step region of
-    // the following stage, so the texture path never receives a burst of
-    // every wave's loads at once; its scalar preparation happens one position
-    // ahead, outside the MFMA regions.  Part 0 goes out right after the sync
-    // that frees its stage, parts 1..KK-1 with the next stage's MFMAs.
+    // A position's DMA is issued in parts, spread over the MFMA regions of the
+    // following stage, so the texture path never receives a burst of every
+    // wave's loads at once: part 0 right after the barrier that frees its
+    // stage, the others with the next stage's first MFMA regions.  With three
+    // or more stages there is one part per region (KK).  With two stages the
+    // data is needed one stage later, so there are two parts: after the
+    // barrier and in the next stage's first region.  The cursor's scalar work
+    // for the position after next happens between k-steps, after the
+    // barrier's wave has issued its MFMAs (a few dozen scalar instructions
+    // ahead of the barrier delay every wave's arrival).
+    //
+    // FLAGS refills a stage only after waiting for its release at the end of
+    // a k-step, so the whole position goes out in the first MFMA region of
+    // the next k-step.
+    constexpr int NPARTS = (C::SYNC == SYNC_FLAGS) ? 1 : (C::S == 2) ? 2 : C::KK;
     sync_next(0, 0);
-    typename Loader<C>::Prep fire_prep = ld.prepare_and_advance(p);      // position S - 1
-    ld.template fire<C::KK>(fire_prep, 0, stage_at(C::S - 1), w, lane);
-    typename Loader<C>::Prep next_prep = ld.prepare_and_advance(p);      // position S
+    typename Loader<C, LONGK>::Prep fire_prep = ld.prepare_and_advance(p);      // position S - 1
+    if constexpr (C::SYNC == SYNC_BARRIER)
+        ld.template fire<NPARTS>(fire_prep, 0, stage_at(C::S - 1), w, lane);
+    typename Loader<C, LONGK>::Prep next_prep = ld.prepare_and_advance(p);      // position S
     read_frags<C>(fr[0], smem, wm, wn, lane, 0);
 
     for (int32_t it = 0; it < n_tiles; ++it) {
         int32_t tm, tn;
         tile_coords(p, b + it * G, G, tm, tn);
+        if constexpr (LONGK)
+            ld.prefetch_next_tile(p, it + 1);
         f32x16_t acc[C::FM][C::FN];
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
@@ -756,41 +883,55 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
             const lds_char* stage = stage_at(s_cur);
             const int s_nxt = (s_cur + 1 == C::S) ? 0 : s_cur + 1;
             const uint32_t g_nxt = gen + (s_nxt == 0 ? 1u : 0u);
-#pragma unroll
-            for (int kk = 0; kk < C::KK; ++kk) {
-                if (kk + 1 < C::KK) {
-                    read_frags<C>(fr[(kk + 1) & 1], stage, wm, wn, lane, kk + 1);
+            // MFMA k-step region kk of this stage (kk is a constant).
+            auto region = [&]<int kk>() {
+                constexpr int M = C::FM * C::FN, D = frag_reads<C>();
+                if constexpr (kk + 1 < C::KK) {
+                    // Fragments of k-step kk + 1; a part of the load of
+                    // position c + S - 1 into the stage of position c - 1
+                    // (BARRIER: part kk + 1, part 0 went out after the last
+                    // barrier; FLAGS: the whole position in region 0).
+                    constexpr int part = (C::SYNC == SYNC_BARRIER) ? kk + 1 : kk;
+                    constexpr int t0 = part < NPARTS ? part_begin(part, NPARTS, C::LOADS) : 0;
+                    constexpr int V = part < NPARTS ? part_begin(part + 1, NPARTS, C::LOADS) - t0 : 0;
+                    const FragReader<C> rdr(wm, wn, lane, kk + 1);
+                    region_memops<M, D, V>(rdr, fr[(kk + 1) & 1], stage, wn, ld, fire_prep, t0, stage_at(s_prev), w,
+                                           lane);
                     mfma_step<C>(acc, fr[kk & 1]);
-                    ld.template fire<C::KK>(fire_prep, kk + 1, stage_at(s_prev), w, lane);
-                    sched_interleave<C::FM * C::FN, frag_reads<C>(), C::LOADS / C::KK>();
+                    sched_slots<M, D, V>();
                 } else if constexpr (C::SYNC == SYNC_BARRIER) {
                     // Last MFMA k-step of this stage: one barrier hands the
                     // stage back and makes the next position readable; then
-                    // the load of position c + S refills this stage and the
-                    // next stage's first fragments are read.  At the end of
-                    // the stream this runs once more on an empty position,
-                    // which keeps the block free of branches.
+                    // part 0 of the load of position c + S refills this stage
+                    // and the next stage's first fragments are read.  At the
+                    // end of the stream this runs once more on an empty
+                    // position, which keeps the block free of branches.
                     wait_lgkm0();
                     sync_next(s_nxt, g_nxt);
-                    ld.template fire<C::KK>(next_prep, 0, stage_at(s_cur), w, lane);
-                    read_frags<C>(fr[0], stage_at(s_nxt), wm, wn, lane, 0);
+                    constexpr int V = part_begin(1, NPARTS, C::LOADS);
+                    const FragReader<C> rdr(wm, wn, lane, 0);
+                    region_memops<M, D, V>(rdr, fr[0], stage_at(s_nxt), wn, ld, next_prep, 0, stage_at(s_cur), w, lane);
                     mfma_step<C>(acc, fr[kk & 1]);
-                    sched_interleave<C::FM * C::FN, frag_reads<C>(), C::LOADS / C::KK>();
+                    sched_slots<M, D, V>();
                 } else {
                     wait_lgkm0();
                     arrive(empty + s_cur);
                     sync_next(s_nxt, g_nxt);
-                    read_frags<C>(fr[0], stage_at(s_nxt), wm, wn, lane, 0);
+                    const FragReader<C> rdr(wm, wn, lane, 0);
+                    region_memops<M, D, 0>(rdr, fr[0], stage_at(s_nxt), wn, ld, next_prep, 0, stage_at(s_cur), w, lane);
                     mfma_step<C>(acc, fr[kk & 1]);
-                    sched_interleave<C::FM * C::FN, frag_reads<C>(), 0>();
+                    sched_slots<M, D, 0>();
                 }
                 __builtin_amdgcn_sched_barrier(0);
-            }
+            };
+            [&]<int... KS>(std::integer_sequence<int, KS...>) {
+                (region.template operator()<KS>(), ...);
+            }(std::make_integer_sequence<int, C::KK>{});
             if constexpr (C::SYNC == SYNC_FLAGS) {
                 // WAR: every wave has released this stage for position c;
                 // placed after this wave's MFMAs for the stage are issued.
+                // Its refill (position c + S) goes out in the next k-step.
                 wait_counter(empty + s_cur, (gen + 1) * C::NW, failed);
-                ld.template fire<C::KK>(next_prep, 0, stage_at(s_cur), w, lane);
             }
             fire_prep = next_prep;
             next_prep = ld.prepare_and_advance(p);
@@ -830,7 +971,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
         // later (the wave keeps D + 1 positions of loads in flight).
         const int lw = w - C::NCW;
         constexpr int D = (C::S - 1 < 2) ? C::S - 1 : 2;
-        Loader<C> ld;
+        Loader<C, false> ld;
         ld.init(p, n_tiles, lw, lane);
         bool failed = false;
         for (int32_t q = 0; q < total; ++q) {
@@ -886,7 +1027,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
                 }
                 mfma_step<C>(acc, fr[kk & 1]);
                 if (kk + 1 < C::KK)
-                    sched_interleave<C::FM * C::FN, frag_reads<C>(), 0>();
+                    sched_slots<C::FM * C::FN, frag_reads<C>(), 0>();
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -927,8 +1068,10 @@ int launch(const Params& p, int64_t grid, hipStream_t stream)
 {
     if constexpr (C::SYNC == SYNC_WAVESPEC)
         hipLaunchKernelGGL(k_gemm_ws<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+    else if (p.k_steps >= C::S + 2)
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm<C, true>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
     else
-        hipLaunchKernelGGL(k_gemm<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm<C, false>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
@@ -958,9 +1101,13 @@ auto with_cfg(int sync_mode, int stages, bool bt, F&& f)
               : f.template operator()<typename Pick<SYNC_WAVESPEC, 4>::template type<false>>();
 }
 
+// Two stages of 64-wide k-steps for the all-wave modes: each DMA instruction
+// then covers 8 rows of 128 bytes instead of 16 rows of 64, which the texture
+// path serves markedly faster.  The wave-specialised mode has 256 x 128 tiles
+// and keeps four 32-wide stages.
 int default_stages(int sync_mode)
 {
-    return sync_mode == GEMM_SYNC_FLAGS ? 2 : 4;
+    return sync_mode == GEMM_SYNC_WAVESPEC ? 4 : 2;
 }
 
 struct DeviceInfo {

@@ -112,6 +112,32 @@ def test_small_parity_all_modes(case, bt, small_refs):
             np.testing.assert_array_equal(got, first, err_msg="modes disagree bitwise")
 
 
+@pytest.mark.parametrize("bt", [False, True], ids=["kn", "nk"])
+@pytest.mark.parametrize("K", [72, 104, 136, 168, 200], ids=lambda k: "K%d" % k)
+def test_many_tiles_per_workgroup(K, bt):
+    """More output tiles than workgroups (33 x 17 = 561 tiles of 256 x 256, so
+    each persistent workgroup walks 2-3 tiles, ragged in M and N), at k-step
+    counts on both sides of the point where the load cursor switches from
+    entering each new tile itself (fewer than stages + 2 k-steps) to having the
+    next tile's origin computed ahead by the compute loop (stages + 2 or more):
+    K = 72, 104, 136, 168, 200 give 3, 4, 5, 6, 7 k-steps of 32 (3 and 4
+    stages) and 2, 2, 3, 3, 4 k-steps of 64 (2 stages).  A workgroup's third
+    tile is where a stale next-tile origin shows: it then repeats the second
+    tile."""
+    M, N = 8448 - 40, 4104
+    A, B = make_operands(M, N, K, b_transposed=bt, seed=K + (1000 if bt else 0))
+    ref = oracle.load().gemm_bf16(bits(A), bits(B), bt)
+    dA, dB = A.cuda(), B.cuda()
+    first = None
+    for sync, stages in MODES:
+        got = run(dA, dB, bt, sync, stages)
+        assert_within_tol(got, ref, "%s/%d" % (sync, stages))
+        if first is None:
+            first = got
+        else:
+            np.testing.assert_array_equal(got, first, err_msg="modes disagree bitwise")
+
+
 def test_layouts_and_modes_bit_identical():
     M, N, K = 520, 776, 392
     A, B = make_operands(M, N, K, b_transposed=False, seed=99)
