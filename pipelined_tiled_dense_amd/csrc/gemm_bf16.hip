@@ -115,6 +115,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
 }
 
+// Byte count for a resource that starts `rem` bytes (rem > 0) before the end
+// of its operand.  Counts of 2^31 and more are capped at kMaxRecords; the cap
+// never cuts off an access the kernel makes, whose offsets stay below
+// 2^31 - 2^23 (leading dimensions are at most 2^22 elements).
+__device__ __forceinline__ uint32_t records(uint64_t rem)
+{
+    return (rem >> 31) ? kMaxRecords : (uint32_t)rem;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_n(const void* base, uint32_t nrec)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nrec, kRsrcWord3);
+}
+
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint32_t voff)
 {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)dst, 16, voff, 0, 0, 0);
@@ -155,6 +169,12 @@ struct Cfg {
     static constexpr int EPI_OFFSET = RING_BYTES;
     static constexpr int FLAG_OFFSET = EPI_OFFSET + NCW * EPI_WAVE_BYTES;
     static constexpr int LDS_BYTES = FLAG_OFFSET + FLAG_BYTES;
+    // Where the all-wave kernel steps its load cursor: inside the second MFMA
+    // region of a k-step when there are three or more regions, else after
+    // the k-step (one position further ahead).  The branch-free cursor needs
+    // at least this many k-steps per tile.
+    static constexpr bool PREP_IN_REGION = KK >= 3;
+    static constexpr int LONGK_MIN_KT = S + (PREP_IN_REGION ? 1 : 2);
 
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(KK % 2 == 0, "fragment double buffering assumes an even number of MFMA k-steps");
@@ -306,7 +326,7 @@ __device__ __forceinline__ void wait_lgkm0()
 //
 // The cursor steps from one position to the next with scalar adds.  Entering a
 // new tile needs its origin (tile_coords, a few integer divisions).  With
-// LONGK (at least S + 2 k-steps per tile) the origin of the cursor's next
+// LONGK (at least LONGK_MIN_KT k-steps per tile) the origin of the cursor's next
 // tile is computed ahead, once per tile, by the compute loop
 // (prefetch_next_tile), so the step itself is a handful of selects and the
 // k-step loop body stays one basic block that the scheduler can interleave with
@@ -388,11 +408,12 @@ struct Loader {
 
     // LONGK: the origin of the tile the cursor enters next.  Called at the
     // start of compute tile t with t + 1.  The compute loop prepares position
-    // c + S + 1 at the end of k-step c, and preparing the last position of a
-    // tile is the step that moves the cursor onto the next tile's origin.  So
-    // the cursor enters tile t + 1 at the end of k-step (t + 1) * KT - S - 2,
-    // which lies inside compute tile t (after this call, before the next one)
-    // exactly when KT >= S + 2.
+    // c + S (or c + S + 1, without PREP_IN_REGION) during k-step c, and
+    // preparing the last position of a tile is the step that moves the cursor
+    // onto the next tile's origin.  So the cursor enters tile t + 1 during
+    // k-step (t + 1) * KT - S - 1 (or one earlier), which lies inside compute
+    // tile t (after this call, before the next one) exactly when
+    // KT >= LONGK_MIN_KT.
     __device__ __forceinline__ void prefetch_next_tile(const Params& p, int32_t t)
     {
         tile_origin(p, t, pa_n, pb_n, nrem_n);
@@ -423,8 +444,8 @@ struct Loader {
         Prep r;
         r.krem = krem;
         r.nrem = nrem;
-        r.ra = make_rsrc(pa, live ? (int64_t)(a_end - pa) : 0);
-        r.rb = make_rsrc(pb, live ? (int64_t)(b_end - pb) : 0);
+        r.ra = rsrc_n(pa, live ? records((uint64_t)(a_end - pa)) : 0u);
+        r.rb = rsrc_n(pb, live ? records((uint64_t)(b_end - pb)) : 0u);
         ++q;
         constexpr int64_t kstep = (int64_t)C::BK * 2;
         const int64_t bstep = C::BT ? kstep : kstep * p.ldb;
@@ -609,17 +630,23 @@ __device__ __forceinline__ void region_memops(const FragReader<C>& rdr, Frags<C>
                          [&](int v) { ld.fire_one(prep, t0 + v, dst, w, lane); });
 }
 
-template <int M, int D, int V, int I = 0>
+// SALU scalar instructions may follow each MFMA (the load cursor's step, in
+// the region that carries it).
+template <int M, int D, int V, int SALU = 0, int I = 0>
 __device__ __forceinline__ void sched_slots()
 {
     if constexpr (I < M) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
         if constexpr (I < D)
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // LDS read
+        // Scalar work before the DMA issue: a DMA's LDS address (M0) is
+        // itself set by a scalar instruction.
+        if constexpr (SALU > 0)
+            __builtin_amdgcn_sched_group_barrier(0x004, SALU, 0);   // SALU
         constexpr int nv = slot_dma_begin<M, V, I + 1>() - slot_dma_begin<M, V, I>();
         if constexpr (nv > 0)
             __builtin_amdgcn_sched_group_barrier(0x020, nv, 0);     // VMEM read
-        sched_slots<M, D, V, I + 1>();
+        sched_slots<M, D, V, SALU, I + 1>();
     } else if constexpr (D > M) {
         __builtin_amdgcn_sched_group_barrier(0x100, D - M, 0);
     }
@@ -851,20 +878,30 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
     // stage, the others with the next stage's first MFMA regions.  With three
     // or more stages there is one part per region (KK).  With two stages the
     // data is needed one stage later, so there are two parts: after the
-    // barrier and in the next stage's first region.  The cursor's scalar work
-    // for the position after next happens between k-steps, after the
-    // barrier's wave has issued its MFMAs (a few dozen scalar instructions
-    // ahead of the barrier delay every wave's arrival).
+    // barrier and in the next stage's first region.
     //
     // FLAGS refills a stage only after waiting for its release at the end of
     // a k-step, so the whole position goes out in the first MFMA region of
     // the next k-step.
     constexpr int NPARTS = (C::SYNC == SYNC_FLAGS) ? 1 : (C::S == 2) ? 2 : C::KK;
+    //
+    // The load cursor's step is several dozen scalar instructions, and all
+    // waves reach it together; they queue for the CU's one scalar unit.  With
+    // three or more MFMA regions per k-step (PREP_IN_REGION), the cursor
+    // prepares position c + S inside region 1 of k-step c, its instructions
+    // spread between the MFMAs; next_prep (position c + S - 1) becomes
+    // fire_prep at the top of the k-step.  With two regions that pattern
+    // cannot be scheduled next to the region's DMA issues, so the cursor
+    // prepares position c + S + 1 after the k-step instead (ahead of the
+    // barrier its instructions would delay every wave's arrival).
+    constexpr bool PIR = C::PREP_IN_REGION;
     sync_next(0, 0);
     typename Loader<C, LONGK>::Prep fire_prep = ld.prepare_and_advance(p);      // position S - 1
     if constexpr (C::SYNC == SYNC_BARRIER)
         ld.template fire<NPARTS>(fire_prep, 0, stage_at(C::S - 1), w, lane);
-    typename Loader<C, LONGK>::Prep next_prep = ld.prepare_and_advance(p);      // position S
+    typename Loader<C, LONGK>::Prep next_prep = fire_prep;
+    if constexpr (!PIR)
+        next_prep = ld.prepare_and_advance(p);                                  // position S
     read_frags<C>(fr[0], smem, wm, wn, lane, 0);
 
     for (int32_t it = 0; it < n_tiles; ++it) {
@@ -883,9 +920,14 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
             const lds_char* stage = stage_at(s_cur);
             const int s_nxt = (s_cur + 1 == C::S) ? 0 : s_cur + 1;
             const uint32_t g_nxt = gen + (s_nxt == 0 ? 1u : 0u);
+            if constexpr (PIR)
+                fire_prep = next_prep;
             // MFMA k-step region kk of this stage (kk is a constant).
             auto region = [&]<int kk>() {
                 constexpr int M = C::FM * C::FN, D = frag_reads<C>();
+                constexpr int SALU = (PIR && kk == 1) ? 6 : 0;
+                if constexpr (PIR && kk == 1)
+                    next_prep = ld.prepare_and_advance(p);
                 if constexpr (kk + 1 < C::KK) {
                     // Fragments of k-step kk + 1; a part of the load of
                     // position c + S - 1 into the stage of position c - 1
@@ -898,7 +940,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
                     region_memops<M, D, V>(rdr, fr[(kk + 1) & 1], stage, wn, ld, fire_prep, t0, stage_at(s_prev), w,
                                            lane);
                     mfma_step<C>(acc, fr[kk & 1]);
-                    sched_slots<M, D, V>();
+                    sched_slots<M, D, V, SALU>();
                 } else if constexpr (C::SYNC == SYNC_BARRIER) {
                     // Last MFMA k-step of this stage: one barrier hands the
                     // stage back and makes the next position readable; then
@@ -933,8 +975,10 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
                 // Its refill (position c + S) goes out in the next k-step.
                 wait_counter(empty + s_cur, (gen + 1) * C::NW, failed);
             }
-            fire_prep = next_prep;
-            next_prep = ld.prepare_and_advance(p);
+            if constexpr (!PIR) {
+                fire_prep = next_prep;
+                next_prep = ld.prepare_and_advance(p);
+            }
             s_prev = s_cur;
             s_cur = s_nxt;
             gen = g_nxt;
@@ -1068,7 +1112,7 @@ int launch(const Params& p, int64_t grid, hipStream_t stream)
 {
     if constexpr (C::SYNC == SYNC_WAVESPEC)
         hipLaunchKernelGGL(k_gemm_ws<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
-    else if (p.k_steps >= C::S + 2)
+    else if (p.k_steps >= C::LONGK_MIN_KT)
         hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm<C, true>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
     else
         hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm<C, false>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);

@@ -118,12 +118,11 @@ def test_many_tiles_per_workgroup(K, bt):
     """More output tiles than workgroups (33 x 17 = 561 tiles of 256 x 256, so
     each persistent workgroup walks 2-3 tiles, ragged in M and N), at k-step
     counts on both sides of the point where the load cursor switches from
-    entering each new tile itself (fewer than stages + 2 k-steps) to having the
-    next tile's origin computed ahead by the compute loop (stages + 2 or more):
-    K = 72, 104, 136, 168, 200 give 3, 4, 5, 6, 7 k-steps of 32 (3 and 4
-    stages) and 2, 2, 3, 3, 4 k-steps of 64 (2 stages).  A workgroup's third
-    tile is where a stale next-tile origin shows: it then repeats the second
-    tile."""
+    entering each new tile itself to having the next tile's origin computed
+    ahead by the compute loop: stages + 1 k-steps for 2 stages of 64 (K = 72,
+    104, 136, 168, 200 give 2, 2, 3, 3, 4), stages + 2 for 3 and 4 stages of
+    32 (3, 4, 5, 6, 7).  A workgroup's third tile is where a stale next-tile
+    origin shows: it then repeats the second tile."""
     M, N = 8448 - 40, 4104
     A, B = make_operands(M, N, K, b_transposed=bt, seed=K + (1000 if bt else 0))
     ref = oracle.load().gemm_bf16(bits(A), bits(B), bt)
