@@ -268,7 +268,10 @@ __device__ __forceinline__ void wait_counter(const lds_u32* ctr, uint32_t target
                 atomicAdd(&g_sync_timeouts, 1ull);
             failed = true;
         }
-        __builtin_amdgcn_s_sleep(1);
+        // The first polls go back to back (one LDS round trip each); a wait
+        // that lasts longer sleeps between polls.
+        if (spins > 8)
+            __builtin_amdgcn_s_sleep(1);
     }
     COMPILER_FENCE();
 }
@@ -1012,9 +1015,13 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
     if (w >= C::NCW) {
         // Loader wave: one flat loop over (tile, k-step) positions.  The data
         // of position q is announced on full[] once it has landed, D positions
-        // later (the wave keeps D + 1 positions of loads in flight).
+        // later (the wave keeps D + 1 positions of loads in flight).  Issuing
+        // position q waits for the release of position q - S, so announcing
+        // q - D then depends on the consumers having finished q - S; D = S - 2
+        // leaves them one computed stage of slack (a larger lag would make
+        // every stage wait for that release-issue-announce chain).
         const int lw = w - C::NCW;
-        constexpr int D = (C::S - 1 < 2) ? C::S - 1 : 2;
+        constexpr int D = (C::S - 2 < 2) ? C::S - 2 : 2;
         Loader<C, false> ld;
         ld.init(p, n_tiles, lw, lane);
         bool failed = false;
@@ -1098,10 +1105,12 @@ __global__ void __launch_bounds__(256) k_zero_fill(char* C, int64_t M, int64_t N
 // use a 256 x 256 tile over 8 waves (2 x 4, each 128 x 64, two waves per SIMD
 // so that one can issue MFMAs while the other waits on a load); the
 // wave-specialised mode uses 4 MFMA waves (2 x 2 over 256 x 128) and 4 loader
-// waves.  Two stages use BK = 64; three and four use BK = 32 (LDS budget).
+// waves.  The k-step width follows the LDS budget (see BK below).
 template <int SYNC, int S>
 struct Pick {
-    static constexpr int BK = (S == 2) ? 64 : 32;
+    // 64-wide k-steps (128-byte rows per DMA instruction) wherever the ring
+    // fits: two stages of 256 x 256, three of the wave-specialised 256 x 128.
+    static constexpr int BK = (S == 2 || (SYNC == SYNC_WAVESPEC && S == 3)) ? 64 : 32;
     template <bool BT>
     using type = Cfg<256, (SYNC == SYNC_WAVESPEC) ? 128 : 256, BK, S, 2, (SYNC == SYNC_WAVESPEC) ? 2 : 4, SYNC, BT,
                      (SYNC == SYNC_WAVESPEC) ? 4 : 0>;
@@ -1145,13 +1154,13 @@ auto with_cfg(int sync_mode, int stages, bool bt, F&& f)
               : f.template operator()<typename Pick<SYNC_WAVESPEC, 4>::template type<false>>();
 }
 
-// Two stages of 64-wide k-steps for the all-wave modes: each DMA instruction
-// then covers 8 rows of 128 bytes instead of 16 rows of 64, which the texture
-// path serves markedly faster.  The wave-specialised mode has 256 x 128 tiles
-// and keeps four 32-wide stages.
+// 64-wide k-steps: each DMA instruction then covers 8 rows of 128 bytes
+// instead of 16 rows of 64, which the texture path serves markedly faster.
+// The LDS holds two such stages of the all-wave modes' 256 x 256 tile and
+// three of the wave-specialised mode's 256 x 128.
 int default_stages(int sync_mode)
 {
-    return sync_mode == GEMM_SYNC_WAVESPEC ? 4 : 2;
+    return sync_mode == GEMM_SYNC_WAVESPEC ? 3 : 2;
 }
 
 struct DeviceInfo {
