@@ -32,8 +32,20 @@
  *
  * Memory ownership: A, B and C are device pointers owned by the caller, on
  * the HIP device that is current when the call is made.  The library never
- * allocates, frees or retains them, and keeps no per-call allocation.  A and
- * B are only read.  C must not overlap A or B.
+ * allocates, frees or retains them.  A and B are only read.  C must not
+ * overlap A or B.
+ *
+ * Split k range: a shape with fewer output tiles than half the compute units
+ * (counted in 256 x 256 tiles) and a long k range -- K a multiple of 64 * s
+ * and K / s >= 512 for some s >= 2 -- is computed as s chunks of k (s <= 16)
+ * so that the GPU fills.  Each output tile's chunks are summed in fp32, in
+ * chunk order, after one fp32 chain per chunk; the result differs from the
+ * unsplit sum only by fp32 rounding, is the same for every sync mode and
+ * stage count, and is deterministic.  The fp32 partial tiles
+ * (plan.workspace_bytes) are allocated stream-ordered on `stream`
+ * (hipMallocAsync) and released (hipFreeAsync) by the same call; a failed
+ * allocation returns GEMM_ERR_DEVICE.  Not a section of the pages: the
+ * persistent schedule there assumes enough output tiles.
  *
  * Asynchrony: a call validates its arguments on the host, enqueues its work
  * on `stream` (a hipStream_t; NULL means the null stream) and returns.  A
@@ -85,8 +97,10 @@ typedef struct gemm_bf16_plan {
     int32_t threads;          /* threads per workgroup */
     int32_t lds_bytes;        /* LDS per workgroup */
     int64_t tiles;            /* output tiles: ceil(M/bm) * ceil(N/bn) */
-    int64_t k_steps;          /* ceil(K/bk) */
-    int64_t grid;             /* persistent workgroups launched: min(tiles, compute units) */
+    int64_t k_steps;          /* k-steps per work item: ceil((K / k_splits) / bk) */
+    int64_t grid;             /* persistent workgroups launched: min(tiles * k_splits, compute units) */
+    int64_t k_splits;         /* chunks the k range is split into (1: no split) */
+    int64_t workspace_bytes;  /* fp32 partial tiles of a split call (0 without a split) */
 } gemm_bf16_plan_t;
 
 /*

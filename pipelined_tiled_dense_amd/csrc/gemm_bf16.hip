@@ -77,6 +77,7 @@ typedef LDS_AS uint32_t lds_u32;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((ext_vector_type(8))) short i16x8_t;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
@@ -186,12 +187,18 @@ struct Cfg {
     static_assert(S >= 2 && S <= 4, "stages");
 };
 
+// A work item is one output tile and one chunk of the k range.  Without a
+// split (splits == 1) the chunk is all of K and work items are output tiles.
 struct Params {
     const char* A;
     const char* B;
     char* C;
+    float* partial;                   // fp32 partial tiles, splits > 1 only
     int64_t M, N, K, lda, ldb, ldc;   // elements
-    int32_t tiles_m, tiles_n, tiles, k_steps;
+    int64_t ksplit;                   // k elements per chunk (K when splits == 1)
+    int32_t tiles_m, tiles_n, tiles_mn, splits;
+    int32_t tiles;                    // work items: tiles_mn * splits
+    int32_t k_steps;                  // k-steps per work item
     int32_t group_m;
 };
 
@@ -214,9 +221,11 @@ __device__ __forceinline__ int swz_k(int row)
 // the 16 (row, chunk) pairs over all 16 bank groups.
 __device__ __forceinline__ int swz_n(int krow) { return (krow & 3) << 2; }
 
-// Output tile (tm, tn) of tile id t, for a grid of G persistent workgroups
-// (workgroup b takes ids b, b + G, b + 2G, ...).  Branch-free scalar code.
-__device__ __forceinline__ void tile_coords(const Params& p, int32_t t, int32_t G, int32_t& tm, int32_t& tn)
+// Output tile (tm, tn) and k chunk sp of work item t, for a grid of G
+// persistent workgroups (workgroup b takes ids b, b + G, b + 2G, ...).
+// Branch-free scalar code.
+__device__ __forceinline__ void tile_coords(const Params& p, int32_t t, int32_t G, int32_t& tm, int32_t& tn,
+                                            int32_t& sp)
 {
     // The hardware deals workgroups to the 8 XCDs round-robin; within every
     // full round of G ids, give XCD x a contiguous run of G/8 ids.
@@ -224,13 +233,16 @@ __device__ __forceinline__ void tile_coords(const Params& p, int32_t t, int32_t 
     const int32_t b = t - round * G;
     const int32_t remapped = round * G + (b & 7) * (G >> 3) + (b >> 3);
     const int32_t L = ((G & 7) == 0 && (round + 1) * G <= p.tiles) ? remapped : t;
-    // Grouped raster: runs of group_m tile rows, walked column by column, so a
-    // run of consecutive ids covers a compact block of output tiles.
+    // Chunk-major: consecutive ids share a k chunk.  Within a chunk, a grouped
+    // raster: runs of group_m tile rows, walked column by column, so a run of
+    // consecutive ids covers a compact block of output tiles.
+    sp = L / p.tiles_mn;
+    const int32_t Lt = L - sp * p.tiles_mn;
     const int32_t per_group = p.group_m * p.tiles_n;
-    const int32_t grp = L / per_group;
+    const int32_t grp = Lt / per_group;
     const int32_t first_m = grp * p.group_m;
     const int32_t gm = min(p.tiles_m - first_m, p.group_m);
-    const int32_t in = L - grp * per_group;
+    const int32_t in = Lt - grp * per_group;
     const int32_t col = in / gm;
     tm = first_m + (in - col * gm);
     tn = col;
@@ -388,25 +400,27 @@ struct Loader {
         total = ntiles * p.k_steps;
         q = 0;
         kt = 0;
-        krem = (int32_t)p.K;
-        tile_origin(p, 0, pa, pb, nrem);
+        tile_origin(p, 0, pa, pb, nrem, krem);
         if constexpr (LONGK)
             prefetch_next_tile(p, 1);
         else
             ti = 0;
     }
 
-    // Origin of the workgroup's ti-th tile at k = 0 (ti is clamped to the last
-    // tile; positions past the end are never read).
+    // Origin of the workgroup's t-th work item: its tile at the first k of
+    // its chunk (t is clamped to the last item; positions past the end are
+    // never read), and the n and k extents left from there for the masks.
     __device__ __forceinline__ void tile_origin(const Params& p, int32_t t, const char*& a, const char*& b,
-                                                int32_t& n_left) const
+                                                int32_t& n_left, int32_t& k_left) const
     {
-        int32_t tm = 0, tn = 0;
-        tile_coords(p, (int32_t)blockIdx.x + min(t, n_tiles - 1) * (int32_t)gridDim.x, (int32_t)gridDim.x, tm, tn);
-        const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
-        a = p.A + m0 * p.lda * 2;
-        b = C::BT ? p.B + n0 * p.ldb * 2 : p.B + n0 * 2;
+        int32_t tm = 0, tn = 0, sp = 0;
+        tile_coords(p, (int32_t)blockIdx.x + min(t, n_tiles - 1) * (int32_t)gridDim.x, (int32_t)gridDim.x, tm, tn,
+                    sp);
+        const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN, k0 = (int64_t)sp * p.ksplit;
+        a = p.A + (m0 * p.lda + k0) * 2;
+        b = C::BT ? p.B + (n0 * p.ldb + k0) * 2 : p.B + (k0 * p.ldb + n0) * 2;
         n_left = (int32_t)(p.N - n0);
+        k_left = (int32_t)(p.K - k0);
     }
 
     // LONGK: the origin of the tile the cursor enters next.  Called at the
@@ -419,7 +433,7 @@ struct Loader {
     // KT >= LONGK_MIN_KT.
     __device__ __forceinline__ void prefetch_next_tile(const Params& p, int32_t t)
     {
-        tile_origin(p, t, pa_n, pb_n, nrem_n);
+        tile_origin(p, t, pa_n, pb_n, nrem_n, krem_n);
     }
 
     // Scalar part of issuing one position: the two buffer resources and the
@@ -437,7 +451,7 @@ struct Loader {
     const char* pb;
     const char* pa_n;
     const char* pb_n;
-    int32_t nrem_n;
+    int32_t nrem_n, krem_n;
 
     // The cursor's position prepared for issue, then the cursor steps on.
     // Positions at or past the end of the stream get empty resources.
@@ -455,15 +469,14 @@ struct Loader {
         if constexpr (LONGK) {
             const bool wrap = ++kt == p.k_steps;
             kt = wrap ? 0 : kt;
-            krem = wrap ? (int32_t)p.K : krem - C::BK;
+            krem = wrap ? krem_n : krem - C::BK;
             nrem = wrap ? nrem_n : nrem;
             pa = wrap ? pa_n : pa + kstep;
             pb = wrap ? pb_n : pb + bstep;
         } else {
             if (++kt == p.k_steps) {
                 kt = 0;
-                krem = (int32_t)p.K;
-                tile_origin(p, ++ti, pa, pb, nrem);
+                tile_origin(p, ++ti, pa, pb, nrem, krem);
             } else {
                 krem -= C::BK;
                 pa += kstep;
@@ -811,6 +824,75 @@ __device__ __forceinline__ void store_tile(const Params& p, f32x16_t (&acc)[C::F
         epilogue_narrow<C>(p, acc, strip, m0, n0, wm, wn, lane);
 }
 
+// Split k range: the work item's fp32 accumulators go, unrounded, to its
+// partial tile (BM x BN fp32, row-major, in the workspace); k_reduce_splits
+// adds the chunks later.  Lane l of block (i, j) holds row l%32 and, per
+// group of 4 registers, 4 consecutive columns: one 16-byte store each.
+template <class C>
+__device__ __forceinline__ void store_partial(const Params& p, f32x16_t (&acc)[C::FM][C::FN], int32_t widx, int wm,
+                                              int wn, int lane_in)
+{
+    const int lane = (int)opaque((uint32_t)lane_in);
+    const __amdgpu_buffer_rsrc_t rp = rsrc_n(p.partial + (int64_t)widx * (C::BM * C::BN), C::BM * C::BN * 4u);
+    const int m = lane & 31, h = lane >> 5;
+    const uint32_t base = opaque((uint32_t)(((wm * C::TM + m) * C::BN + wn * C::TN + 4 * h) * 4));
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (C::FM * C::FN * 16 > 128)
+                asm volatile("" : "+a"(acc[i][j]));
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x16_t& a = acc[i][j];
+                // Whole vectors only: a bit cast of a single vector element
+                // is not what this needs.
+                const f32x4_t v = {a[4 * g + 0], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+                const uint32_t off = base + (uint32_t)((32 * i * C::BN + 32 * j + 8 * g) * 4);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rp, off, 0, 0);
+            }
+        }
+    }
+}
+
+// C = bf16_rne(sum of the work items' partial tiles over the k chunks, in
+// chunk order).  One thread per 8 consecutive output columns (N % 8 == 0).
+__global__ void __launch_bounds__(256) k_reduce_splits(Params p, int32_t bm, int32_t bn)
+{
+    const int64_t groups_per_row = p.N / 8;
+    const int64_t total = p.M * groups_per_row;
+    const int64_t tile_elems = (int64_t)bm * bn;
+    const int64_t chunk_stride = (int64_t)p.tiles_mn * tile_elems;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = q / groups_per_row;
+        const int64_t c0 = (q - r * groups_per_row) * 8;
+        const int64_t tm = r / bm, tn = c0 / bn;
+        const float* src = p.partial + (tm * p.tiles_n + tn) * tile_elems + (r - tm * bm) * bn + (c0 - tn * bn);
+        float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int32_t sp = 0; sp < p.splits; ++sp) {
+            // 32-byte aligned: tiles, rows and column groups are multiples of 8 floats.
+            const f32x4_t* part = (const f32x4_t*)(src + sp * chunk_stride);
+            const f32x4_t lo = part[0], hi = part[1];
+            sum[0] += lo.x;
+            sum[1] += lo.y;
+            sum[2] += lo.z;
+            sum[3] += lo.w;
+            sum[4] += hi.x;
+            sum[5] += hi.y;
+            sum[6] += hi.z;
+            sum[7] += hi.w;
+        }
+        u32x4_t out;
+        out.x = pack_bf16x2(sum[0], sum[1]);
+        out.y = pack_bf16x2(sum[2], sum[3]);
+        out.z = pack_bf16x2(sum[4], sum[5]);
+        out.w = pack_bf16x2(sum[6], sum[7]);
+        *(u32x4_t*)(p.C + (r * p.ldc + c0) * 2) = out;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Kernel: every wave loads and computes (GEMM_SYNC_BARRIER, GEMM_SYNC_FLAGS).
 // ---------------------------------------------------------------------------
@@ -909,7 +991,8 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
 
     for (int32_t it = 0; it < n_tiles; ++it) {
         int32_t tm, tn;
-        tile_coords(p, b + it * G, G, tm, tn);
+        int32_t sp;
+        tile_coords(p, b + it * G, G, tm, tn, sp);
         if constexpr (LONGK)
             ld.prefetch_next_tile(p, it + 1);
         f32x16_t acc[C::FM][C::FN];
@@ -986,7 +1069,10 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
             s_cur = s_nxt;
             gen = g_nxt;
         }
-        store_tile<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
+        if (p.splits > 1)
+            store_partial<C>(p, acc, (sp * p.tiles_mn + tm * p.tiles_n + tn), wm, wn, lane);
+        else
+            store_tile<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
     }
 }
 
@@ -1054,7 +1140,8 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
     int32_t c = 0;
     for (int32_t it = 0; it < n_tiles; ++it) {
         int32_t tm, tn;
-        tile_coords(p, b + it * G, G, tm, tn);
+        int32_t sp;
+        tile_coords(p, b + it * G, G, tm, tn, sp);
         f32x16_t acc[C::FM][C::FN];
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
@@ -1082,7 +1169,10 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        store_tile<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
+        if (p.splits > 1)
+            store_partial<C>(p, acc, (sp * p.tiles_mn + tm * p.tiles_n + tn), wm, wn, lane);
+        else
+            store_tile<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
     }
 }
 
@@ -1208,6 +1298,7 @@ int64_t span_bytes(int64_t rows, int64_t cols, int64_t ld)
 }
 
 constexpr int64_t kMaxLd = (int64_t)1 << 22;
+constexpr int64_t kMaxSplits = 16;
 
 int validate_shape(int64_t M, int64_t N, int64_t K, int stages, int sync_mode)
 {
@@ -1222,6 +1313,25 @@ int validate_shape(int64_t M, int64_t N, int64_t K, int stages, int sync_mode)
     if (M > ((int64_t)1 << 31) - 1 || N > ((int64_t)1 << 31) - 1 || K > ((int64_t)1 << 31) - 1)
         return GEMM_ERR_UNSUPPORTED_SHAPE;
     return GEMM_OK;
+}
+
+// Number of k chunks.  Shapes with fewer output tiles than half the compute
+// units (counted at 256 x 256, so that every sync mode splits alike and the
+// results stay bit-identical across modes) and a long k range are split into
+// equal chunks of a multiple of 64 elements, each at least 512 long, so that
+// tiles x chunks work items can fill the GPU.
+int64_t choose_splits(int64_t M, int64_t N, int64_t K, int cus)
+{
+    const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
+    if (tiles256 <= 0 || 2 * tiles256 >= cus)
+        return 1;
+    int64_t s = cus / tiles256;
+    if (s > kMaxSplits)
+        s = kMaxSplits;
+    for (; s >= 2; --s)
+        if (K % (64 * s) == 0 && K / s >= 512)
+            return s;
+    return 1;
 }
 
 int fill_plan(int64_t M, int64_t N, int64_t K, int b_transposed, int stages, int sync_mode, int cus,
@@ -1243,9 +1353,12 @@ int fill_plan(int64_t M, int64_t N, int64_t K, int b_transposed, int stages, int
     pl.lds_bytes = v.lds_bytes;
     const int64_t tm = (M + v.bm - 1) / v.bm, tn = (N + v.bn - 1) / v.bn;
     pl.tiles = tm * tn;
-    pl.k_steps = (K + v.bk - 1) / v.bk;
-    pl.grid = pl.tiles < cus ? pl.tiles : cus;
-    if (pl.tiles > ((int64_t)1 << 30) || pl.tiles * pl.k_steps > ((int64_t)1 << 30))
+    pl.k_splits = choose_splits(M, N, K, cus);
+    pl.k_steps = (K / pl.k_splits + v.bk - 1) / v.bk;
+    const int64_t items = pl.tiles * pl.k_splits;
+    pl.grid = items < cus ? items : cus;
+    pl.workspace_bytes = pl.k_splits > 1 ? items * v.bm * v.bn * 4 : 0;
+    if (items > ((int64_t)1 << 30) || items * pl.k_steps > ((int64_t)1 << 30))
         return GEMM_ERR_UNSUPPORTED_SHAPE;
     *out = pl;
     return GEMM_OK;
@@ -1304,11 +1417,35 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
     p.ldc = ldc;
     p.tiles_m = (int32_t)((M + pl.bm - 1) / pl.bm);
     p.tiles_n = (int32_t)((N + pl.bn - 1) / pl.bn);
-    p.tiles = (int32_t)pl.tiles;
+    p.tiles_mn = (int32_t)pl.tiles;
+    p.splits = (int32_t)pl.k_splits;
+    p.ksplit = K / pl.k_splits;
+    p.tiles = (int32_t)(pl.tiles * pl.k_splits);
     p.k_steps = (int32_t)pl.k_steps;
     p.group_m = 4;
+    p.partial = nullptr;
     const int64_t grid = pl.grid;
-    return with_cfg(sync_mode, pl.stages, bt, [&]<class C>() { return launch<C>(p, grid, s); });
+    if (p.splits == 1)
+        return with_cfg(sync_mode, pl.stages, bt, [&]<class C>() { return launch<C>(p, grid, s); });
+
+    // Split k range: fp32 partial tiles in stream-ordered memory that lives
+    // for this call only, so calls on different streams never share it.
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, (size_t)pl.workspace_bytes, s) != hipSuccess || !ws)
+        return GEMM_ERR_DEVICE;
+    p.partial = (float*)ws;
+    rc = with_cfg(sync_mode, pl.stages, bt, [&]<class C>() { return launch<C>(p, grid, s); });
+    if (rc == GEMM_OK) {
+        const int64_t groups = M * (N / 8);
+        int64_t blocks = (groups + 255) / 256;
+        if (blocks > 65536)
+            blocks = 65536;
+        hipLaunchKernelGGL(k_reduce_splits, dim3((unsigned)blocks), dim3(256), 0, s, p, pl.bm, pl.bn);
+        rc = hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+    }
+    if (hipFreeAsync(ws, s) != hipSuccess && rc == GEMM_OK)
+        rc = GEMM_ERR_DEVICE;
+    return rc;
 }
 
 }  // namespace

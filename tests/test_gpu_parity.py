@@ -137,6 +137,37 @@ def test_many_tiles_per_workgroup(K, bt):
             np.testing.assert_array_equal(got, first, err_msg="modes disagree bitwise")
 
 
+@pytest.mark.parametrize("bt", [False, True], ids=["kn", "nk"])
+def test_split_k(bt):
+    """Few output tiles and a long k range: the k range is cut into chunks whose
+    fp32 partial tiles are summed in chunk order.  1000 x 1032 has 20 tiles of
+    256 x 256, so K = 8192 splits into 8 chunks of 1024 (ragged M and N).  The
+    chunking depends on the shape only, so every mode gives the same bits, run
+    after run and on any stream; a K with no valid chunking stays unsplit."""
+    M, N, K = 1000, 1032, 8192
+    for sync, stages in MODES:
+        plan = bd.gemm_bf16_plan(M, N, K, bt, stages, bd.SYNC_MODES[sync])
+        assert plan["k_splits"] == 8, (sync, stages, plan)
+        assert plan["workspace_bytes"] == plan["tiles"] * 8 * plan["bm"] * plan["bn"] * 4
+    assert bd.gemm_bf16_plan(M, N, K + 8, bt, 0, 0)["k_splits"] == 1
+    A, B = make_operands(M, N, K, b_transposed=bt, seed=4242 + bt)
+    ref = oracle.load().gemm_bf16(bits(A), bits(B), bt)
+    dA, dB = A.cuda(), B.cuda()
+    first = None
+    for sync, stages in MODES:
+        got = run(dA, dB, bt, sync, stages)
+        assert_within_tol(got, ref, "split %s/%d" % (sync, stages))
+        if first is None:
+            first = got
+        else:
+            np.testing.assert_array_equal(got, first, err_msg="modes disagree bitwise")
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        C = bd.gemm(dA, dB, b_transposed=bt)
+    side.synchronize()
+    np.testing.assert_array_equal(bits(C.cpu()), first)
+
+
 def test_layouts_and_modes_bit_identical():
     M, N, K = 520, 776, 392
     A, B = make_operands(M, N, K, b_transposed=False, seed=99)
