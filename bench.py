@@ -45,8 +45,8 @@ def kernel_sha():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sync", default="all", choices=["all", "barrier", "flags", "wavespec"])
     ap.add_argument("--stages", type=int, default=0)
     ap.add_argument("--workload", default="gemm8192_nk")
@@ -63,6 +63,8 @@ def parse():
                     help="kernel configuration the counter CSVs were taken for (a substring of "
                          "the kernel name: Cfg<BM, BN, BK, S, WM, WN, SYNC, B_NxK, loader waves>)")
     ap.add_argument("--no-reference", action="store_true", help="skip the torch.matmul timing")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the per-workload summary of the other configurations")
     return ap.parse_args()
 
 
@@ -199,6 +201,37 @@ def reference_matmul(dA, dB, C, w, steps, warmup, torch):
             "ms_per_step": round(ms, 4)}
 
 
+def other_workloads(bd, skip, args, torch):
+    """The other configurations, each at every sync mode's default stage count:
+    best mode's TFLOP/s (HIP events around all launches) and torch.matmul on
+    the same operands."""
+    from pipelined_tiled_dense_amd.inputs import WORKLOADS, workload_operands
+    out = {}
+    for name, w in WORKLOADS.items():
+        if name == skip:
+            continue
+        A, B = workload_operands(w)
+        dA, dB = A.cuda(), B.cuda()
+        C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+        flops = 2.0 * w.M * w.N * w.K
+        per_mode = {}
+        for m in ("barrier", "flags", "wavespec"):
+            _, per = time_mode(bd, dA, dB, C, w, m, 0, args.steps, args.warmup, torch)
+            per_mode[m] = flops / (sum(per) / len(per) * 1e-3) / 1e12
+        best = max(per_mode, key=per_mode.get)
+        plan = bd.gemm_bf16_plan(w.M, w.N, w.K, w.b_transposed, 0, bd.SYNC_MODES[best])
+        entry = {"M": w.M, "N": w.N, "K": w.K, "b_layout": "N x K" if w.b_transposed else "K x N",
+                 "best_mode": best, "tflops": round(per_mode[best], 2),
+                 "modes_tflops": {m: round(v, 2) for m, v in per_mode.items()},
+                 "k_splits": plan["k_splits"]}
+        if not args.no_reference:
+            entry["reference_tflops"] = reference_matmul(dA, dB, C, w, args.steps, args.warmup, torch)["tflops"]
+        out[name] = entry
+        print("# workload %s: %s" % (name, json.dumps(entry)), file=sys.stderr, flush=True)
+        del dA, dB, C
+    return out
+
+
 def main():
     args = parse()
     if args.summarize_traffic:
@@ -243,7 +276,8 @@ def main():
         mean_ms = sum(per) / len(per)
         results[m] = {"stages": plan["stages"], "tile": "%dx%dx%d" % (plan["bm"], plan["bn"], plan["bk"]),
                       "grid": plan["grid"], "ms_per_step": wall * 1e3 / args.steps,
-                      "kernel_ms_mean": mean_ms, "kernel_ms_min": min(per),
+                      "kernel_ms_mean": mean_ms, "kernel_ms_median": sorted(per)[len(per) // 2],
+                      "kernel_ms_min": min(per),
                       "tflops": flops / (wall / args.steps) / 1e12,
                       "kernel_tflops": flops / (mean_ms * 1e-3) / 1e12}
         print("# %s: %s" % (m, json.dumps(results[m])), file=sys.stderr, flush=True)
@@ -271,7 +305,8 @@ def main():
                    "accumulate": "fp32", "output": "bf16 (RNE)"},
         "pct_of_peak": round(100.0 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
         "modes": {m: {"tflops": round(v["tflops"], 2), "pct_of_peak": round(100 * v["tflops"] / PEAK_BF16_TFLOPS, 2),
-                      "stages": v["stages"], "tile": v["tile"], "kernel_ms_mean": round(v["kernel_ms_mean"], 4)}
+                      "stages": v["stages"], "tile": v["tile"], "kernel_ms_mean": round(v["kernel_ms_mean"], 4),
+                      "kernel_ms_median": round(v["kernel_ms_median"], 4), "kernel_ms_min": round(v["kernel_ms_min"], 4)}
                   for m, v in results.items()},
         "sync_timeouts": timeouts,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -282,6 +317,8 @@ def main():
     }
     if not args.no_reference:
         line["reference"] = reference_matmul(dA, dB, C, w, args.steps, args.warmup, torch)
+    if not args.no_workloads:
+        line["workloads"] = other_workloads(bd, w.name, args, torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_seconds)
     print(json.dumps(line), flush=True)
