@@ -677,6 +677,16 @@ __device__ __forceinline__ bf16x8_t b_frag(const Frags<C>& f, int j)
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// MFMAs LO .. HI-1 of one k-step (block x = i * FN + j).
+template <class C, int LO, int HI>
+__device__ __forceinline__ void mfma_range(f32x16_t (&acc)[C::FM][C::FN], const Frags<C>& f)
+{
+#pragma unroll
+    for (int x = LO; x < HI; ++x)
+        acc[x / C::FN][x % C::FN] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(b_frag<C>(f, x % C::FN), f.a[x / C::FN], acc[x / C::FN][x % C::FN], 0, 0, 0);
+}
+
 template <class C>
 __device__ __forceinline__ void mfma_step(f32x16_t (&acc)[C::FM][C::FN], const Frags<C>& f)
 {
@@ -1033,14 +1043,21 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
                     // part 0 of the load of position c + S refills this stage
                     // and the next stage's first fragments are read.  At the
                     // end of the stream this runs once more on an empty
-                    // position, which keeps the block free of branches.
+                    // position, which keeps the block free of branches.  The
+                    // first PRE MFMAs (their fragments are in registers) go
+                    // out ahead of the barrier and keep the pipe busy while
+                    // the workgroup gathers.
+                    constexpr int PRE = 2;
+                    mfma_range<C, 0, PRE>(acc, fr[kk & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
                     wait_lgkm0();
                     sync_next(s_nxt, g_nxt);
                     constexpr int V = part_begin(1, NPARTS, C::LOADS);
                     const FragReader<C> rdr(wm, wn, lane, 0);
-                    region_memops<M, D, V>(rdr, fr[0], stage_at(s_nxt), wn, ld, next_prep, 0, stage_at(s_cur), w, lane);
-                    mfma_step<C>(acc, fr[kk & 1]);
-                    sched_slots<M, D, V>();
+                    region_memops<M - PRE, D, V>(rdr, fr[0], stage_at(s_nxt), wn, ld, next_prep, 0, stage_at(s_cur), w,
+                                                 lane);
+                    mfma_range<C, PRE, M>(acc, fr[kk & 1]);
+                    sched_slots<M - PRE, D, V>();
                 } else {
                     wait_lgkm0();
                     arrive(empty + s_cur);
