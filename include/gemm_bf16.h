@@ -70,6 +70,22 @@ enum {
     GEMM_SYNC_WAVESPEC = 2  /* per-stage counters between loader waves and MFMA waves */
 };
 
+/*
+ * The `stages` value that selects the split-window ring (GEMM_SYNC_BARRIER
+ * only): instead of whole stages, the LDS holds five windows of one operand
+ * tile each (256 x 64 bf16, 32 KiB).  A k-step's A tile and B tile sit in two
+ * windows; when a k-step's windows are drained, one takes the B tile of the
+ * k-step after next and the other the A tile of the one after that, so A
+ * tiles get two k-steps to land and B tiles one.  The output tile's epilogue
+ * is staged in a drained window, so the whole 160 KiB serves the ring.  The
+ * split follows the shared-memory reduction strategies of "[WIP] SM120 fused
+ * backward kernel: exploratory shared-memory reduction" (section
+ * "Shared-memory reduction strategies": buffer aliasing, and a producer that
+ * streams one half of an operand while the consumer computes on the other).
+ * Results are bit-identical to every other mode.
+ */
+enum { GEMM_STAGES_WINDOWS = 5 };
+
 /* Status codes.  Every entry point returns GEMM_OK (0) or one of these. */
 enum {
     GEMM_OK = 0,
@@ -79,7 +95,8 @@ enum {
                                         dimension not a multiple of 8 elements */
     GEMM_ERR_UNSUPPORTED_SHAPE = -3, /* N or K not a multiple of 8, or a leading dimension
                                         above 2^22 elements */
-    GEMM_ERR_STAGES = -4,            /* stages not 0 (default) or 2..4 */
+    GEMM_ERR_STAGES = -4,            /* stages not 0 (default), 2..4, or GEMM_STAGES_WINDOWS
+                                        with GEMM_SYNC_BARRIER */
     GEMM_ERR_SYNC_MODE = -5,         /* sync_mode not one of GEMM_SYNC_* */
     GEMM_ERR_DEVICE = -6,            /* no HIP device, or the current device is not gfx950 */
     GEMM_ERR_LAUNCH = -7,            /* the kernel launch was rejected by the runtime */
@@ -89,7 +106,7 @@ enum {
 /* The tiling and launch shape chosen for a problem (see gemm_bf16_plan). */
 typedef struct gemm_bf16_plan {
     int32_t bm, bn, bk;       /* output tile BM x BN, k-step BK */
-    int32_t stages;           /* depth of the LDS ring */
+    int32_t stages;           /* depth of the LDS ring (GEMM_STAGES_WINDOWS: the split-window ring) */
     int32_t sync_mode;        /* GEMM_SYNC_* */
     int32_t b_transposed;     /* 1 for gemm_bf16_bt */
     int32_t mfma_waves;       /* waves that run the matrix-core loop */
@@ -113,7 +130,8 @@ typedef struct gemm_bf16_plan {
  * operands that are read or written).  M == 0 or N == 0 is a no-op.  K == 0
  * writes +0 to every element of C.
  *
- * stages: 0 picks the default for the sync mode; otherwise 2, 3 or 4.
+ * stages: 0 picks the default for the sync mode; otherwise 2, 3 or 4 whole
+ * stages, or GEMM_STAGES_WINDOWS (barrier sync only).
  * sync_mode: GEMM_SYNC_BARRIER, GEMM_SYNC_FLAGS or GEMM_SYNC_WAVESPEC.
  * stream: a hipStream_t (NULL for the null stream).
  *

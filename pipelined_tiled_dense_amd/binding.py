@@ -23,6 +23,7 @@ GEMM_ERR_LAUNCH = -7
 GEMM_ERR_ALIAS = -8
 
 SYNC_MODES = {"barrier": 0, "flags": 1, "wavespec": 2}
+STAGES_WINDOWS = 5          # GEMM_STAGES_WINDOWS: the split-window ring (barrier sync)
 
 
 class GemmError(RuntimeError):

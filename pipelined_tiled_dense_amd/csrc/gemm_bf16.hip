@@ -140,11 +140,16 @@ enum { SYNC_BARRIER = GEMM_SYNC_BARRIER, SYNC_FLAGS = GEMM_SYNC_FLAGS, SYNC_WAVE
 // ---------------------------------------------------------------------------
 // Compile-time configuration of one kernel instance.
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, int SYNC_, bool BT_, int NP_>
+template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, int SYNC_, bool BT_, int NP_, bool WIN_ = false>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_;
     static constexpr int SYNC = SYNC_;
     static constexpr bool BT = BT_;                 // B stored N x K
+    // Split-window ring: the LDS holds NWIN windows of one operand tile each
+    // (a position's A tile and its B tile occupy two windows), instead of S
+    // whole stages; the epilogue stages through a drained window.
+    static constexpr bool WIN = WIN_;
+    static constexpr int NWIN = WIN ? 5 : 0;
     static constexpr int NCW = WM * WN;             // MFMA waves
     static constexpr int NP = (SYNC == SYNC_WAVESPEC) ? NP_ : 0;   // dedicated loader waves
     static constexpr int NLW = (SYNC == SYNC_WAVESPEC) ? NP : NCW; // waves that load
@@ -161,21 +166,23 @@ struct Cfg {
     static constexpr int LOADS = A_LOADS + B_LOADS;
     static constexpr int CPR_K = BK / 8;                             // 16-byte chunks per K-contiguous row
     static constexpr int CPR_N = BN / 8;                             // chunks per row of a K x N B tile
-    static constexpr int RING_BYTES = S * STAGE_BYTES;
+    static constexpr int RING_BYTES = WIN ? NWIN * A_BYTES : S * STAGE_BYTES;
     static constexpr int FLAG_BYTES = (SYNC != SYNC_BARRIER) ? 2 * S * 4 : 0;
     // Epilogue strip per MFMA wave: 32 rows x 64 columns of bf16 when that
-    // fits next to the ring, else 32 rows x 32 columns.
-    static constexpr int EPI_W = (RING_BYTES + NCW * 32 * 64 * 2 + FLAG_BYTES <= 160 * 1024) ? 64 : 32;
+    // fits next to the ring (or, with windows, inside one window), else 32
+    // rows x 32 columns.
+    static constexpr int EPI_W =
+        (WIN ? NCW * 32 * 64 * 2 <= A_BYTES : RING_BYTES + NCW * 32 * 64 * 2 + FLAG_BYTES <= 160 * 1024) ? 64 : 32;
     static constexpr int EPI_WAVE_BYTES = 32 * EPI_W * 2;
     static constexpr int EPI_OFFSET = RING_BYTES;
-    static constexpr int FLAG_OFFSET = EPI_OFFSET + NCW * EPI_WAVE_BYTES;
+    static constexpr int FLAG_OFFSET = WIN ? RING_BYTES : EPI_OFFSET + NCW * EPI_WAVE_BYTES;
     static constexpr int LDS_BYTES = FLAG_OFFSET + FLAG_BYTES;
     // Where the all-wave kernel steps its load cursor: inside the second MFMA
     // region of a k-step when there are three or more regions, else after
     // the k-step (one position further ahead).  The branch-free cursor needs
     // at least this many k-steps per tile.
     static constexpr bool PREP_IN_REGION = KK >= 3;
-    static constexpr int LONGK_MIN_KT = S + (PREP_IN_REGION ? 1 : 2);
+    static constexpr int LONGK_MIN_KT = WIN ? 3 : S + (PREP_IN_REGION ? 1 : 2);
 
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(KK % 2 == 0, "fragment double buffering assumes an even number of MFMA k-steps");
@@ -185,6 +192,9 @@ struct Cfg {
     static_assert(CPR_N == 16 || CPR_N == 32, "a DMA window covers whole K x N rows of B");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(S >= 2 && S <= 4, "stages");
+    static_assert(!WIN || (SYNC == SYNC_BARRIER && S == 2 && KK == 4 && A_BYTES == B_BYTES &&
+                           NCW * EPI_WAVE_BYTES <= A_BYTES),
+                  "the window ring runs the barrier kernel on equal A and B tiles");
 };
 
 // A work item is one output tile and one chunk of the k range.  Without a
@@ -487,18 +497,25 @@ struct Loader {
     }
 
     // DMA instruction t (0 <= t < LOADS; A first, then B) of this wave for a
-    // prepared position.
-    __device__ __forceinline__ void fire_one(const Prep& r, int t, lds_char* stage, int lw, int lane) const
+    // prepared position, into the A tile at a_tile or the B tile at b_tile.
+    __device__ __forceinline__ void fire_one(const Prep& r, int t, lds_char* a_tile, lds_char* b_tile, int lw,
+                                             int lane) const
     {
         if (t < C::A_LOADS) {
             const bool ok = kofs_k(slot(t, lw, lane)) < r.krem;
-            lds_dma16(r.ra, stage + (t * C::NLW + lw) * 1024, ok ? voffA[t] : kOOB);
+            lds_dma16(r.ra, a_tile + (t * C::NLW + lw) * 1024, ok ? voffA[t] : kOOB);
         } else {
             const int tb = t - C::A_LOADS;
             const int s = slot(tb, lw, lane);
             const bool ok = C::BT ? (kofs_k(s) < r.krem) : (nofs_n(s) < r.nrem);
-            lds_dma16(r.rb, stage + C::A_BYTES + (tb * C::NLW + lw) * 1024, ok ? voffB[tb] : kOOB);
+            lds_dma16(r.rb, b_tile + (tb * C::NLW + lw) * 1024, ok ? voffB[tb] : kOOB);
         }
+    }
+
+    // The same into a whole stage (A tile, then B tile).
+    __device__ __forceinline__ void fire_one(const Prep& r, int t, lds_char* stage, int lw, int lane) const
+    {
+        fire_one(r, t, stage, stage + C::A_BYTES, lw, lane);
     }
 
     // Part `part` of NPARTS of the wave's DMA instructions for a prepared
@@ -563,32 +580,40 @@ struct FragReader {
         const uint32_t xk = (uint32_t)(((2 * kk + h) ^ swz_k<C::BK>(r32)) << 4);
         a_off = opaque((uint32_t)((wm * C::TM + r32) * (C::BK * 2)) + xk);
         if constexpr (C::BT) {
-            b_off = opaque((uint32_t)((wn * C::TN + r32) * (C::BK * 2)) + xk) + C::A_BYTES;
+            b_off = opaque((uint32_t)((wn * C::TN + r32) * (C::BK * 2)) + xk);
             r = 0;
         } else {
             const int g = lane >> 4, i16 = lane & 15, q = i16 & 3;
             r = i16 >> 2;
             const int low = 2 * (g & 1) + (q >> 1);
             const uint32_t krow0 = (uint32_t)(16 * kk + 8 * (g >> 1) + r);
-            b_off = opaque(krow0 * (C::BN * 2) + (uint32_t)(low * 16 + (q & 1) * 8)) + C::A_BYTES;
+            b_off = opaque(krow0 * (C::BN * 2) + (uint32_t)(low * 16 + (q & 1) * 8));
         }
     }
 
-    // Read instruction d: A blocks first, then B.
-    __device__ __forceinline__ void read(Frags<C>& f, const lds_char* stage, int wn, int d) const
+    // Read instruction d: A blocks first (from the A tile at a_tile), then B
+    // (from the B tile at b_tile).
+    __device__ __forceinline__ void read(Frags<C>& f, const lds_char* a_tile, const lds_char* b_tile, int wn,
+                                         int d) const
     {
         if (d < C::FM) {
-            f.a[d] = *(const LDS_AS bf16x8_t*)(stage + a_off + d * (32 * C::BK * 2));
+            f.a[d] = *(const LDS_AS bf16x8_t*)(a_tile + a_off + d * (32 * C::BK * 2));
         } else if constexpr (C::BT) {
             const int j = d - C::FM;
-            f.b[j] = *(const LDS_AS bf16x8_t*)(stage + b_off + j * (32 * C::BK * 2));
+            f.b[j] = *(const LDS_AS bf16x8_t*)(b_tile + b_off + j * (32 * C::BK * 2));
         } else {
             const int j = (d - C::FM) >> 1, hh = (d - C::FM) & 1;
             const int J = wn * (C::TN / 32) + j;
             const uint32_t jchunk = (uint32_t)(4 * (J ^ r)) * 16u;
-            const lds_char* addr = stage + b_off + (uint32_t)(4 * hh * (C::BN * 2)) + jchunk;
+            const lds_char* addr = b_tile + b_off + (uint32_t)(4 * hh * (C::BN * 2)) + jchunk;
             f.bh[j][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)addr);
         }
+    }
+
+    // The same from a whole stage (A tile, then B tile).
+    __device__ __forceinline__ void read(Frags<C>& f, const lds_char* stage, int wn, int d) const
+    {
+        read(f, stage, stage + C::A_BYTES, wn, d);
     }
 };
 
@@ -644,6 +669,20 @@ __device__ __forceinline__ void region_memops(const FragReader<C>& rdr, Frags<C>
 {
     emit_memops<M, D, V>([&](int d) { rdr.read(f, src, wn, d); },
                          [&](int v) { ld.fire_one(prep, t0 + v, dst, w, lane); });
+}
+
+// The same for the window ring: fragment reads from the A and B windows of
+// one position, DMA instructions t0 .. t0 + V - 1 (all of them A, or all B)
+// into a third window.
+template <int M, int D, int V, class C, class LD>
+__device__ __forceinline__ void region_memops_win(const FragReader<C>& rdr, Frags<C>& f,
+                                                  const lds_char* __restrict__ a_src,
+                                                  const lds_char* __restrict__ b_src, int wn, const LD& ld,
+                                                  const typename LD::Prep& prep, int t0, lds_char* __restrict__ dst,
+                                                  int w, int lane)
+{
+    emit_memops<M, D, V>([&](int d) { rdr.read(f, a_src, b_src, wn, d); },
+                         [&](int v) { ld.fire_one(prep, t0 + v, dst, dst, w, lane); });
 }
 
 // SALU scalar instructions may follow each MFMA (the load cursor's step, in
@@ -1094,6 +1133,134 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
 }
 
 // ---------------------------------------------------------------------------
+// Kernel: barrier sync over the split-window ring.
+//
+// The LDS is five windows of one operand tile (32 KiB at 256 x 64 bf16).
+// Position c keeps its A tile in window 2c mod 5 and its B tile in window
+// 2c+1 mod 5.  The barrier of k-step c (in its last MFMA region) frees the two
+// windows of position c, and they take the B tile of position c+2 and the A
+// tile of position c+3.  So every B tile has one k-step to land (as in a
+// two-stage ring) but every A tile has two, and the barrier only waits for
+// the B tile of the next position: the loads in flight at a barrier are
+// spread over twice the time.  The epilogue stages through the window that
+// held the tile's last B tile; the A load that reuses it is issued after a
+// barrier that follows the epilogue.
+//
+// Per k-step c (DMA parts are halves of one operand tile per wave):
+//   region 0: second half of B(c+1); the cursor prepares position c+2
+//   region 1: first half of A(c+2)
+//   region 2: second half of A(c+2)
+//   region 3: PRE MFMAs; wait until B(c+1) has landed (only the A(c+2)
+//             loads may still be outstanding); barrier; first half of
+//             B(c+2); fragments of k-step 0 of position c+1
+// ---------------------------------------------------------------------------
+template <class C, bool LONGK>
+__global__ void __launch_bounds__(C::THREADS) k_gemm_win(Params p)
+{
+    static_assert(C::WIN && C::SYNC == SYNC_BARRIER, "window-ring configs only");
+    __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS_BYTES];
+    lds_char* smem = (lds_char*)smem_raw;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = w / C::WN, wn = w % C::WN;
+
+    const int32_t G = gridDim.x, b = blockIdx.x;
+    const int32_t n_tiles = (b < p.tiles) ? (p.tiles - 1 - b) / G + 1 : 0;
+    const int32_t KT = p.k_steps;
+    if (n_tiles == 0 || KT == 0)
+        return;
+
+    constexpr int AH = C::A_LOADS / 2, BH = C::B_LOADS / 2;   // DMA instructions per half tile
+    auto win = [&](int i) { return smem + i * C::A_BYTES; };
+    auto step5 = [](int i, int d) { return i + d >= 5 ? i + d - 5 : i + d; };
+    using Prep = typename Loader<C, LONGK>::Prep;
+
+    Loader<C, LONGK> ld;
+    ld.init(p, n_tiles, w, lane);
+    // Prologue: positions 0 and 1 whole except the second half of B(1),
+    // which region 0 of k-step 0 issues like any other.
+    Prep prep_b = ld.prepare_and_advance(p);
+#pragma unroll
+    for (int t = 0; t < C::LOADS; ++t)
+        ld.fire_one(prep_b, t, win(0), win(1), w, lane);
+    prep_b = ld.prepare_and_advance(p);
+#pragma unroll
+    for (int t = 0; t < C::A_LOADS + BH; ++t)
+        ld.fire_one(prep_b, t, win(2), win(3), w, lane);
+    wait_vmcnt<C::A_LOADS + BH>();
+    block_barrier();
+
+    Frags<C> fr[2];
+    read_frags<C>(fr[0], win(0), wm, wn, lane, 0);   // A at window 0, B at window 1
+    int wa = 0;                                      // A window of the position being computed
+    Prep prep_a = prep_b;
+
+    for (int32_t it = 0; it < n_tiles; ++it) {
+        int32_t tm, tn;
+        int32_t sp;
+        tile_coords(p, b + it * G, G, tm, tn, sp);
+        if constexpr (LONGK)
+            ld.prefetch_next_tile(p, it + 1);
+        f32x16_t acc[C::FM][C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                acc[i][j] = f32x16_t{};
+
+        for (int32_t kt = 0; kt < KT; ++kt) {
+            const lds_char* a_cur = win(wa);
+            const lds_char* b_cur = win(step5(wa, 1));
+            auto region = [&]<int kk>() {
+                constexpr int M = C::FM * C::FN, D = frag_reads<C>();
+                if constexpr (kk < 3) {
+                    constexpr int SALU = (kk == 0) ? 6 : 0;
+                    if constexpr (kk == 0)
+                        prep_a = ld.prepare_and_advance(p);                     // position c + 2
+                    const FragReader<C> rdr(wm, wn, lane, kk + 1);
+                    if constexpr (kk == 0)
+                        region_memops_win<M, D, C::B_LOADS - BH>(rdr, fr[1], a_cur, b_cur, wn, ld, prep_b,
+                                                                 C::A_LOADS + BH, win(step5(wa, 3)), w, lane);
+                    else
+                        region_memops_win<M, D, (kk == 1) ? AH : C::A_LOADS - AH>(
+                            rdr, fr[(kk + 1) & 1], a_cur, b_cur, wn, ld, prep_a, (kk == 1) ? 0 : AH,
+                            win(step5(wa, 4)), w, lane);
+                    mfma_step<C>(acc, fr[kk & 1]);
+                    sched_slots<M, D, (kk == 0) ? C::B_LOADS - BH : (kk == 1) ? AH : C::A_LOADS - AH, SALU>();
+                } else {
+                    constexpr int PRE = 2;
+                    mfma_range<C, 0, PRE>(acc, fr[1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    wait_lgkm0();
+                    wait_vmcnt<C::A_LOADS>();
+                    block_barrier();
+                    const FragReader<C> rdr(wm, wn, lane, 0);
+                    region_memops_win<M - PRE, D, BH>(rdr, fr[0], win(step5(wa, 2)), win(step5(wa, 3)), wn, ld,
+                                                      prep_a, C::A_LOADS, win(wa), w, lane);
+                    mfma_range<C, PRE, M>(acc, fr[1]);
+                    sched_slots<M - PRE, D, BH>();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            [&]<int... KS>(std::integer_sequence<int, KS...>) {
+                (region.template operator()<KS>(), ...);
+            }(std::make_integer_sequence<int, C::KK>{});
+            prep_b = prep_a;
+            wa = step5(wa, 2);
+        }
+        if (p.splits > 1) {
+            store_partial<C>(p, acc, (sp * p.tiles_mn + tm * p.tiles_n + tn), wm, wn, lane);
+        } else {
+            // The window of the last position's B tile is free until region 1
+            // of the next k-step reloads it.
+            store_tile<C>(p, acc, win(step5(wa, 4)) + w * C::EPI_WAVE_BYTES, tm * C::BM, tn * C::BN, wm, wn, lane);
+            wait_lgkm0();
+            block_barrier();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Kernel: dedicated loader waves and MFMA waves (GEMM_SYNC_WAVESPEC).
 // ---------------------------------------------------------------------------
 template <class C>
@@ -1223,12 +1390,27 @@ struct Pick {
                      (SYNC == SYNC_WAVESPEC) ? 4 : 0>;
 };
 
+// The split-window ring: the two-stage barrier instance's tile, waves and
+// k-step over five windows (stages == GEMM_STAGES_WINDOWS).
+template <>
+struct Pick<SYNC_BARRIER, GEMM_STAGES_WINDOWS> {
+    template <bool BT>
+    using type = Cfg<256, 256, 64, 2, 2, 4, SYNC_BARRIER, BT, 0, true>;
+};
+
 template <class C>
 int launch(const Params& p, int64_t grid, hipStream_t stream)
 {
     if constexpr (C::SYNC == SYNC_WAVESPEC)
         hipLaunchKernelGGL(k_gemm_ws<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
-    else if (p.k_steps >= C::LONGK_MIN_KT)
+    else if constexpr (C::WIN) {
+        if (p.k_steps >= C::LONGK_MIN_KT)
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_win<C, true>), dim3((unsigned)grid), dim3(C::THREADS), 0,
+                               stream, p);
+        else
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_win<C, false>), dim3((unsigned)grid), dim3(C::THREADS), 0,
+                               stream, p);
+    } else if (p.k_steps >= C::LONGK_MIN_KT)
         hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm<C, true>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
     else
         hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm<C, false>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
@@ -1254,6 +1436,7 @@ auto with_cfg(int sync_mode, int stages, bool bt, F&& f)
         return bt ? f.template operator()<typename Pick<SY, ST>::template type<true>>() \
                   : f.template operator()<typename Pick<SY, ST>::template type<false>>();
     PTD_PICK(SYNC_BARRIER, 2) PTD_PICK(SYNC_BARRIER, 3) PTD_PICK(SYNC_BARRIER, 4)
+    PTD_PICK(SYNC_BARRIER, GEMM_STAGES_WINDOWS)
     PTD_PICK(SYNC_FLAGS, 2) PTD_PICK(SYNC_FLAGS, 3) PTD_PICK(SYNC_FLAGS, 4)
     PTD_PICK(SYNC_WAVESPEC, 2) PTD_PICK(SYNC_WAVESPEC, 3)
 #undef PTD_PICK
@@ -1321,7 +1504,8 @@ int validate_shape(int64_t M, int64_t N, int64_t K, int stages, int sync_mode)
 {
     if (sync_mode != GEMM_SYNC_BARRIER && sync_mode != GEMM_SYNC_FLAGS && sync_mode != GEMM_SYNC_WAVESPEC)
         return GEMM_ERR_SYNC_MODE;
-    if (stages != 0 && (stages < 2 || stages > 4))
+    if (stages != 0 && (stages < 2 || stages > 4) &&
+        !(stages == GEMM_STAGES_WINDOWS && sync_mode == GEMM_SYNC_BARRIER))
         return GEMM_ERR_STAGES;
     if (M < 0 || N < 0 || K < 0)
         return GEMM_ERR_INVALID_VALUE;
@@ -1503,7 +1687,7 @@ const char* gemm_bf16_strerror(int status)
     case GEMM_ERR_INVALID_VALUE: return "invalid value (negative size, NULL pointer or leading dimension too small)";
     case GEMM_ERR_MISALIGNED: return "misaligned operand (pointers need 16-byte alignment, leading dimensions a multiple of 8)";
     case GEMM_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (N and K must be multiples of 8; leading dimensions at most 2^22)";
-    case GEMM_ERR_STAGES: return "stages must be 0 (default), 2, 3 or 4";
+    case GEMM_ERR_STAGES: return "stages must be 0 (default), 2, 3, 4, or 5 (split-window ring, barrier sync)";
     case GEMM_ERR_SYNC_MODE: return "sync_mode must be GEMM_SYNC_BARRIER, GEMM_SYNC_FLAGS or GEMM_SYNC_WAVESPEC";
     case GEMM_ERR_DEVICE: return "no usable device (the current HIP device must be gfx950)";
     case GEMM_ERR_LAUNCH: return "kernel launch failed";

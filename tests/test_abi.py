@@ -77,7 +77,10 @@ def test_validation_errors(fn):
     assert call(fn, sync=3) == bd.GEMM_ERR_SYNC_MODE
     assert call(fn, sync=-1) == bd.GEMM_ERR_SYNC_MODE
     assert call(fn, stages=1) == bd.GEMM_ERR_STAGES
-    assert call(fn, stages=5) == bd.GEMM_ERR_STAGES
+    assert call(fn, stages=6) == bd.GEMM_ERR_STAGES
+    # the split-window ring exists for barrier sync only
+    assert call(fn, stages=bd.STAGES_WINDOWS, sync=1) == bd.GEMM_ERR_STAGES
+    assert call(fn, stages=bd.STAGES_WINDOWS, sync=2) == bd.GEMM_ERR_STAGES
     assert call(fn, M=-1) == bd.GEMM_ERR_INVALID_VALUE
     assert call(fn, K=-8) == bd.GEMM_ERR_INVALID_VALUE
     assert call(fn, N=60) == bd.GEMM_ERR_UNSUPPORTED_SHAPE

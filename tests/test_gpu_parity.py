@@ -22,7 +22,7 @@ from pipelined_tiled_dense_amd.inputs import WORKLOADS, bits, make_operands, wor
 
 pytestmark = pytest.mark.gpu
 
-MODES = [("barrier", 2), ("barrier", 3), ("barrier", 4),
+MODES = [("barrier", 2), ("barrier", 3), ("barrier", 4), ("barrier", bd.STAGES_WINDOWS),
          ("flags", 2), ("flags", 3), ("flags", 4),
          ("wavespec", 2), ("wavespec", 3), ("wavespec", 4)]
 TOL = 1e-2
@@ -119,10 +119,12 @@ def test_many_tiles_per_workgroup(K, bt):
     each persistent workgroup walks 2-3 tiles, ragged in M and N), at k-step
     counts on both sides of the point where the load cursor switches from
     entering each new tile itself to having the next tile's origin computed
-    ahead by the compute loop: stages + 1 k-steps for 2 stages of 64 (K = 72,
-    104, 136, 168, 200 give 2, 2, 3, 3, 4), stages + 2 for 3 and 4 stages of
-    32 (3, 4, 5, 6, 7).  A workgroup's third tile is where a stale next-tile
-    origin shows: it then repeats the second tile."""
+    ahead by the compute loop: stages + 1 k-steps for 2 stages of 64 and 3
+    for the split-window ring (K = 72, 104, 136, 168, 200 give 2, 2, 3, 3, 4),
+    stages + 2 for 3 and 4 stages of 32 (3, 4, 5, 6, 7).  A workgroup's third
+    tile is where a stale next-tile origin shows: it then repeats the second
+    tile.  The split-window ring also stages each tile's epilogue in a window
+    the next tile reloads right after."""
     M, N = 8448 - 40, 4104
     A, B = make_operands(M, N, K, b_transposed=bt, seed=K + (1000 if bt else 0))
     ref = oracle.load().gemm_bf16(bits(A), bits(B), bt)
@@ -166,6 +168,29 @@ def test_split_k(bt):
         C = bd.gemm(dA, dB, b_transposed=bt)
     side.synchronize()
     np.testing.assert_array_equal(bits(C.cpu()), first)
+
+
+def test_plans():
+    """The launch shape each (sync mode, stages) resolves to: 256 x 256 tiles over
+    8 waves for the all-wave modes (64-wide k-steps with 2 stages or the split
+    window ring, 32-wide with 3 and 4), 256 x 128 over 4 + 4 waves for the
+    wave-specialised mode; the LDS never exceeds 160 KiB, and the split-window
+    ring (five 32 KiB windows, epilogue staged inside one) uses all of it."""
+    want = {("barrier", 2): (256, 64, 8, 0), ("barrier", 3): (256, 32, 8, 0), ("barrier", 4): (256, 32, 8, 0),
+            ("barrier", bd.STAGES_WINDOWS): (256, 64, 8, 0),
+            ("flags", 2): (256, 64, 8, 0), ("flags", 3): (256, 32, 8, 0), ("flags", 4): (256, 32, 8, 0),
+            ("wavespec", 2): (128, 64, 4, 4), ("wavespec", 3): (128, 64, 4, 4), ("wavespec", 4): (128, 32, 4, 4)}
+    for (sync, stages), (bn, bk, mw, pw) in want.items():
+        for bt in (False, True):
+            pl = bd.gemm_bf16_plan(8192, 8192, 8192, bt, stages, bd.SYNC_MODES[sync])
+            assert (pl["bm"], pl["bn"], pl["bk"], pl["mfma_waves"], pl["producer_waves"]) == (256, bn, bk, mw, pw), \
+                (sync, stages, pl)
+            assert pl["stages"] == stages and pl["threads"] == 64 * (mw + pw), (sync, stages, pl)
+            assert pl["lds_bytes"] <= 160 * 1024, (sync, stages, pl)
+    pl = bd.gemm_bf16_plan(8192, 8192, 8192, True, bd.STAGES_WINDOWS, 0)
+    assert pl["lds_bytes"] == 5 * 256 * 64 * 2
+    assert bd.gemm_bf16_plan(8192, 8192, 8192, True, 0, 0)["stages"] == 2
+    assert bd.gemm_bf16_plan(8192, 8192, 8192, True, 0, 2)["stages"] == 3
 
 
 def test_layouts_and_modes_bit_identical():
@@ -237,10 +262,12 @@ def test_output_outside_the_matrix_untouched():
 # --- the five workloads at full size ------------------------------------------
 FULL = {
     "gemm256_kn": [("barrier", 2), ("flags", 2), ("wavespec", 4)],
-    "gemm4096_kn": [("barrier", 2), ("barrier", 3), ("barrier", 4), ("flags", 2), ("flags", 3), ("flags", 4)],
-    "gemm8192_nk": [("barrier", 2), ("barrier", 4), ("flags", 2), ("wavespec", 4)],
+    "gemm4096_kn": [("barrier", 2), ("barrier", 3), ("barrier", 4), ("flags", 2), ("flags", 3), ("flags", 4),
+                    ("barrier", bd.STAGES_WINDOWS)],
+    "gemm8192_nk": [("barrier", 2), ("barrier", bd.STAGES_WINDOWS), ("barrier", 4), ("flags", 2), ("wavespec", 4)],
     "longk1024_k32768_kn": [("barrier", 2), ("barrier", 3), ("barrier", 4), ("flags", 2), ("flags", 3), ("flags", 4)],
-    "tall32768x1024_k4096_kn": [("wavespec", 2), ("wavespec", 3), ("wavespec", 4), ("barrier", 2), ("flags", 2)],
+    "tall32768x1024_k4096_kn": [("wavespec", 2), ("wavespec", 3), ("wavespec", 4), ("barrier", 2), ("flags", 2),
+                                ("barrier", bd.STAGES_WINDOWS)],
 }
 
 
