@@ -4,7 +4,8 @@
 A step is one C = A * B over the whole throughput workload (8192 x 8192 x 8192,
 B stored N x K, seeded uniform[-1, 1) bf16 inputs already resident in HBM).
 Each sync mode (barrier, flags, wave-specialised) is timed at its default
-stage count; ``value`` is the fastest mode and every mode is listed under
+stage count, and barrier sync also over the split-window ring
+("barrier-windows"); ``value`` is the fastest and every one is listed under
 ``modes``.  Prints one JSON line.
 
 Also reports:
@@ -19,7 +20,7 @@ Also reports:
                 process, as context: under the board's power limit the
                 attainable clock varies from one GPU to the next.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sync all|barrier|flags|wavespec]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sync all|barrier|flags|wavespec|barrier-windows]
                        [--stages S] [--workload NAME] [--no-cpu-baseline] [--copy-calibration]
 """
 import argparse
@@ -47,7 +48,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--sync", default="all", choices=["all", "barrier", "flags", "wavespec"])
+    ap.add_argument("--sync", default="all", choices=["all", "barrier", "flags", "wavespec", "barrier-windows"])
     ap.add_argument("--stages", type=int, default=0)
     ap.add_argument("--workload", default="gemm8192_nk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -59,9 +60,9 @@ def parse():
                                                             "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into the traffic "
                          "summary read by the roofline line (no GPU needed)")
-    ap.add_argument("--traffic-kernel", default="Cfg<256, 256, 64, 2, 2, 4, 0, true, 0>",
+    ap.add_argument("--traffic-kernel", default="Cfg<256, 256, 64, 2, 2, 4, 0, true, 0, false>",
                     help="kernel configuration the counter CSVs were taken for (a substring of "
-                         "the kernel name: Cfg<BM, BN, BK, S, WM, WN, SYNC, B_NxK, loader waves>)")
+                         "the kernel name: Cfg<BM, BN, BK, S, WM, WN, SYNC, B_NxK, loader waves, windows>)")
     ap.add_argument("--no-reference", action="store_true", help="skip the torch.matmul timing")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the per-workload summary of the other configurations")
@@ -87,18 +88,30 @@ def _counter_per_dispatch(path, counter, name_filter):
 
 
 SYNC_NAMES = {0: "barrier", 1: "flags", 2: "wavespec"}
+# Timed configurations: label -> (sync mode, stages; 0 = the mode's default).
+# "barrier-windows" is barrier sync over the split-window ring.
+# They run in this order: the first launches of a process meet a cool chip
+# whose clock then settles under the power limit, so the slowest mode (never
+# the headline) goes first.
+MODE_RUNS = {"wavespec": ("wavespec", 0), "flags": ("flags", 0), "barrier": ("barrier", 0),
+             "barrier-windows": ("barrier", 5)}
 
 
 def cfg_fields(kname):
-    """(sync mode, stages) of a Cfg<BM, BN, BK, S, WM, WN, SYNC, ...> string."""
+    """(sync mode, stages) of a Cfg<BM, BN, BK, S, WM, WN, SYNC, B_NxK, NP,
+    windows> string; the split-window ring reports its stages value, 5."""
     f = [x.strip() for x in kname[kname.index("<") + 1:].rstrip(">").split(",")]
+    if len(f) > 9 and f[9] == "true":
+        return SYNC_NAMES[int(f[6])], 5
     return SYNC_NAMES[int(f[6])], int(f[3])
 
 
 def summarize_traffic(paths, kname):
     """FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  Each is scaled by
     the ratio of the known bytes a plain 1 GiB device copy moves to what the
-    same counter reads for that copy."""
+    same counter reads for that copy.  The result is stored in the traffic
+    summary under "<sync>/<stages>", next to the entries of other kernel
+    configurations profiled on the same kernel source."""
     gf, gw, cf, cw = paths
     sync, stages = cfg_fields(kname)
     fetch_kib, n_f = _counter_per_dispatch(gf, "FETCH_SIZE", kname)
@@ -109,16 +122,23 @@ def summarize_traffic(paths, kname):
     w_scale = COPY_BYTES / (copy_w_kib * 1024.0)
     fetch = fetch_kib * 1024.0 * f_scale
     write = write_kib * 1024.0 * w_scale
-    out = {
-        "kernel": "k_gemm %s" % kname,
+    try:
+        with open(TRAFFIC_FILE) as f:
+            out = json.load(f)
+        if out.get("kernel_source_sha256") != kernel_sha() or "entries" not in out:
+            out = None
+    except (OSError, ValueError):
+        out = None
+    if out is None:
+        out = {"workload": "gemm8192_nk", "kernel_source_sha256": kernel_sha(),
+               "compulsory_bytes_per_launch": 2 * (3 * 8192 * 8192), "entries": {}}
+    out["entries"]["%s/%d" % (sync, stages)] = {
+        "kernel": kname,
         "sync_mode": sync,
         "stages": stages,
-        "workload": "gemm8192_nk",
-        "kernel_source_sha256": kernel_sha(),
         "fetch_bytes_per_launch": round(fetch),
         "write_bytes_per_launch": round(write),
         "hbm_bytes_per_launch": round(fetch + write),
-        "compulsory_bytes_per_launch": 2 * (3 * 8192 * 8192),
         "raw_fetch_kib": fetch_kib, "raw_write_kib": write_kib,
         "copy_fetch_kib": copy_f_kib, "copy_write_kib": copy_w_kib,
         "fetch_scale": f_scale, "write_scale": w_scale,
@@ -173,15 +193,16 @@ def cpu_baseline(w, A, B, target_s):
 
 def traffic_per_launch(workload, sync, stages):
     """HBM bytes per launch from the committed counter summary, or None when
-    it was taken for another kernel configuration or an older kernel source."""
+    it holds no entry for this kernel configuration or was taken on an older
+    kernel source."""
     try:
         info = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if (info.get("kernel_source_sha256") != kernel_sha() or info.get("workload") != workload
-            or info.get("sync_mode") != sync or info.get("stages") != stages):
+    if info.get("kernel_source_sha256") != kernel_sha() or info.get("workload") != workload:
         return None
-    return info.get("hbm_bytes_per_launch")
+    entry = info.get("entries", {}).get("%s/%d" % (sync, stages))
+    return entry.get("hbm_bytes_per_launch") if entry else None
 
 
 def reference_matmul(dA, dB, C, w, steps, warmup, torch):
@@ -215,7 +236,7 @@ def other_workloads(bd, skip, args, torch):
         C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
         flops = 2.0 * w.M * w.N * w.K
         per_mode = {}
-        for m in ("barrier", "flags", "wavespec"):
+        for m in ("wavespec", "flags", "barrier"):
             _, per = time_mode(bd, dA, dB, C, w, m, 0, args.steps, args.warmup, torch)
             per_mode[m] = flops / (sum(per) / len(per) * 1e-3) / 1e12
         best = max(per_mode, key=per_mode.get)
@@ -267,14 +288,18 @@ def main():
     A, B = workload_operands(w)
     dA, dB = A.cuda(), B.cuda()
     C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
-    modes = ["barrier", "flags", "wavespec"] if args.sync == "all" else [args.sync]
+    modes = list(MODE_RUNS) if args.sync == "all" else [args.sync]
+    if args.stages != 0 and args.sync == "all":
+        modes = ["wavespec", "flags", "barrier"]
     flops = 2.0 * w.M * w.N * w.K
     results = {}
     for m in modes:
-        plan = bd.gemm_bf16_plan(w.M, w.N, w.K, w.b_transposed, args.stages, bd.SYNC_MODES[m])
-        wall, per = time_mode(bd, dA, dB, C, w, m, args.stages, args.steps, args.warmup, torch)
+        sync, stages = MODE_RUNS[m]
+        stages = stages or args.stages
+        plan = bd.gemm_bf16_plan(w.M, w.N, w.K, w.b_transposed, stages, bd.SYNC_MODES[sync])
+        wall, per = time_mode(bd, dA, dB, C, w, sync, stages, args.steps, args.warmup, torch)
         mean_ms = sum(per) / len(per)
-        results[m] = {"stages": plan["stages"], "tile": "%dx%dx%d" % (plan["bm"], plan["bn"], plan["bk"]),
+        results[m] = {"sync": sync, "stages": plan["stages"], "tile": "%dx%dx%d" % (plan["bm"], plan["bn"], plan["bk"]),
                       "grid": plan["grid"], "ms_per_step": wall * 1e3 / args.steps,
                       "kernel_ms_mean": mean_ms, "kernel_ms_median": sorted(per)[len(per) // 2],
                       "kernel_ms_min": min(per),
@@ -301,7 +326,7 @@ def main():
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
                    "b_layout": "N x K (K contiguous)" if w.b_transposed else "K x N",
                    "inputs": "seeded uniform[-1,1) rounded to bf16, seed %d" % w.seed,
-                   "sync_mode": best, "stages": r["stages"], "tile": r["tile"], "grid": r["grid"],
+                   "sync_mode": r["sync"], "stages": r["stages"], "tile": r["tile"], "grid": r["grid"],
                    "accumulate": "fp32", "output": "bf16 (RNE)"},
         "pct_of_peak": round(100.0 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
         "modes": {m: {"tflops": round(v["tflops"], 2), "pct_of_peak": round(100 * v["tflops"] / PEAK_BF16_TFLOPS, 2),
@@ -311,9 +336,10 @@ def main():
         "sync_timeouts": timeouts,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_per_launch(w.name, best, r["stages"]),
-                     "kernel": "k_gemm (%s, %d stages)" % (best, r["stages"]) if best != "wavespec"
-                               else "k_gemm_ws (%d stages)" % r["stages"]},
+                     "traffic": traffic_per_launch(w.name, r["sync"], r["stages"]),
+                     "kernel": ("k_gemm_ws (%d stages)" % r["stages"] if r["sync"] == "wavespec"
+                                else "k_gemm_win (split-window ring)" if r["stages"] == 5
+                                else "k_gemm (%s, %d stages)" % (r["sync"], r["stages"]))},
     }
     if not args.no_reference:
         line["reference"] = reference_matmul(dA, dB, C, w, args.steps, args.warmup, torch)
