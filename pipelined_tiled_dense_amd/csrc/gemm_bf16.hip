@@ -130,9 +130,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_n(const void* base, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nrec, kRsrcWord3);
 }
 
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint32_t voff)
+// One 16-byte-per-lane global-to-LDS load at byte offset voff + soff of the
+// resource.  The hardware range check counts both offsets: a lane whose 16
+// bytes start at or past the resource's byte count writes zeros.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint32_t voff, uint32_t soff)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)dst, 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)dst, 16, voff, (int)soff, 0, 0);
 }
 
 enum { SYNC_BARRIER = GEMM_SYNC_BARRIER, SYNC_FLAGS = GEMM_SYNC_FLAGS, SYNC_WAVESPEC = GEMM_SYNC_WAVESPEC };
@@ -210,6 +213,7 @@ struct Params {
     int32_t tiles;                    // work items: tiles_mn * splits
     int32_t k_steps;                  // k-steps per work item
     int32_t group_m;
+    int32_t small_span;               // A and B each span fewer than kMaxRecords bytes
 };
 
 // Swizzles.  The LDS has 64 four-byte banks (256 bytes per cycle); a 16-byte
@@ -337,26 +341,30 @@ __device__ __forceinline__ void wait_lgkm0()
 // for the wave's t-th 1 KiB DMA instruction) holds row s / CPR and physical
 // chunk s % CPR; the lane fetches the logical chunk that the swizzle places
 // there.  These per-lane byte offsets do not depend on the tile, so they are
-// computed once.  Per position only the buffer resources move (scalar work):
-// their base is the tile origin at k0 and their byte count ends at the last
-// element of the operand, so rows past M (A), past N (B stored N x K) and
-// k-rows past K (B stored K x N) read as zeros by themselves.  The two edges a
-// byte count cannot express -- the k tail inside a row, and columns past N of
-// a K x N B tile -- are masked per lane with a select.
+// computed once.  Per position only scalar values move.  A resource's byte
+// count ends at the last element of the operand, so rows past M (A), past N
+// (B stored N x K) and k-rows past K (B stored K x N) read as zeros by
+// themselves.  The two edges a byte count cannot express -- the k tail inside
+// a row, and columns past N of a K x N B tile -- are masked per lane with a
+// select.
 //
 // Every call emits exactly LOADS DMA instructions, also for a position past the
 // end of the stream (it gets resources of zero bytes, so it writes zeros and
 // touches no memory).  That keeps the vector-memory counter arithmetic of the
 // waits exact.
 //
-// The cursor steps from one position to the next with scalar adds.  Entering a
-// new tile needs its origin (tile_coords, a few integer divisions).  With
-// LONGK (at least LONGK_MIN_KT k-steps per tile) the origin of the cursor's next
-// tile is computed ahead, once per tile, by the compute loop
-// (prefetch_next_tile), so the step itself is a handful of selects and the
-// k-step loop body stays one basic block that the scheduler can interleave with
-// MFMAs.  Without LONGK the cursor can cross several tiles during one compute
-// tile, and the step enters the new tile itself (a uniform branch).
+// Two cursors.  The stepping cursor (LONGK: at least LONGK_MIN_KT k-steps per
+// tile, and each operand spanning less than kMaxRecords bytes) keeps both
+// resources at the tile origin for the whole tile and moves through the k
+// range with the loads' scalar offset, which the range check counts as well:
+// a step is three scalar adds.  The compute loop computes the next tile's
+// resources once per tile (prefetch_next_tile) and switches the cursor to
+// them at a fixed k-step (enter_next_tile, a uniform branch at the top of the
+// k-step), so the scheduled MFMA regions stay free of branches.  A tile past
+// the end gets resources of zero bytes.  The other cursor rebuilds the
+// resources at every position from its origin and enters a new tile itself
+// (a uniform branch); it serves short k ranges, where the cursor can cross
+// several tiles during one compute tile, and operands of 2 GiB or more.
 // ---------------------------------------------------------------------------
 // First DMA instruction of part `part` when a wave's `loads` instructions
 // for one position are cut into `nparts` contiguous runs.
@@ -408,13 +416,16 @@ struct Loader {
         b_end = C::BT ? p.B + ((p.N - 1) * p.ldb + p.K) * 2 : p.B + ((p.K - 1) * p.ldb + p.N) * 2;
         n_tiles = ntiles;
         total = ntiles * p.k_steps;
-        q = 0;
-        kt = 0;
-        tile_origin(p, 0, pa, pb, nrem, krem);
-        if constexpr (LONGK)
+        if constexpr (LONGK) {
+            bstep = C::BT ? (uint32_t)C::BK * 2u : (uint32_t)C::BK * 2u * (uint32_t)p.ldb;
+            cur = tile_prep(p, 0);
             prefetch_next_tile(p, 1);
-        else
+        } else {
+            q = 0;
+            kt = 0;
             ti = 0;
+            tile_origin(p, 0, pa, pb, nrem, krem);
+        }
     }
 
     // Origin of the workgroup's t-th work item: its tile at the first k of
@@ -433,67 +444,88 @@ struct Loader {
         k_left = (int32_t)(p.K - k0);
     }
 
-    // LONGK: the origin of the tile the cursor enters next.  Called at the
-    // start of compute tile t with t + 1.  The compute loop prepares position
-    // c + S (or c + S + 1, without PREP_IN_REGION) during k-step c, and
-    // preparing the last position of a tile is the step that moves the cursor
-    // onto the next tile's origin.  So the cursor enters tile t + 1 during
-    // k-step (t + 1) * KT - S - 1 (or one earlier), which lies inside compute
-    // tile t (after this call, before the next one) exactly when
-    // KT >= LONGK_MIN_KT.
-    __device__ __forceinline__ void prefetch_next_tile(const Params& p, int32_t t)
-    {
-        tile_origin(p, t, pa_n, pb_n, nrem_n, krem_n);
-    }
-
-    // Scalar part of issuing one position: the two buffer resources and the
-    // remaining k / n extents used by the edge masks.
+    // Scalar part of issuing one position: the two buffer resources, the
+    // scalar offsets of the position within them, and the remaining k / n
+    // extents used by the edge masks.
     struct Prep {
         __amdgpu_buffer_rsrc_t ra, rb;
         int32_t krem, nrem;
+        uint32_t soa, sob;
     };
 
-    // The cursor: position q, k-step kt within its tile, the operand origins
-    // at that position, and the k / n extents left for the edge masks.
+    // Stepping cursor: the resources of the workgroup's t-th work item at its
+    // origin, or of zero bytes for t >= n_tiles.  Each operand spans less than
+    // kMaxRecords bytes, so the byte counts are exact.
+    __device__ __forceinline__ Prep tile_prep(const Params& p, int32_t t) const
+    {
+        const char* a;
+        const char* b;
+        Prep r;
+        tile_origin(p, t, a, b, r.nrem, r.krem);
+        const bool live = t < n_tiles;
+        r.ra = rsrc_n(a, live ? (uint32_t)(a_end - a) : 0u);
+        r.rb = rsrc_n(b, live ? (uint32_t)(b_end - b) : 0u);
+        r.soa = 0;
+        r.sob = 0;
+        return r;
+    }
+
+    // Stepping cursor: the resources of the tile the cursor enters next.
+    // Called at the start of compute tile t with t + 1; enter_next_tile then
+    // switches to them inside compute tile t.
+    __device__ __forceinline__ void prefetch_next_tile(const Params& p, int32_t t)
+    {
+        nxt = tile_prep(p, t);
+    }
+
+    // Stepping cursor: move onto the prefetched tile's origin.  The compute
+    // loop calls this at the top of the k-step whose preparation is the first
+    // position of the next tile.
+    __device__ __forceinline__ void enter_next_tile() { cur = nxt; }
+
+    // Stepping cursor: the current position and the next tile's origin, and
+    // the scalar-offset step of B per k-step.
+    Prep cur, nxt;
+    uint32_t bstep;
+
+    // Rebuilding cursor: position q, k-step kt within its tile, the operand
+    // origins at that position, and the k / n extents left for the edge masks.
     int32_t q, kt, ti;
     int32_t krem, nrem;
     const char* pa;
     const char* pb;
-    const char* pa_n;
-    const char* pb_n;
-    int32_t nrem_n, krem_n;
 
     // The cursor's position prepared for issue, then the cursor steps on.
     // Positions at or past the end of the stream get empty resources.
     __device__ __forceinline__ Prep prepare_and_advance(const Params& p)
     {
-        const bool live = q < total;
-        Prep r;
-        r.krem = krem;
-        r.nrem = nrem;
-        r.ra = rsrc_n(pa, live ? records((uint64_t)(a_end - pa)) : 0u);
-        r.rb = rsrc_n(pb, live ? records((uint64_t)(b_end - pb)) : 0u);
-        ++q;
-        constexpr int64_t kstep = (int64_t)C::BK * 2;
-        const int64_t bstep = C::BT ? kstep : kstep * p.ldb;
+        constexpr uint32_t kstep = (uint32_t)C::BK * 2u;
         if constexpr (LONGK) {
-            const bool wrap = ++kt == p.k_steps;
-            kt = wrap ? 0 : kt;
-            krem = wrap ? krem_n : krem - C::BK;
-            nrem = wrap ? nrem_n : nrem;
-            pa = wrap ? pa_n : pa + kstep;
-            pb = wrap ? pb_n : pb + bstep;
+            const Prep r = cur;
+            cur.soa += kstep;
+            cur.sob += bstep;
+            cur.krem -= C::BK;
+            return r;
         } else {
+            const bool live = q < total;
+            Prep r;
+            r.krem = krem;
+            r.nrem = nrem;
+            r.ra = rsrc_n(pa, live ? records((uint64_t)(a_end - pa)) : 0u);
+            r.rb = rsrc_n(pb, live ? records((uint64_t)(b_end - pb)) : 0u);
+            r.soa = 0;
+            r.sob = 0;
+            ++q;
             if (++kt == p.k_steps) {
                 kt = 0;
                 tile_origin(p, ++ti, pa, pb, nrem, krem);
             } else {
                 krem -= C::BK;
                 pa += kstep;
-                pb += bstep;
+                pb += C::BT ? (int64_t)kstep : (int64_t)kstep * p.ldb;
             }
+            return r;
         }
-        return r;
     }
 
     // DMA instruction t (0 <= t < LOADS; A first, then B) of this wave for a
@@ -503,12 +535,12 @@ struct Loader {
     {
         if (t < C::A_LOADS) {
             const bool ok = kofs_k(slot(t, lw, lane)) < r.krem;
-            lds_dma16(r.ra, a_tile + (t * C::NLW + lw) * 1024, ok ? voffA[t] : kOOB);
+            lds_dma16(r.ra, a_tile + (t * C::NLW + lw) * 1024, ok ? voffA[t] : kOOB, r.soa);
         } else {
             const int tb = t - C::A_LOADS;
             const int s = slot(tb, lw, lane);
             const bool ok = C::BT ? (kofs_k(s) < r.krem) : (nofs_n(s) < r.nrem);
-            lds_dma16(r.rb, b_tile + (tb * C::NLW + lw) * 1024, ok ? voffB[tb] : kOOB);
+            lds_dma16(r.rb, b_tile + (tb * C::NLW + lw) * 1024, ok ? voffB[tb] : kOOB, r.sob);
         }
     }
 
@@ -1052,6 +1084,12 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
                 acc[i][j] = f32x16_t{};
 
         for (int32_t kt = 0; kt < KT; ++kt) {
+            // The cursor prepares position c + S (or c + S + 1) during
+            // k-step c: from this k-step on, that is the next tile.
+            if constexpr (LONGK) {
+                if (kt == KT - (PIR ? C::S : C::S + 1))
+                    ld.enter_next_tile();
+            }
             const lds_char* stage = stage_at(s_cur);
             const int s_nxt = (s_cur + 1 == C::S) ? 0 : s_cur + 1;
             const uint32_t g_nxt = gen + (s_nxt == 0 ? 1u : 0u);
@@ -1209,6 +1247,12 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_win(Params p)
                 acc[i][j] = f32x16_t{};
 
         for (int32_t kt = 0; kt < KT; ++kt) {
+            // Region 0 prepares position c + 2: from this k-step on, that is
+            // the next tile.
+            if constexpr (LONGK) {
+                if (kt == KT - 2)
+                    ld.enter_next_tile();
+            }
             const lds_char* a_cur = win(wa);
             const lds_char* b_cur = win(step5(wa, 1));
             auto region = [&]<int kk>() {
@@ -1404,13 +1448,13 @@ int launch(const Params& p, int64_t grid, hipStream_t stream)
     if constexpr (C::SYNC == SYNC_WAVESPEC)
         hipLaunchKernelGGL(k_gemm_ws<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
     else if constexpr (C::WIN) {
-        if (p.k_steps >= C::LONGK_MIN_KT)
+        if (p.k_steps >= C::LONGK_MIN_KT && p.small_span)
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_win<C, true>), dim3((unsigned)grid), dim3(C::THREADS), 0,
                                stream, p);
         else
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_win<C, false>), dim3((unsigned)grid), dim3(C::THREADS), 0,
                                stream, p);
-    } else if (p.k_steps >= C::LONGK_MIN_KT)
+    } else if (p.k_steps >= C::LONGK_MIN_KT && p.small_span)
         hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm<C, true>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
     else
         hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm<C, false>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
@@ -1624,6 +1668,10 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
     p.tiles = (int32_t)(pl.tiles * pl.k_splits);
     p.k_steps = (int32_t)pl.k_steps;
     p.group_m = 4;
+    // The stepping load cursor addresses a whole operand from one resource
+    // per tile, so it needs exact byte counts below kMaxRecords.
+    p.small_span = span_bytes(M, K, lda) < (int64_t)kMaxRecords &&
+                   (bt ? span_bytes(N, K, ldb) : span_bytes(K, N, ldb)) < (int64_t)kMaxRecords;
     p.partial = nullptr;
     const int64_t grid = pl.grid;
     if (p.splits == 1)

@@ -8,7 +8,8 @@
 //     in, and that s_waitcnt vmcnt(0) covers the LDS write;
 //   - v_mfma_f32_32x32x16_bf16: the operand and accumulator lane layouts;
 //   - ds_read_b64_tr_b16: which lane receives which 16-bit element;
-//   - the fp32 -> bf16 conversion used by the epilogue (rounding mode).
+//   - the fp32 -> bf16 conversion used by the epilogue (rounding mode);
+//   - buffer range checking, with and without a scalar offset.
 // All accesses stay inside the buffers whose sizes are stated per entry
 // point; the host wrapper checks pointer arguments before launching.
 #include <hip/hip_runtime.h>
@@ -83,6 +84,32 @@ __global__ void __launch_bounds__(64) k_buffer_oob(const void* __restrict__ src,
     u32x4_t v = *(u32x4_t LDS_AS*)((char LDS_AS*)lds + 16 * l);
     __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, dst_nrec, 0x00020000);
     __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
+}
+
+// The same raw buffer load into LDS with a scalar offset: lane l loads 16
+// bytes at byte offset (voff[l] mod 8 KiB, rounded down to 16) + soff into
+// LDS at 16*l, against a resource of src_nrec bytes, and the LDS window is
+// copied to dump.  Whether the hardware's range check counts the scalar
+// offset decides which lanes read zeros.  soff is at most 4 KiB and the
+// caller provides at least 12 KiB + 16 bytes of src, so every address the
+// hardware could form lies inside it either way.
+__global__ void __launch_bounds__(64) k_buffer_soffset(const void* __restrict__ src, int src_nrec,
+                                                       const uint32_t* __restrict__ voff, uint32_t soff,
+                                                       uint32_t* __restrict__ dump)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t lds[kProbeLdsWords];
+    const int l = threadIdx.x;
+    for (int i = l; i < kProbeLdsWords; i += 64)
+        lds[i] = 0xDEADBEEFu;
+    __syncthreads();
+    const uint32_t off = voff[l] & 0x1FF0u;
+    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, src_nrec,
+                                                                  0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void LDS_AS*)lds, 16, off, (int)soff, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    for (int i = l; i < kProbeLdsWords; i += 64)
+        dump[i] = lds[i];
 }
 
 // One MFMA with zero accumulator: lane l supplies a[8l..8l+7] and
@@ -166,6 +193,16 @@ int gemm_probe_buffer_oob(const void* src, int src_nrec, const uint32_t* voff, u
         return -1;
     hipLaunchKernelGGL(k_buffer_oob, dim3(1), dim3(64), 0, (hipStream_t)stream, src, src_nrec,
                        voff, dump, dst, dst_nrec);
+    return launch_status();
+}
+
+int gemm_probe_buffer_soffset(const void* src, int src_nrec, const uint32_t* voff, uint32_t soff, uint32_t* dump,
+                              void* stream)
+{
+    if (!src || !voff || !dump || src_nrec < 0 || soff > 4096u || soff % 4u != 0)
+        return -1;
+    hipLaunchKernelGGL(k_buffer_soffset, dim3(1), dim3(64), 0, (hipStream_t)stream, src, src_nrec, voff, soff,
+                       dump);
     return launch_status();
 }
 

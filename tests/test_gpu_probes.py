@@ -29,8 +29,9 @@ def probes():
     lib.gemm_probe_ds_read_tr.argtypes = [p, p, p, p]
     lib.gemm_probe_cvt_bf16.argtypes = [p, p, ctypes.c_int64, p]
     lib.gemm_probe_buffer_oob.argtypes = [p, ctypes.c_int, p, p, p, ctypes.c_int, p]
+    lib.gemm_probe_buffer_soffset.argtypes = [p, ctypes.c_int, p, ctypes.c_uint32, p, p]
     for f in (lib.gemm_probe_lds_dma, lib.gemm_probe_mfma, lib.gemm_probe_ds_read_tr,
-              lib.gemm_probe_cvt_bf16, lib.gemm_probe_buffer_oob):
+              lib.gemm_probe_cvt_bf16, lib.gemm_probe_buffer_oob, lib.gemm_probe_buffer_soffset):
         f.restype = ctypes.c_int
     return lib
 
@@ -187,3 +188,33 @@ def test_cvt_bf16_is_round_to_nearest_even(probes):
     bad = np.flatnonzero(got[finite] != want[finite])
     assert bad.size == 0, "first mismatch x=%r got %#06x want %#06x" % (
         x[finite][bad[0]], got[finite][bad[0]], want[finite][bad[0]])
+
+
+def test_buffer_range_check_counts_scalar_offset(probes):
+    """A raw buffer load with a scalar offset is out of range when vector offset
+    plus scalar offset reaches the resource's byte count.  The kernels keep a
+    tile's operand resource at the tile origin and move through the k range
+    with the scalar offset, so the k-rows of a K x N B tile past K read zeros
+    through this check alone."""
+    print("probe buffer_soffset", flush=True)
+    src = (np.arange(16 * 1024 // 4 + 4, dtype=np.uint32) | 0x20000000)
+    nrec, soff = 4096, 1024
+    voff = np.zeros(64, dtype=np.uint32)
+    voff[:32] = 16 * np.arange(32)                      # below nrec - soff: in range either way
+    voff[32:48] = 3072 + 64 * np.arange(16)             # in [nrec - soff, nrec): decides the semantics
+    voff[48:] = 4096 + 16 * np.arange(16)               # at or past nrec: out of range either way
+    d_src = torch.from_numpy(src.view(np.int32)).cuda()
+    d_voff = torch.from_numpy(voff.view(np.int32)).cuda()
+    d_dump = torch.zeros(2048, dtype=torch.int32, device="cuda")
+    assert probes.gemm_probe_buffer_soffset(d_src.data_ptr(), nrec, d_voff.data_ptr(), soff,
+                                            d_dump.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    got = d_dump.cpu().numpy().view(np.uint32)[:256].reshape(64, 4)
+    data = np.array([src[(soff + int(v)) // 4:(soff + int(v)) // 4 + 4] for v in voff])
+    zero = np.zeros((64, 4), dtype=np.uint32)
+    mid = "zeros" if np.array_equal(got[32:48], zero[32:48]) else (
+        "data" if np.array_equal(got[32:48], data[32:48]) else "mixed")
+    print("  lanes with voff < nrec <= voff + soff read: %s" % mid, flush=True)
+    np.testing.assert_array_equal(got[:32], data[:32])
+    np.testing.assert_array_equal(got[48:], zero[48:])
+    np.testing.assert_array_equal(got[32:48], zero[32:48])
