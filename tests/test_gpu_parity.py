@@ -309,3 +309,34 @@ def test_workload_all_ones_exact(name):
         C = bd.gemm(A, B, b_transposed=w.b_transposed, sync=sync, stages=stages)
         torch.cuda.synchronize()
         assert torch.all(C == float(w.K)), (name, sync, stages)
+
+
+@pytest.mark.parametrize("which", ["A_nk", "A_kn", "B_kn"])
+def test_operand_over_2gib(which):
+    """An operand spanning more than 2^31 bytes: the loads then rebuild their
+    buffer resources at every position with a capped byte count instead of
+    stepping one resource per tile.  Ragged in M, N and K; compared with the
+    oracle on sampled rows (A's sampled rows are copied back from the GPU)."""
+    K = 8264
+    if which.startswith("A"):
+        M, N, bt = 131112, 264, which == "A_nk"
+    else:
+        M, N, bt = 264, 131112, False
+    g = torch.Generator(device="cuda").manual_seed(2024 + len(which) + bt)
+    A = (torch.rand(M, K, generator=g, device="cuda") * 2 - 1).to(torch.bfloat16)
+    B = (torch.rand(*((N, K) if bt else (K, N)), generator=g, device="cuda") * 2 - 1).to(torch.bfloat16)
+    assert max(A.numel(), B.numel()) * 2 > 2 ** 31
+    rows = sample_rows(M)
+    ref = oracle.load().gemm_bf16(bits(A[torch.from_numpy(rows).cuda()].cpu()), bits(B.cpu()), bt)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    first = None
+    for sync, stages in [("barrier", 2), ("barrier", bd.STAGES_WINDOWS), ("flags", 2), ("wavespec", 3)]:
+        C.fill_(7.0)
+        got = run(A, B, bt, sync, stages, out=C)
+        assert_within_tol(got[rows], ref, "%s %s/%d (sampled %d rows)" % (which, sync, stages, len(rows)))
+        if first is None:
+            first = got
+        else:
+            np.testing.assert_array_equal(got, first, err_msg="modes disagree bitwise")
+    del A, B, C
+    torch.cuda.empty_cache()
