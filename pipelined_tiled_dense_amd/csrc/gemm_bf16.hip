@@ -370,7 +370,10 @@ __device__ __forceinline__ void wait_lgkm0()
 // for one position are cut into `nparts` contiguous runs.
 constexpr int part_begin(int part, int nparts, int loads) { return part * loads / nparts; }
 
-template <class C, bool LONGK>
+// EDGE: the loads mask the k tail inside a row and the columns past N of a
+// K x N B tile per lane.  Without EDGE every position is whole (K a multiple
+// of BK, and N of BN for a K x N B), so there is nothing to mask.
+template <class C, bool LONGK, bool EDGE = true>
 struct Loader {
     int32_t total;                // positions in this workgroup's stream
     int32_t n_tiles;
@@ -534,12 +537,12 @@ struct Loader {
                                              int lane) const
     {
         if (t < C::A_LOADS) {
-            const bool ok = kofs_k(slot(t, lw, lane)) < r.krem;
+            const bool ok = !EDGE || kofs_k(slot(t, lw, lane)) < r.krem;
             lds_dma16(r.ra, a_tile + (t * C::NLW + lw) * 1024, ok ? voffA[t] : kOOB, r.soa);
         } else {
             const int tb = t - C::A_LOADS;
             const int s = slot(tb, lw, lane);
-            const bool ok = C::BT ? (kofs_k(s) < r.krem) : (nofs_n(s) < r.nrem);
+            const bool ok = !EDGE || (C::BT ? (kofs_k(s) < r.krem) : (nofs_n(s) < r.nrem));
             lds_dma16(r.rb, b_tile + (tb * C::NLW + lw) * 1024, ok ? voffB[tb] : kOOB, r.sob);
         }
     }
@@ -977,7 +980,7 @@ __global__ void __launch_bounds__(256) k_reduce_splits(Params p, int32_t bm, int
 // ---------------------------------------------------------------------------
 // Kernel: every wave loads and computes (GEMM_SYNC_BARRIER, GEMM_SYNC_FLAGS).
 // ---------------------------------------------------------------------------
-template <class C, bool LONGK>
+template <class C, bool LONGK, bool EDGE>
 __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
 {
     static_assert(C::SYNC != SYNC_WAVESPEC, "wave-specialised configs use k_gemm_ws");
@@ -1002,7 +1005,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
 
     if (total == 0)
         return;
-    Loader<C, LONGK> ld;
+    Loader<C, LONGK, EDGE> ld;
     ld.init(p, n_tiles, w, lane);
 #pragma unroll
     for (int q = 0; q < C::S - 1; ++q)
@@ -1062,10 +1065,10 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
     // barrier its instructions would delay every wave's arrival).
     constexpr bool PIR = C::PREP_IN_REGION;
     sync_next(0, 0);
-    typename Loader<C, LONGK>::Prep fire_prep = ld.prepare_and_advance(p);      // position S - 1
+    typename Loader<C, LONGK, EDGE>::Prep fire_prep = ld.prepare_and_advance(p);      // position S - 1
     if constexpr (C::SYNC == SYNC_BARRIER)
         ld.template fire<NPARTS>(fire_prep, 0, stage_at(C::S - 1), w, lane);
-    typename Loader<C, LONGK>::Prep next_prep = fire_prep;
+    typename Loader<C, LONGK, EDGE>::Prep next_prep = fire_prep;
     if constexpr (!PIR)
         next_prep = ld.prepare_and_advance(p);                                  // position S
     read_frags<C>(fr[0], smem, wm, wn, lane, 0);
@@ -1192,7 +1195,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
 //             loads may still be outstanding); barrier; first half of
 //             B(c+2); fragments of k-step 0 of position c+1
 // ---------------------------------------------------------------------------
-template <class C, bool LONGK>
+template <class C, bool LONGK, bool EDGE>
 __global__ void __launch_bounds__(C::THREADS) k_gemm_win(Params p)
 {
     static_assert(C::WIN && C::SYNC == SYNC_BARRIER, "window-ring configs only");
@@ -1211,9 +1214,9 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_win(Params p)
     constexpr int AH = C::A_LOADS / 2, BH = C::B_LOADS / 2;   // DMA instructions per half tile
     auto win = [&](int i) { return smem + i * C::A_BYTES; };
     auto step5 = [](int i, int d) { return i + d >= 5 ? i + d - 5 : i + d; };
-    using Prep = typename Loader<C, LONGK>::Prep;
+    using Prep = typename Loader<C, LONGK, EDGE>::Prep;
 
-    Loader<C, LONGK> ld;
+    Loader<C, LONGK, EDGE> ld;
     ld.init(p, n_tiles, w, lane);
     // Prologue: positions 0 and 1 whole except the second half of B(1),
     // which region 0 of k-step 0 issues like any other.
@@ -1445,19 +1448,29 @@ struct Pick<SYNC_BARRIER, GEMM_STAGES_WINDOWS> {
 template <class C>
 int launch(const Params& p, int64_t grid, hipStream_t stream)
 {
+    // Whole positions only (no per-lane edge masks) when K is a multiple of
+    // the k-step and, for a K x N B, N of the tile width.  Split chunks are
+    // multiples of 64 elements, so they split K evenly.
+    const bool edge = (p.ksplit % C::BK != 0) || (!C::BT && p.N % C::BN != 0);
+    const bool longk = p.k_steps >= C::LONGK_MIN_KT && p.small_span;
+    const dim3 g((unsigned)grid), b(C::THREADS);
     if constexpr (C::SYNC == SYNC_WAVESPEC)
-        hipLaunchKernelGGL(k_gemm_ws<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+        hipLaunchKernelGGL(k_gemm_ws<C>, g, b, 0, stream, p);
     else if constexpr (C::WIN) {
-        if (p.k_steps >= C::LONGK_MIN_KT && p.small_span)
-            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_win<C, true>), dim3((unsigned)grid), dim3(C::THREADS), 0,
-                               stream, p);
+        if (longk && !edge)
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_win<C, true, false>), g, b, 0, stream, p);
+        else if (longk)
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_win<C, true, true>), g, b, 0, stream, p);
         else
-            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_win<C, false>), dim3((unsigned)grid), dim3(C::THREADS), 0,
-                               stream, p);
-    } else if (p.k_steps >= C::LONGK_MIN_KT && p.small_span)
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm<C, true>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
-    else
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm<C, false>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_win<C, false, true>), g, b, 0, stream, p);
+    } else {
+        if (longk && !edge)
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm<C, true, false>), g, b, 0, stream, p);
+        else if (longk)
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm<C, true, true>), g, b, 0, stream, p);
+        else
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm<C, false, true>), g, b, 0, stream, p);
+    }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
