@@ -48,7 +48,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--sync", default="all", choices=["all", "barrier", "flags", "wavespec", "barrier-windows"])
+    ap.add_argument("--sync", default="all",
+                    choices=["all", "barrier", "flags", "wavespec", "pingpong", "barrier-windows"])
     ap.add_argument("--stages", type=int, default=0)
     ap.add_argument("--workload", default="gemm8192_nk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -87,14 +88,14 @@ def _counter_per_dispatch(path, counter, name_filter):
     return sum(per.values()) / len(per), len(per)
 
 
-SYNC_NAMES = {0: "barrier", 1: "flags", 2: "wavespec"}
+SYNC_NAMES = {0: "barrier", 1: "flags", 2: "wavespec", 3: "pingpong"}
 # Timed configurations: label -> (sync mode, stages; 0 = the mode's default).
 # "barrier-windows" is barrier sync over the split-window ring.
 # They run in this order: the first launches of a process meet a cool chip
 # whose clock then settles under the power limit, so the slowest mode (never
 # the headline) goes first.
-MODE_RUNS = {"wavespec": ("wavespec", 0), "flags": ("flags", 0), "barrier": ("barrier", 0),
-             "barrier-windows": ("barrier", 5)}
+MODE_RUNS = {"pingpong": ("pingpong", 0), "wavespec": ("wavespec", 0), "flags": ("flags", 0),
+             "barrier": ("barrier", 0), "barrier-windows": ("barrier", 5)}
 
 
 def cfg_fields(kname):
@@ -236,7 +237,7 @@ def other_workloads(bd, skip, args, torch):
         C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
         flops = 2.0 * w.M * w.N * w.K
         per_mode = {}
-        for m in ("wavespec", "flags", "barrier"):
+        for m in ("pingpong", "wavespec", "flags", "barrier"):
             _, per = time_mode(bd, dA, dB, C, w, m, 0, args.steps, args.warmup, torch)
             per_mode[m] = flops / (sum(per) / len(per) * 1e-3) / 1e12
         best = max(per_mode, key=per_mode.get)
@@ -290,7 +291,7 @@ def main():
     C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
     modes = list(MODE_RUNS) if args.sync == "all" else [args.sync]
     if args.stages != 0 and args.sync == "all":
-        modes = ["wavespec", "flags", "barrier"]
+        modes = ["pingpong", "wavespec", "flags", "barrier"]
     flops = 2.0 * w.M * w.N * w.K
     results = {}
     for m in modes:
@@ -338,6 +339,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_per_launch(w.name, r["sync"], r["stages"]),
                      "kernel": ("k_gemm_ws (%d stages)" % r["stages"] if r["sync"] == "wavespec"
+                                else "k_gemm_pp (%d stages)" % r["stages"] if r["sync"] == "pingpong"
                                 else "k_gemm_win (split-window ring)" if r["stages"] == 5
                                 else "k_gemm (%s, %d stages)" % (r["sync"], r["stages"]))},
     }

@@ -28,7 +28,10 @@
  *     "loaded" (RAW) and "fully read" (WAR) counters (GEMM_SYNC_FLAGS, that
  *     page's second listing), or by the same counters between dedicated
  *     loader waves and MFMA waves (GEMM_SYNC_WAVESPEC, the producer/consumer
- *     split of "Allow separate sub-DAG ...", section "Pseudo-code").
+ *     split of "Allow separate sub-DAG ...", section "Pseudo-code"), or by
+ *     those counters between loader waves and two groups of MFMA waves that
+ *     take the output tiles in turn (GEMM_SYNC_PINGPONG, the ping-pong matmul
+ *     that page's section "Why?" names).
  *
  * Memory ownership: A, B and C are device pointers owned by the caller, on
  * the HIP device that is current when the call is made.  The library never
@@ -67,7 +70,9 @@ extern "C" {
 enum {
     GEMM_SYNC_BARRIER = 0,  /* one s_barrier per k-step covers RAW and WAR */
     GEMM_SYNC_FLAGS = 1,    /* per-stage full/empty LDS counters, every wave loads and computes */
-    GEMM_SYNC_WAVESPEC = 2  /* per-stage counters between loader waves and MFMA waves */
+    GEMM_SYNC_WAVESPEC = 2, /* per-stage counters between loader waves and MFMA waves */
+    GEMM_SYNC_PINGPONG = 3  /* as GEMM_SYNC_WAVESPEC, with two MFMA wave groups taking output
+                               tiles in turn: one group's epilogue overlaps the other's MFMAs */
 };
 
 /*
@@ -110,7 +115,7 @@ typedef struct gemm_bf16_plan {
     int32_t sync_mode;        /* GEMM_SYNC_* */
     int32_t b_transposed;     /* 1 for gemm_bf16_bt */
     int32_t mfma_waves;       /* waves that run the matrix-core loop */
-    int32_t producer_waves;   /* dedicated loader waves (GEMM_SYNC_WAVESPEC), else 0 */
+    int32_t producer_waves;   /* dedicated loader waves (GEMM_SYNC_WAVESPEC, GEMM_SYNC_PINGPONG), else 0 */
     int32_t threads;          /* threads per workgroup */
     int32_t lds_bytes;        /* LDS per workgroup */
     int64_t tiles;            /* output tiles: ceil(M/bm) * ceil(N/bn) */
@@ -132,7 +137,8 @@ typedef struct gemm_bf16_plan {
  *
  * stages: 0 picks the default for the sync mode; otherwise 2, 3 or 4 whole
  * stages, or GEMM_STAGES_WINDOWS (barrier sync only).
- * sync_mode: GEMM_SYNC_BARRIER, GEMM_SYNC_FLAGS or GEMM_SYNC_WAVESPEC.
+ * sync_mode: GEMM_SYNC_BARRIER, GEMM_SYNC_FLAGS, GEMM_SYNC_WAVESPEC or
+ * GEMM_SYNC_PINGPONG.
  * stream: a hipStream_t (NULL for the null stream).
  *
  * Returns GEMM_OK once the work is enqueued, else a negative status; on a

@@ -22,7 +22,7 @@ GEMM_ERR_DEVICE = -6
 GEMM_ERR_LAUNCH = -7
 GEMM_ERR_ALIAS = -8
 
-SYNC_MODES = {"barrier": 0, "flags": 1, "wavespec": 2}
+SYNC_MODES = {"barrier": 0, "flags": 1, "wavespec": 2, "pingpong": 3}
 STAGES_WINDOWS = 5          # GEMM_STAGES_WINDOWS: the split-window ring (barrier sync)
 
 

@@ -138,7 +138,12 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_char* ds
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)dst, 16, voff, (int)soff, 0, 0);
 }
 
-enum { SYNC_BARRIER = GEMM_SYNC_BARRIER, SYNC_FLAGS = GEMM_SYNC_FLAGS, SYNC_WAVESPEC = GEMM_SYNC_WAVESPEC };
+enum {
+    SYNC_BARRIER = GEMM_SYNC_BARRIER,
+    SYNC_FLAGS = GEMM_SYNC_FLAGS,
+    SYNC_WAVESPEC = GEMM_SYNC_WAVESPEC,
+    SYNC_PINGPONG = GEMM_SYNC_PINGPONG
+};
 
 // ---------------------------------------------------------------------------
 // Compile-time configuration of one kernel instance.
@@ -153,9 +158,13 @@ struct Cfg {
     // whole stages; the epilogue stages through a drained window.
     static constexpr bool WIN = WIN_;
     static constexpr int NWIN = WIN ? 5 : 0;
-    static constexpr int NCW = WM * WN;             // MFMA waves
-    static constexpr int NP = (SYNC == SYNC_WAVESPEC) ? NP_ : 0;   // dedicated loader waves
-    static constexpr int NLW = (SYNC == SYNC_WAVESPEC) ? NP : NCW; // waves that load
+    // Dedicated loader waves in the wave-specialised and ping-pong modes.
+    static constexpr bool PRODUCERS = SYNC == SYNC_WAVESPEC || SYNC == SYNC_PINGPONG;
+    static constexpr int GROUPS = (SYNC == SYNC_PINGPONG) ? 2 : 1; // MFMA wave groups taking tiles in turn
+    static constexpr int NCWG = WM * WN;            // MFMA waves per group: one output tile
+    static constexpr int NCW = GROUPS * NCWG;       // MFMA waves
+    static constexpr int NP = PRODUCERS ? NP_ : 0;  // dedicated loader waves
+    static constexpr int NLW = PRODUCERS ? NP : NCW; // waves that load
     static constexpr int NW = NCW + NP;
     static constexpr int THREADS = NW * 64;
     static constexpr int TM = BM / WM, TN = BN / WN;                 // wave tile
@@ -983,7 +992,7 @@ __global__ void __launch_bounds__(256) k_reduce_splits(Params p, int32_t bm, int
 template <class C, bool LONGK, bool EDGE>
 __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
 {
-    static_assert(C::SYNC != SYNC_WAVESPEC, "wave-specialised configs use k_gemm_ws");
+    static_assert(!C::PRODUCERS, "configs with loader waves use k_gemm_ws / k_gemm_pp");
     __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS_BYTES];
     lds_char* smem = (lds_char*)smem_raw;
     const int lane = threadIdx.x & 63;
@@ -1308,6 +1317,42 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_win(Params p)
 }
 
 // ---------------------------------------------------------------------------
+// Loader waves of the wave-specialised and ping-pong kernels.
+// ---------------------------------------------------------------------------
+template <class C>
+__device__ __forceinline__ void producer_loop(const Params& p, lds_char* smem, lds_u32* full, lds_u32* empty,
+                                              int32_t n_tiles, int lw, int lane)
+{
+    const int32_t total = n_tiles * p.k_steps;
+    // Loader wave: one flat loop over (tile, k-step) positions.  The data
+    // of position q is announced on full[] once it has landed, D positions
+    // later (the wave keeps D + 1 positions of loads in flight).  Issuing
+    // position q waits for the release of position q - S, so announcing
+    // q - D then depends on the consumers having finished q - S; D = S - 2
+    // leaves them one computed stage of slack (a larger lag would make
+    // every stage wait for that release-issue-announce chain).
+    constexpr int D = (C::S - 2 < 2) ? C::S - 2 : 2;
+    Loader<C, false> ld;
+    ld.init(p, n_tiles, lw, lane);
+    bool failed = false;
+    for (int32_t q = 0; q < total; ++q) {
+        const int s = q % C::S;
+        // Each use of a stage is released by the NCWG MFMA waves of the one
+        // group that computes the position.
+        if (q >= C::S)
+            wait_counter(empty + s, (uint32_t)(q / C::S) * C::NCWG, failed);
+        ld.issue_next(p, smem + s * C::STAGE_BYTES, lw, lane);
+        if (q >= D) {
+            wait_vmcnt<C::LOADS * D>();
+            arrive(full + (q - D) % C::S);
+        }
+    }
+    wait_vmcnt<0>();
+    for (int32_t q = (total > D ? total - D : 0); q < total; ++q)
+        arrive(full + q % C::S);
+}
+
+// ---------------------------------------------------------------------------
 // Kernel: dedicated loader waves and MFMA waves (GEMM_SYNC_WAVESPEC).
 // ---------------------------------------------------------------------------
 template <class C>
@@ -1330,31 +1375,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
     const int32_t total = n_tiles * KT;
 
     if (w >= C::NCW) {
-        // Loader wave: one flat loop over (tile, k-step) positions.  The data
-        // of position q is announced on full[] once it has landed, D positions
-        // later (the wave keeps D + 1 positions of loads in flight).  Issuing
-        // position q waits for the release of position q - S, so announcing
-        // q - D then depends on the consumers having finished q - S; D = S - 2
-        // leaves them one computed stage of slack (a larger lag would make
-        // every stage wait for that release-issue-announce chain).
-        const int lw = w - C::NCW;
-        constexpr int D = (C::S - 2 < 2) ? C::S - 2 : 2;
-        Loader<C, false> ld;
-        ld.init(p, n_tiles, lw, lane);
-        bool failed = false;
-        for (int32_t q = 0; q < total; ++q) {
-            const int s = q % C::S;
-            if (q >= C::S)
-                wait_counter(empty + s, (uint32_t)(q / C::S) * C::NCW, failed);
-            ld.issue_next(p, smem + s * C::STAGE_BYTES, lw, lane);
-            if (q >= D) {
-                wait_vmcnt<C::LOADS * D>();
-                arrive(full + (q - D) % C::S);
-            }
-        }
-        wait_vmcnt<0>();
-        for (int32_t q = (total > D ? total - D : 0); q < total; ++q)
-            arrive(full + q % C::S);
+        producer_loop<C>(p, smem, full, empty, n_tiles, w - C::NCW, lane);
         return;
     }
 
@@ -1407,6 +1428,92 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Kernel: loader waves and two MFMA wave groups that take the output tiles in
+// turn (GEMM_SYNC_PINGPONG).
+//
+// The loader waves stream the workgroup's (tile, k-step) positions in order,
+// exactly as in the wave-specialised kernel.  MFMA group g computes the
+// workgroup's tiles g, g + 2, ...: it waits for and releases only the
+// positions of its own tiles, and each position is released by the one
+// group that computes it.  While group g converts and stores its tile, the
+// other group is already computing the next tile from the positions the
+// loaders keep streaming, so the epilogue overlaps MFMA work; the two
+// groups' main loops alternate.  A group's first wait for a tile lasts about
+// one tile of the other group (far inside the bounded wait).
+// ---------------------------------------------------------------------------
+template <class C>
+__global__ void __launch_bounds__(C::THREADS) k_gemm_pp(Params p)
+{
+    static_assert(C::SYNC == SYNC_PINGPONG && C::GROUPS == 2, "k_gemm_pp");
+    __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS_BYTES];
+    lds_char* smem = (lds_char*)smem_raw;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    lds_u32* full = (lds_u32*)(smem + C::FLAG_OFFSET);
+    lds_u32* empty = full + C::S;
+    if (threadIdx.x < 2 * C::S)
+        full[threadIdx.x] = 0u;
+    __syncthreads();   // counters are initialised before the roles split
+
+    const int32_t G = gridDim.x, b = blockIdx.x;
+    const int32_t n_tiles = (b < p.tiles) ? (p.tiles - 1 - b) / G + 1 : 0;
+    const int32_t KT = p.k_steps;
+
+    if (w >= C::NCW) {
+        producer_loop<C>(p, smem, full, empty, n_tiles, w - C::NCW, lane);
+        return;
+    }
+
+    // MFMA wave of group g: its tiles { wait full; read; release; MFMA } epilogue.
+    const int g = w / C::NCWG, wg = w % C::NCWG;
+    const int wm = wg / C::WN, wn = wg % C::WN;
+    lds_char* strip = smem + C::EPI_OFFSET + w * C::EPI_WAVE_BYTES;
+    auto stage_of = [&](int32_t q) { return smem + (q % C::S) * C::STAGE_BYTES; };
+    Frags<C> fr[2];
+    bool failed = false;
+    for (int32_t it = g; it < n_tiles; it += 2) {
+        int32_t tm, tn;
+        int32_t sp;
+        tile_coords(p, b + it * G, G, tm, tn, sp);
+        int32_t c = it * KT;
+        wait_counter(full + c % C::S, (uint32_t)(c / C::S + 1) * C::NP, failed);
+        read_frags<C>(fr[0], stage_of(c), wm, wn, lane, 0);
+        f32x16_t acc[C::FM][C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                acc[i][j] = f32x16_t{};
+        for (int32_t kt = 0; kt < KT; ++kt, ++c) {
+            const lds_char* stage = stage_of(c);
+#pragma unroll
+            for (int kk = 0; kk < C::KK; ++kk) {
+                if (kk + 1 < C::KK) {
+                    read_frags<C>(fr[(kk + 1) & 1], stage, wm, wn, lane, kk + 1);
+                } else {
+                    wait_lgkm0();
+                    arrive(empty + c % C::S);
+                    // The group's next position within this tile; the next
+                    // tile's first position is waited for after the epilogue.
+                    if (kt + 1 < KT) {
+                        wait_counter(full + (c + 1) % C::S, (uint32_t)((c + 1) / C::S + 1) * C::NP, failed);
+                        read_frags<C>(fr[0], stage_of(c + 1), wm, wn, lane, 0);
+                    }
+                }
+                mfma_step<C>(acc, fr[kk & 1]);
+                if (kk + 1 < C::KK)
+                    sched_slots<C::FM * C::FN, frag_reads<C>(), 0>();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if (p.splits > 1)
+            store_partial<C>(p, acc, (sp * p.tiles_mn + tm * p.tiles_n + tn), wm, wn, lane);
+        else
+            store_tile<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
+    }
+}
+
 // C = 0 for K == 0 (16-byte stores, range-checked like the epilogue).
 __global__ void __launch_bounds__(256) k_zero_fill(char* C, int64_t M, int64_t N, int64_t ldc)
 {
@@ -1437,6 +1544,16 @@ struct Pick {
                      (SYNC == SYNC_WAVESPEC) ? 4 : 0>;
 };
 
+// Ping-pong: each of the two MFMA groups needs a wave on every SIMD, so
+// with the loader waves a SIMD holds three waves and each has about a third
+// of the register file: the groups' tiles are 128 x 128 (4 waves of 64 x 64).
+// A stage is 32 KiB at 64-wide k-steps, so up to 4 stages fit.
+template <int S>
+struct Pick<SYNC_PINGPONG, S> {
+    template <bool BT>
+    using type = Cfg<128, 128, 64, S, 2, 2, SYNC_PINGPONG, BT, 4>;
+};
+
 // The split-window ring: the two-stage barrier instance's tile, waves and
 // k-step over five windows (stages == GEMM_STAGES_WINDOWS).
 template <>
@@ -1456,6 +1573,8 @@ int launch(const Params& p, int64_t grid, hipStream_t stream)
     const dim3 g((unsigned)grid), b(C::THREADS);
     if constexpr (C::SYNC == SYNC_WAVESPEC)
         hipLaunchKernelGGL(k_gemm_ws<C>, g, b, 0, stream, p);
+    else if constexpr (C::SYNC == SYNC_PINGPONG)
+        hipLaunchKernelGGL(k_gemm_pp<C>, g, b, 0, stream, p);
     else if constexpr (C::WIN) {
         if (longk && !edge)
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_win<C, true, false>), g, b, 0, stream, p);
@@ -1496,6 +1615,7 @@ auto with_cfg(int sync_mode, int stages, bool bt, F&& f)
     PTD_PICK(SYNC_BARRIER, GEMM_STAGES_WINDOWS)
     PTD_PICK(SYNC_FLAGS, 2) PTD_PICK(SYNC_FLAGS, 3) PTD_PICK(SYNC_FLAGS, 4)
     PTD_PICK(SYNC_WAVESPEC, 2) PTD_PICK(SYNC_WAVESPEC, 3)
+    PTD_PICK(SYNC_PINGPONG, 2) PTD_PICK(SYNC_PINGPONG, 3) PTD_PICK(SYNC_PINGPONG, 4)
 #undef PTD_PICK
     return bt ? f.template operator()<typename Pick<SYNC_WAVESPEC, 4>::template type<true>>()
               : f.template operator()<typename Pick<SYNC_WAVESPEC, 4>::template type<false>>();
@@ -1507,7 +1627,7 @@ auto with_cfg(int sync_mode, int stages, bool bt, F&& f)
 // three of the wave-specialised mode's 256 x 128.
 int default_stages(int sync_mode)
 {
-    return sync_mode == GEMM_SYNC_WAVESPEC ? 3 : 2;
+    return (sync_mode == GEMM_SYNC_WAVESPEC || sync_mode == GEMM_SYNC_PINGPONG) ? 3 : 2;
 }
 
 struct DeviceInfo {
@@ -1559,7 +1679,8 @@ constexpr int64_t kMaxSplits = 16;
 
 int validate_shape(int64_t M, int64_t N, int64_t K, int stages, int sync_mode)
 {
-    if (sync_mode != GEMM_SYNC_BARRIER && sync_mode != GEMM_SYNC_FLAGS && sync_mode != GEMM_SYNC_WAVESPEC)
+    if (sync_mode != GEMM_SYNC_BARRIER && sync_mode != GEMM_SYNC_FLAGS && sync_mode != GEMM_SYNC_WAVESPEC &&
+        sync_mode != GEMM_SYNC_PINGPONG)
         return GEMM_ERR_SYNC_MODE;
     if (stages != 0 && (stages < 2 || stages > 4) &&
         !(stages == GEMM_STAGES_WINDOWS && sync_mode == GEMM_SYNC_BARRIER))
@@ -1749,7 +1870,8 @@ const char* gemm_bf16_strerror(int status)
     case GEMM_ERR_MISALIGNED: return "misaligned operand (pointers need 16-byte alignment, leading dimensions a multiple of 8)";
     case GEMM_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (N and K must be multiples of 8; leading dimensions at most 2^22)";
     case GEMM_ERR_STAGES: return "stages must be 0 (default), 2, 3, 4, or 5 (split-window ring, barrier sync)";
-    case GEMM_ERR_SYNC_MODE: return "sync_mode must be GEMM_SYNC_BARRIER, GEMM_SYNC_FLAGS or GEMM_SYNC_WAVESPEC";
+    case GEMM_ERR_SYNC_MODE:
+        return "sync_mode must be GEMM_SYNC_BARRIER, GEMM_SYNC_FLAGS, GEMM_SYNC_WAVESPEC or GEMM_SYNC_PINGPONG";
     case GEMM_ERR_DEVICE: return "no usable device (the current HIP device must be gfx950)";
     case GEMM_ERR_LAUNCH: return "kernel launch failed";
     case GEMM_ERR_ALIAS: return "C overlaps A or B";

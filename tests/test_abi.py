@@ -74,13 +74,14 @@ def call(fn, M=64, N=64, K=64, A=ALIGNED, lda=64, B=2 * ALIGNED, ldb=64, C=4 * A
 
 @pytest.mark.parametrize("fn", [bd.gemm_bf16, bd.gemm_bf16_bt], ids=["kn", "nk"])
 def test_validation_errors(fn):
-    assert call(fn, sync=3) == bd.GEMM_ERR_SYNC_MODE
+    assert call(fn, sync=4) == bd.GEMM_ERR_SYNC_MODE
     assert call(fn, sync=-1) == bd.GEMM_ERR_SYNC_MODE
     assert call(fn, stages=1) == bd.GEMM_ERR_STAGES
     assert call(fn, stages=6) == bd.GEMM_ERR_STAGES
     # the split-window ring exists for barrier sync only
     assert call(fn, stages=bd.STAGES_WINDOWS, sync=1) == bd.GEMM_ERR_STAGES
     assert call(fn, stages=bd.STAGES_WINDOWS, sync=2) == bd.GEMM_ERR_STAGES
+    assert call(fn, stages=bd.STAGES_WINDOWS, sync=3) == bd.GEMM_ERR_STAGES
     assert call(fn, M=-1) == bd.GEMM_ERR_INVALID_VALUE
     assert call(fn, K=-8) == bd.GEMM_ERR_INVALID_VALUE
     assert call(fn, N=60) == bd.GEMM_ERR_UNSUPPORTED_SHAPE

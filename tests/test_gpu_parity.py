@@ -24,7 +24,8 @@ pytestmark = pytest.mark.gpu
 
 MODES = [("barrier", 2), ("barrier", 3), ("barrier", 4), ("barrier", bd.STAGES_WINDOWS),
          ("flags", 2), ("flags", 3), ("flags", 4),
-         ("wavespec", 2), ("wavespec", 3), ("wavespec", 4)]
+         ("wavespec", 2), ("wavespec", 3), ("wavespec", 4),
+         ("pingpong", 2), ("pingpong", 3), ("pingpong", 4)]
 TOL = 1e-2
 
 
@@ -179,11 +180,13 @@ def test_plans():
     want = {("barrier", 2): (256, 64, 8, 0), ("barrier", 3): (256, 32, 8, 0), ("barrier", 4): (256, 32, 8, 0),
             ("barrier", bd.STAGES_WINDOWS): (256, 64, 8, 0),
             ("flags", 2): (256, 64, 8, 0), ("flags", 3): (256, 32, 8, 0), ("flags", 4): (256, 32, 8, 0),
-            ("wavespec", 2): (128, 64, 4, 4), ("wavespec", 3): (128, 64, 4, 4), ("wavespec", 4): (128, 32, 4, 4)}
+            ("wavespec", 2): (128, 64, 4, 4), ("wavespec", 3): (128, 64, 4, 4), ("wavespec", 4): (128, 32, 4, 4),
+            ("pingpong", 2): (128, 64, 8, 4), ("pingpong", 3): (128, 64, 8, 4), ("pingpong", 4): (128, 64, 8, 4)}
     for (sync, stages), (bn, bk, mw, pw) in want.items():
+        bm = 128 if sync == "pingpong" else 256
         for bt in (False, True):
             pl = bd.gemm_bf16_plan(8192, 8192, 8192, bt, stages, bd.SYNC_MODES[sync])
-            assert (pl["bm"], pl["bn"], pl["bk"], pl["mfma_waves"], pl["producer_waves"]) == (256, bn, bk, mw, pw), \
+            assert (pl["bm"], pl["bn"], pl["bk"], pl["mfma_waves"], pl["producer_waves"]) == (bm, bn, bk, mw, pw), \
                 (sync, stages, pl)
             assert pl["stages"] == stages and pl["threads"] == 64 * (mw + pw), (sync, stages, pl)
             assert pl["lds_bytes"] <= 160 * 1024, (sync, stages, pl)
@@ -191,6 +194,8 @@ def test_plans():
     assert pl["lds_bytes"] == 5 * 256 * 64 * 2
     assert bd.gemm_bf16_plan(8192, 8192, 8192, True, 0, 0)["stages"] == 2
     assert bd.gemm_bf16_plan(8192, 8192, 8192, True, 0, 2)["stages"] == 3
+    assert bd.gemm_bf16_plan(8192, 8192, 8192, True, 0, 3)["stages"] == 3
+    assert bd.gemm_bf16_plan(8192, 8192, 8192, True, 0, 3)["tiles"] == 64 * 64
 
 
 def test_layouts_and_modes_bit_identical():
@@ -233,7 +238,7 @@ def test_degenerate_sizes():
     C = torch.full((4, 0), 7.0, dtype=torch.bfloat16, device=dev)
     bd.gemm(A, B[:, :0], out=C)
     # K == 0: C is set to +0 everywhere
-    for sync in ("barrier", "flags", "wavespec"):
+    for sync in ("barrier", "flags", "wavespec", "pingpong"):
         C = torch.full((300, 264), 7.0, dtype=torch.bfloat16, device=dev)
         bd.gemm(A[:0].new_empty((300, 0)), B.new_empty((0, 264)), out=C, sync=sync)
         torch.cuda.synchronize()
@@ -264,10 +269,12 @@ FULL = {
     "gemm256_kn": [("barrier", 2), ("flags", 2), ("wavespec", 4)],
     "gemm4096_kn": [("barrier", 2), ("barrier", 3), ("barrier", 4), ("flags", 2), ("flags", 3), ("flags", 4),
                     ("barrier", bd.STAGES_WINDOWS)],
-    "gemm8192_nk": [("barrier", 2), ("barrier", bd.STAGES_WINDOWS), ("barrier", 4), ("flags", 2), ("wavespec", 4)],
-    "longk1024_k32768_kn": [("barrier", 2), ("barrier", 3), ("barrier", 4), ("flags", 2), ("flags", 3), ("flags", 4)],
+    "gemm8192_nk": [("barrier", 2), ("barrier", bd.STAGES_WINDOWS), ("barrier", 4), ("flags", 2), ("wavespec", 4),
+                    ("pingpong", 3)],
+    "longk1024_k32768_kn": [("barrier", 2), ("barrier", 3), ("barrier", 4), ("flags", 2), ("flags", 3), ("flags", 4),
+                            ("pingpong", 2)],
     "tall32768x1024_k4096_kn": [("wavespec", 2), ("wavespec", 3), ("wavespec", 4), ("barrier", 2), ("flags", 2),
-                                ("barrier", bd.STAGES_WINDOWS)],
+                                ("barrier", bd.STAGES_WINDOWS), ("pingpong", 3)],
 }
 
 
@@ -330,7 +337,8 @@ def test_operand_over_2gib(which):
     ref = oracle.load().gemm_bf16(bits(A[torch.from_numpy(rows).cuda()].cpu()), bits(B.cpu()), bt)
     C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     first = None
-    for sync, stages in [("barrier", 2), ("barrier", bd.STAGES_WINDOWS), ("flags", 2), ("wavespec", 3)]:
+    for sync, stages in [("barrier", 2), ("barrier", bd.STAGES_WINDOWS), ("flags", 2), ("wavespec", 3),
+                         ("pingpong", 3)]:
         C.fill_(7.0)
         got = run(A, B, bt, sync, stages, out=C)
         assert_within_tol(got[rows], ref, "%s %s/%d (sampled %d rows)" % (which, sync, stages, len(rows)))
