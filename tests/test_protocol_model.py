@@ -1,0 +1,462 @@
+"""A CPU model of the ring protocols the kernels run, explored under random
+interleavings of their waves.
+
+Each wave is a generator that follows its kernel's sequence of operations on
+the LDS ring: DMA issues (which land later, in issue order per wave), waits on
+its own loads (vmcnt), arrivals on and waits for the per-stage "full" and
+"empty" counters, workgroup barriers, and the span during which it reads a
+stage's fragments.  A random scheduler interleaves the waves and lands loads
+at random moments.  The model checks, at every step:
+
+  - RAW: a wave starts reading a position only when every part of it has
+    landed in the position's stage;
+  - WAR: no load lands into or is issued to a stage while a wave reads it;
+  - liveness: the run ends with every wave finished (no deadlock);
+  - every position is read by exactly the waves that compute it.
+
+The configurations mirror the kernels: the all-wave kernel with full/empty
+counters (flags) and with one barrier per k-step (barrier), the loader/MFMA
+split (wavespec), and loader waves with two MFMA groups taking tiles in turn
+(pingpong), and the barrier kernel over the split-window ring (windows).
+Injected faults -- a wrong arrival count, a skipped WAR or RAW wait, an
+off-by-one RAW target, counters that do not start at zero, an announcement
+lag too long for the ring, a refill or an epilogue that is not fenced by the
+barrier -- must each be caught.
+"""
+import random
+
+import pytest
+
+
+class Violation(Exception):
+    pass
+
+
+class Deadlock(Exception):
+    pass
+
+
+class Ring:
+    """Shared state: the stages' contents, the counters, the readers."""
+
+    def __init__(self, S, parts, init_full=0, init_empty=0):
+        self.S = S
+        self.parts = parts                     # loading waves per position
+        self.full = [init_full] * S
+        self.empty = [init_empty] * S
+        self.landed = [dict() for _ in range(S)]   # stage -> {part: position}
+        self.readers = [set() for _ in range(S)]   # stage -> waves reading it
+        self.reads = {}                            # position -> waves that read it
+        self.barrier_count = 0
+
+    def issue(self, s, q):
+        if self.readers[s]:
+            raise Violation("WAR: load of position %r issued into stage %d while %s read it"
+                            % (q, s, sorted(self.readers[s])))
+
+    def land(self, s, part, q):
+        if self.readers[s]:
+            raise Violation("WAR: load of position %r landed in stage %d while %s read it"
+                            % (q, s, sorted(self.readers[s])))
+        self.landed[s][part] = q
+
+    def begin_read(self, w, s, q):
+        have = self.landed[s]
+        if len(have) != self.parts or any(v != q for v in have.values()):
+            raise Violation("RAW: wave %d reads position %r from stage %d holding %r" % (w, q, s, have))
+        self.readers[s].add(w)
+        self.reads.setdefault(q, set()).add(w)
+
+    def end_read(self, w, s):
+        self.readers[s].discard(w)
+
+
+class Wave:
+    """A wave's generator plus its queue of DMA loads in flight."""
+
+    def __init__(self, wid, gen):
+        self.wid = wid
+        self.gen = gen
+        self.inflight = []          # (stage, part, position), oldest first
+        self.cond = None            # callable: may the wave continue?
+        self.done = False
+
+
+def run(ring, waves, seed, max_steps=200000):
+    rng = random.Random(seed)
+    for w in waves:
+        w.cond = None
+    steps = 0
+    while True:
+        steps += 1
+        if steps > max_steps:
+            raise Deadlock("step limit")
+        live = [w for w in waves if not w.done]
+        landable = [w for w in waves if w.inflight]
+        if not live and not landable:
+            return
+        runnable = [w for w in live if w.cond is None or w.cond()]
+        choices = [("run", w) for w in runnable] + [("land", w) for w in landable]
+        if not choices:
+            raise Deadlock("no wave can move: %s" % [(w.wid, w.done) for w in waves])
+        kind, w = rng.choice(choices)
+        if kind == "land":
+            s, part, q = w.inflight.pop(0)
+            ring.land(s, part, q)
+            continue
+        try:
+            w.cond = next(w.gen)
+        except StopIteration:
+            w.done = True
+            w.cond = None
+
+
+def vm_wait(wave, n):
+    """Yield until at most n of the wave's loads are in flight."""
+    return lambda: len(wave.inflight) <= n
+
+
+def at_least(arr, i, target):
+    return lambda: arr[i] >= target
+
+
+# --- loader waves (wave-specialised and ping-pong kernels) ---------------------
+def loader(ring, wave, part, total, S, D, releasers, skip_war_wait=False):
+    for q in range(total):
+        s = q % S
+        if q >= S and not skip_war_wait:
+            yield at_least(ring.empty, s, (q // S) * releasers)
+        ring.issue(s, q)
+        wave.inflight.append((s, part, q))
+        yield None
+        if q >= D:
+            yield vm_wait(wave, D)
+            ring.full[(q - D) % S] += 1
+            yield None
+    yield vm_wait(wave, 0)
+    for q in range(max(total - D, 0), total):
+        ring.full[q % S] += 1
+        yield None
+
+
+# --- MFMA waves of the wave-specialised and ping-pong kernels -------------------
+def consumer(ring, wave, positions, S, NP, raw_off=0):
+    """positions: the flat positions this wave computes, in order (its group's
+    tiles).  It waits for a position's announcement, reads it, then releases."""
+    for q in positions:
+        s = q % S
+        yield at_least(ring.full, s, (q // S + 1) * NP - raw_off)
+        ring.begin_read(wave.wid, s, q)
+        yield None          # reading the stage's fragments
+        yield None
+        ring.end_read(wave.wid, s)
+        ring.empty[s] += 1
+        yield None
+
+
+# --- all-wave kernel, full/empty counters ----------------------------------------
+def flags_wave(ring, wave, total, S, NW, empty_target_scale=1, skip_full_wait=False):
+    """Each of the NW waves loads its part of every position and computes every
+    position.  Prologue: positions 0 .. S-2.  Then per k-step c: the load of
+    position c+S-1 goes out (its stage was released at the end of k-step c-1),
+    the wave reads position c, releases it, makes position c+1 readable (own
+    loads landed, arrive full, wait full), and at the end of the k-step waits
+    for every wave's release of position c."""
+    w = wave.wid
+    for q in range(S - 1):
+        ring.issue(q % S, q)
+        wave.inflight.append((q % S, w, q))
+        yield None
+    # position 0 readable
+    yield vm_wait(wave, S - 2)
+    ring.full[0] += 1
+    yield at_least(ring.full, 0, NW)
+    for c in range(total):
+        s_cur = c % S
+        q_new = c + S - 1                       # positions past the end load zeros
+        s_new = q_new % S
+        ring.issue(s_new, q_new)
+        wave.inflight.append((s_new, w, q_new))
+        ring.begin_read(w, s_cur, c)
+        yield None
+        ring.end_read(w, s_cur)
+        ring.empty[s_cur] += 1
+        s_nxt, g_nxt = (c + 1) % S, (c + 1) // S
+        yield vm_wait(wave, S - 2)
+        ring.full[s_nxt] += 1
+        if not skip_full_wait:
+            yield at_least(ring.full, s_nxt, (g_nxt + 1) * NW)
+        yield at_least(ring.empty, s_cur, (c // S + 1) * NW * empty_target_scale)
+    yield vm_wait(wave, 0)
+
+
+# --- all-wave kernel, one barrier per k-step ---------------------------------------
+def barrier_wave(ring, wave, total, S, NW, barrier, skip_vm=False):
+    """Loads of position c+S-1 go out after the barrier that ends k-step c-1
+    (every wave has finished reading that stage).  Before the barrier that
+    ends k-step c the wave waits for its own loads of position c+1."""
+    w = wave.wid
+    for q in range(S - 1):
+        ring.issue(q % S, q)
+        wave.inflight.append((q % S, w, q))
+        yield None
+    yield vm_wait(wave, S - 2)
+    yield from barrier(wave)
+    for c in range(total):
+        s_cur = c % S
+        q_new = c + S - 1
+        ring.issue(q_new % S, q_new)
+        wave.inflight.append((q_new % S, w, q_new))
+        ring.begin_read(w, s_cur, c)
+        yield None
+        ring.end_read(w, s_cur)
+        if not skip_vm:
+            yield vm_wait(wave, S - 2)
+        yield from barrier(wave)
+    yield vm_wait(wave, 0)
+
+
+def make_barrier(NW):
+    state = {"arrived": 0}
+
+    def barrier(wave):
+        state["arrived"] += 1
+        target = -(-state["arrived"] // NW) * NW     # the generation this wave joined
+        yield lambda: state["arrived"] >= target
+    return barrier
+
+
+# --- all-wave kernel over the split-window ring ----------------------------------
+def window_wave(ring, wave, total, KT, NW, barrier, skip_epi_barrier=False, vm_slack=0,
+                early_refill=False):
+    """Five windows; position q keeps its A tile in window 2q mod 5 and its B
+    tile in window 2q+1 mod 5.  Every wave loads two parts of each tile.  Per
+    k-step c: region 0 issues the second part of B(c+1); regions 1-2 the two
+    parts of A(c+2); region 3 ends the reads of position c, waits for its own
+    loads up to B(c+1), passes the barrier, issues the first part of B(c+2)
+    into A(c)'s window and starts reading position c+1.  After a tile's last
+    k-step the wave stages its epilogue in B(c)'s window, then a barrier,
+    before A(c+3) reuses that window."""
+    w = wave.wid
+    win_a = lambda q: (2 * q) % 5
+    win_b = lambda q: (2 * q + 1) % 5
+
+    def issue(win, tag, q, part):
+        ring.issue(win, q)
+        wave.inflight.append((win, (w, part), (tag, q)))
+
+    for part in (0, 1):
+        issue(win_a(0), "A", 0, part)
+    for part in (0, 1):
+        issue(win_b(0), "B", 0, part)
+    for part in (0, 1):
+        issue(win_a(1), "A", 1, part)
+    issue(win_b(1), "B", 1, 0)
+    yield None
+    yield vm_wait(wave, 3)                      # A(1) and B(1) part 0 may be in flight
+    yield from barrier(wave)
+    ring.begin_read(w, win_a(0), ("A", 0))
+    ring.begin_read(w, win_b(0), ("B", 0))
+    for c in range(total):
+        issue(win_b(c + 1), "B", c + 1, 1)      # region 0
+        yield None
+        issue(win_a(c + 2), "A", c + 2, 0)      # region 1
+        yield None
+        issue(win_a(c + 2), "A", c + 2, 1)      # region 2
+        yield None
+        if early_refill:
+            issue(win_b(c + 2), "B", c + 2, 0)
+        ring.end_read(w, win_a(c))              # region 3: reads of c done
+        ring.end_read(w, win_b(c))
+        yield vm_wait(wave, 2 + vm_slack)       # only A(c+2) may be in flight
+        yield from barrier(wave)
+        if not early_refill:
+            issue(win_b(c + 2), "B", c + 2, 0)
+        if c + 1 < total:
+            ring.begin_read(w, win_a(c + 1), ("A", c + 1))
+            ring.begin_read(w, win_b(c + 1), ("B", c + 1))
+        yield None
+        if c % KT == KT - 1:                    # epilogue in B(c)'s window
+            # wave-private strips: other waves' strips may share the window,
+            # fragment reads and loads may not (landing checks the strips)
+            busy = [r for r in ring.readers[win_b(c)] if not (isinstance(r, tuple) and r[0] == "strip")]
+            if busy:
+                raise Violation("epilogue strip in window %d while %s read it" % (win_b(c), busy))
+            ring.readers[win_b(c)].add(("strip", w))
+            yield None
+            ring.readers[win_b(c)].discard(("strip", w))
+            if not skip_epi_barrier:
+                yield from barrier(wave)
+    yield vm_wait(wave, 0)
+
+
+def run_windows(NW, n_tiles, KT, seed, **faults):
+    ring = Ring(5, 2 * NW)
+    barrier = make_barrier(NW)
+    waves = []
+    for w in range(NW):
+        wv = Wave(w, None)
+        wv.gen = window_wave(ring, wv, n_tiles * KT, KT, NW, barrier, **faults)
+        waves.append(wv)
+    run(ring, waves, seed)
+    for q in range(n_tiles * KT):
+        assert ring.reads.get(("A", q)) == set(range(NW)), q
+        assert ring.reads.get(("B", q)) == set(range(NW)), q
+
+
+# --- harnesses -------------------------------------------------------------------
+def run_producer_consumer(S, NP, NCWG, groups, n_tiles, KT, seed, releasers=None, D=None,
+                          skip_war_wait=False, raw_off=0, init=0):
+    total = n_tiles * KT
+    ring = Ring(S, NP, init_full=init, init_empty=init)
+    D = (min(S - 2, 2) if D is None else D)
+    releasers = NCWG if releasers is None else releasers
+    waves = []
+    for g in range(groups):
+        tiles = range(g, n_tiles, groups)
+        positions = [it * KT + kt for it in tiles for kt in range(KT)]
+        for i in range(NCWG):
+            wv = Wave(len(waves), None)
+            wv.gen = consumer(ring, wv, positions, S, NP, raw_off)
+            waves.append(wv)
+    for part in range(NP):
+        wv = Wave(len(waves), None)
+        wv.gen = loader(ring, wv, part, total, S, D, releasers, skip_war_wait)
+        waves.append(wv)
+    run(ring, waves, seed)
+    # every position read by exactly the NCWG waves of the group that owns its tile
+    for q in range(total):
+        g = (q // KT) % groups
+        want = set(range(g * NCWG, (g + 1) * NCWG))
+        assert ring.reads.get(q) == want, (q, ring.reads.get(q), want)
+
+
+def run_flags(S, NW, total, seed, empty_target_scale=1, init=0, skip_full_wait=False):
+    ring = Ring(S, NW, init_full=init, init_empty=init)
+    waves = []
+    for w in range(NW):
+        wv = Wave(w, None)
+        wv.gen = flags_wave(ring, wv, total, S, NW, empty_target_scale, skip_full_wait)
+        waves.append(wv)
+    run(ring, waves, seed)
+    for q in range(total):
+        assert ring.reads.get(q) == set(range(NW)), q
+
+
+def run_barrier(S, NW, total, seed, skip_vm=False):
+    ring = Ring(S, NW)
+    barrier = make_barrier(NW)
+    waves = []
+    for w in range(NW):
+        wv = Wave(w, None)
+        wv.gen = barrier_wave(ring, wv, total, S, NW, barrier, skip_vm)
+        waves.append(wv)
+    run(ring, waves, seed)
+    for q in range(total):
+        assert ring.reads.get(q) == set(range(NW)), q
+
+
+SEEDS = range(12)
+
+
+@pytest.mark.parametrize("S", [2, 3, 4])
+@pytest.mark.parametrize("seed", SEEDS)
+def test_wavespec_protocol(S, seed):
+    run_producer_consumer(S, NP=4, NCWG=4, groups=1, n_tiles=3, KT=5, seed=seed)
+
+
+@pytest.mark.parametrize("S", [2, 3, 4])
+@pytest.mark.parametrize("seed", SEEDS)
+def test_pingpong_protocol(S, seed):
+    run_producer_consumer(S, NP=4, NCWG=4, groups=2, n_tiles=5, KT=4, seed=seed)
+
+
+@pytest.mark.parametrize("S", [2, 3, 4])
+@pytest.mark.parametrize("seed", SEEDS)
+def test_flags_protocol(S, seed):
+    run_flags(S, NW=4, total=11, seed=seed)
+
+
+@pytest.mark.parametrize("S", [2, 3, 4])
+@pytest.mark.parametrize("seed", SEEDS)
+def test_barrier_protocol(S, seed):
+    run_barrier(S, NW=4, total=11, seed=seed)
+
+
+@pytest.mark.parametrize("KT", [1, 2, 3, 5])
+@pytest.mark.parametrize("seed", SEEDS)
+def test_window_ring_protocol(KT, seed):
+    run_windows(NW=4, n_tiles=3, KT=KT, seed=seed)
+
+
+def test_one_tile_pingpong_second_group_idle():
+    for seed in SEEDS:
+        run_producer_consumer(3, NP=4, NCWG=4, groups=2, n_tiles=1, KT=6, seed=seed)
+
+
+# --- injected faults: each must be caught for some interleaving -----------------
+def caught(fn, seeds=range(40)):
+    for seed in seeds:
+        try:
+            fn(seed)
+        except (Violation, Deadlock, AssertionError):
+            return True
+    return False
+
+
+def test_fault_pingpong_release_count_of_all_mfma_waves():
+    """Loaders waiting for releases by all 8 MFMA waves, when one group of 4
+    releases each position, never see the stage freed."""
+    assert caught(lambda sd: run_producer_consumer(3, 4, 4, 2, 4, 4, sd, releasers=8))
+
+
+def test_fault_loader_skips_war_wait():
+    assert caught(lambda sd: run_producer_consumer(2, 4, 4, 1, 3, 5, sd, skip_war_wait=True))
+
+
+def test_fault_consumer_raw_target_off_by_one():
+    assert caught(lambda sd: run_producer_consumer(3, 4, 4, 1, 3, 5, sd, raw_off=1))
+
+
+def test_fault_counters_not_zeroed():
+    """Counters that start at a stale value let a consumer read a stage before
+    its loads land (the initialisation the counters rely on)."""
+    assert caught(lambda sd: run_producer_consumer(3, 4, 4, 1, 3, 5, sd, init=4))
+
+
+def test_fault_announce_lag_too_long():
+    """Announcing position q - D only after issuing q, with D = S - 1, makes
+    the announcement of a stage wait on its own release: no progress."""
+    assert caught(lambda sd: run_producer_consumer(3, 4, 4, 1, 3, 5, sd, D=3))
+
+
+@pytest.mark.parametrize("S", [2, 3, 4])
+def test_flags_war_wait_is_implied_by_the_raw_wait(S):
+    """In the all-wave kernel every wave releases position c before it announces
+    position c + 1, and the refill of c's stage goes out only after the wait
+    for c + 1's announcements.  So that wait already covers WAR: the model
+    stays safe with the empty-counter wait removed altogether."""
+    for seed in SEEDS:
+        run_flags(S, 4, 11, seed, empty_target_scale=0)
+
+
+def test_fault_flags_skip_full_wait():
+    assert caught(lambda sd: run_flags(2, 4, 9, sd, skip_full_wait=True))
+
+
+def test_fault_barrier_without_load_wait():
+    assert caught(lambda sd: run_barrier(2, 4, 9, sd, skip_vm=True))
+
+
+def test_fault_window_epilogue_without_barrier():
+    """Without the barrier after the epilogue, one wave's A(c+3) load can land
+    in the window another wave still stages its output tile in."""
+    assert caught(lambda sd: run_windows(4, 3, 2, sd, skip_epi_barrier=True))
+
+
+def test_fault_window_load_wait_misses_next_b():
+    assert caught(lambda sd: run_windows(4, 3, 3, sd, vm_slack=1))
+
+
+def test_fault_window_refill_before_barrier():
+    assert caught(lambda sd: run_windows(4, 3, 3, sd, early_refill=True))
