@@ -16,7 +16,7 @@
 //   every loading wave issues its own share and learns that its data has
 //   landed from its vector-memory counter (s_waitcnt vmcnt).
 //
-// * Two ring synchronisation schemes.  GEMM_SYNC_BARRIER: one workgroup
+// * Ring synchronisation.  GEMM_SYNC_BARRIER: one workgroup
 //   s_barrier per k-step, after each wave's own loads for the stage landed and
 //   its reads of the previous stage completed, covers both the read-after-write
 //   and the write-after-read hazard (the page's first listing, whose WAR guard
@@ -35,6 +35,20 @@
 //   zero and are read as "free" for a stage's first use, which is what the
 //   consumer's initial arrive on every empty barrier achieves there.  gfx950
 //   cannot move registers between roles, so all waves get one register budget.
+//
+// * Ping-pong (same page, section "Why?", which names ping-pong matmul
+//   kernels as a goal).  GEMM_SYNC_PINGPONG keeps the loader waves and splits
+//   the MFMA waves into two groups that take the workgroup's output tiles in
+//   turn; each position is released by the group that computes it, so one
+//   group's epilogue overlaps the other's main loop.
+//
+// * Split windows ("[WIP] SM120 fused backward kernel: exploratory
+//   shared-memory reduction", section "Shared-memory reduction strategies":
+//   buffer aliasing, and streaming one half of an operand while the other is
+//   computed on).  With barrier sync the ring can instead be five windows of
+//   one operand tile each: a k-step's A tile and B tile live in separate
+//   windows, the B tile of the k-step after next refills a drained window
+//   first, and the epilogue stages through a drained window.
 //
 // * Persistent scheduling (same page, sections "Context" and "Scheduling
 //   Proposal").  A grid of min(tiles, CUs) workgroups walks the output tiles
