@@ -348,3 +348,34 @@ def test_operand_over_2gib(which):
             np.testing.assert_array_equal(got, first, err_msg="modes disagree bitwise")
     del A, B, C
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("bt", [False, True], ids=["kn", "nk"])
+def test_max_leading_dimensions_with_poisoned_padding(bt):
+    """Leading dimensions at the accepted maximum (2^22 elements, so every
+    operand spans more than 2 GiB) with everything outside the operands'
+    M x K, K x N (or N x K) and M x N windows filled with NaN in A and B and a
+    sentinel in C: a load past K or N would put NaN into C, a store past N
+    would overwrite the sentinel.  Ragged in M, N and K; all modes."""
+    LD = 1 << 22
+    M, N, K = 300, 264, 1000 if bt else 264
+    A, B = make_operands(M, N, K, b_transposed=bt, seed=77 + bt)
+    dA = torch.full((M, LD), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dA[:, :K] = A.cuda()
+    rows_b, cols_b = (N, K) if bt else (K, N)
+    dB = torch.full((rows_b, LD), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dB[:, :cols_b] = B.cuda()
+    ref = oracle.load().gemm_bf16(bits(A), bits(B), bt)
+    Cbuf = torch.empty((M, LD), dtype=torch.bfloat16, device="cuda")
+    first = None
+    for sync, stages in MODES:
+        Cbuf[:, :N + 4096].fill_(3.0)
+        got = run(dA[:, :K], dB[:, :cols_b], bt, sync, stages, out=Cbuf[:, :N])
+        assert_within_tol(got, ref, "ld 2^22 %s/%d" % (sync, stages))
+        assert bool(torch.all(Cbuf[:, N:N + 4096] == 3.0)), (sync, stages)
+        if first is None:
+            first = got
+        else:
+            np.testing.assert_array_equal(got, first, err_msg="modes disagree bitwise")
+    del dA, dB, Cbuf
+    torch.cuda.empty_cache()
