@@ -96,6 +96,11 @@ SYNC_NAMES = {0: "barrier", 1: "flags", 2: "wavespec", 3: "pingpong"}
 # the headline) goes first.
 MODE_RUNS = {"pingpong": ("pingpong", 0), "wavespec": ("wavespec", 0), "flags": ("flags", 0),
              "barrier": ("barrier", 0), "barrier-windows": ("barrier", 5)}
+# Workloads whose configuration asks for a comparison of the two all-wave
+# synchronisation schemes over the ring depth: (sync, stages) runs, reported
+# as "sync/stages" -> TFLOP/s (stages 5 is the split-window ring).
+STAGE_SWEEPS = {"gemm4096_kn": (("flags", 2), ("flags", 3), ("flags", 4),
+                                ("barrier", 2), ("barrier", 3), ("barrier", 4), ("barrier", 5))}
 
 
 def cfg_fields(kname):
@@ -246,6 +251,12 @@ def other_workloads(bd, skip, args, torch):
                  "best_mode": best, "tflops": round(per_mode[best], 2),
                  "modes_tflops": {m: round(v, 2) for m, v in per_mode.items()},
                  "k_splits": plan["k_splits"]}
+        if name in STAGE_SWEEPS:
+            sweep = {}
+            for sync, stages in STAGE_SWEEPS[name]:
+                _, per = time_mode(bd, dA, dB, C, w, sync, stages, args.steps, args.warmup, torch)
+                sweep["%s/%d" % (sync, stages)] = round(flops / (sum(per) / len(per) * 1e-3) / 1e12, 2)
+            entry["sync_stages_tflops"] = sweep
         if not args.no_reference:
             entry["reference_tflops"] = reference_matmul(dA, dB, C, w, args.steps, args.warmup, torch)["tflops"]
         out[name] = entry

@@ -23,9 +23,9 @@
 //   is a block-wide barrier).  GEMM_SYNC_FLAGS: two monotonic counters per
 //   stage in LDS -- "full" (every loading wave's data for this use has landed)
 //   and "empty" (every reading wave has finished with it) -- the page's two
-//   signals per stage (the second listing).  The WAR wait is placed after the
-//   wave has issued its matrix-core work for the stage, so an MFMA never waits
-//   for a buffer it does not read (the page's motivation paragraph).
+//   signals per stage (the second listing).  A wave releases a stage as soon as
+//   its fragment reads have landed, ahead of its last MFMAs on them; the reads
+//   of both counters go out together and their round trip overlaps MFMAs.
 //
 // * Wave specialisation ("Allow separate sub-DAG for load and compute warp
 //   groups with warp-specialized circular buffering", section "Pseudo-code").
@@ -88,6 +88,7 @@ namespace {
 #define LDS_AS __attribute__((address_space(3)))
 typedef LDS_AS char lds_char;
 typedef LDS_AS uint32_t lds_u32;
+typedef LDS_AS uint64_t lds_u64;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
@@ -322,6 +323,77 @@ __device__ __forceinline__ void wait_counter(const lds_u32* ctr, uint32_t target
         if (spins > 8)
             __builtin_amdgcn_s_sleep(1);
     }
+    COMPILER_FENCE();
+}
+
+// The all-wave FLAGS kernel packs two signals into one 64-bit word per stage s:
+// the low half counts announcements of the position held in stage s ("full",
+// RAW), the high half counts releases of the position held in the stage
+// before it, s - 1 mod S ("empty", WAR).  Each wave moves from position c to
+// c + 1 by releasing c and announcing c + 1 in one atomic add, and one read
+// checks both signals.  Neither half carries into the other: each counts what
+// a separate 32-bit counter would, NW per use of a stage, which stays far
+// below 2^32 for every launch the host accepts.
+constexpr uint64_t kAnnounce = 1ull;
+constexpr uint64_t kRelease = 1ull << 32;
+
+__device__ __forceinline__ uint32_t lds_addr(const lds_u64* p)
+{
+    return (uint32_t)(uintptr_t)p;
+}
+
+__device__ __forceinline__ void arrive_pair(lds_u64* word, uint64_t inc)
+{
+    COMPILER_FENCE();
+    if ((threadIdx.x & 63) == 0)
+        asm volatile("ds_add_u64 %0, %1" ::"v"(lds_addr(word)), "v"(inc) : "memory");
+    COMPILER_FENCE();
+}
+
+// The read goes out now; wait_pair_issued, called after unrelated work,
+// completes it and polls again until both halves reach their targets.
+__device__ __forceinline__ uint64_t pair_read_issue(const lds_u64* word)
+{
+    uint64_t v;
+    asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(lds_addr(word)) : "memory");
+    return v;
+}
+
+__device__ __forceinline__ bool pair_reached(uint64_t v, uint32_t full_target, uint32_t empty_target)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return lo >= full_target && hi >= empty_target;
+}
+
+// Bounded like wait_counter.
+__device__ __forceinline__ void wait_pair(const lds_u64* word, uint32_t full_target, uint32_t empty_target,
+                                          bool& failed)
+{
+    uint32_t spins = 0;
+    for (;;) {
+        uint64_t v;
+        asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(word)) : "memory");
+        if (failed || pair_reached(v, full_target, empty_target))
+            break;
+        if (++spins > kSpinLimit) {
+            if ((threadIdx.x & 63) == 0)
+                atomicAdd(&g_sync_timeouts, 1ull);
+            failed = true;
+        }
+        if (spins > 8)
+            __builtin_amdgcn_s_sleep(1);
+    }
+    COMPILER_FENCE();
+}
+
+// Completes a read from pair_read_issue; polls on only if it came back short.
+__device__ __forceinline__ void wait_pair_issued(uint64_t v, const lds_u64* word, uint32_t full_target,
+                                                 uint32_t empty_target, bool& failed)
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v) : : "memory");
+    if (!pair_reached(v, full_target, empty_target))
+        wait_pair(word, full_target, empty_target, failed);
     COMPILER_FENCE();
 }
 
@@ -1012,12 +1084,12 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = w / C::WN, wn = w % C::WN;
-    lds_u32* full = (lds_u32*)(smem + C::FLAG_OFFSET);
-    lds_u32* empty = full + C::S;
+    static_assert(C::FLAG_OFFSET % 8 == 0, "64-bit signal words");
+    lds_u64* sig = (lds_u64*)(smem + C::FLAG_OFFSET);
 
     if constexpr (C::SYNC == SYNC_FLAGS) {
-        if (threadIdx.x < 2 * C::S)
-            full[threadIdx.x] = 0u;
+        if (threadIdx.x < C::S)
+            sig[threadIdx.x] = 0ull;
     }
     __syncthreads();   // counters are initialised before any wave can arrive
 
@@ -1059,23 +1131,20 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
         if constexpr (C::SYNC == SYNC_BARRIER) {
             block_barrier();
         } else {
-            arrive(full + s_nxt);
-            wait_counter(full + s_nxt, (g_nxt + 1) * C::NW, failed);
+            arrive_pair(sig + s_nxt, kAnnounce);
+            wait_pair_issued(pair_read_issue(sig + s_nxt), sig + s_nxt, (g_nxt + 1) * C::NW, 0u, failed);
         }
     };
 
     // A position's DMA is issued in parts, spread over the MFMA regions of the
     // following stage, so the texture path never receives a burst of every
-    // wave's loads at once: part 0 right after the barrier that frees its
-    // stage, the others with the next stage's first MFMA regions.  With three
-    // or more stages there is one part per region (KK).  With two stages the
-    // data is needed one stage later, so there are two parts: after the
-    // barrier and in the next stage's first region.
-    //
-    // FLAGS refills a stage only after waiting for its release at the end of
-    // a k-step, so the whole position goes out in the first MFMA region of
-    // the next k-step.
-    constexpr int NPARTS = (C::SYNC == SYNC_FLAGS) ? 1 : (C::S == 2) ? 2 : C::KK;
+    // wave's loads at once: part 0 right after the synchronisation that frees
+    // its stage, the others with the next stage's first MFMA regions.  With
+    // three or more stages there is one part per region (KK).  With two stages
+    // the data is needed one stage later, so there are two parts: after the
+    // synchronisation and in the next stage's first region.  Both sync modes
+    // share this schedule; they differ only in how the workgroup synchronises.
+    constexpr int NPARTS = (C::S == 2) ? 2 : C::KK;
     //
     // The load cursor's step is several dozen scalar instructions, and all
     // waves reach it together; they queue for the CU's one scalar unit.  With
@@ -1089,8 +1158,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
     constexpr bool PIR = C::PREP_IN_REGION;
     sync_next(0, 0);
     typename Loader<C, LONGK, EDGE>::Prep fire_prep = ld.prepare_and_advance(p);      // position S - 1
-    if constexpr (C::SYNC == SYNC_BARRIER)
-        ld.template fire<NPARTS>(fire_prep, 0, stage_at(C::S - 1), w, lane);
+    ld.template fire<NPARTS>(fire_prep, 0, stage_at(C::S - 1), w, lane);
     typename Loader<C, LONGK, EDGE>::Prep next_prep = fire_prep;
     if constexpr (!PIR)
         next_prep = ld.prepare_and_advance(p);                                  // position S
@@ -1128,11 +1196,10 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
                 if constexpr (PIR && kk == 1)
                     next_prep = ld.prepare_and_advance(p);
                 if constexpr (kk + 1 < C::KK) {
-                    // Fragments of k-step kk + 1; a part of the load of
+                    // Fragments of k-step kk + 1; part kk + 1 of the load of
                     // position c + S - 1 into the stage of position c - 1
-                    // (BARRIER: part kk + 1, part 0 went out after the last
-                    // barrier; FLAGS: the whole position in region 0).
-                    constexpr int part = (C::SYNC == SYNC_BARRIER) ? kk + 1 : kk;
+                    // (part 0 went out right after the last synchronisation).
+                    constexpr int part = kk + 1;
                     constexpr int t0 = part < NPARTS ? part_begin(part, NPARTS, C::LOADS) : 0;
                     constexpr int V = part < NPARTS ? part_begin(part + 1, NPARTS, C::LOADS) - t0 : 0;
                     const FragReader<C> rdr(wm, wn, lane, kk + 1);
@@ -1140,47 +1207,56 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
                                            lane);
                     mfma_step<C>(acc, fr[kk & 1]);
                     sched_slots<M, D, V, SALU>();
-                } else if constexpr (C::SYNC == SYNC_BARRIER) {
-                    // Last MFMA k-step of this stage: one barrier hands the
+                } else {
+                    // Last MFMA k-step of this stage: the workgroup hands the
                     // stage back and makes the next position readable; then
                     // part 0 of the load of position c + S refills this stage
                     // and the next stage's first fragments are read.  At the
                     // end of the stream this runs once more on an empty
                     // position, which keeps the block free of branches.  The
-                    // first PRE MFMAs (their fragments are in registers) go
-                    // out ahead of the barrier and keep the pipe busy while
-                    // the workgroup gathers.
-                    constexpr int PRE = 2;
-                    mfma_range<C, 0, PRE>(acc, fr[kk & 1]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    wait_lgkm0();
-                    sync_next(s_nxt, g_nxt);
+                    // first MFMAs (their fragments are in registers) keep the
+                    // pipe busy while the workgroup gathers.
+                    //
+                    // BARRIER: PRE MFMAs, then one s_barrier.
+                    //
+                    // FLAGS: after one MFMA the wave waits for its fragment
+                    // reads of position c (it may release the stage) and its
+                    // loads of position c + 1 (it may announce them), does
+                    // both in one atomic add, and sends out the read of the
+                    // signal word; two more MFMAs cover its round trip.  The
+                    // refill needs the stage released by every wave (WAR) and
+                    // the next position announced by every wave (RAW): both
+                    // halves of the word reach their targets together.
+                    constexpr int PRE = (C::SYNC == SYNC_FLAGS) ? 3 : 2;
+                    if constexpr (C::SYNC == SYNC_FLAGS) {
+                        mfma_range<C, 0, 1>(acc, fr[kk & 1]);
+                        __builtin_amdgcn_sched_barrier(0);
+                        wait_lgkm0();
+                        wait_vmcnt<C::LOADS * (C::S - 2)>();
+                        arrive_pair(sig + s_nxt, kAnnounce | kRelease);
+                        const uint64_t v = pair_read_issue(sig + s_nxt);
+                        __builtin_amdgcn_sched_barrier(0);
+                        mfma_range<C, 1, PRE>(acc, fr[kk & 1]);
+                        __builtin_amdgcn_sched_barrier(0);
+                        wait_pair_issued(v, sig + s_nxt, (g_nxt + 1) * C::NW, (gen + 1) * C::NW, failed);
+                    } else {
+                        mfma_range<C, 0, PRE>(acc, fr[kk & 1]);
+                        __builtin_amdgcn_sched_barrier(0);
+                        wait_lgkm0();
+                        sync_next(s_nxt, g_nxt);
+                    }
                     constexpr int V = part_begin(1, NPARTS, C::LOADS);
                     const FragReader<C> rdr(wm, wn, lane, 0);
                     region_memops<M - PRE, D, V>(rdr, fr[0], stage_at(s_nxt), wn, ld, next_prep, 0, stage_at(s_cur), w,
                                                  lane);
                     mfma_range<C, PRE, M>(acc, fr[kk & 1]);
                     sched_slots<M - PRE, D, V>();
-                } else {
-                    wait_lgkm0();
-                    arrive(empty + s_cur);
-                    sync_next(s_nxt, g_nxt);
-                    const FragReader<C> rdr(wm, wn, lane, 0);
-                    region_memops<M, D, 0>(rdr, fr[0], stage_at(s_nxt), wn, ld, next_prep, 0, stage_at(s_cur), w, lane);
-                    mfma_step<C>(acc, fr[kk & 1]);
-                    sched_slots<M, D, 0>();
                 }
                 __builtin_amdgcn_sched_barrier(0);
             };
             [&]<int... KS>(std::integer_sequence<int, KS...>) {
                 (region.template operator()<KS>(), ...);
             }(std::make_integer_sequence<int, C::KK>{});
-            if constexpr (C::SYNC == SYNC_FLAGS) {
-                // WAR: every wave has released this stage for position c;
-                // placed after this wave's MFMAs for the stage are issued.
-                // Its refill (position c + S) goes out in the next k-step.
-                wait_counter(empty + s_cur, (gen + 1) * C::NW, failed);
-            }
             if constexpr (!PIR) {
                 fire_prep = next_prep;
                 next_prep = ld.prepare_and_advance(p);

@@ -65,3 +65,15 @@ def test_helpers_present():
     called = {n.func.id for n in ast.walk(tree) if isinstance(n, ast.Call) and isinstance(n.func, ast.Name)}
     missing = {c for c in called if c not in defined and not hasattr(builtins, c) and c not in dir(bench)}
     assert not missing, missing
+
+
+def test_stage_sweep_compares_both_all_wave_schemes_at_2_3_4_stages():
+    """The 4096^3 configuration compares barrier and flag synchronisation at
+    2, 3 and 4 ring stages; every sweep entry must be a valid (sync, stages)
+    pair of the library."""
+    sweep = bench.STAGE_SWEEPS["gemm4096_kn"]
+    for sync in ("barrier", "flags"):
+        assert {st for s, st in sweep if s == sync} >= {2, 3, 4}
+    for sync, stages in sweep:
+        assert sync in ("barrier", "flags")
+        assert stages in (2, 3, 4) or (sync, stages) == ("barrier", 5)

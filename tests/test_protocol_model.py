@@ -155,13 +155,14 @@ def consumer(ring, wave, positions, S, NP, raw_off=0):
 
 
 # --- all-wave kernel, full/empty counters ----------------------------------------
-def flags_wave(ring, wave, total, S, NW, empty_target_scale=1, skip_full_wait=False):
+def flags_wave(ring, wave, total, S, NW, empty_target_scale=1, skip_full_wait=False, announce_first=False):
     """Each of the NW waves loads its part of every position and computes every
-    position.  Prologue: positions 0 .. S-2.  Then per k-step c: the load of
-    position c+S-1 goes out (its stage was released at the end of k-step c-1),
-    the wave reads position c, releases it, makes position c+1 readable (own
-    loads landed, arrive full, wait full), and at the end of the k-step waits
-    for every wave's release of position c."""
+    position.  Prologue: positions 0 .. S-2, then position 0 announced.  Per
+    k-step c: the load of position c+S-1 goes out into the stage of position
+    c-1 (checked free at the end of k-step c-1), the wave reads position c,
+    waits for its own loads of position c+1, then releases c and announces
+    c+1 in one atomic step (the kernel's single add on a word that holds both
+    counters), and waits until every wave has done both."""
     w = wave.wid
     for q in range(S - 1):
         ring.issue(q % S, q)
@@ -179,14 +180,23 @@ def flags_wave(ring, wave, total, S, NW, empty_target_scale=1, skip_full_wait=Fa
         wave.inflight.append((s_new, w, q_new))
         ring.begin_read(w, s_cur, c)
         yield None
-        ring.end_read(w, s_cur)
-        ring.empty[s_cur] += 1
         s_nxt, g_nxt = (c + 1) % S, (c + 1) // S
-        yield vm_wait(wave, S - 2)
-        ring.full[s_nxt] += 1
-        if not skip_full_wait:
-            yield at_least(ring.full, s_nxt, (g_nxt + 1) * NW)
-        yield at_least(ring.empty, s_cur, (c // S + 1) * NW * empty_target_scale)
+        if announce_first:
+            # fault: the announcement of c+1 goes out while c is still read
+            yield vm_wait(wave, S - 2)
+            ring.full[s_nxt] += 1
+            yield None
+            ring.end_read(w, s_cur)
+            ring.empty[s_cur] += 1
+        else:
+            ring.end_read(w, s_cur)
+            yield vm_wait(wave, S - 2)
+            ring.empty[s_cur] += 1
+            ring.full[s_nxt] += 1
+        full_target = 0 if skip_full_wait else (g_nxt + 1) * NW
+        empty_target = (c // S + 1) * NW * empty_target_scale
+        yield (lambda f=s_nxt, e=s_cur, ft=full_target, et=empty_target:
+               ring.full[f] >= ft and ring.empty[e] >= et)
     yield vm_wait(wave, 0)
 
 
@@ -331,12 +341,12 @@ def run_producer_consumer(S, NP, NCWG, groups, n_tiles, KT, seed, releasers=None
         assert ring.reads.get(q) == want, (q, ring.reads.get(q), want)
 
 
-def run_flags(S, NW, total, seed, empty_target_scale=1, init=0, skip_full_wait=False):
+def run_flags(S, NW, total, seed, empty_target_scale=1, init=0, skip_full_wait=False, announce_first=False):
     ring = Ring(S, NW, init_full=init, init_empty=init)
     waves = []
     for w in range(NW):
         wv = Wave(w, None)
-        wv.gen = flags_wave(ring, wv, total, S, NW, empty_target_scale, skip_full_wait)
+        wv.gen = flags_wave(ring, wv, total, S, NW, empty_target_scale, skip_full_wait, announce_first)
         waves.append(wv)
     run(ring, waves, seed)
     for q in range(total):
@@ -432,16 +442,41 @@ def test_fault_announce_lag_too_long():
 
 @pytest.mark.parametrize("S", [2, 3, 4])
 def test_flags_war_wait_is_implied_by_the_raw_wait(S):
-    """In the all-wave kernel every wave releases position c before it announces
-    position c + 1, and the refill of c's stage goes out only after the wait
-    for c + 1's announcements.  So that wait already covers WAR: the model
-    stays safe with the empty-counter wait removed altogether."""
+    """Every wave releases position c no later than it announces position
+    c + 1, and the refill of c's stage goes out only after every wave's
+    announcement.  So the announcement wait already covers WAR: the model stays
+    safe with the release check removed altogether.  (The kernel keeps the
+    check; it costs nothing because both counters are read at once.)"""
     for seed in SEEDS:
         run_flags(S, 4, 11, seed, empty_target_scale=0)
 
 
-def test_fault_flags_skip_full_wait():
-    assert caught(lambda sd: run_flags(2, 4, 9, sd, skip_full_wait=True))
+def test_fault_flags_announce_before_release_without_war_check():
+    """Announcing position c + 1 while still reading c is safe only because the
+    release check catches it; with the check removed as well, a refill lands
+    in a stage that a wave still reads."""
+    assert caught(lambda sd: run_flags(2, 4, 9, sd, empty_target_scale=0, announce_first=True))
+
+
+@pytest.mark.parametrize("S", [2, 3, 4])
+def test_flags_release_check_guards_an_early_announcement(S):
+    """The same early announcement with the release check in place stays safe:
+    the check is what makes the two signals independent."""
+    for seed in SEEDS:
+        run_flags(S, 4, 11, seed, announce_first=True)
+
+
+@pytest.mark.parametrize("S", [2, 3, 4])
+def test_flags_raw_wait_is_implied_by_the_release_check(S):
+    """One atomic step carries a wave's release of c and its announcement of
+    c + 1, made after its own loads of c + 1 landed.  So a complete release
+    count implies a complete announcement, too: each check alone is safe."""
+    for seed in SEEDS:
+        run_flags(S, 4, 11, seed, skip_full_wait=True)
+
+
+def test_fault_flags_no_wait_at_all():
+    assert caught(lambda sd: run_flags(2, 4, 9, sd, skip_full_wait=True, empty_target_scale=0))
 
 
 def test_fault_barrier_without_load_wait():
