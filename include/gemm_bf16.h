@@ -50,6 +50,18 @@
  * allocation returns GEMM_ERR_DEVICE.  Not a section of the pages: the
  * persistent schedule there assumes enough output tiles.
  *
+ * Split tail: when the output tiles (in the chosen configuration's tile) do
+ * not fill whole rounds of the persistent grid and the last round would hold
+ * at most half the compute units' worth, the last r tiles of the schedule
+ * run as a second launch with the k range split into s chunks (K a multiple
+ * of 64 * s, K / s >= 1024, K - K / s >= 2048, 2 <= s <= min(16,
+ * compute units / r)), then
+ * reduced as above.  The
+ * tiles of that tail differ from an unsplit result by fp32 rounding only,
+ * and deterministically; since the tail depends on the tile, modes with
+ * different tiles (see gemm_bf16_plan) can differ there in the last bit.
+ * plan.tail_tiles and plan.tail_splits report it.
+ *
  * Asynchrony: a call validates its arguments on the host, enqueues its work
  * on `stream` (a hipStream_t; NULL means the null stream) and returns.  A
  * return of GEMM_OK means "enqueued"; faults during execution surface at the
@@ -120,9 +132,13 @@ typedef struct gemm_bf16_plan {
     int32_t lds_bytes;        /* LDS per workgroup */
     int64_t tiles;            /* output tiles: ceil(M/bm) * ceil(N/bn) */
     int64_t k_steps;          /* k-steps per work item: ceil((K / k_splits) / bk) */
-    int64_t grid;             /* persistent workgroups launched: min(tiles * k_splits, compute units) */
+    int64_t grid;             /* persistent workgroups of the main launch:
+                                 min((tiles - tail_tiles) * k_splits, compute units) */
     int64_t k_splits;         /* chunks the k range is split into (1: no split) */
-    int64_t workspace_bytes;  /* fp32 partial tiles of a split call (0 without a split) */
+    int64_t workspace_bytes;  /* fp32 partial tiles of a split call or a split tail (0 without either) */
+    int64_t tail_tiles;       /* split tail: the last tail_tiles tiles of the raster run as a second
+                                 launch with the k range split in tail_splits chunks (0: none) */
+    int64_t tail_splits;      /* chunks of the split tail (0 without one) */
 } gemm_bf16_plan_t;
 
 /*

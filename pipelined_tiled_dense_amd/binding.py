@@ -39,7 +39,8 @@ class Plan(ctypes.Structure):
                 ("producer_waves", ctypes.c_int32), ("threads", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32), ("tiles", ctypes.c_int64),
                 ("k_steps", ctypes.c_int64), ("grid", ctypes.c_int64),
-                ("k_splits", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+                ("k_splits", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+                ("tail_tiles", ctypes.c_int64), ("tail_splits", ctypes.c_int64)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

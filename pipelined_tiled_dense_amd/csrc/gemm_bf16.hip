@@ -226,6 +226,8 @@ struct Cfg {
 
 // A work item is one output tile and one chunk of the k range.  Without a
 // split (splits == 1) the chunk is all of K and work items are output tiles.
+// A launch covers the `span` output tiles that start at raster position
+// `tile_base`: all tiles, or, for a split tail, the last few.
 struct Params {
     const char* A;
     const char* B;
@@ -234,7 +236,8 @@ struct Params {
     int64_t M, N, K, lda, ldb, ldc;   // elements
     int64_t ksplit;                   // k elements per chunk (K when splits == 1)
     int32_t tiles_m, tiles_n, tiles_mn, splits;
-    int32_t tiles;                    // work items: tiles_mn * splits
+    int32_t tiles;                    // work items of this launch: span * splits
+    int32_t span, tile_base;          // the launch's output tiles: raster positions tile_base .. + span - 1
     int32_t k_steps;                  // k-steps per work item
     int32_t group_m;
     int32_t small_span;               // A and B each span fewer than kMaxRecords bytes
@@ -259,23 +262,11 @@ __device__ __forceinline__ int swz_k(int row)
 // the 16 (row, chunk) pairs over all 16 bank groups.
 __device__ __forceinline__ int swz_n(int krow) { return (krow & 3) << 2; }
 
-// Output tile (tm, tn) and k chunk sp of work item t, for a grid of G
-// persistent workgroups (workgroup b takes ids b, b + G, b + 2G, ...).
-// Branch-free scalar code.
-__device__ __forceinline__ void tile_coords(const Params& p, int32_t t, int32_t G, int32_t& tm, int32_t& tn,
-                                            int32_t& sp)
+// Output tile at raster position Lt (0 <= Lt < tiles_mn): a grouped raster,
+// runs of group_m tile rows walked column by column, so a run of consecutive
+// positions covers a compact block of output tiles.
+__device__ __forceinline__ void raster_tile(const Params& p, int32_t Lt, int32_t& tm, int32_t& tn)
 {
-    // The hardware deals workgroups to the 8 XCDs round-robin; within every
-    // full round of G ids, give XCD x a contiguous run of G/8 ids.
-    const int32_t round = t / G;
-    const int32_t b = t - round * G;
-    const int32_t remapped = round * G + (b & 7) * (G >> 3) + (b >> 3);
-    const int32_t L = ((G & 7) == 0 && (round + 1) * G <= p.tiles) ? remapped : t;
-    // Chunk-major: consecutive ids share a k chunk.  Within a chunk, a grouped
-    // raster: runs of group_m tile rows, walked column by column, so a run of
-    // consecutive ids covers a compact block of output tiles.
-    sp = L / p.tiles_mn;
-    const int32_t Lt = L - sp * p.tiles_mn;
     const int32_t per_group = p.group_m * p.tiles_n;
     const int32_t grp = Lt / per_group;
     const int32_t first_m = grp * p.group_m;
@@ -284,6 +275,24 @@ __device__ __forceinline__ void tile_coords(const Params& p, int32_t t, int32_t 
     const int32_t col = in / gm;
     tm = first_m + (in - col * gm);
     tn = col;
+}
+
+// Output tile (tm, tn), k chunk sp and the tile's index u within the launch's
+// span, of work item t, for a grid of G persistent workgroups (workgroup b
+// takes ids b, b + G, b + 2G, ...).  Branch-free scalar code.
+__device__ __forceinline__ void tile_coords(const Params& p, int32_t t, int32_t G, int32_t& tm, int32_t& tn,
+                                            int32_t& sp, int32_t& u)
+{
+    // The hardware deals workgroups to the 8 XCDs round-robin; within every
+    // full round of G ids, give XCD x a contiguous run of G/8 ids.
+    const int32_t round = t / G;
+    const int32_t b = t - round * G;
+    const int32_t remapped = round * G + (b & 7) * (G >> 3) + (b >> 3);
+    const int32_t L = ((G & 7) == 0 && (round + 1) * G <= p.tiles) ? remapped : t;
+    // Chunk-major: consecutive ids share a k chunk and walk the raster.
+    sp = L / p.span;
+    u = L - sp * p.span;
+    raster_tile(p, p.tile_base + u, tm, tn);
 }
 
 // The ring counters live in their own LDS words, apart from every stage.  Their
@@ -532,9 +541,9 @@ struct Loader {
     __device__ __forceinline__ void tile_origin(const Params& p, int32_t t, const char*& a, const char*& b,
                                                 int32_t& n_left, int32_t& k_left) const
     {
-        int32_t tm = 0, tn = 0, sp = 0;
+        int32_t tm = 0, tn = 0, sp = 0, u = 0;
         tile_coords(p, (int32_t)blockIdx.x + min(t, n_tiles - 1) * (int32_t)gridDim.x, (int32_t)gridDim.x, tm, tn,
-                    sp);
+                    sp, u);
         const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN, k0 = (int64_t)sp * p.ksplit;
         a = p.A + (m0 * p.lda + k0) * 2;
         b = C::BT ? p.B + (n0 * p.ldb + k0) * 2 : p.B + (k0 * p.ldb + n0) * 2;
@@ -1035,20 +1044,30 @@ __device__ __forceinline__ void store_partial(const Params& p, f32x16_t (&acc)[C
     }
 }
 
-// C = bf16_rne(sum of the work items' partial tiles over the k chunks, in
-// chunk order).  One thread per 8 consecutive output columns (N % 8 == 0).
+// C = bf16_rne(sum of the partial tiles over the k chunks, in chunk order),
+// for the launch's span of output tiles.  The partial tile of chunk sp and
+// of the launch's u-th tile (raster position tile_base + u) is number
+// sp * span + u.  One thread per 8 consecutive columns of a tile row
+// (N % 8 == 0); groups outside the matrix are skipped.
 __global__ void __launch_bounds__(256) k_reduce_splits(Params p, int32_t bm, int32_t bn)
 {
-    const int64_t groups_per_row = p.N / 8;
-    const int64_t total = p.M * groups_per_row;
+    const int64_t groups_per_row = bn / 8;
+    const int64_t groups_per_tile = (int64_t)bm * groups_per_row;
+    const int64_t total = (int64_t)p.span * groups_per_tile;
     const int64_t tile_elems = (int64_t)bm * bn;
-    const int64_t chunk_stride = (int64_t)p.tiles_mn * tile_elems;
+    const int64_t chunk_stride = (int64_t)p.span * tile_elems;
     for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
          q += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = q / groups_per_row;
-        const int64_t c0 = (q - r * groups_per_row) * 8;
-        const int64_t tm = r / bm, tn = c0 / bn;
-        const float* src = p.partial + (tm * p.tiles_n + tn) * tile_elems + (r - tm * bm) * bn + (c0 - tn * bn);
+        const int32_t u = (int32_t)(q / groups_per_tile);
+        const int64_t in = q - (int64_t)u * groups_per_tile;
+        const int64_t row = in / groups_per_row;
+        const int64_t col = (in - row * groups_per_row) * 8;
+        int32_t tm, tn;
+        raster_tile(p, p.tile_base + u, tm, tn);
+        const int64_t r = (int64_t)tm * bm + row, c0 = (int64_t)tn * bn + col;
+        if (r >= p.M || c0 >= p.N)
+            continue;
+        const float* src = p.partial + u * tile_elems + row * bn + col;
         float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int32_t sp = 0; sp < p.splits; ++sp) {
             // 32-byte aligned: tiles, rows and column groups are multiples of 8 floats.
@@ -1166,8 +1185,8 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
 
     for (int32_t it = 0; it < n_tiles; ++it) {
         int32_t tm, tn;
-        int32_t sp;
-        tile_coords(p, b + it * G, G, tm, tn, sp);
+        int32_t sp, u;
+        tile_coords(p, b + it * G, G, tm, tn, sp, u);
         if constexpr (LONGK)
             ld.prefetch_next_tile(p, it + 1);
         f32x16_t acc[C::FM][C::FN];
@@ -1266,7 +1285,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
             gen = g_nxt;
         }
         if (p.splits > 1)
-            store_partial<C>(p, acc, (sp * p.tiles_mn + tm * p.tiles_n + tn), wm, wn, lane);
+            store_partial<C>(p, acc, sp * p.span + u, wm, wn, lane);
         else
             store_tile<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
     }
@@ -1337,8 +1356,8 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_win(Params p)
 
     for (int32_t it = 0; it < n_tiles; ++it) {
         int32_t tm, tn;
-        int32_t sp;
-        tile_coords(p, b + it * G, G, tm, tn, sp);
+        int32_t sp, u;
+        tile_coords(p, b + it * G, G, tm, tn, sp, u);
         if constexpr (LONGK)
             ld.prefetch_next_tile(p, it + 1);
         f32x16_t acc[C::FM][C::FN];
@@ -1395,7 +1414,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_win(Params p)
             wa = step5(wa, 2);
         }
         if (p.splits > 1) {
-            store_partial<C>(p, acc, (sp * p.tiles_mn + tm * p.tiles_n + tn), wm, wn, lane);
+            store_partial<C>(p, acc, sp * p.span + u, wm, wn, lane);
         } else {
             // The window of the last position's B tile is free until region 1
             // of the next k-step reloads it.
@@ -1482,8 +1501,8 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
     int32_t c = 0;
     for (int32_t it = 0; it < n_tiles; ++it) {
         int32_t tm, tn;
-        int32_t sp;
-        tile_coords(p, b + it * G, G, tm, tn, sp);
+        int32_t sp, u;
+        tile_coords(p, b + it * G, G, tm, tn, sp, u);
         f32x16_t acc[C::FM][C::FN];
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
@@ -1512,7 +1531,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
             }
         }
         if (p.splits > 1)
-            store_partial<C>(p, acc, (sp * p.tiles_mn + tm * p.tiles_n + tn), wm, wn, lane);
+            store_partial<C>(p, acc, sp * p.span + u, wm, wn, lane);
         else
             store_tile<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
     }
@@ -1564,8 +1583,8 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_pp(Params p)
     bool failed = false;
     for (int32_t it = g; it < n_tiles; it += 2) {
         int32_t tm, tn;
-        int32_t sp;
-        tile_coords(p, b + it * G, G, tm, tn, sp);
+        int32_t sp, u;
+        tile_coords(p, b + it * G, G, tm, tn, sp, u);
         int32_t c = it * KT;
         wait_counter(full + c % C::S, (uint32_t)(c / C::S + 1) * C::NP, failed);
         read_frags<C>(fr[0], stage_of(c), wm, wn, lane, 0);
@@ -1598,7 +1617,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_pp(Params p)
             }
         }
         if (p.splits > 1)
-            store_partial<C>(p, acc, (sp * p.tiles_mn + tm * p.tiles_n + tn), wm, wn, lane);
+            store_partial<C>(p, acc, sp * p.span + u, wm, wn, lane);
         else
             store_tile<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
     }
@@ -1724,13 +1743,18 @@ struct DeviceInfo {
     bool probed = false;
     int status = GEMM_OK;
     int cus = 0;
+    // Split workspaces come from this stream-ordered pool, which keeps freed
+    // memory for the next call instead of returning it to the device at
+    // every synchronisation (the default pool's behaviour), so a split call
+    // does not pay for a fresh allocation.  Null if it could not be created.
+    hipMemPool_t pool = nullptr;
 };
 
 constexpr int kMaxDevices = 64;
 std::mutex g_dev_mutex;
 DeviceInfo g_dev[kMaxDevices];
 
-int device_info(int* cus)
+int device_info(int* cus, hipMemPool_t* pool = nullptr)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
@@ -1745,9 +1769,27 @@ int device_info(int* cus)
             d.status = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? GEMM_OK : GEMM_ERR_DEVICE;
             d.cus = prop.multiProcessorCount;
         }
+        if (d.status == GEMM_OK) {
+            hipMemPoolProps props;
+            memset(&props, 0, sizeof props);
+            props.allocType = hipMemAllocationTypePinned;
+            props.handleTypes = hipMemHandleTypeNone;
+            props.location.type = hipMemLocationTypeDevice;
+            props.location.id = dev;
+            hipMemPool_t pl = nullptr;
+            if (hipMemPoolCreate(&pl, &props) == hipSuccess && pl) {
+                uint64_t keep = UINT64_MAX;
+                if (hipMemPoolSetAttribute(pl, hipMemPoolAttrReleaseThreshold, &keep) == hipSuccess)
+                    d.pool = pl;
+                else
+                    (void)hipMemPoolDestroy(pl);
+            }
+        }
         d.probed = true;
     }
     *cus = d.cus;
+    if (pool)
+        *pool = d.pool;
     return d.status;
 }
 
@@ -1803,6 +1845,35 @@ int64_t choose_splits(int64_t M, int64_t N, int64_t K, int cus)
     return 1;
 }
 
+// Split tail.  When the output tiles do not fill whole rounds of the
+// persistent grid and the last round would leave at least half the compute
+// units idle, the last r tiles of the raster become a second launch whose k
+// range is split into s chunks: that round then takes about 1/s of a tile's
+// time, plus one fp32 partial tile per chunk and a reduction.  A nearly idle
+// last round runs at a raised clock under the board's power limit, so the
+// split only pays when it removes much work from that round: chunks of at
+// least 1024 elements (a multiple of 64), and at least 2048 elements of the
+// k range taken off each tail tile (measured: K = 2048 lost with 2 or 4
+// chunks, K = 4096 gained 3-14%).  Returns s (0: no split tail) and sets r.
+int64_t choose_tail_splits(int64_t tiles, int64_t K, int cus, int64_t& r)
+{
+    r = 0;
+    if (tiles <= cus)
+        return 0;
+    const int64_t rem = tiles % cus;
+    if (rem == 0 || 2 * rem > cus)
+        return 0;
+    int64_t s = cus / rem;
+    if (s > kMaxSplits)
+        s = kMaxSplits;
+    for (; s >= 2; --s)
+        if (K % (64 * s) == 0 && K / s >= 1024 && K - K / s >= 2048) {
+            r = rem;
+            return s;
+        }
+    return 0;
+}
+
 int fill_plan(int64_t M, int64_t N, int64_t K, int b_transposed, int stages, int sync_mode, int cus,
               gemm_bf16_plan_t* out)
 {
@@ -1824,9 +1895,11 @@ int fill_plan(int64_t M, int64_t N, int64_t K, int b_transposed, int stages, int
     pl.tiles = tm * tn;
     pl.k_splits = choose_splits(M, N, K, cus);
     pl.k_steps = (K / pl.k_splits + v.bk - 1) / v.bk;
-    const int64_t items = pl.tiles * pl.k_splits;
+    if (pl.k_splits == 1)
+        pl.tail_splits = choose_tail_splits(pl.tiles, K, cus, pl.tail_tiles);
+    const int64_t items = (pl.tiles - pl.tail_tiles) * pl.k_splits;
     pl.grid = items < cus ? items : cus;
-    pl.workspace_bytes = pl.k_splits > 1 ? items * v.bm * v.bn * 4 : 0;
+    pl.workspace_bytes = pl.k_splits > 1 ? items * v.bm * v.bn * 4 : pl.tail_tiles * pl.tail_splits * v.bm * v.bn * 4;
     if (items > ((int64_t)1 << 30) || items * pl.k_steps > ((int64_t)1 << 30))
         return GEMM_ERR_UNSUPPORTED_SHAPE;
     *out = pl;
@@ -1858,7 +1931,8 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
         return GEMM_ERR_ALIAS;
 
     int cus = 0;
-    rc = device_info(&cus);
+    hipMemPool_t pool = nullptr;
+    rc = device_info(&cus, &pool);
     if (rc != GEMM_OK)
         return rc;
     hipStream_t s = (hipStream_t)stream;
@@ -1889,7 +1963,9 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
     p.tiles_mn = (int32_t)pl.tiles;
     p.splits = (int32_t)pl.k_splits;
     p.ksplit = K / pl.k_splits;
-    p.tiles = (int32_t)(pl.tiles * pl.k_splits);
+    p.span = (int32_t)(pl.tiles - pl.tail_tiles);
+    p.tile_base = 0;
+    p.tiles = p.span * p.splits;
     p.k_steps = (int32_t)pl.k_steps;
     p.group_m = 4;
     // The stepping load cursor addresses a whole operand from one resource
@@ -1898,22 +1974,39 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
                    (bt ? span_bytes(N, K, ldb) : span_bytes(K, N, ldb)) < (int64_t)kMaxRecords;
     p.partial = nullptr;
     const int64_t grid = pl.grid;
-    if (p.splits == 1)
+    if (p.splits == 1 && pl.tail_tiles == 0)
         return with_cfg(sync_mode, pl.stages, bt, [&]<class C>() { return launch<C>(p, grid, s); });
 
-    // Split k range: fp32 partial tiles in stream-ordered memory that lives
-    // for this call only, so calls on different streams never share it.
+    // Split k range (all tiles, or the tail): fp32 partial tiles in
+    // stream-ordered memory that lives for this call only, so calls on
+    // different streams never share it.
     void* ws = nullptr;
-    if (hipMallocAsync(&ws, (size_t)pl.workspace_bytes, s) != hipSuccess || !ws)
+    const hipError_t ae = pool ? hipMallocFromPoolAsync(&ws, (size_t)pl.workspace_bytes, pool, s)
+                               : hipMallocAsync(&ws, (size_t)pl.workspace_bytes, s);
+    if (ae != hipSuccess || !ws)
         return GEMM_ERR_DEVICE;
-    p.partial = (float*)ws;
-    rc = with_cfg(sync_mode, pl.stages, bt, [&]<class C>() { return launch<C>(p, grid, s); });
+    Params q = p;   // the launch whose partial tiles are reduced
+    if (pl.tail_tiles > 0) {
+        rc = with_cfg(sync_mode, pl.stages, bt, [&]<class C>() { return launch<C>(p, grid, s); });
+        q.splits = (int32_t)pl.tail_splits;
+        q.ksplit = K / pl.tail_splits;
+        q.span = (int32_t)pl.tail_tiles;
+        q.tile_base = p.span;
+        q.tiles = q.span * q.splits;
+        q.k_steps = (int32_t)((q.ksplit + pl.bk - 1) / pl.bk);
+    }
+    q.partial = (float*)ws;
     if (rc == GEMM_OK) {
-        const int64_t groups = M * (N / 8);
+        const int64_t tail_grid = q.tiles < cus ? q.tiles : cus;
+        rc = with_cfg(sync_mode, pl.stages, bt,
+                      [&]<class C>() { return launch<C>(q, pl.tail_tiles > 0 ? tail_grid : grid, s); });
+    }
+    if (rc == GEMM_OK) {
+        const int64_t groups = (int64_t)q.span * pl.bm * (pl.bn / 8);
         int64_t blocks = (groups + 255) / 256;
         if (blocks > 65536)
             blocks = 65536;
-        hipLaunchKernelGGL(k_reduce_splits, dim3((unsigned)blocks), dim3(256), 0, s, p, pl.bm, pl.bn);
+        hipLaunchKernelGGL(k_reduce_splits, dim3((unsigned)blocks), dim3(256), 0, s, q, pl.bm, pl.bn);
         rc = hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
     }
     if (hipFreeAsync(ws, s) != hipSuccess && rc == GEMM_OK)

@@ -5,7 +5,9 @@ every element, computed in fp64 from the bf16 results.  Where fp32
 accumulation is exact (small-integer inputs) the bar is bit equality.  All
 sync modes, stage counts and both B layouts run the same MFMA chain per
 output element (k in increasing order), so their outputs must also be
-bit-identical to each other and from run to run.
+bit-identical to each other and from run to run -- except on the tiles of a
+split tail, which depends on the mode's tile: there modes whose plans split
+alike must agree bit for bit.
 
 Small cases span several 256 x 256 tiles and ragged tails and are compared in
 full.  The five benchmark workloads run at their full sizes in the launch
@@ -196,6 +198,98 @@ def test_plans():
     assert bd.gemm_bf16_plan(8192, 8192, 8192, True, 0, 2)["stages"] == 3
     assert bd.gemm_bf16_plan(8192, 8192, 8192, True, 0, 3)["stages"] == 3
     assert bd.gemm_bf16_plan(8192, 8192, 8192, True, 0, 3)["tiles"] == 64 * 64
+
+
+def expected_tail(tiles, K, cus):
+    """The split-tail rule: a last round of at most half the compute units
+    that a k split of s chunks (s <= cus / r, 64 * s | K, K / s >= 1024,
+    K - K / s >= 2048) can spread."""
+    if tiles <= cus or tiles % cus == 0 or 2 * (tiles % cus) > cus:
+        return 0, 0
+    r = tiles % cus
+    for s in range(min(cus // r, 16), 1, -1):
+        if K % (64 * s) == 0 and K // s >= 1024 and K - K // s >= 2048:
+            return r, s
+    return 0, 0
+
+
+def test_split_tail_plans():
+    """4352 x 4352 x 4096: 289 tiles of 256 x 256 are one full round of the 256
+    compute units plus 33, so the last 33 tiles of the schedule run split into
+    4 chunks of 1024.  In 256 x 128 tiles: 578 = 512 + 66 -> 3 would leave
+    chunks that are no multiple of 64, so 2 chunks; in 128 x 128 tiles:
+    1156 = 1024 + 132, more than half a round -> no tail.  Whole rounds
+    (8192^3), chunks shorter than 1024, a split that takes less than 2048 off
+    the k range (K = 2048) and a K with no valid chunking have none."""
+    cus = bd.gemm_bf16_plan(8192, 8192, 8192, True, 0, 0)["grid"]
+    for sync, stages in MODES:
+        for bt in (False, True):
+            pl = bd.gemm_bf16_plan(4352, 4352, 4096, bt, stages, bd.SYNC_MODES[sync])
+            r, sp = expected_tail(pl["tiles"], 4096, cus)
+            assert (pl["tail_tiles"], pl["tail_splits"]) == (r, sp), (sync, stages, pl)
+            assert pl["k_splits"] == 1 and pl["grid"] == min(pl["tiles"] - r, cus), (sync, stages, pl)
+            assert pl["workspace_bytes"] == r * sp * pl["bm"] * pl["bn"] * 4, (sync, stages, pl)
+            pl = bd.gemm_bf16_plan(8192, 8192, 8192, bt, stages, bd.SYNC_MODES[sync])
+            assert (pl["tail_tiles"], pl["tail_splits"], pl["workspace_bytes"]) == (0, 0, 0), (sync, stages, pl)
+    if cus == 256:
+        pl = bd.gemm_bf16_plan(4352, 4352, 4096, True, 2, 0)
+        assert (pl["tail_tiles"], pl["tail_splits"]) == (33, 4)
+        assert bd.gemm_bf16_plan(4352, 4352, 4096, True, 3, 2)["tail_splits"] == 2
+        assert bd.gemm_bf16_plan(4352, 4352, 4096, True, 3, 3)["tail_tiles"] == 0
+        assert bd.gemm_bf16_plan(4352, 4352, 1536, True, 2, 0)["tail_tiles"] == 0
+        assert bd.gemm_bf16_plan(4352, 4352, 2048, True, 2, 0)["tail_tiles"] == 0
+    assert bd.gemm_bf16_plan(4352, 4352, 4104, True, 2, 0)["tail_tiles"] == 0
+
+
+def split_signature(M, N, K, bt, sync, stages):
+    pl = bd.gemm_bf16_plan(M, N, K, bt, stages, bd.SYNC_MODES[sync])
+    return (pl["bm"], pl["bn"], pl["k_splits"], pl["tail_tiles"], pl["tail_splits"])
+
+
+@pytest.mark.parametrize("bt", [False, True], ids=["kn", "nk"])
+def test_split_tail(bt):
+    """A split tail on a ragged shape: 4300 x 4344 has 17 x 17 tiles of
+    256 x 256 (the last tile row and column partial), K = 4096.  Sampled rows
+    cover tile rows 12 and 16, i.e. tiles of the main launch and of the tail,
+    and both ragged edges.  Modes whose plans split alike agree bit for bit,
+    run after run."""
+    M, N, K = 4300, 4344, 4096
+    A, B = make_operands(M, N, K, b_transposed=bt, seed=5151 + bt)
+    rows = np.array([0, 255, 3072, 3101, 3327, 3328, 4095, 4096, 4150, 4299], dtype=np.int64)
+    Ab, Bb = bits(A), bits(B)
+    ref = oracle.load().gemm_bf16(np.ascontiguousarray(Ab[rows]), Bb, bt)
+    dA, dB = A.cuda(), B.cuda()
+    by_sig = {}
+    tails = 0
+    for sync, stages in MODES:
+        sig = split_signature(M, N, K, bt, sync, stages)
+        tails += sig[3] > 0
+        got = run(dA, dB, bt, sync, stages)
+        assert_within_tol(got[rows], ref, "tail %s/%d %s" % (sync, stages, sig))
+        if sig in by_sig:
+            np.testing.assert_array_equal(got, by_sig[sig], err_msg="same split, different bits")
+        else:
+            by_sig[sig] = got
+    assert tails > 0
+    again = run(dA, dB, bt, "barrier", 2)
+    np.testing.assert_array_equal(again, by_sig[split_signature(M, N, K, bt, "barrier", 2)])
+
+
+def test_split_tail_exact_integer_inputs():
+    """Small integers make every fp32 sum exact, so with or without a split
+    tail, and whatever the tile, every mode equals the oracle bit for bit."""
+    rng = np.random.default_rng(11)
+    M, N, K = 4300, 4344, 4096
+    Av = rng.integers(-4, 5, size=(M, K)).astype(np.float32)
+    Bv = rng.integers(-4, 5, size=(N, K)).astype(np.float32)
+    A = torch.from_numpy(Av).to(torch.bfloat16)
+    B = torch.from_numpy(Bv).to(torch.bfloat16)
+    rows = np.array([0, 3100, 3327, 3328, 4096, 4299], dtype=np.int64)
+    ref = oracle.load().gemm_bf16(np.ascontiguousarray(bits(A)[rows]), bits(B), True)
+    dA, dB = A.cuda(), B.cuda()
+    for sync, stages in MODES:
+        got = run(dA, dB, True, sync, stages)
+        np.testing.assert_array_equal(got[rows], ref, err_msg="%s/%d" % (sync, stages))
 
 
 def test_layouts_and_modes_bit_identical():
