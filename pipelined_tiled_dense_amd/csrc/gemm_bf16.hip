@@ -406,6 +406,24 @@ __device__ __forceinline__ void wait_pair_issued(uint64_t v, const lds_u64* word
     COMPILER_FENCE();
 }
 
+// A poll split in two: the read goes out now; wait_counter_issued, called
+// after unrelated work, completes it and falls back to wait_counter if the
+// value is still short of the target.
+__device__ __forceinline__ uint32_t counter_read_issue(const lds_u32* ctr)
+{
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(lds_addr(ctr)) : "memory");
+    return v;
+}
+
+__device__ __forceinline__ void wait_counter_issued(uint32_t v, const lds_u32* ctr, uint32_t target, bool& failed)
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v) : : "memory");
+    if (__builtin_amdgcn_readfirstlane(v) < target)
+        wait_counter(ctr, target, failed);
+    COMPILER_FENCE();
+}
+
 // One arrival (lane 0 adds 1).
 __device__ __forceinline__ void arrive(lds_u32* ctr)
 {
@@ -1461,6 +1479,34 @@ __device__ __forceinline__ void producer_loop(const Params& p, lds_char* smem, l
         arrive(full + q % C::S);
 }
 
+// Last MFMA k-step of a position in an MFMA wave of the loader/MFMA kernels.
+// The wave releases the stage (its fragment reads have landed) and sends out
+// the read of the next position's announcement counter; PRE MFMAs, whose
+// fragments are in registers, cover its round trip.  Once every loader has
+// announced, the next position's first fragments are read beside the
+// remaining MFMAs.  Without a next position (has_next false) only the MFMAs
+// run.
+template <class C>
+__device__ __forceinline__ void consumer_last_kstep(f32x16_t (&acc)[C::FM][C::FN], Frags<C> (&fr)[2],
+                                                    lds_u32* empty_cur, const lds_u32* full_next,
+                                                    uint32_t next_target, bool has_next, const lds_char* next_stage,
+                                                    int wm, int wn, int lane, bool& failed)
+{
+    constexpr int M = C::FM * C::FN, PRE = (M > 4) ? M - 3 : M / 2;
+    constexpr int LAST = (C::KK - 1) & 1;
+    wait_lgkm0();
+    arrive(empty_cur);
+    const uint32_t v = counter_read_issue(full_next);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_range<C, 0, PRE>(acc, fr[LAST]);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_counter_issued(v, full_next, has_next ? next_target : 0u, failed);
+    if (has_next)
+        read_frags<C>(fr[0], next_stage, wm, wn, lane, 0);
+    mfma_range<C, PRE, M>(acc, fr[LAST]);
+    sched_slots<M - PRE, frag_reads<C>(), 0>();
+}
+
 // ---------------------------------------------------------------------------
 // Kernel: dedicated loader waves and MFMA waves (GEMM_SYNC_WAVESPEC).
 // ---------------------------------------------------------------------------
@@ -1515,18 +1561,14 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
             for (int kk = 0; kk < C::KK; ++kk) {
                 if (kk + 1 < C::KK) {
                     read_frags<C>(fr[(kk + 1) & 1], stage, wm, wn, lane, kk + 1);
-                } else {
-                    wait_lgkm0();
-                    arrive(empty + c % C::S);
-                    if (c + 1 < total) {
-                        const int s1 = (c + 1) % C::S;
-                        wait_counter(full + s1, (uint32_t)((c + 1) / C::S + 1) * C::NP, failed);
-                        read_frags<C>(fr[0], smem + s1 * C::STAGE_BYTES, wm, wn, lane, 0);
-                    }
-                }
-                mfma_step<C>(acc, fr[kk & 1]);
-                if (kk + 1 < C::KK)
+                    mfma_step<C>(acc, fr[kk & 1]);
                     sched_slots<C::FM * C::FN, frag_reads<C>(), 0>();
+                } else {
+                    const int s1 = (c + 1) % C::S;
+                    consumer_last_kstep<C>(acc, fr, empty + c % C::S, full + s1,
+                                           (uint32_t)((c + 1) / C::S + 1) * C::NP, c + 1 < total,
+                                           smem + s1 * C::STAGE_BYTES, wm, wn, lane, failed);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -1600,19 +1642,15 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_pp(Params p)
             for (int kk = 0; kk < C::KK; ++kk) {
                 if (kk + 1 < C::KK) {
                     read_frags<C>(fr[(kk + 1) & 1], stage, wm, wn, lane, kk + 1);
+                    mfma_step<C>(acc, fr[kk & 1]);
+                    sched_slots<C::FM * C::FN, frag_reads<C>(), 0>();
                 } else {
-                    wait_lgkm0();
-                    arrive(empty + c % C::S);
                     // The group's next position within this tile; the next
                     // tile's first position is waited for after the epilogue.
-                    if (kt + 1 < KT) {
-                        wait_counter(full + (c + 1) % C::S, (uint32_t)((c + 1) / C::S + 1) * C::NP, failed);
-                        read_frags<C>(fr[0], stage_of(c + 1), wm, wn, lane, 0);
-                    }
+                    consumer_last_kstep<C>(acc, fr, empty + c % C::S, full + (c + 1) % C::S,
+                                           (uint32_t)((c + 1) / C::S + 1) * C::NP, kt + 1 < KT, stage_of(c + 1),
+                                           wm, wn, lane, failed);
                 }
-                mfma_step<C>(acc, fr[kk & 1]);
-                if (kk + 1 < C::KK)
-                    sched_slots<C::FM * C::FN, frag_reads<C>(), 0>();
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
