@@ -1031,17 +1031,20 @@ __device__ __forceinline__ void store_tile(const Params& p, f32x16_t (&acc)[C::F
 }
 
 // Split k range: the work item's fp32 accumulators go, unrounded, to its
-// partial tile (BM x BN fp32, row-major, in the workspace); k_reduce_splits
-// adds the chunks later.  Lane l of block (i, j) holds row l%32 and, per
-// group of 4 registers, 4 consecutive columns: one 16-byte store each.
+// partial tile (BM x BN fp32 in the workspace); k_reduce_splits adds the
+// chunks later.  The partial tile keeps the registers' order: 16-byte unit
+// (((wave * FM + i) * FN + j) * 4 + g) * 64 + lane holds registers 4g..4g+3
+// of lane `lane` in block (i, j) of MFMA wave `wave` (wm * WN + wn), so each
+// store instruction writes 1 KiB contiguously.  Those registers hold row
+// wm*TM + 32i + lane%32 and columns wn*TN + 32j + 8g + 4*(lane/32) + 0..3.
 template <class C>
 __device__ __forceinline__ void store_partial(const Params& p, f32x16_t (&acc)[C::FM][C::FN], int32_t widx, int wm,
                                               int wn, int lane_in)
 {
     const int lane = (int)opaque((uint32_t)lane_in);
     const __amdgpu_buffer_rsrc_t rp = rsrc_n(p.partial + (int64_t)widx * (C::BM * C::BN), C::BM * C::BN * 4u);
-    const int m = lane & 31, h = lane >> 5;
-    const uint32_t base = opaque((uint32_t)(((wm * C::TM + m) * C::BN + wn * C::TN + 4 * h) * 4));
+    const int wave = wm * C::WN + wn;
+    const uint32_t base = opaque((uint32_t)(wave * C::FM * C::FN * 4 * 1024 + lane * 16));
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
@@ -1055,7 +1058,7 @@ __device__ __forceinline__ void store_partial(const Params& p, f32x16_t (&acc)[C
                 // Whole vectors only: a bit cast of a single vector element
                 // is not what this needs.
                 const f32x4_t v = {a[4 * g + 0], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-                const uint32_t off = base + (uint32_t)((32 * i * C::BN + 32 * j + 8 * g) * 4);
+                const uint32_t off = base + (uint32_t)(((i * C::FN + j) * 4 + g) * 1024);
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rp, off, 0, 0);
             }
         }
@@ -1065,47 +1068,48 @@ __device__ __forceinline__ void store_partial(const Params& p, f32x16_t (&acc)[C
 // C = bf16_rne(sum of the partial tiles over the k chunks, in chunk order),
 // for the launch's span of output tiles.  The partial tile of chunk sp and
 // of the launch's u-th tile (raster position tile_base + u) is number
-// sp * span + u.  One thread per 8 consecutive columns of a tile row
-// (N % 8 == 0); groups outside the matrix are skipped.
-__global__ void __launch_bounds__(256) k_reduce_splits(Params p, int32_t bm, int32_t bn)
+// sp * span + u.  One thread per 16-byte unit of the partial tiles' register
+// order (4 consecutive output columns), so reads are contiguous across
+// lanes; units outside the matrix are skipped (N % 8 == 0 keeps a unit
+// whole).
+template <class C>
+__global__ void __launch_bounds__(256) k_reduce_splits(Params p)
 {
-    const int64_t groups_per_row = bn / 8;
-    const int64_t groups_per_tile = (int64_t)bm * groups_per_row;
-    const int64_t total = (int64_t)p.span * groups_per_tile;
-    const int64_t tile_elems = (int64_t)bm * bn;
-    const int64_t chunk_stride = (int64_t)p.span * tile_elems;
+    constexpr int64_t UNITS = (int64_t)C::BM * C::BN / 4;   // 16-byte units per tile
+    const int64_t total = (int64_t)p.span * UNITS;
+    const int64_t chunk_stride = (int64_t)p.span * C::BM * C::BN;
     for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
          q += (int64_t)gridDim.x * blockDim.x) {
-        const int32_t u = (int32_t)(q / groups_per_tile);
-        const int64_t in = q - (int64_t)u * groups_per_tile;
-        const int64_t row = in / groups_per_row;
-        const int64_t col = (in - row * groups_per_row) * 8;
+        const int32_t u = (int32_t)(q / UNITS);
+        const int32_t unit = (int32_t)(q - (int64_t)u * UNITS);
+        const int lane = unit & 63;
+        int rest = unit >> 6;
+        const int g = rest & 3;
+        rest >>= 2;
+        const int j = rest % C::FN;
+        rest /= C::FN;
+        const int i = rest % C::FM;
+        const int wave = rest / C::FM;
+        const int wm = wave / C::WN, wn = wave % C::WN;
         int32_t tm, tn;
         raster_tile(p, p.tile_base + u, tm, tn);
-        const int64_t r = (int64_t)tm * bm + row, c0 = (int64_t)tn * bn + col;
+        const int64_t r = (int64_t)tm * C::BM + wm * C::TM + 32 * i + (lane & 31);
+        const int64_t c0 = (int64_t)tn * C::BN + wn * C::TN + 32 * j + 8 * g + 4 * (lane >> 5);
         if (r >= p.M || c0 >= p.N)
             continue;
-        const float* src = p.partial + u * tile_elems + row * bn + col;
-        float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        const f32x4_t* src = (const f32x4_t*)(p.partial + (int64_t)u * C::BM * C::BN) + unit;
+        f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
         for (int32_t sp = 0; sp < p.splits; ++sp) {
-            // 32-byte aligned: tiles, rows and column groups are multiples of 8 floats.
-            const f32x4_t* part = (const f32x4_t*)(src + sp * chunk_stride);
-            const f32x4_t lo = part[0], hi = part[1];
-            sum[0] += lo.x;
-            sum[1] += lo.y;
-            sum[2] += lo.z;
-            sum[3] += lo.w;
-            sum[4] += hi.x;
-            sum[5] += hi.y;
-            sum[6] += hi.z;
-            sum[7] += hi.w;
+            const f32x4_t v = src[sp * chunk_stride / 4];
+            sum.x += v.x;
+            sum.y += v.y;
+            sum.z += v.z;
+            sum.w += v.w;
         }
-        u32x4_t out;
-        out.x = pack_bf16x2(sum[0], sum[1]);
-        out.y = pack_bf16x2(sum[2], sum[3]);
-        out.z = pack_bf16x2(sum[4], sum[5]);
-        out.w = pack_bf16x2(sum[6], sum[7]);
-        *(u32x4_t*)(p.C + (r * p.ldc + c0) * 2) = out;
+        u32x2_t out;
+        out.x = pack_bf16x2(sum.x, sum.y);
+        out.y = pack_bf16x2(sum.z, sum.w);
+        *(u32x2_t*)(p.C + (r * p.ldc + c0) * 2) = out;
     }
 }
 
@@ -2040,12 +2044,14 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
                       [&]<class C>() { return launch<C>(q, pl.tail_tiles > 0 ? tail_grid : grid, s); });
     }
     if (rc == GEMM_OK) {
-        const int64_t groups = (int64_t)q.span * pl.bm * (pl.bn / 8);
-        int64_t blocks = (groups + 255) / 256;
+        const int64_t units = (int64_t)q.span * pl.bm * pl.bn / 4;
+        int64_t blocks = (units + 255) / 256;
         if (blocks > 65536)
             blocks = 65536;
-        hipLaunchKernelGGL(k_reduce_splits, dim3((unsigned)blocks), dim3(256), 0, s, q, pl.bm, pl.bn);
-        rc = hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+        rc = with_cfg(sync_mode, pl.stages, bt, [&]<class C>() {
+            hipLaunchKernelGGL(k_reduce_splits<C>, dim3((unsigned)blocks), dim3(256), 0, s, q);
+            return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+        });
     }
     if (hipFreeAsync(ws, s) != hipSuccess && rc == GEMM_OK)
         rc = GEMM_ERR_DEVICE;
