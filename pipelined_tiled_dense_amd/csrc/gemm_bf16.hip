@@ -63,6 +63,12 @@
 //   segments and stored with 16-byte buffer stores; being wave-private, the
 //   strip needs no block-wide sync.
 //
+// * Split k range and split tail (not sections of the pages, whose persistent
+//   schedule assumes enough output tiles).  Shapes with few output tiles, and
+//   the last few tiles of a mostly empty last round, run as k chunks; each
+//   chunk's fp32 partial tile is stored in register order and a reduction
+//   kernel adds the chunks in chunk order, then rounds once.
+//
 // * Counter initialisation happens before any wave can arrive on a counter
 //   ("[Tutorial] Fix race condition in 2SM TMEM alloc ...", sections
 //   "Problem" and "Fix"): counters are zeroed, then one workgroup barrier,
