@@ -45,9 +45,12 @@
  * chunk order, after one fp32 chain per chunk; the result differs from the
  * unsplit sum only by fp32 rounding, is the same for every sync mode and
  * stage count, and is deterministic.  The fp32 partial tiles
- * (plan.workspace_bytes) are allocated stream-ordered on `stream`
- * (hipMallocAsync) and released (hipFreeAsync) by the same call; a failed
- * allocation returns GEMM_ERR_DEVICE.  Not a section of the pages: the
+ * (plan.workspace_bytes) are allocated stream-ordered on `stream` and
+ * released (hipFreeAsync) by the same call, from a memory pool the library
+ * creates once per device (hipMallocFromPoolAsync; hipMallocAsync if the pool
+ * could not be created).  The pool keeps freed memory for later calls until
+ * the process ends, so it holds as much as the largest workspaces in flight
+ * at once.  A failed allocation returns GEMM_ERR_DEVICE.  Not a section of the pages: the
  * persistent schedule there assumes enough output tiles.
  *
  * Split tail: when the output tiles (in the chosen configuration's tile) do
