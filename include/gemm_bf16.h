@@ -192,6 +192,16 @@ int gemm_bf16_plan(int64_t M, int64_t N, int64_t K, int b_transposed,
                    int stages, int sync_mode, gemm_bf16_plan_t* out);
 
 /*
+ * gemm_bf16_plan_cus: gemm_bf16_plan for a device with `compute_units`
+ * compute units, without querying any device (host code only; usable where
+ * no GPU is present).  gemm_bf16 on a device with that many compute units
+ * uses exactly this plan.  Returns GEMM_ERR_INVALID_VALUE for a null `out`
+ * or compute_units < 1, otherwise as gemm_bf16_plan.
+ */
+int gemm_bf16_plan_cus(int64_t M, int64_t N, int64_t K, int b_transposed,
+                       int stages, int sync_mode, int compute_units, gemm_bf16_plan_t* out);
+
+/*
  * gemm_bf16_strerror: a static, NUL-terminated description of a status code
  * (never NULL; unknown codes give "unknown status").
  */

@@ -65,6 +65,8 @@ def library() -> ctypes.CDLL:
         lib.gemm_bf16_bt.restype = i32
         lib.gemm_bf16_plan.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(Plan)]
         lib.gemm_bf16_plan.restype = i32
+        lib.gemm_bf16_plan_cus.argtypes = [i64, i64, i64, i32, i32, i32, i32, ctypes.POINTER(Plan)]
+        lib.gemm_bf16_plan_cus.restype = i32
         lib.gemm_bf16_strerror.argtypes = [i32]
         lib.gemm_bf16_strerror.restype = ctypes.c_char_p
         lib.gemm_bf16_sync_timeouts.argtypes = [i32]
@@ -88,6 +90,15 @@ def gemm_bf16_plan(M, N, K, b_transposed, stages, sync_mode) -> dict:
                                   ctypes.byref(out))
     if rc != GEMM_OK:
         raise GemmError(rc, "gemm_bf16_plan")
+    return out.as_dict()
+
+
+def gemm_bf16_plan_cus(M, N, K, b_transposed, stages, sync_mode, compute_units) -> dict:
+    out = Plan()
+    rc = library().gemm_bf16_plan_cus(M, N, K, int(bool(b_transposed)), stages, sync_mode, compute_units,
+                                      ctypes.byref(out))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_bf16_plan_cus")
     return out.as_dict()
 
 

@@ -2095,6 +2095,17 @@ int gemm_bf16_plan(int64_t M, int64_t N, int64_t K, int b_transposed, int stages
     return fill_plan(M, N, K, b_transposed, stages, sync_mode, cus, out);
 }
 
+int gemm_bf16_plan_cus(int64_t M, int64_t N, int64_t K, int b_transposed, int stages, int sync_mode,
+                       int compute_units, gemm_bf16_plan_t* out)
+{
+    if (!out || compute_units < 1)
+        return GEMM_ERR_INVALID_VALUE;
+    const int rc = validate_shape(M, N, K, stages, sync_mode);
+    if (rc != GEMM_OK)
+        return rc;
+    return fill_plan(M, N, K, b_transposed, stages, sync_mode, compute_units, out);
+}
+
 const char* gemm_bf16_strerror(int status)
 {
     switch (status) {
