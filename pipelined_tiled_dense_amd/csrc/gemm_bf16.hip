@@ -1270,11 +1270,12 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
                     // reads of position c (it may release the stage) and its
                     // loads of position c + 1 (it may announce them), does
                     // both in one atomic add, and sends out the read of the
-                    // signal word; two more MFMAs cover its round trip.  The
-                    // refill needs the stage released by every wave (WAR) and
-                    // the next position announced by every wave (RAW): both
-                    // halves of the word reach their targets together.
-                    constexpr int PRE = (C::SYNC == SYNC_FLAGS) ? 3 : 2;
+                    // signal word; two more MFMAs (three with 32-wide k-steps,
+                    // measured) cover its round trip.  The refill needs the
+                    // stage released by every wave (WAR) and the next
+                    // position announced by every wave (RAW): both halves of
+                    // the word reach their targets together.
+                    constexpr int PRE = (C::SYNC == SYNC_FLAGS) ? (C::S == 2 ? 3 : 4) : 2;
                     if constexpr (C::SYNC == SYNC_FLAGS) {
                         mfma_range<C, 0, 1>(acc, fr[kk & 1]);
                         __builtin_amdgcn_sched_barrier(0);

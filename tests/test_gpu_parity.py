@@ -239,6 +239,10 @@ def test_split_tail_plans():
         assert bd.gemm_bf16_plan(4352, 4352, 1536, True, 2, 0)["tail_tiles"] == 0
         assert bd.gemm_bf16_plan(4352, 4352, 2048, True, 2, 0)["tail_tiles"] == 0
     assert bd.gemm_bf16_plan(4352, 4352, 4104, True, 2, 0)["tail_tiles"] == 0
+    for sync, stages in MODES:   # the device's plan is the host-only plan for its compute units
+        for shape in ((4352, 4352, 4096), (1000, 1032, 8192), (300, 264, 200)):
+            assert bd.gemm_bf16_plan(*shape, True, stages, bd.SYNC_MODES[sync]) == \
+                bd.gemm_bf16_plan_cus(*shape, True, stages, bd.SYNC_MODES[sync], cus), (sync, stages, shape)
 
 
 def split_signature(M, N, K, bt, sync, stages):
