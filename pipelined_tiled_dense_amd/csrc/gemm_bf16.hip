@@ -430,6 +430,27 @@ __device__ __forceinline__ void wait_counter_issued(uint32_t v, const lds_u32* c
     COMPILER_FENCE();
 }
 
+// wait_counter for a wait that usually lasts long (a ping-pong group waiting
+// through the other group's tile): after the first polls it sleeps longer,
+// so a waiting wave takes fewer issue slots from the waves computing on its
+// SIMD.  Still bounded: kSpinLimit polls of at most 512 cycles' sleep.
+__device__ __forceinline__ void wait_counter_long(const lds_u32* ctr, uint32_t target, bool& failed)
+{
+    uint32_t spins = 0;
+    while (!failed && load_counter(ctr) < target) {
+        if (++spins > kSpinLimit) {
+            if ((threadIdx.x & 63) == 0)
+                atomicAdd(&g_sync_timeouts, 1ull);
+            failed = true;
+        }
+        if (spins > 64)
+            __builtin_amdgcn_s_sleep(8);
+        else if (spins > 8)
+            __builtin_amdgcn_s_sleep(1);
+    }
+    COMPILER_FENCE();
+}
+
 // One arrival (lane 0 adds 1).
 __device__ __forceinline__ void arrive(lds_u32* ctr)
 {
@@ -1639,7 +1660,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_pp(Params p)
         int32_t sp, u;
         tile_coords(p, b + it * G, G, tm, tn, sp, u);
         int32_t c = it * KT;
-        wait_counter(full + c % C::S, (uint32_t)(c / C::S + 1) * C::NP, failed);
+        wait_counter_long(full + c % C::S, (uint32_t)(c / C::S + 1) * C::NP, failed);
         read_frags<C>(fr[0], stage_of(c), wm, wn, lane, 0);
         f32x16_t acc[C::FM][C::FN];
 #pragma unroll
