@@ -111,10 +111,9 @@ enum {
     GEMM_OK = 0,
     GEMM_ERR_INVALID_VALUE = -1,     /* negative size, NULL pointer with a nonzero extent,
                                         leading dimension too small, NULL output struct */
-    GEMM_ERR_MISALIGNED = -2,        /* a pointer not 16-byte aligned, or a leading
-                                        dimension not a multiple of 8 elements */
-    GEMM_ERR_UNSUPPORTED_SHAPE = -3, /* N or K not a multiple of 8, or a leading dimension
-                                        above 2^22 elements */
+    GEMM_ERR_MISALIGNED = -2,        /* a pointer not 2-byte aligned */
+    GEMM_ERR_UNSUPPORTED_SHAPE = -3, /* N or K above 2^22, M above 2^31 - 1, or more work
+                                        items than the schedule indexes */
     GEMM_ERR_STAGES = -4,            /* stages not 0 (default), 2..4, or GEMM_STAGES_WINDOWS
                                         with GEMM_SYNC_BARRIER */
     GEMM_ERR_SYNC_MODE = -5,         /* sync_mode not one of GEMM_SYNC_* */
@@ -142,6 +141,8 @@ typedef struct gemm_bf16_plan {
     int64_t tail_tiles;       /* split tail: the last tail_tiles tiles of the raster run as a second
                                  launch with the k range split in tail_splits chunks (0: none) */
     int64_t tail_splits;      /* chunks of the split tail (0 without one) */
+    int64_t pad_bytes;        /* zero-padded operand copies when N or K is not a multiple of 8 (0 otherwise);
+                                 the plan's other fields then describe the padded problem */
 } gemm_bf16_plan_t;
 
 /*
@@ -149,10 +150,17 @@ typedef struct gemm_bf16_plan {
  * K x N (ldb >= N), C row-major (ldc >= N).  Sizes and leading dimensions are
  * in elements.
  *
- * Requirements: M, N, K >= 0; N and K multiples of 8; lda, ldb, ldc
- * multiples of 8 and at most 2^22; A, B, C 16-byte aligned (checked only for
- * operands that are read or written).  M == 0 or N == 0 is a no-op.  K == 0
- * writes +0 to every element of C.
+ * Requirements: M, N, K >= 0; N and K at most 2^22; A, B, C 2-byte aligned
+ * (checked only for operands that are read or written).  M == 0 or N == 0 is
+ * a no-op.  K == 0 writes +0 to every element of C.
+ *
+ * Fast path: N and K multiples of 8, lda, ldb, ldc multiples of 8 and at most
+ * 2^22, A, B, C 16-byte aligned.  Any other call copies A and B, zero-padded
+ * to multiples of 8 elements, into compact buffers (plan.pad_bytes, from the
+ * library's stream-ordered pool, released by the call), runs the fast path on
+ * them and copies the N valid columns of the result into C.  The zero padding
+ * along K contributes only zero products, so results are those of the
+ * unpadded problem.
  *
  * stages: 0 picks the default for the sync mode; otherwise 2, 3 or 4 whole
  * stages, or GEMM_STAGES_WINDOWS (barrier sync only).
@@ -160,9 +168,11 @@ typedef struct gemm_bf16_plan {
  * GEMM_SYNC_PINGPONG.
  * stream: a hipStream_t (NULL for the null stream).
  *
- * Returns GEMM_OK once the work is enqueued, else a negative status; on a
- * negative status nothing was enqueued.  Validation that does not need the
- * device happens before any HIP call.
+ * Returns GEMM_OK once the work is enqueued, else a negative status.
+ * Validation that does not need the device happens before any HIP call; after
+ * a validation error nothing was enqueued.  A failed allocation or launch
+ * later in the call may leave earlier steps enqueued, and C is then
+ * unspecified.
  */
 int gemm_bf16(int64_t M, int64_t N, int64_t K,
               const void* A, int64_t lda,

@@ -1705,6 +1705,22 @@ __global__ void __launch_bounds__(256) k_zero_fill(char* C, int64_t M, int64_t N
     }
 }
 
+// dst[r][c] = src[r][c] inside the src_rows x src_cols source, 0 outside it,
+// for the dst_rows x dst_cols destination (2-byte elements, any leading
+// dimensions and alignment).  Pads operands to multiples of 8 elements and
+// copies a padded result back.
+__global__ void __launch_bounds__(256) k_pad_copy(const uint16_t* src, int64_t src_rows, int64_t src_cols,
+                                                  int64_t ld_src, uint16_t* dst, int64_t dst_rows,
+                                                  int64_t dst_cols, int64_t ld_dst)
+{
+    const int64_t total = dst_rows * dst_cols;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = q / dst_cols, c = q - r * dst_cols;
+        dst[r * ld_dst + c] = (r < src_rows && c < src_cols) ? src[r * ld_src + c] : (uint16_t)0;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
@@ -1889,11 +1905,27 @@ int validate_shape(int64_t M, int64_t N, int64_t K, int stages, int sync_mode)
         return GEMM_ERR_STAGES;
     if (M < 0 || N < 0 || K < 0)
         return GEMM_ERR_INVALID_VALUE;
-    if (N % 8 != 0 || K % 8 != 0)
-        return GEMM_ERR_UNSUPPORTED_SHAPE;
-    if (M > ((int64_t)1 << 31) - 1 || N > ((int64_t)1 << 31) - 1 || K > ((int64_t)1 << 31) - 1)
+    // Leading dimensions of at least N and K, rounded up to 8, must fit the
+    // loads' 2^22-element row stride.
+    if (M > ((int64_t)1 << 31) - 1 || N > kMaxLd || K > kMaxLd)
         return GEMM_ERR_UNSUPPORTED_SHAPE;
     return GEMM_OK;
+}
+
+int64_t round8(int64_t x)
+{
+    return (x + 7) & ~(int64_t)7;
+}
+
+// Bytes of the zero-padded copies a call pads into (A and B to multiples of 8
+// columns and k-rows, C to a multiple of 8 columns), 256-byte aligned parts.
+int64_t pad_bytes(int64_t M, int64_t N, int64_t K, bool bt)
+{
+    auto up = [](int64_t b) { return (b + 255) & ~(int64_t)255; };
+    const int64_t N8 = round8(N), K8 = round8(K);
+    const int64_t a = K > 0 ? M * K8 * 2 : 0;
+    const int64_t b = K > 0 ? (bt ? N8 * K8 : K8 * N8) * 2 : 0;
+    return up(a) + up(b) + up(M * N8 * 2);
 }
 
 // Number of k chunks.  Shapes with fewer output tiles than half the compute
@@ -1944,9 +1976,13 @@ int64_t choose_tail_splits(int64_t tiles, int64_t K, int cus, int64_t& r)
     return 0;
 }
 
-int fill_plan(int64_t M, int64_t N, int64_t K, int b_transposed, int stages, int sync_mode, int cus,
+// The plan of the kernels' launch.  N or K that is not a multiple of 8 is
+// run on zero-padded copies (N and K rounded up to 8), so the plan is that of
+// the padded problem.
+int fill_plan(int64_t M, int64_t N_in, int64_t K_in, int b_transposed, int stages, int sync_mode, int cus,
               gemm_bf16_plan_t* out)
 {
+    const int64_t N = round8(N_in), K = round8(K_in);
     const int st = stages == 0 ? default_stages(sync_mode) : stages;
     const Shape v = with_cfg(sync_mode, st, b_transposed != 0, []<class C>() { return shape_of<C>(); });
     gemm_bf16_plan_t pl;
@@ -1972,8 +2008,64 @@ int fill_plan(int64_t M, int64_t N, int64_t K, int b_transposed, int stages, int
     pl.workspace_bytes = pl.k_splits > 1 ? items * v.bm * v.bn * 4 : pl.tail_tiles * pl.tail_splits * v.bm * v.bn * 4;
     if (items > ((int64_t)1 << 30) || items * pl.k_steps > ((int64_t)1 << 30))
         return GEMM_ERR_UNSUPPORTED_SHAPE;
+    pl.pad_bytes = (N != N_in || K != K_in) ? pad_bytes(M, N_in, K_in, b_transposed != 0) : 0;
     *out = pl;
     return GEMM_OK;
+}
+
+int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                void* C, int64_t ldc, int stages, int sync_mode, void* stream, bool bt);
+
+int launch_pad_copy(const void* src, int64_t src_rows, int64_t src_cols, int64_t ld_src, void* dst, int64_t dst_rows,
+                    int64_t dst_cols, int64_t ld_dst, hipStream_t s)
+{
+    const int64_t total = dst_rows * dst_cols;
+    if (total == 0)
+        return GEMM_OK;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536)
+        blocks = 65536;
+    hipLaunchKernelGGL(k_pad_copy, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t*)src, src_rows, src_cols,
+                       ld_src, (uint16_t*)dst, dst_rows, dst_cols, ld_dst);
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+// Shapes, leading dimensions or pointers the kernels cannot address directly:
+// A and B are copied, zero-padded, into compact buffers whose rows are
+// multiples of 8 elements (N and K rounded up to 8), the GEMM runs on those,
+// and the valid N columns of the padded result are copied into C.  Zero
+// k-columns add only zero products, so the result is that of the unpadded
+// problem.  The copies live in stream-ordered memory from the library's pool
+// for this call only.
+int gemm_padded(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                int64_t ldc, int stages, int sync_mode, hipStream_t s, bool bt, hipMemPool_t pool)
+{
+    auto up = [](int64_t b) { return (b + 255) & ~(int64_t)255; };
+    const int64_t N8 = round8(N), K8 = round8(K);
+    const int64_t b_rows = bt ? N8 : K8, b_cols = bt ? K8 : N8;
+    const int64_t a_bytes = K > 0 ? M * K8 * 2 : 0, b_bytes = K > 0 ? b_rows * b_cols * 2 : 0;
+    const int64_t bytes = pad_bytes(M, N, K, bt);
+    void* ws = nullptr;
+    const hipError_t ae = pool ? hipMallocFromPoolAsync(&ws, (size_t)bytes, pool, s) : hipMallocAsync(&ws, (size_t)bytes, s);
+    if (ae != hipSuccess || !ws)
+        return GEMM_ERR_DEVICE;
+    char* a2 = (char*)ws;
+    char* b2 = a2 + up(a_bytes);
+    char* c2 = b2 + up(b_bytes);
+    int rc = GEMM_OK;
+    if (K > 0) {
+        rc = launch_pad_copy(A, M, K, lda, a2, M, K8, K8, s);
+        if (rc == GEMM_OK)
+            rc = launch_pad_copy(B, bt ? N : K, bt ? K : N, ldb, b2, b_rows, b_cols, b_cols, s);
+    }
+    if (rc == GEMM_OK)
+        rc = gemm_common(M, N8, K8, K > 0 ? a2 : nullptr, K8, K > 0 ? b2 : nullptr, b_cols, c2, N8, stages, sync_mode,
+                         s, bt);
+    if (rc == GEMM_OK)
+        rc = launch_pad_copy(c2, M, N8, N8, C, M, N, ldc, s);
+    if (hipFreeAsync(ws, s) != hipSuccess && rc == GEMM_OK)
+        rc = GEMM_ERR_DEVICE;
+    return rc;
 }
 
 int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
@@ -1989,12 +2081,8 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
         return GEMM_ERR_INVALID_VALUE;
     if (ldc < N || (reads && (lda < K || ldb < (bt ? K : N))))
         return GEMM_ERR_INVALID_VALUE;
-    if (ldc % 8 != 0 || ((uintptr_t)C & 15) != 0)
+    if (((uintptr_t)C & 1) != 0 || (reads && (((uintptr_t)A & 1) != 0 || ((uintptr_t)B & 1) != 0)))
         return GEMM_ERR_MISALIGNED;
-    if (reads && (lda % 8 != 0 || ldb % 8 != 0 || ((uintptr_t)A & 15) != 0 || ((uintptr_t)B & 15) != 0))
-        return GEMM_ERR_MISALIGNED;
-    if (ldc > kMaxLd || (reads && (lda > kMaxLd || ldb > kMaxLd)))
-        return GEMM_ERR_UNSUPPORTED_SHAPE;
     const int64_t c_bytes = span_bytes(M, N, ldc);
     if (reads && (overlaps(C, c_bytes, A, span_bytes(M, K, lda)) ||
                   overlaps(C, c_bytes, B, bt ? span_bytes(N, K, ldb) : span_bytes(K, N, ldb))))
@@ -2006,6 +2094,14 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
     if (rc != GEMM_OK)
         return rc;
     hipStream_t s = (hipStream_t)stream;
+    // The kernels load and store 16-byte row segments: every row must start on
+    // a 16-byte boundary, and a row stride must fit the loads' offsets.
+    // Anything else runs on zero-padded copies.
+    const bool direct = N % 8 == 0 && K % 8 == 0 && ldc % 8 == 0 && ldc <= kMaxLd && ((uintptr_t)C & 15) == 0 &&
+                        (!reads || (lda % 8 == 0 && ldb % 8 == 0 && lda <= kMaxLd && ldb <= kMaxLd &&
+                                    ((uintptr_t)A & 15) == 0 && ((uintptr_t)B & 15) == 0));
+    if (!direct)
+        return gemm_padded(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, s, bt, pool);
     if (!reads) {
         const int64_t chunks = M * (N / 8);
         int64_t blocks = (chunks + 255) / 256;
@@ -2133,8 +2229,8 @@ const char* gemm_bf16_strerror(int status)
     switch (status) {
     case GEMM_OK: return "success";
     case GEMM_ERR_INVALID_VALUE: return "invalid value (negative size, NULL pointer or leading dimension too small)";
-    case GEMM_ERR_MISALIGNED: return "misaligned operand (pointers need 16-byte alignment, leading dimensions a multiple of 8)";
-    case GEMM_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (N and K must be multiples of 8; leading dimensions at most 2^22)";
+    case GEMM_ERR_MISALIGNED: return "misaligned operand (bf16 pointers need 2-byte alignment)";
+    case GEMM_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (N and K at most 2^22, M below 2^31)";
     case GEMM_ERR_STAGES: return "stages must be 0 (default), 2, 3, 4, or 5 (split-window ring, barrier sync)";
     case GEMM_ERR_SYNC_MODE:
         return "sync_mode must be GEMM_SYNC_BARRIER, GEMM_SYNC_FLAGS, GEMM_SYNC_WAVESPEC or GEMM_SYNC_PINGPONG";

@@ -84,25 +84,39 @@ def test_validation_errors(fn):
     assert call(fn, stages=bd.STAGES_WINDOWS, sync=3) == bd.GEMM_ERR_STAGES
     assert call(fn, M=-1) == bd.GEMM_ERR_INVALID_VALUE
     assert call(fn, K=-8) == bd.GEMM_ERR_INVALID_VALUE
-    assert call(fn, N=60) == bd.GEMM_ERR_UNSUPPORTED_SHAPE
-    assert call(fn, K=60) == bd.GEMM_ERR_UNSUPPORTED_SHAPE
+    assert call(fn, N=(1 << 22) + 8, ldb=(1 << 22) + 8, ldc=(1 << 22) + 8) == bd.GEMM_ERR_UNSUPPORTED_SHAPE
+    assert call(fn, K=(1 << 22) + 8, lda=(1 << 22) + 8, ldb=(1 << 22) + 8) == bd.GEMM_ERR_UNSUPPORTED_SHAPE
     assert call(fn, A=0) == bd.GEMM_ERR_INVALID_VALUE
     assert call(fn, B=0) == bd.GEMM_ERR_INVALID_VALUE
     assert call(fn, C=0) == bd.GEMM_ERR_INVALID_VALUE
     assert call(fn, lda=56) == bd.GEMM_ERR_INVALID_VALUE
     assert call(fn, ldb=56) == bd.GEMM_ERR_INVALID_VALUE
     assert call(fn, ldc=56) == bd.GEMM_ERR_INVALID_VALUE
-    assert call(fn, lda=68) == bd.GEMM_ERR_MISALIGNED
-    assert call(fn, ldc=68) == bd.GEMM_ERR_MISALIGNED
-    assert call(fn, A=ALIGNED + 2) == bd.GEMM_ERR_MISALIGNED
-    assert call(fn, C=4 * ALIGNED + 8) == bd.GEMM_ERR_MISALIGNED
-    assert call(fn, lda=(1 << 22) + 8) == bd.GEMM_ERR_UNSUPPORTED_SHAPE
+    # bf16 pointers must be 2-byte aligned
+    assert call(fn, A=ALIGNED + 1) == bd.GEMM_ERR_MISALIGNED
+    assert call(fn, B=2 * ALIGNED + 3) == bd.GEMM_ERR_MISALIGNED
+    assert call(fn, C=4 * ALIGNED + 5) == bd.GEMM_ERR_MISALIGNED
     # C overlapping A or B
     assert call(fn, C=ALIGNED + 64) == bd.GEMM_ERR_ALIAS
     assert call(fn, C=2 * ALIGNED) == bd.GEMM_ERR_ALIAS
     # degenerate sizes are no-ops that need no pointers and no device
     assert call(fn, M=0, A=0, C=0) == bd.GEMM_OK
     assert call(fn, N=0, B=0, C=0) == bd.GEMM_OK
+
+
+@pytest.mark.parametrize("fn", [bd.gemm_bf16, bd.gemm_bf16_bt], ids=["kn", "nk"])
+def test_unaligned_calls_pass_validation(fn):
+    """N or K not a multiple of 8, leading dimensions not a multiple of 8 or
+    above 2^22, and 2-byte aligned pointers are valid calls (they run on
+    zero-padded copies): validation lets them through to the device query.
+    Only checked where no GPU is visible, since the addresses are fake."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; these calls would launch on fake addresses")
+    for kw in ({"N": 60, "ldb": 64, "ldc": 64}, {"K": 60}, {"N": 1, "K": 3}, {"lda": 68}, {"ldc": 68},
+               {"A": ALIGNED + 2}, {"C": 4 * ALIGNED + 8}, {"lda": (1 << 22) + 8, "B": 1 << 40, "C": 1 << 41},
+               {"M": 3, "N": 5, "K": 7}):
+        assert call(fn, **kw) == bd.GEMM_ERR_DEVICE, kw
 
 
 def test_ld_rules_follow_layout():
@@ -119,7 +133,7 @@ def test_plan_validation():
         bd.gemm_bf16_plan(64, 64, 64, 0, 0, 9)
     assert e.value.code == bd.GEMM_ERR_SYNC_MODE
     with pytest.raises(bd.GemmError) as e:
-        bd.gemm_bf16_plan(64, 60, 64, 0, 0, 0)
+        bd.gemm_bf16_plan(64, (1 << 22) + 8, 64, 0, 0, 0)
     assert e.value.code == bd.GEMM_ERR_UNSUPPORTED_SHAPE
 
 

@@ -296,6 +296,78 @@ def test_split_tail_exact_integer_inputs():
         np.testing.assert_array_equal(got[rows], ref, err_msg="%s/%d" % (sync, stages))
 
 
+UNALIGNED = [(37, 45, 33), (300, 263, 1001), (1, 1, 1), (513, 1031, 77), (2, 9, 4100)]
+PAD_MODES = [("barrier", 2), ("barrier", bd.STAGES_WINDOWS), ("flags", 2), ("wavespec", 3), ("pingpong", 3)]
+
+
+def padded(X, rows, cols):
+    Y = torch.zeros((rows, cols), dtype=torch.bfloat16)
+    Y[:X.shape[0], :X.shape[1]] = X
+    return Y
+
+
+@pytest.mark.parametrize("bt", [False, True], ids=["kn", "nk"])
+@pytest.mark.parametrize("shape", UNALIGNED, ids=lambda c: "%dx%dx%d" % c)
+def test_unaligned_shapes(shape, bt):
+    """N or K not a multiple of 8 (with sentinel-filled row padding): the call
+    runs on zero-padded copies.  It matches the oracle, and equals bit for bit
+    the direct call on operands padded by hand to multiples of 8."""
+    M, N, K = shape
+    N8, K8 = -(-N // 8) * 8, -(-K // 8) * 8
+    A, B = make_operands(M, N, K, b_transposed=bt, seed=M + 3 * N + 7 * K, lda=K + 5, ldb=(K if bt else N) + 3)
+    ref = oracle.load().gemm_bf16(bits(A), bits(B), bt)
+    Ap = padded(A, M, K8).cuda()
+    Bp = (padded(B, N8, K8) if bt else padded(B, K8, N8)).cuda()
+    dA, dB = A.cuda(), B.cuda()
+    for sync, stages in PAD_MODES:
+        plan = bd.gemm_bf16_plan(M, N, K, bt, stages, bd.SYNC_MODES[sync])
+        assert plan["pad_bytes"] > 0
+        got = run(dA, dB, bt, sync, stages)
+        assert_within_tol(got, ref, "unaligned %s/%d" % (sync, stages))
+        direct = run(Ap, Bp, bt, sync, stages)
+        np.testing.assert_array_equal(got, direct[:, :N], err_msg="%s/%d" % (sync, stages))
+
+
+@pytest.mark.parametrize("bt", [False, True], ids=["kn", "nk"])
+def test_unaligned_pointers_and_leading_dimensions(bt):
+    """Aligned sizes, but operands at 2- and 4-byte offsets with odd leading
+    dimensions (views into sentinel-filled buffers) and an odd-strided C: the
+    padded path, bit-identical to the direct call on contiguous copies."""
+    M, N, K = 200, 136, 264
+    A, B = make_operands(M, N, K, b_transposed=bt, seed=606 + bt)
+    ref = oracle.load().gemm_bf16(bits(A), bits(B), bt)
+
+    def offset_view(X, left, extra):
+        buf = torch.full((X.shape[0], X.shape[1] + left + extra), 1.0e30, dtype=torch.bfloat16, device="cuda")
+        buf[:, left:left + X.shape[1]] = X.cuda()
+        return buf[:, left:left + X.shape[1]]
+
+    vA, vB = offset_view(A, 1, 2), offset_view(B, 2, 3)
+    assert vA.data_ptr() % 16 == 2 and vB.data_ptr() % 16 == 4 and vA.stride(0) % 8 != 0
+    Cbuf = torch.full((M, N + 5), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = Cbuf[:, 1:N + 1]
+    C = bd.gemm(vA, vB, b_transposed=bt, out=out)
+    torch.cuda.synchronize()
+    got = bits(C.cpu()).copy()
+    assert_within_tol(got, ref, "offset views")
+    direct = run(A.cuda(), B.cuda(), bt, "barrier", 2)
+    np.testing.assert_array_equal(got, direct)
+    # the columns around the view are untouched
+    assert (Cbuf[:, 0] == 7.0).all() and (Cbuf[:, N + 1:] == 7.0).all()
+
+
+def test_unaligned_zero_k():
+    """K == 0 with an odd N: C is +0 everywhere, columns outside untouched."""
+    Cbuf = torch.full((5, 14), 3.0, dtype=torch.bfloat16, device="cuda")
+    out = Cbuf[:, 1:12]
+    A = torch.empty((5, 0), dtype=torch.bfloat16, device="cuda")
+    B = torch.empty((0, 11), dtype=torch.bfloat16, device="cuda")
+    bd.gemm(A, B, out=out)
+    torch.cuda.synchronize()
+    assert (bits(out.cpu()) == 0).all()
+    assert (Cbuf[:, 0] == 3.0).all() and (Cbuf[:, 12:] == 3.0).all()
+
+
 def test_layouts_and_modes_bit_identical():
     M, N, K = 520, 776, 392
     A, B = make_operands(M, N, K, b_transposed=False, seed=99)

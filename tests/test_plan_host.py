@@ -159,6 +159,36 @@ def test_random_shapes_follow_the_rules():
             assert pl["workspace_bytes"] == 0
 
 
+def up256(b):
+    return (b + 255) // 256 * 256
+
+
+def want_pad(M, N, K, bt):
+    """Zero-padded copies: A as M x K8, B as N8 x K8 (stored N x K) or K8 x N8,
+    C as M x N8 (bf16, each part rounded up to 256 bytes); none if N and K are
+    multiples of 8."""
+    N8, K8 = -(-N // 8) * 8, -(-K // 8) * 8
+    if N8 == N and K8 == K:
+        return 0
+    a = M * K8 * 2 if K else 0
+    b = (N8 * K8 if bt else K8 * N8) * 2 if K else 0
+    return up256(a) + up256(b) + up256(M * N8 * 2)
+
+
+def test_padded_plans():
+    """N or K that is not a multiple of 8: the plan is that of the problem
+    padded to multiples of 8, plus the bytes of the padded copies."""
+    for (M, N, K) in ((37, 45, 33), (300, 263, 1001), (1, 1, 1), (4100, 4352, 4095), (5, 7, 0)):
+        for bt in (0, 1):
+            for sync, stages in MODES:
+                pl = plan(M, N, K, bt, sync, stages)
+                ref = plan(M, -(-N // 8) * 8, -(-K // 8) * 8, bt, sync, stages)
+                assert pl["pad_bytes"] == want_pad(M, N, K, bt) > 0, (M, N, K, bt, pl)
+                ref["pad_bytes"] = pl["pad_bytes"]
+                assert pl == ref, (M, N, K, bt, sync, stages)
+    assert plan(64, 64, 64, 0, "barrier", 2)["pad_bytes"] == 0
+
+
 def test_errors():
     with pytest.raises(bd.GemmError) as e:
         plan(64, 64, 64, 0, "barrier", 2, cus=0)
@@ -167,7 +197,10 @@ def test_errors():
         bd.gemm_bf16_plan_cus(64, 64, 64, 0, 7, 0, CUS)
     assert e.value.code == bd.GEMM_ERR_STAGES
     with pytest.raises(bd.GemmError) as e:
-        bd.gemm_bf16_plan_cus(64, 60, 64, 0, 0, 0, CUS)
+        bd.gemm_bf16_plan_cus(64, (1 << 22) + 1, 64, 0, 0, 0, CUS)
+    assert e.value.code == bd.GEMM_ERR_UNSUPPORTED_SHAPE
+    with pytest.raises(bd.GemmError) as e:
+        bd.gemm_bf16_plan_cus(1 << 31, 64, 64, 0, 0, 0, CUS)
     assert e.value.code == bd.GEMM_ERR_UNSUPPORTED_SHAPE
     with pytest.raises(bd.GemmError) as e:
         bd.gemm_bf16_plan_cus(64, 64, 64, 0, 5, 1, CUS)           # split windows need barrier sync
