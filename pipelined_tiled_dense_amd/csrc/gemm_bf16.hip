@@ -1707,17 +1707,40 @@ __global__ void __launch_bounds__(256) k_zero_fill(char* C, int64_t M, int64_t N
 
 // dst[r][c] = src[r][c] inside the src_rows x src_cols source, 0 outside it,
 // for the dst_rows x dst_cols destination (2-byte elements, any leading
-// dimensions and alignment).  Pads operands to multiples of 8 elements and
-// copies a padded result back.
+// dimensions and 2-byte alignment).  Pads operands to multiples of 8 elements
+// and copies a padded result back.  One thread per group of 8 destination
+// columns: a 16-byte load or store where the address is 16-byte aligned and
+// the whole group lies inside the matrix, element accesses otherwise.
 __global__ void __launch_bounds__(256) k_pad_copy(const uint16_t* src, int64_t src_rows, int64_t src_cols,
                                                   int64_t ld_src, uint16_t* dst, int64_t dst_rows,
                                                   int64_t dst_cols, int64_t ld_dst)
 {
-    const int64_t total = dst_rows * dst_cols;
+    const int64_t groups_per_row = (dst_cols + 7) / 8;
+    const int64_t total = dst_rows * groups_per_row;
     for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
          q += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = q / dst_cols, c = q - r * dst_cols;
-        dst[r * ld_dst + c] = (r < src_rows && c < src_cols) ? src[r * ld_src + c] : (uint16_t)0;
+        const int64_t r = q / groups_per_row, c0 = (q - r * groups_per_row) * 8;
+        uint16_t v[8];
+        const uint16_t* s = src + r * ld_src + c0;
+        if (r < src_rows && c0 + 8 <= src_cols && ((uintptr_t)s & 15) == 0) {
+            const u32x4_t x = *(const u32x4_t*)s;
+            __builtin_memcpy(v, &x, 16);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = (r < src_rows && c0 + e < src_cols) ? s[e] : (uint16_t)0;
+        }
+        uint16_t* d = dst + r * ld_dst + c0;
+        if (c0 + 8 <= dst_cols && ((uintptr_t)d & 15) == 0) {
+            u32x4_t x;
+            __builtin_memcpy(&x, v, 16);
+            *(u32x4_t*)d = x;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (c0 + e < dst_cols)
+                    d[e] = v[e];
+        }
     }
 }
 
@@ -1917,15 +1940,30 @@ int64_t round8(int64_t x)
     return (x + 7) & ~(int64_t)7;
 }
 
-// Bytes of the zero-padded copies a call pads into (A and B to multiples of 8
-// columns and k-rows, C to a multiple of 8 columns), 256-byte aligned parts.
-int64_t pad_bytes(int64_t M, int64_t N, int64_t K, bool bt)
+// Which operands a call copies into zero-padded compact buffers.  K off the
+// 8-element grid pads A and B along k; N off the grid pads B's n extent and
+// C's columns; otherwise an operand is copied only if its own leading
+// dimension or pointer does not suit the kernels' 16-byte row segments.
+struct PadSet {
+    bool a, b, c;
+};
+
+PadSet pad_set(int64_t N, int64_t K, bool bt, bool a_ok, bool b_ok, bool c_ok)
+{
+    const bool k_off = K % 8 != 0, n_off = N % 8 != 0;
+    return PadSet{k_off || !a_ok, k_off || n_off || !b_ok, n_off || !c_ok};
+}
+
+// Bytes of those copies (256-byte aligned parts): A as M x K8, B as N8 x K8
+// (stored N x K) or K8 x N8, C as M x N8.
+int64_t pad_bytes(int64_t M, int64_t N, int64_t K, bool bt, PadSet ps)
 {
     auto up = [](int64_t b) { return (b + 255) & ~(int64_t)255; };
     const int64_t N8 = round8(N), K8 = round8(K);
-    const int64_t a = K > 0 ? M * K8 * 2 : 0;
-    const int64_t b = K > 0 ? (bt ? N8 * K8 : K8 * N8) * 2 : 0;
-    return up(a) + up(b) + up(M * N8 * 2);
+    const int64_t a = (ps.a && K > 0) ? M * K8 * 2 : 0;
+    const int64_t b = (ps.b && K > 0) ? N8 * K8 * 2 : 0;
+    const int64_t c = ps.c ? M * N8 * 2 : 0;
+    return up(a) + up(b) + up(c);
 }
 
 // Number of k chunks.  Shapes with fewer output tiles than half the compute
@@ -2008,7 +2046,9 @@ int fill_plan(int64_t M, int64_t N_in, int64_t K_in, int b_transposed, int stage
     pl.workspace_bytes = pl.k_splits > 1 ? items * v.bm * v.bn * 4 : pl.tail_tiles * pl.tail_splits * v.bm * v.bn * 4;
     if (items > ((int64_t)1 << 30) || items * pl.k_steps > ((int64_t)1 << 30))
         return GEMM_ERR_UNSUPPORTED_SHAPE;
-    pl.pad_bytes = (N != N_in || K != K_in) ? pad_bytes(M, N_in, K_in, b_transposed != 0) : 0;
+    pl.pad_bytes = (N != N_in || K != K_in)
+                       ? pad_bytes(M, N_in, K_in, b_transposed != 0, pad_set(N_in, K_in, b_transposed != 0, true, true, true))
+                       : 0;
     *out = pl;
     return GEMM_OK;
 }
@@ -2019,7 +2059,7 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
 int launch_pad_copy(const void* src, int64_t src_rows, int64_t src_cols, int64_t ld_src, void* dst, int64_t dst_rows,
                     int64_t dst_cols, int64_t ld_dst, hipStream_t s)
 {
-    const int64_t total = dst_rows * dst_cols;
+    const int64_t total = dst_rows * ((dst_cols + 7) / 8);
     if (total == 0)
         return GEMM_OK;
     int64_t blocks = (total + 255) / 256;
@@ -2031,20 +2071,21 @@ int launch_pad_copy(const void* src, int64_t src_rows, int64_t src_cols, int64_t
 }
 
 // Shapes, leading dimensions or pointers the kernels cannot address directly:
-// A and B are copied, zero-padded, into compact buffers whose rows are
-// multiples of 8 elements (N and K rounded up to 8), the GEMM runs on those,
-// and the valid N columns of the padded result are copied into C.  Zero
-// k-columns add only zero products, so the result is that of the unpadded
-// problem.  The copies live in stream-ordered memory from the library's pool
-// for this call only.
+// the operands pad_set names are copied, zero-padded, into compact buffers
+// whose rows are multiples of 8 elements (N and K rounded up to 8), the GEMM
+// runs on those (and on the operands used in place), and the valid N columns
+// of a padded result are copied into C.  Zero k-columns add only zero
+// products, so the result is that of the unpadded problem.  The copies live
+// in stream-ordered memory from the library's pool for this call only.
 int gemm_padded(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
-                int64_t ldc, int stages, int sync_mode, hipStream_t s, bool bt, hipMemPool_t pool)
+                int64_t ldc, int stages, int sync_mode, hipStream_t s, bool bt, hipMemPool_t pool, PadSet ps)
 {
     auto up = [](int64_t b) { return (b + 255) & ~(int64_t)255; };
     const int64_t N8 = round8(N), K8 = round8(K);
     const int64_t b_rows = bt ? N8 : K8, b_cols = bt ? K8 : N8;
-    const int64_t a_bytes = K > 0 ? M * K8 * 2 : 0, b_bytes = K > 0 ? b_rows * b_cols * 2 : 0;
-    const int64_t bytes = pad_bytes(M, N, K, bt);
+    const int64_t a_bytes = (ps.a && K > 0) ? M * K8 * 2 : 0;
+    const int64_t b_bytes = (ps.b && K > 0) ? b_rows * b_cols * 2 : 0;
+    const int64_t bytes = pad_bytes(M, N, K, bt, ps);
     void* ws = nullptr;
     const hipError_t ae = pool ? hipMallocFromPoolAsync(&ws, (size_t)bytes, pool, s) : hipMallocAsync(&ws, (size_t)bytes, s);
     if (ae != hipSuccess || !ws)
@@ -2052,16 +2093,25 @@ int gemm_padded(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
     char* a2 = (char*)ws;
     char* b2 = a2 + up(a_bytes);
     char* c2 = b2 + up(b_bytes);
+    const void* a_use = A;
+    const void* b_use = B;
+    void* c_use = ps.c ? (void*)c2 : C;
+    int64_t lda_use = lda, ldb_use = ldb, ldc_use = ps.c ? N8 : ldc;
     int rc = GEMM_OK;
-    if (K > 0) {
+    if (K > 0 && ps.a) {
         rc = launch_pad_copy(A, M, K, lda, a2, M, K8, K8, s);
-        if (rc == GEMM_OK)
-            rc = launch_pad_copy(B, bt ? N : K, bt ? K : N, ldb, b2, b_rows, b_cols, b_cols, s);
+        a_use = a2;
+        lda_use = K8;
+    }
+    if (K > 0 && ps.b && rc == GEMM_OK) {
+        rc = launch_pad_copy(B, bt ? N : K, bt ? K : N, ldb, b2, b_rows, b_cols, b_cols, s);
+        b_use = b2;
+        ldb_use = b_cols;
     }
     if (rc == GEMM_OK)
-        rc = gemm_common(M, N8, K8, K > 0 ? a2 : nullptr, K8, K > 0 ? b2 : nullptr, b_cols, c2, N8, stages, sync_mode,
-                         s, bt);
-    if (rc == GEMM_OK)
+        rc = gemm_common(M, N8, K8, K > 0 ? a_use : nullptr, lda_use, K > 0 ? b_use : nullptr, ldb_use, c_use, ldc_use,
+                         stages, sync_mode, s, bt);
+    if (rc == GEMM_OK && ps.c)
         rc = launch_pad_copy(c2, M, N8, N8, C, M, N, ldc, s);
     if (hipFreeAsync(ws, s) != hipSuccess && rc == GEMM_OK)
         rc = GEMM_ERR_DEVICE;
@@ -2096,12 +2146,11 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
     hipStream_t s = (hipStream_t)stream;
     // The kernels load and store 16-byte row segments: every row must start on
     // a 16-byte boundary, and a row stride must fit the loads' offsets.
-    // Anything else runs on zero-padded copies.
-    const bool direct = N % 8 == 0 && K % 8 == 0 && ldc % 8 == 0 && ldc <= kMaxLd && ((uintptr_t)C & 15) == 0 &&
-                        (!reads || (lda % 8 == 0 && ldb % 8 == 0 && lda <= kMaxLd && ldb <= kMaxLd &&
-                                    ((uintptr_t)A & 15) == 0 && ((uintptr_t)B & 15) == 0));
-    if (!direct)
-        return gemm_padded(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, s, bt, pool);
+    // Anything else runs on zero-padded copies of the operands that need them.
+    auto fits = [](const void* ptr, int64_t ld) { return ld % 8 == 0 && ld <= kMaxLd && ((uintptr_t)ptr & 15) == 0; };
+    const PadSet ps = pad_set(N, K, bt, !reads || fits(A, lda), !reads || fits(B, ldb), fits(C, ldc));
+    if (ps.a || ps.b || ps.c)
+        return gemm_padded(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, s, bt, pool, ps);
     if (!reads) {
         const int64_t chunks = M * (N / 8);
         int64_t blocks = (chunks + 255) / 256;

@@ -164,21 +164,22 @@ def up256(b):
 
 
 def want_pad(M, N, K, bt):
-    """Zero-padded copies: A as M x K8, B as N8 x K8 (stored N x K) or K8 x N8,
-    C as M x N8 (bf16, each part rounded up to 256 bytes); none if N and K are
-    multiples of 8."""
+    """Zero-padded copies for aligned operands: K off the 8-element grid pads
+    A (M x K8) and B; N off the grid pads B (N8 x K8 or K8 x N8) and C
+    (M x N8); each part is rounded up to 256 bytes."""
     N8, K8 = -(-N // 8) * 8, -(-K // 8) * 8
-    if N8 == N and K8 == K:
-        return 0
-    a = M * K8 * 2 if K else 0
-    b = (N8 * K8 if bt else K8 * N8) * 2 if K else 0
-    return up256(a) + up256(b) + up256(M * N8 * 2)
+    k_off, n_off = K8 != K, N8 != N
+    a = M * K8 * 2 if (k_off and K) else 0
+    b = N8 * K8 * 2 if ((k_off or n_off) and K) else 0
+    c = M * N8 * 2 if n_off else 0
+    return up256(a) + up256(b) + up256(c)
 
 
 def test_padded_plans():
     """N or K that is not a multiple of 8: the plan is that of the problem
     padded to multiples of 8, plus the bytes of the padded copies."""
-    for (M, N, K) in ((37, 45, 33), (300, 263, 1001), (1, 1, 1), (4100, 4352, 4095), (5, 7, 0)):
+    for (M, N, K) in ((37, 45, 33), (300, 263, 1001), (1, 1, 1), (4100, 4352, 4095), (5, 7, 0), (64, 60, 64),
+                      (64, 64, 60)):
         for bt in (0, 1):
             for sync, stages in MODES:
                 pl = plan(M, N, K, bt, sync, stages)
