@@ -368,6 +368,31 @@ def test_unaligned_zero_k():
     assert (Cbuf[:, 0] == 3.0).all() and (Cbuf[:, 12:] == 3.0).all()
 
 
+def test_concurrent_split_calls_on_two_streams():
+    """Split calls take their workspaces from one stream-ordered pool.  Calls
+    on two streams, interleaved with no synchronisation between them (a split
+    k range on one, a split tail and an off-grid shape on the other), must
+    each give the bits of the same call run alone."""
+    cases = [((1000, 1032, 8192), True), ((4300, 4344, 4096), False), ((37, 45, 4100), True)]
+    ops, want = [], []
+    for (M, N, K), bt in cases:
+        A, B = make_operands(M, N, K, b_transposed=bt, seed=M + N + K)
+        dA, dB = A.cuda(), B.cuda()
+        ops.append((dA, dB, bt))
+        want.append(run(dA, dB, bt, "barrier", 2))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(3):
+        for i, (dA, dB, bt) in enumerate(ops):
+            st = streams[(i + rep) % 2]
+            with torch.cuda.stream(st):
+                outs.append((i, bd.gemm(dA, dB, b_transposed=bt, sync="barrier", stages=2)))
+    torch.cuda.synchronize()
+    for i, C in outs:
+        np.testing.assert_array_equal(bits(C.cpu()), want[i], err_msg="case %d" % i)
+
+
 def test_layouts_and_modes_bit_identical():
     M, N, K = 520, 776, 392
     A, B = make_operands(M, N, K, b_transposed=False, seed=99)
