@@ -14,7 +14,11 @@
  * sum is accumulated in fp32 by the matrix cores; the order of the fp32
  * additions is the library's, so results may differ from an exactly rounded
  * product by the fp32 rounding of the partial sums (well under one bf16 ulp
- * for K up to ~10^5 at unit-size inputs).  There is no alpha/beta: C is
+ * for K up to ~10^5 at unit-size inputs).  Calls whose plans report the
+ * same MFMA block (plan.mfma_block: 16 x 16 x 32 or 32 x 32 x 16 MFMAs) run
+ * the same chain of MFMA accumulations for every element and give the same
+ * bits, whatever the sync mode, stage count or B layout; across block shapes
+ * results may differ by fp32 rounding.  There is no alpha/beta: C is
  * overwritten.
  *
  * How the work is done (none of this changes the result):
@@ -44,7 +48,7 @@
  * so that the GPU fills.  Each output tile's chunks are summed in fp32, in
  * chunk order, after one fp32 chain per chunk; the result differs from the
  * unsplit sum only by fp32 rounding, is the same for every sync mode and
- * stage count, and is deterministic.  The fp32 partial tiles
+ * stage count with the same MFMA block, and is deterministic.  The fp32 partial tiles
  * (plan.workspace_bytes) are allocated stream-ordered on `stream` and
  * released (hipFreeAsync) by the same call, from a memory pool the library
  * creates once per device (hipMallocFromPoolAsync; hipMallocAsync if the pool
@@ -102,7 +106,7 @@ enum {
  * backward kernel: exploratory shared-memory reduction" (section
  * "Shared-memory reduction strategies": buffer aliasing, and a producer that
  * streams one half of an operand while the consumer computes on the other).
- * Results are bit-identical to every other mode.
+ * Results are bit-identical to every other mode with 16 x 16 MFMA blocks.
  */
 enum { GEMM_STAGES_WINDOWS = 5 };
 
@@ -143,6 +147,10 @@ typedef struct gemm_bf16_plan {
     int64_t tail_splits;      /* chunks of the split tail (0 without one) */
     int64_t pad_bytes;        /* zero-padded operand copies when N or K is not a multiple of 8 (0 otherwise);
                                  the plan's other fields then describe the padded problem */
+    int64_t mfma_block;       /* MFMA block edge: 16 (v_mfma_f32_16x16x32_bf16, 32 k per instruction) or 32
+                                 (v_mfma_f32_32x32x16_bf16, 16 k per instruction).  Calls whose plans agree
+                                 on it and on the k split (k_splits, tail_tiles, tail_splits, bm, bn) run
+                                 the same chain of MFMAs for every element and give the same bits. */
 } gemm_bf16_plan_t;
 
 /*

@@ -85,6 +85,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <type_traits>
 #include <utility>
 
 #include "gemm_bf16.h"
@@ -169,7 +170,8 @@ enum {
 // ---------------------------------------------------------------------------
 // Compile-time configuration of one kernel instance.
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, int SYNC_, bool BT_, int NP_, bool WIN_ = false>
+template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, int SYNC_, bool BT_, int NP_, bool WIN_ = false,
+          int MF_ = 32>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_;
     static constexpr int SYNC = SYNC_;
@@ -189,8 +191,15 @@ struct Cfg {
     static constexpr int NW = NCW + NP;
     static constexpr int THREADS = NW * 64;
     static constexpr int TM = BM / WM, TN = BN / WN;                 // wave tile
-    static constexpr int FM = TM / 32, FN = TN / 32;                 // 32x32 MFMA blocks per wave
-    static constexpr int KK = BK / 16;                               // MFMA k-steps per stage
+    // MFMA block edge.  32: v_mfma_f32_32x32x16_bf16, one 16-wide k-step per
+    // MFMA region.  16: v_mfma_f32_16x16x32_bf16, whose 32-wide k-step takes
+    // two regions, each over half of the wave's block rows.  At equal LDS
+    // bytes per FLOP the 16 x 16 form moves half the accumulator register
+    // traffic per FLOP and sustains a higher clock under the power limit.
+    static constexpr int MF = MF_;
+    using Acc = std::conditional_t<MF == 16, f32x4_t, f32x16_t>;
+    static constexpr int FM = TM / MF, FN = TN / MF;                 // MFMA blocks per wave
+    static constexpr int KK = BK / 16;                               // MFMA regions (16 k each) per stage
     static constexpr int A_BYTES = BM * BK * 2;
     static constexpr int B_BYTES = BN * BK * 2;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
@@ -220,6 +229,8 @@ struct Cfg {
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(KK % 2 == 0, "fragment double buffering assumes an even number of MFMA k-steps");
     static_assert(FM >= 1 && FN >= 2 && FN % 2 == 0, "wave tile");
+    static_assert(MF == 32 || (MF == 16 && BK == 64 && FM % 2 == 0 && !PRODUCERS),
+                  "16 x 16 blocks: all-wave kernels, 64-wide stages (two 32-wide k-steps)");
     static_assert(A_BYTES % (1024 * NLW) == 0 && B_BYTES % (1024 * NLW) == 0, "DMA split");
     static_assert(64 % CPR_K == 0, "a DMA window covers whole K-contiguous rows");
     static_assert(CPR_N == 16 || CPR_N == 32, "a DMA window covers whole K x N rows of B");
@@ -263,10 +274,16 @@ __device__ __forceinline__ int swz_k(int row)
     return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
 }
 // K x N tiles of B hold rows of BN elements (512 or 256 bytes, so every row
-// starts on the same bank).  A transposing read has lanes 0..31 on 4
-// consecutive k-rows x 4 chunks; XORing chunk bits 2-3 with (k mod 4) spreads
-// the 16 (row, chunk) pairs over all 16 bank groups.
-__device__ __forceinline__ int swz_n(int krow) { return (krow & 3) << 2; }
+// starts on the same bank).  With 32 x 32 blocks a transposing read has lanes
+// 0..31 on 4 consecutive k-rows x 4 chunks; XORing chunk bits 2-3 with
+// (k mod 4) spreads the 16 (row, chunk) pairs over all 16 bank groups.  With
+// 16 x 16 blocks lanes 0..31 cover k-rows r and r + 8 (r = 0..3) x 2 chunks,
+// so chunk bit 1 is also XORed with k-row bit 3.
+template <int MF>
+__device__ __forceinline__ int swz_n(int krow)
+{
+    return MF == 16 ? (((krow & 3) << 2) | (((krow >> 3) & 1) << 1)) : ((krow & 3) << 2);
+}
 
 // Output tile at raster position Lt (0 <= Lt < tiles_mn): a grouped raster,
 // runs of group_m tile rows walked column by column, so a run of consecutive
@@ -545,7 +562,7 @@ struct Loader {
     __device__ __forceinline__ static int nofs_n(int s)
     {
         const int row = s / C::CPR_N;
-        return ((s % C::CPR_N) ^ swz_n(row)) * 8;
+        return ((s % C::CPR_N) ^ swz_n<C::MF>(row)) * 8;
     }
 
     __device__ __forceinline__ void init(const Params& p, int32_t ntiles, int lw, int lane)
@@ -738,7 +755,16 @@ constexpr int frag_reads() { return C::FM + (C::BT ? 1 : 2) * C::FN; }
 // The frag_reads<C>() LDS read instructions of MFMA k-step kk, one at a time.
 // The MFMA runs with the B fragment as its first operand, so accumulator
 // block (i, j) holds C^T: lane l owns column m = l%32 and rows
-// n = 8*(r/4) + 4*(l/32) + r%4.
+// n = 8*(r/4) + 4*(l/32) + r%4 (32 x 32 blocks), or column m = l%16 and rows
+// n = 4*(l/16) + r (16 x 16 blocks).
+//
+// 16 x 16 blocks (32-wide k-step kk): lane l reads row (base + 16*i + l%16),
+// logical chunk 4*kk + l/16; with B stored K x N, group g = l/16 of a
+// transposing read takes k-rows 32*kk + 8*g + 4*hh + r and the chunk of
+// column 16*J + 4*q, 2*J + q/2, which the swizzle XORs with 4*r + 2*(g%2):
+// it becomes 2*(J ^ (2*r + g%2)) + q/2.  The reads go A block 0, then B,
+// then the other A blocks: the first MFMAs of a k-step need A block 0 and
+// every B block.
 //
 // K-contiguous tiles: lane l reads row (base + 32*i + l%32), logical chunk
 // 2*kk + l/32.  Every block starts on a multiple of 8 rows, so the swizzle
@@ -759,6 +785,21 @@ struct FragReader {
 
     __device__ __forceinline__ FragReader(int wm, int wn, int lane, int kk)
     {
+        if constexpr (C::MF == 16) {
+            const int h = lane >> 4, r16 = lane & 15;
+            const uint32_t xk = (uint32_t)(((4 * kk + h) ^ swz_k<C::BK>(r16)) << 4);
+            a_off = opaque((uint32_t)((wm * C::TM + r16) * (C::BK * 2)) + xk);
+            if constexpr (C::BT) {
+                b_off = opaque((uint32_t)((wn * C::TN + r16) * (C::BK * 2)) + xk);
+                r = 0;
+            } else {
+                const int q = r16 & 3, rr = r16 >> 2;
+                r = 2 * rr + (h & 1);
+                const uint32_t krow0 = (uint32_t)(32 * kk + 8 * h + rr);
+                b_off = opaque(krow0 * (C::BN * 2) + (uint32_t)((q >> 1) * 16 + (q & 1) * 8));
+            }
+            return;
+        }
         const int h = lane >> 5;
         const int r32 = lane & 31;
         const uint32_t xk = (uint32_t)(((2 * kk + h) ^ swz_k<C::BK>(r32)) << 4);
@@ -780,6 +821,22 @@ struct FragReader {
     __device__ __forceinline__ void read(Frags<C>& f, const lds_char* a_tile, const lds_char* b_tile, int wn,
                                          int d) const
     {
+        if constexpr (C::MF == 16) {
+            constexpr int NB = (C::BT ? 1 : 2) * C::FN;   // B reads
+            if (d == 0 || d > NB) {
+                const int i = (d == 0) ? 0 : d - NB;
+                f.a[i] = *(const LDS_AS bf16x8_t*)(a_tile + a_off + i * (16 * C::BK * 2));
+            } else if constexpr (C::BT) {
+                f.b[d - 1] = *(const LDS_AS bf16x8_t*)(b_tile + b_off + (d - 1) * (16 * C::BK * 2));
+            } else {
+                const int j = (d - 1) >> 1, hh = (d - 1) & 1;
+                const int J = wn * C::FN + j;
+                const uint32_t jchunk = (uint32_t)(2 * (J ^ r)) * 16u;
+                const lds_char* addr = b_tile + b_off + (uint32_t)(4 * hh * (C::BN * 2)) + jchunk;
+                f.bh[j][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)addr);
+            }
+            return;
+        }
         if (d < C::FM) {
             f.a[d] = *(const LDS_AS bf16x8_t*)(a_tile + a_off + d * (32 * C::BK * 2));
         } else if constexpr (C::BT) {
@@ -846,26 +903,26 @@ __device__ __forceinline__ void emit_memops(RD&& rd, FR&& fr)
 // compiler keep the reads apart from the in-flight DMA writes: without it,
 // every read that follows a DMA in program order waits for all of the wave's
 // outstanding loads.
-template <int M, int D, int V, class C, class LD>
+template <int M, int D, int V, int OFF = 0, class C, class LD>
 __device__ __forceinline__ void region_memops(const FragReader<C>& rdr, Frags<C>& f, const lds_char* __restrict__ src,
                                               int wn, const LD& ld, const typename LD::Prep& prep, int t0,
                                               lds_char* __restrict__ dst, int w, int lane)
 {
-    emit_memops<M, D, V>([&](int d) { rdr.read(f, src, wn, d); },
+    emit_memops<M, D, V>([&](int d) { rdr.read(f, src, wn, d + OFF); },
                          [&](int v) { ld.fire_one(prep, t0 + v, dst, w, lane); });
 }
 
 // The same for the window ring: fragment reads from the A and B windows of
 // one position, DMA instructions t0 .. t0 + V - 1 (all of them A, or all B)
 // into a third window.
-template <int M, int D, int V, class C, class LD>
+template <int M, int D, int V, int OFF = 0, class C, class LD>
 __device__ __forceinline__ void region_memops_win(const FragReader<C>& rdr, Frags<C>& f,
                                                   const lds_char* __restrict__ a_src,
                                                   const lds_char* __restrict__ b_src, int wn, const LD& ld,
                                                   const typename LD::Prep& prep, int t0, lds_char* __restrict__ dst,
                                                   int w, int lane)
 {
-    emit_memops<M, D, V>([&](int d) { rdr.read(f, a_src, b_src, wn, d); },
+    emit_memops<M, D, V>([&](int d) { rdr.read(f, a_src, b_src, wn, d + OFF); },
                          [&](int v) { ld.fire_one(prep, t0 + v, dst, dst, w, lane); });
 }
 
@@ -918,6 +975,56 @@ __device__ __forceinline__ void mfma_step(f32x16_t (&acc)[C::FM][C::FN], const F
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b_frag<C>(f, j), f.a[i], acc[i][j], 0, 0, 0);
+}
+
+// MFMA region kk of a stage in the all-wave kernels.  32 x 32 blocks: the
+// region is 16-wide k-step kk over every block, from fragment buffer kk & 1.
+// 16 x 16 blocks: the region is half of 32-wide k-step kk / 2, block rows
+// (kk & 1) * FM/2 .. + FM/2 - 1 (MFMA x = i' * FN + j), from buffer
+// (kk / 2) & 1.
+template <class C>
+constexpr int region_mfmas() { return C::MF == 16 ? C::FM * C::FN / 2 : C::FM * C::FN; }
+
+template <class C, int KKI, int LO, int HI>
+__device__ __forceinline__ void region_mfma(typename C::Acc (&acc)[C::FM][C::FN], const Frags<C> (&fr)[2])
+{
+    if constexpr (C::MF == 16) {
+        const Frags<C>& f = fr[(KKI >> 1) & 1];
+        constexpr int I0 = (KKI & 1) * (C::FM / 2);
+#pragma unroll
+        for (int x = LO; x < HI; ++x)
+            acc[I0 + x / C::FN][x % C::FN] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                b_frag<C>(f, x % C::FN), f.a[I0 + x / C::FN], acc[I0 + x / C::FN][x % C::FN], 0, 0, 0);
+    } else {
+        mfma_range<C, LO, HI>(acc, fr[KKI & 1]);
+    }
+}
+
+// The fragment reads that region kk (not the last of its stage) issues for
+// the next k-step of the same stage: that k-step, the number of reads, the
+// first read's index and the buffer.  A 32 x 32 region reads all of k-step
+// kk + 1.  The two regions of a 16 x 16 k-step each read half of the next
+// one; the last k-step's first region reads nothing, since the next
+// stage's fragments are readable only after the synchronisation in the
+// stage's last region.
+struct RegionReads {
+    int ks, d, off, buf;
+};
+
+template <class C, int KKI>
+constexpr RegionReads region_reads()
+{
+    constexpr int D = frag_reads<C>();
+    if constexpr (C::MF == 16) {
+        static_assert(D % 2 == 0, "two halves of a k-step's reads");
+        constexpr int ks = (KKI >> 1) + 1;
+        if constexpr (ks < C::KK / 2)
+            return RegionReads{ks, D / 2, (KKI & 1) * (D / 2), ks & 1};
+        else
+            return RegionReads{0, 0, 0, 0};
+    } else {
+        return RegionReads{KKI + 1, D, 0, (KKI + 1) & 1};
+    }
 }
 
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
@@ -1047,11 +1154,73 @@ __device__ __forceinline__ void epilogue_narrow(const Params& p, f32x16_t (&acc)
     }
 }
 
+// 16 x 16 blocks: lane l of block (i, j) holds row 16i + l%16 and columns
+// 16j + 4*(l/16) + 0..3.  A pass converts two block rows (32 rows) by W/16
+// blocks (W columns, the strip's width: 64, or 32 when LDS is short) into
+// the strip, then stores it.  Writes: the 32 lanes of a write cycle cover 16
+// rows at one chunk (both 8-byte halves); the chunk is XORed with
+// (row / 2) mod 8 (128-byte rows, two per 256-byte bank window) or with
+// (row / 4) mod 4 (64-byte rows, four per window), which puts them on 32
+// different 8-byte bank slots.  Reads: W/8 lanes cover one row segment of C,
+// 16 lanes (2 or 4 rows) per cycle on 16 different 16-byte slots.
 template <class C>
-__device__ __forceinline__ void store_tile(const Params& p, f32x16_t (&acc)[C::FM][C::FN], lds_char* strip,
+__device__ __forceinline__ void epilogue16(const Params& p, f32x4_t (&acc)[C::FM][C::FN], lds_char* strip,
+                                           int32_t m0, int32_t n0, int wm, int wn, int lane_in)
+{
+    constexpr int W = C::EPI_W, RB = 2 * W, JB = W / 16;   // columns, row bytes and blocks per pass
+    constexpr int LPR = RB / 16, RPI = 64 / LPR;           // lanes per strip row, rows per read
+    static_assert(C::FN % JB == 0, "whole passes");
+    const int lane = (int)opaque((uint32_t)lane_in);
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(p.C + ((int64_t)m0 * p.ldc + n0) * 2, ((p.M - m0 - 1) * p.ldc + (p.N - n0)) * 2);
+    const int32_t mrem = (int32_t)min(p.M - m0, (int64_t)C::BM);
+    const int32_t nrem = (int32_t)min(p.N - n0, (int64_t)C::BN);
+    const uint32_t ldc2 = (uint32_t)p.ldc * 2u;
+    auto swz = [](int row) { return W == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3); };
+    const int wrow = lane & 15, wq = lane >> 4;
+    const int rrow = lane / LPR, rchunk = lane % LPR;
+#pragma unroll
+    for (int i2 = 0; i2 < C::FM / 2; ++i2) {
+#pragma unroll
+        for (int jp = 0; jp < C::FN / JB; ++jp) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+#pragma unroll
+                for (int jj = 0; jj < JB; ++jj) {
+                    const f32x4_t& a = acc[2 * i2 + ii][JB * jp + jj];
+                    u32x2_t v;
+                    v.x = pack_bf16x2(a[0], a[1]);
+                    v.y = pack_bf16x2(a[2], a[3]);
+                    const int row = 16 * ii + wrow;
+                    const int cb = 32 * jj + 8 * wq;             // byte column in the strip row
+                    const uint32_t off = opaque((uint32_t)(row * RB + (((cb >> 4) ^ swz(row)) << 4) + (cb & 15)));
+                    *(LDS_AS u32x2_t*)(strip + off) = v;
+                }
+            }
+            wait_lgkm0();
+            const int gr0 = wm * C::TM + 32 * i2 + rrow;         // tile row of read slot 0
+            const int gc = wn * C::TN + W * jp + 8 * rchunk;     // tile column of this lane's chunk
+            const uint32_t obase = opaque((uint32_t)gr0 * ldc2 + (uint32_t)gc * 2u);
+#pragma unroll
+            for (int u = 0; u < 32 / RPI; ++u) {
+                const int row = rrow + RPI * u;
+                const u32x4_t v = *(const LDS_AS u32x4_t*)(strip + row * RB + ((rchunk ^ swz(row)) << 4));
+                const bool ok = (gr0 + RPI * u < mrem) && (gc < nrem);
+                __builtin_amdgcn_raw_buffer_store_b128(v, rc, ok ? obase + (uint32_t)(RPI * u) * ldc2 : kOOB, 0, 0);
+            }
+            wait_lgkm0();
+        }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void store_tile(const Params& p, typename C::Acc (&acc)[C::FM][C::FN], lds_char* strip,
                                            int32_t m0, int32_t n0, int wm, int wn, int lane)
 {
-    if constexpr (C::EPI_W == 64)
+    if constexpr (C::MF == 16)
+        epilogue16<C>(p, acc, strip, m0, n0, wm, wn, lane);
+    else if constexpr (C::EPI_W == 64)
         epilogue<C>(p, acc, strip, m0, n0, wm, wn, lane);
     else
         epilogue_narrow<C>(p, acc, strip, m0, n0, wm, wn, lane);
@@ -1060,32 +1229,40 @@ __device__ __forceinline__ void store_tile(const Params& p, f32x16_t (&acc)[C::F
 // Split k range: the work item's fp32 accumulators go, unrounded, to its
 // partial tile (BM x BN fp32 in the workspace); k_reduce_splits adds the
 // chunks later.  The partial tile keeps the registers' order: 16-byte unit
-// (((wave * FM + i) * FN + j) * 4 + g) * 64 + lane holds registers 4g..4g+3
-// of lane `lane` in block (i, j) of MFMA wave `wave` (wm * WN + wn), so each
-// store instruction writes 1 KiB contiguously.  Those registers hold row
-// wm*TM + 32i + lane%32 and columns wn*TN + 32j + 8g + 4*(lane/32) + 0..3.
+// (((wave * FM + i) * FN + j) * NG + g) * 64 + lane holds registers
+// 4g..4g+3 of lane `lane` in block (i, j) of MFMA wave `wave` (wm * WN + wn),
+// NG = MF * MF / 256 groups per block (4 or 1), so each store instruction writes 1 KiB
+// contiguously.  Those registers hold row wm*TM + MF*i + lane%MF and four
+// consecutive columns from unit_col<C>(j, g, lane).
 template <class C>
-__device__ __forceinline__ void store_partial(const Params& p, f32x16_t (&acc)[C::FM][C::FN], int32_t widx, int wm,
-                                              int wn, int lane_in)
+__device__ __forceinline__ int unit_col(int j, int g, int lane)
 {
+    return C::MF == 16 ? 16 * j + 4 * (lane >> 4) : 32 * j + 8 * g + 4 * (lane >> 5);
+}
+
+template <class C>
+__device__ __forceinline__ void store_partial(const Params& p, typename C::Acc (&acc)[C::FM][C::FN], int32_t widx,
+                                              int wm, int wn, int lane_in)
+{
+    constexpr int NG = C::MF * C::MF / 256;
     const int lane = (int)opaque((uint32_t)lane_in);
     const __amdgpu_buffer_rsrc_t rp = rsrc_n(p.partial + (int64_t)widx * (C::BM * C::BN), C::BM * C::BN * 4u);
     const int wave = wm * C::WN + wn;
-    const uint32_t base = opaque((uint32_t)(wave * C::FM * C::FN * 4 * 1024 + lane * 16));
+    const uint32_t base = opaque((uint32_t)(wave * C::FM * C::FN * NG * 1024 + lane * 16));
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (C::FM * C::FN * 16 > 128)
+            if constexpr (C::MF == 32 && C::FM * C::FN * 16 > 128)
                 asm volatile("" : "+a"(acc[i][j]));
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x16_t& a = acc[i][j];
+            for (int g = 0; g < NG; ++g) {
+                const typename C::Acc& a = acc[i][j];
                 // Whole vectors only: a bit cast of a single vector element
                 // is not what this needs.
                 const f32x4_t v = {a[4 * g + 0], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-                const uint32_t off = base + (uint32_t)(((i * C::FN + j) * 4 + g) * 1024);
+                const uint32_t off = base + (uint32_t)(((i * C::FN + j) * NG + g) * 1024);
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rp, off, 0, 0);
             }
         }
@@ -1109,10 +1286,11 @@ __global__ void __launch_bounds__(256) k_reduce_splits(Params p)
          q += (int64_t)gridDim.x * blockDim.x) {
         const int32_t u = (int32_t)(q / UNITS);
         const int32_t unit = (int32_t)(q - (int64_t)u * UNITS);
+        constexpr int NG = C::MF * C::MF / 256;
         const int lane = unit & 63;
         int rest = unit >> 6;
-        const int g = rest & 3;
-        rest >>= 2;
+        const int g = rest % NG;
+        rest /= NG;
         const int j = rest % C::FN;
         rest /= C::FN;
         const int i = rest % C::FM;
@@ -1120,8 +1298,8 @@ __global__ void __launch_bounds__(256) k_reduce_splits(Params p)
         const int wm = wave / C::WN, wn = wave % C::WN;
         int32_t tm, tn;
         raster_tile(p, p.tile_base + u, tm, tn);
-        const int64_t r = (int64_t)tm * C::BM + wm * C::TM + 32 * i + (lane & 31);
-        const int64_t c0 = (int64_t)tn * C::BN + wn * C::TN + 32 * j + 8 * g + 4 * (lane >> 5);
+        const int64_t r = (int64_t)tm * C::BM + wm * C::TM + C::MF * i + (lane % C::MF);
+        const int64_t c0 = (int64_t)tn * C::BN + wn * C::TN + unit_col<C>(j, g, lane);
         if (r >= p.M || c0 >= p.N)
             continue;
         const f32x4_t* src = (const f32x4_t*)(p.partial + (int64_t)u * C::BM * C::BN) + unit;
@@ -1238,12 +1416,12 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
         tile_coords(p, b + it * G, G, tm, tn, sp, u);
         if constexpr (LONGK)
             ld.prefetch_next_tile(p, it + 1);
-        f32x16_t acc[C::FM][C::FN];
+        typename C::Acc acc[C::FM][C::FN];
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
             for (int j = 0; j < C::FN; ++j)
-                acc[i][j] = f32x16_t{};
+                acc[i][j] = typename C::Acc{};
 
         for (int32_t kt = 0; kt < KT; ++kt) {
             // The cursor prepares position c + S (or c + S + 1) during
@@ -1259,7 +1437,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
                 fire_prep = next_prep;
             // MFMA k-step region kk of this stage (kk is a constant).
             auto region = [&]<int kk>() {
-                constexpr int M = C::FM * C::FN, D = frag_reads<C>();
+                constexpr int M = region_mfmas<C>(), D = frag_reads<C>();
                 constexpr int SALU = (PIR && kk == 1) ? 6 : 0;
                 if constexpr (PIR && kk == 1)
                     next_prep = ld.prepare_and_advance(p);
@@ -1270,11 +1448,12 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
                     constexpr int part = kk + 1;
                     constexpr int t0 = part < NPARTS ? part_begin(part, NPARTS, C::LOADS) : 0;
                     constexpr int V = part < NPARTS ? part_begin(part + 1, NPARTS, C::LOADS) - t0 : 0;
-                    const FragReader<C> rdr(wm, wn, lane, kk + 1);
-                    region_memops<M, D, V>(rdr, fr[(kk + 1) & 1], stage, wn, ld, fire_prep, t0, stage_at(s_prev), w,
-                                           lane);
-                    mfma_step<C>(acc, fr[kk & 1]);
-                    sched_slots<M, D, V, SALU>();
+                    constexpr RegionReads rr = region_reads<C, kk>();
+                    const FragReader<C> rdr(wm, wn, lane, rr.ks);
+                    region_memops<M, rr.d, V, rr.off>(rdr, fr[rr.buf], stage, wn, ld, fire_prep, t0, stage_at(s_prev),
+                                                      w, lane);
+                    region_mfma<C, kk, 0, M>(acc, fr);
+                    sched_slots<M, rr.d, V, SALU>();
                 } else {
                     // Last MFMA k-step of this stage: the workgroup hands the
                     // stage back and makes the next position readable; then
@@ -1298,18 +1477,18 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
                     // the word reach their targets together.
                     constexpr int PRE = (C::SYNC == SYNC_FLAGS) ? (C::S == 2 ? 3 : 4) : 2;
                     if constexpr (C::SYNC == SYNC_FLAGS) {
-                        mfma_range<C, 0, 1>(acc, fr[kk & 1]);
+                        region_mfma<C, kk, 0, 1>(acc, fr);
                         __builtin_amdgcn_sched_barrier(0);
                         wait_lgkm0();
                         wait_vmcnt<C::LOADS * (C::S - 2)>();
                         arrive_pair(sig + s_nxt, kAnnounce | kRelease);
                         const uint64_t v = pair_read_issue(sig + s_nxt);
                         __builtin_amdgcn_sched_barrier(0);
-                        mfma_range<C, 1, PRE>(acc, fr[kk & 1]);
+                        region_mfma<C, kk, 1, PRE>(acc, fr);
                         __builtin_amdgcn_sched_barrier(0);
                         wait_pair_issued(v, sig + s_nxt, (g_nxt + 1) * C::NW, (gen + 1) * C::NW, failed);
                     } else {
-                        mfma_range<C, 0, PRE>(acc, fr[kk & 1]);
+                        region_mfma<C, kk, 0, PRE>(acc, fr);
                         __builtin_amdgcn_sched_barrier(0);
                         wait_lgkm0();
                         sync_next(s_nxt, g_nxt);
@@ -1318,7 +1497,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
                     const FragReader<C> rdr(wm, wn, lane, 0);
                     region_memops<M - PRE, D, V>(rdr, fr[0], stage_at(s_nxt), wn, ld, next_prep, 0, stage_at(s_cur), w,
                                                  lane);
-                    mfma_range<C, PRE, M>(acc, fr[kk & 1]);
+                    region_mfma<C, kk, PRE, M>(acc, fr);
                     sched_slots<M - PRE, D, V>();
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -1410,12 +1589,12 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_win(Params p)
         tile_coords(p, b + it * G, G, tm, tn, sp, u);
         if constexpr (LONGK)
             ld.prefetch_next_tile(p, it + 1);
-        f32x16_t acc[C::FM][C::FN];
+        typename C::Acc acc[C::FM][C::FN];
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
             for (int j = 0; j < C::FN; ++j)
-                acc[i][j] = f32x16_t{};
+                acc[i][j] = typename C::Acc{};
 
         for (int32_t kt = 0; kt < KT; ++kt) {
             // Region 0 prepares position c + 2: from this k-step on, that is
@@ -1427,24 +1606,26 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_win(Params p)
             const lds_char* a_cur = win(wa);
             const lds_char* b_cur = win(step5(wa, 1));
             auto region = [&]<int kk>() {
-                constexpr int M = C::FM * C::FN, D = frag_reads<C>();
+                constexpr int M = region_mfmas<C>(), D = frag_reads<C>();
                 if constexpr (kk < 3) {
                     constexpr int SALU = (kk == 0) ? 6 : 0;
                     if constexpr (kk == 0)
                         prep_a = ld.prepare_and_advance(p);                     // position c + 2
-                    const FragReader<C> rdr(wm, wn, lane, kk + 1);
+                    constexpr RegionReads rr = region_reads<C, kk>();
+                    const FragReader<C> rdr(wm, wn, lane, rr.ks);
                     if constexpr (kk == 0)
-                        region_memops_win<M, D, C::B_LOADS - BH>(rdr, fr[1], a_cur, b_cur, wn, ld, prep_b,
-                                                                 C::A_LOADS + BH, win(step5(wa, 3)), w, lane);
+                        region_memops_win<M, rr.d, C::B_LOADS - BH, rr.off>(rdr, fr[rr.buf], a_cur, b_cur, wn, ld,
+                                                                            prep_b, C::A_LOADS + BH,
+                                                                            win(step5(wa, 3)), w, lane);
                     else
-                        region_memops_win<M, D, (kk == 1) ? AH : C::A_LOADS - AH>(
-                            rdr, fr[(kk + 1) & 1], a_cur, b_cur, wn, ld, prep_a, (kk == 1) ? 0 : AH,
+                        region_memops_win<M, rr.d, (kk == 1) ? AH : C::A_LOADS - AH, rr.off>(
+                            rdr, fr[rr.buf], a_cur, b_cur, wn, ld, prep_a, (kk == 1) ? 0 : AH,
                             win(step5(wa, 4)), w, lane);
-                    mfma_step<C>(acc, fr[kk & 1]);
-                    sched_slots<M, D, (kk == 0) ? C::B_LOADS - BH : (kk == 1) ? AH : C::A_LOADS - AH, SALU>();
+                    region_mfma<C, kk, 0, M>(acc, fr);
+                    sched_slots<M, rr.d, (kk == 0) ? C::B_LOADS - BH : (kk == 1) ? AH : C::A_LOADS - AH, SALU>();
                 } else {
                     constexpr int PRE = 2;
-                    mfma_range<C, 0, PRE>(acc, fr[1]);
+                    region_mfma<C, kk, 0, PRE>(acc, fr);
                     __builtin_amdgcn_sched_barrier(0);
                     wait_lgkm0();
                     wait_vmcnt<C::A_LOADS>();
@@ -1452,7 +1633,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_win(Params p)
                     const FragReader<C> rdr(wm, wn, lane, 0);
                     region_memops_win<M - PRE, D, BH>(rdr, fr[0], win(step5(wa, 2)), win(step5(wa, 3)), wn, ld,
                                                       prep_a, C::A_LOADS, win(wa), w, lane);
-                    mfma_range<C, PRE, M>(acc, fr[1]);
+                    region_mfma<C, kk, PRE, M>(acc, fr);
                     sched_slots<M - PRE, D, BH>();
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -1751,15 +1932,19 @@ __global__ void __launch_bounds__(256) k_pad_copy(const uint16_t* src, int64_t s
 // use a 256 x 256 tile over 8 waves (2 x 4, each 128 x 64, two waves per SIMD
 // so that one can issue MFMAs while the other waits on a load); the
 // wave-specialised mode uses 4 MFMA waves (2 x 2 over 256 x 128) and 4 loader
-// waves.  The k-step width follows the LDS budget (see BK below).
+// waves.  The k-step width follows the LDS budget (see BK below).  The
+// all-wave kernels with 64-wide stages use 16 x 16 MFMA blocks; the others
+// keep 32 x 32 blocks (a 32-wide stage holds a single 16 x 16 k-step, and the
+// loader/MFMA kernels' schedules are built around 32 x 32 blocks).
 template <int SYNC, int S>
 struct Pick {
     // 64-wide k-steps (128-byte rows per DMA instruction) wherever the ring
     // fits: two stages of 256 x 256, three of the wave-specialised 256 x 128.
     static constexpr int BK = (S == 2 || (SYNC == SYNC_WAVESPEC && S == 3)) ? 64 : 32;
+    static constexpr int MF = (BK == 64 && SYNC != SYNC_WAVESPEC) ? 16 : 32;
     template <bool BT>
     using type = Cfg<256, (SYNC == SYNC_WAVESPEC) ? 128 : 256, BK, S, 2, (SYNC == SYNC_WAVESPEC) ? 2 : 4, SYNC, BT,
-                     (SYNC == SYNC_WAVESPEC) ? 4 : 0>;
+                     (SYNC == SYNC_WAVESPEC) ? 4 : 0, false, MF>;
 };
 
 // Ping-pong: each of the two MFMA groups needs a wave on every SIMD, so
@@ -1777,7 +1962,7 @@ struct Pick<SYNC_PINGPONG, S> {
 template <>
 struct Pick<SYNC_BARRIER, GEMM_STAGES_WINDOWS> {
     template <bool BT>
-    using type = Cfg<256, 256, 64, 2, 2, 4, SYNC_BARRIER, BT, 0, true>;
+    using type = Cfg<256, 256, 64, 2, 2, 4, SYNC_BARRIER, BT, 0, true, 16>;
 };
 
 template <class C>
@@ -1812,13 +1997,13 @@ int launch(const Params& p, int64_t grid, hipStream_t stream)
 }
 
 struct Shape {
-    int bm, bn, bk, mfma_waves, producer_waves, threads, lds_bytes;
+    int bm, bn, bk, mfma_waves, producer_waves, threads, lds_bytes, mfma_block;
 };
 
 template <class C>
 Shape shape_of()
 {
-    return Shape{C::BM, C::BN, C::BK, C::NCW, C::NP, C::THREADS, C::LDS_BYTES};
+    return Shape{C::BM, C::BN, C::BK, C::NCW, C::NP, C::THREADS, C::LDS_BYTES, C::MF};
 }
 
 // Calls f.template operator()<Cfg>() for the instance of (sync, stages, bt).
@@ -2035,6 +2220,7 @@ int fill_plan(int64_t M, int64_t N_in, int64_t K_in, int b_transposed, int stage
     pl.producer_waves = v.producer_waves;
     pl.threads = v.threads;
     pl.lds_bytes = v.lds_bytes;
+    pl.mfma_block = v.mfma_block;
     const int64_t tm = (M + v.bm - 1) / v.bm, tn = (N + v.bn - 1) / v.bn;
     pl.tiles = tm * tn;
     pl.k_splits = choose_splits(M, N, K, cus);

@@ -2,12 +2,14 @@
 
 Bar (the method's stated acceptance): |gpu - ref| <= 1e-2 * max(1, |ref|) for
 every element, computed in fp64 from the bf16 results.  Where fp32
-accumulation is exact (small-integer inputs) the bar is bit equality.  All
-sync modes, stage counts and both B layouts run the same MFMA chain per
-output element (k in increasing order), so their outputs must also be
-bit-identical to each other and from run to run -- except on the tiles of a
-split tail, which depends on the mode's tile: there modes whose plans split
-alike must agree bit for bit.
+accumulation is exact (small-integer inputs) the bar is bit equality.  Sync
+modes, stage counts and B layouts with the same MFMA block (plan field
+mfma_block: 16 x 16 x 32 or 32 x 32 x 16) run the same MFMA chain per output
+element (k in increasing order, 32 or 16 products per MFMA), so their outputs
+must also be bit-identical to each other and from run to run -- except on
+the tiles of a split tail, which depends on the mode's tile: there modes
+whose plans split alike must agree bit for bit.  Across block shapes the
+products are grouped differently, and results agree to within rounding.
 
 Small cases span several 256 x 256 tiles and ragged tails and are compared in
 full.  The five benchmark workloads run at their full sizes in the launch
@@ -47,6 +49,22 @@ def run(A, B, bt, sync, stages, out=None):
     C = bd.gemm(A, B, b_transposed=bt, sync=sync, stages=stages, out=out)
     torch.cuda.synchronize()
     return bits(C.cpu()).copy()
+
+
+def block_of(M, N, K, bt, sync, stages):
+    return bd.gemm_bf16_plan(M, N, K, bt, stages, bd.SYNC_MODES[sync])["mfma_block"]
+
+
+def assert_same_bits_per_block(outs, what="modes disagree bitwise"):
+    """outs: (mfma block, result) pairs; results of one block shape agree bit for bit."""
+    first = {}
+    for blk, got in outs:
+        if blk in first:
+            np.testing.assert_array_equal(got, first[blk], err_msg="%s (%dx%d blocks)" % (what, blk, blk))
+        else:
+            first[blk] = got
+    assert set(first) == {16, 32}, sorted(first)
+    return first
 
 
 def decode(b):
@@ -105,14 +123,12 @@ def small_refs():
 def test_small_parity_all_modes(case, bt, small_refs):
     A, B, ref = small_refs(case, bt)
     dA, dB = A.cuda(), B.cuda()
-    first = None
+    outs = []
     for sync, stages in MODES:
         got = run(dA, dB, bt, sync, stages)
         assert_within_tol(got, ref, "%s/%d" % (sync, stages))
-        if first is None:
-            first = got
-        else:
-            np.testing.assert_array_equal(got, first, err_msg="modes disagree bitwise")
+        outs.append((block_of(A.shape[0], B.shape[0] if bt else B.shape[1], A.shape[1], bt, sync, stages), got))
+    assert_same_bits_per_block(outs)
 
 
 @pytest.mark.parametrize("bt", [False, True], ids=["kn", "nk"])
@@ -132,14 +148,12 @@ def test_many_tiles_per_workgroup(K, bt):
     A, B = make_operands(M, N, K, b_transposed=bt, seed=K + (1000 if bt else 0))
     ref = oracle.load().gemm_bf16(bits(A), bits(B), bt)
     dA, dB = A.cuda(), B.cuda()
-    first = None
+    outs = []
     for sync, stages in MODES:
         got = run(dA, dB, bt, sync, stages)
         assert_within_tol(got, ref, "%s/%d" % (sync, stages))
-        if first is None:
-            first = got
-        else:
-            np.testing.assert_array_equal(got, first, err_msg="modes disagree bitwise")
+        outs.append((block_of(M, N, K, bt, sync, stages), got))
+    assert_same_bits_per_block(outs)
 
 
 @pytest.mark.parametrize("bt", [False, True], ids=["kn", "nk"])
@@ -147,8 +161,9 @@ def test_split_k(bt):
     """Few output tiles and a long k range: the k range is cut into chunks whose
     fp32 partial tiles are summed in chunk order.  1000 x 1032 has 20 tiles of
     256 x 256, so K = 8192 splits into 8 chunks of 1024 (ragged M and N).  The
-    chunking depends on the shape only, so every mode gives the same bits, run
-    after run and on any stream; a K with no valid chunking stays unsplit."""
+    chunking depends on the shape only, so every mode with the same MFMA block
+    gives the same bits, run after run and on any stream; a K with no valid
+    chunking stays unsplit."""
     M, N, K = 1000, 1032, 8192
     for sync, stages in MODES:
         plan = bd.gemm_bf16_plan(M, N, K, bt, stages, bd.SYNC_MODES[sync])
@@ -158,19 +173,17 @@ def test_split_k(bt):
     A, B = make_operands(M, N, K, b_transposed=bt, seed=4242 + bt)
     ref = oracle.load().gemm_bf16(bits(A), bits(B), bt)
     dA, dB = A.cuda(), B.cuda()
-    first = None
+    outs = []
     for sync, stages in MODES:
         got = run(dA, dB, bt, sync, stages)
         assert_within_tol(got, ref, "split %s/%d" % (sync, stages))
-        if first is None:
-            first = got
-        else:
-            np.testing.assert_array_equal(got, first, err_msg="modes disagree bitwise")
+        outs.append((block_of(M, N, K, bt, sync, stages), got))
+    first = assert_same_bits_per_block(outs)
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         C = bd.gemm(dA, dB, b_transposed=bt)
     side.synchronize()
-    np.testing.assert_array_equal(bits(C.cpu()), first)
+    np.testing.assert_array_equal(bits(C.cpu()), first[block_of(M, N, K, bt, "barrier", 0)])
 
 
 def test_plans():
@@ -247,7 +260,7 @@ def test_split_tail_plans():
 
 def split_signature(M, N, K, bt, sync, stages):
     pl = bd.gemm_bf16_plan(M, N, K, bt, stages, bd.SYNC_MODES[sync])
-    return (pl["bm"], pl["bn"], pl["k_splits"], pl["tail_tiles"], pl["tail_splits"])
+    return (pl["bm"], pl["bn"], pl["k_splits"], pl["tail_tiles"], pl["tail_splits"], pl["mfma_block"])
 
 
 @pytest.mark.parametrize("bt", [False, True], ids=["kn", "nk"])
@@ -397,14 +410,17 @@ def test_layouts_and_modes_bit_identical():
     M, N, K = 520, 776, 392
     A, B = make_operands(M, N, K, b_transposed=False, seed=99)
     dA, dB, dBt = A.cuda(), B.cuda(), B.t().contiguous().cuda()
+    ref = oracle.load().gemm_bf16(bits(A), bits(B), False)
     outs = []
     for sync, stages in MODES:
-        outs.append(run(dA, dB, False, sync, stages))
-        outs.append(run(dA, dBt, True, sync, stages))
-    for o in outs[1:]:
-        np.testing.assert_array_equal(o, outs[0])
-    again = run(dA, dB, False, "flags", 3)
-    np.testing.assert_array_equal(again, outs[0])
+        for bt, b in ((False, dB), (True, dBt)):
+            got = run(dA, b, bt, sync, stages)
+            assert_within_tol(got, ref, "%s/%d bt=%s" % (sync, stages, bt))
+            outs.append((block_of(M, N, K, bt, sync, stages), got))
+    first = assert_same_bits_per_block(outs, "layouts or modes disagree bitwise")
+    for sync, stages in (("flags", 3), ("flags", 2)):
+        again = run(dA, dB, False, sync, stages)
+        np.testing.assert_array_equal(again, first[block_of(M, N, K, False, sync, stages)])
 
 
 @pytest.mark.parametrize("bt", [False, True], ids=["kn", "nk"])

@@ -28,6 +28,11 @@ SHAPES = {("barrier", 2): (256, 256, 64, 8, 0), ("barrier", 3): (256, 256, 32, 8
           ("pingpong", 4): (128, 128, 64, 8, 4)}
 
 
+# MFMA block edge: 16 x 16 x 32 MFMAs for the all-wave kernels with 64-wide
+# stages, 32 x 32 x 16 for the rest.
+MFMA_BLOCK = {mode: (16 if mode[0] in ("barrier", "flags") and SHAPES[mode][2] == 64 else 32) for mode in SHAPES}
+
+
 def plan(M, N, K, bt, sync, stages, cus=CUS):
     return bd.gemm_bf16_plan_cus(M, N, K, bt, stages, bd.SYNC_MODES[sync], cus)
 
@@ -68,6 +73,7 @@ def test_tile_configuration(sync, stages, bt):
     assert (pl["bm"], pl["bn"], pl["bk"], pl["mfma_waves"], pl["producer_waves"]) == (bm, bn, bk, mw, pw)
     assert pl["stages"] == stages and pl["sync_mode"] == bd.SYNC_MODES[sync] and pl["b_transposed"] == bt
     assert pl["threads"] == 64 * (mw + pw)
+    assert pl["mfma_block"] == MFMA_BLOCK[(sync, stages)]
     assert 0 < pl["lds_bytes"] <= 160 * 1024
     assert pl["tiles"] == (8192 // bm) * (8192 // bn)
     assert pl["k_steps"] == 8192 // bk
