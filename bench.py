@@ -61,9 +61,9 @@ def parse():
                                                             "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into the traffic "
                          "summary read by the roofline line (no GPU needed)")
-    ap.add_argument("--traffic-kernel", default="Cfg<256, 256, 64, 2, 2, 4, 0, true, 0, false>",
+    ap.add_argument("--traffic-kernel", default="Cfg<256, 256, 64, 2, 2, 4, 0, true, 0, false, 16>",
                     help="kernel configuration the counter CSVs were taken for (a substring of "
-                         "the kernel name: Cfg<BM, BN, BK, S, WM, WN, SYNC, B_NxK, loader waves, windows>)")
+                         "the kernel name: Cfg<BM, BN, BK, S, WM, WN, SYNC, B_NxK, loader waves, windows, MFMA block>)")
     ap.add_argument("--no-reference", action="store_true", help="skip the torch.matmul timing")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the per-workload summary of the other configurations")
@@ -105,7 +105,7 @@ STAGE_SWEEPS = {"gemm4096_kn": (("flags", 2), ("flags", 3), ("flags", 4),
 
 def cfg_fields(kname):
     """(sync mode, stages) of a Cfg<BM, BN, BK, S, WM, WN, SYNC, B_NxK, NP,
-    windows> string; the split-window ring reports its stages value, 5."""
+    windows, MFMA block> string; the split-window ring reports its stages value, 5."""
     f = [x.strip() for x in kname[kname.index("<") + 1:].rstrip(">").split(",")]
     if len(f) > 9 and f[9] == "true":
         return SYNC_NAMES[int(f[6])], 5

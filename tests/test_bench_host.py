@@ -12,11 +12,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def test_cfg_fields():
-    assert bench.cfg_fields("Cfg<256, 256, 64, 2, 2, 4, 0, true, 0, false>") == ("barrier", 2)
-    assert bench.cfg_fields("Cfg<256, 256, 32, 4, 2, 4, 1, false, 0, false>") == ("flags", 4)
-    assert bench.cfg_fields("Cfg<256, 128, 64, 3, 2, 2, 2, true, 4, false>") == ("wavespec", 3)
+    assert bench.cfg_fields("Cfg<256, 256, 64, 2, 2, 4, 0, true, 0, false, 16>") == ("barrier", 2)
+    assert bench.cfg_fields("Cfg<256, 256, 32, 4, 2, 4, 1, false, 0, false, 32>") == ("flags", 4)
+    assert bench.cfg_fields("Cfg<256, 128, 64, 3, 2, 2, 2, true, 4, false, 32>") == ("wavespec", 3)
     # the split-window ring reports the stages value that selects it
-    assert bench.cfg_fields("Cfg<256, 256, 64, 2, 2, 4, 0, true, 0, true>") == ("barrier", 5)
+    assert bench.cfg_fields("Cfg<256, 256, 64, 2, 2, 4, 0, true, 0, true, 16>") == ("barrier", 5)
 
 
 def test_mode_runs_cover_every_sync_mode():
