@@ -229,8 +229,8 @@ struct Cfg {
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(KK % 2 == 0, "fragment double buffering assumes an even number of MFMA k-steps");
     static_assert(FM >= 1 && FN >= 2 && FN % 2 == 0, "wave tile");
-    static_assert(MF == 32 || (MF == 16 && BK == 64 && FM % 2 == 0 && !PRODUCERS),
-                  "16 x 16 blocks: all-wave kernels, 64-wide stages (two 32-wide k-steps)");
+    static_assert(MF == 32 || (MF == 16 && BK == 64 && FM % 2 == 0 && SYNC != SYNC_PINGPONG),
+                  "16 x 16 blocks: 64-wide stages (two 32-wide k-steps), not ping-pong");
     static_assert(A_BYTES % (1024 * NLW) == 0 && B_BYTES % (1024 * NLW) == 0, "DMA split");
     static_assert(64 % CPR_K == 0, "a DMA window covers whole K-contiguous rows");
     static_assert(CPR_N == 16 || CPR_N == 32, "a DMA window covers whole K x N rows of B");
@@ -1699,24 +1699,28 @@ __device__ __forceinline__ void producer_loop(const Params& p, lds_char* smem, l
 // announced, the next position's first fragments are read beside the
 // remaining MFMAs.  Without a next position (has_next false) only the MFMAs
 // run.
+//
+// With 16 x 16 blocks the last region is the second half of the last 32-wide
+// k-step; half of its MFMAs go before the wait, so that the other half can
+// cover the next position's fragment reads.
 template <class C>
-__device__ __forceinline__ void consumer_last_kstep(f32x16_t (&acc)[C::FM][C::FN], Frags<C> (&fr)[2],
+__device__ __forceinline__ void consumer_last_kstep(typename C::Acc (&acc)[C::FM][C::FN], Frags<C> (&fr)[2],
                                                     lds_u32* empty_cur, const lds_u32* full_next,
                                                     uint32_t next_target, bool has_next, const lds_char* next_stage,
                                                     int wm, int wn, int lane, bool& failed)
 {
-    constexpr int M = C::FM * C::FN, PRE = (M > 4) ? M - 3 : M / 2;
-    constexpr int LAST = (C::KK - 1) & 1;
+    constexpr int M = region_mfmas<C>();
+    constexpr int PRE = (C::MF == 16) ? M / 2 : (M > 4) ? M - 3 : M / 2;
     wait_lgkm0();
     arrive(empty_cur);
     const uint32_t v = counter_read_issue(full_next);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_range<C, 0, PRE>(acc, fr[LAST]);
+    region_mfma<C, C::KK - 1, 0, PRE>(acc, fr);
     __builtin_amdgcn_sched_barrier(0);
     wait_counter_issued(v, full_next, has_next ? next_target : 0u, failed);
     if (has_next)
         read_frags<C>(fr[0], next_stage, wm, wn, lane, 0);
-    mfma_range<C, PRE, M>(acc, fr[LAST]);
+    region_mfma<C, C::KK - 1, PRE, M>(acc, fr);
     sched_slots<M - PRE, frag_reads<C>(), 0>();
 }
 
@@ -1762,20 +1766,27 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
         int32_t tm, tn;
         int32_t sp, u;
         tile_coords(p, b + it * G, G, tm, tn, sp, u);
-        f32x16_t acc[C::FM][C::FN];
+        typename C::Acc acc[C::FM][C::FN];
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
             for (int j = 0; j < C::FN; ++j)
-                acc[i][j] = f32x16_t{};
+                acc[i][j] = typename C::Acc{};
         for (int32_t kt = 0; kt < KT; ++kt, ++c) {
             const lds_char* stage = smem + (c % C::S) * C::STAGE_BYTES;
+            // MFMA region kk of the stage: the next k-step's fragment reads
+            // (region_reads) beside this region's MFMAs; the last region
+            // hands the stage back.
+            auto region = [&]<int kk>() {
+                constexpr int M = region_mfmas<C>();
+                if constexpr (kk + 1 < C::KK) {
+                    constexpr RegionReads rr = region_reads<C, kk>();
+                    const FragReader<C> rdr(wm, wn, lane, rr.ks);
 #pragma unroll
-            for (int kk = 0; kk < C::KK; ++kk) {
-                if (kk + 1 < C::KK) {
-                    read_frags<C>(fr[(kk + 1) & 1], stage, wm, wn, lane, kk + 1);
-                    mfma_step<C>(acc, fr[kk & 1]);
-                    sched_slots<C::FM * C::FN, frag_reads<C>(), 0>();
+                    for (int d = 0; d < rr.d; ++d)
+                        rdr.read(fr[rr.buf], stage, wn, d + rr.off);
+                    region_mfma<C, kk, 0, M>(acc, fr);
+                    sched_slots<M, rr.d, 0>();
                 } else {
                     const int s1 = (c + 1) % C::S;
                     consumer_last_kstep<C>(acc, fr, empty + c % C::S, full + s1,
@@ -1783,7 +1794,10 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
                                            smem + s1 * C::STAGE_BYTES, wm, wn, lane, failed);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-            }
+            };
+            [&]<int... KS>(std::integer_sequence<int, KS...>) {
+                (region.template operator()<KS>(), ...);
+            }(std::make_integer_sequence<int, C::KK>{});
         }
         if (p.splits > 1)
             store_partial<C>(p, acc, sp * p.span + u, wm, wn, lane);
@@ -1932,16 +1946,17 @@ __global__ void __launch_bounds__(256) k_pad_copy(const uint16_t* src, int64_t s
 // use a 256 x 256 tile over 8 waves (2 x 4, each 128 x 64, two waves per SIMD
 // so that one can issue MFMAs while the other waits on a load); the
 // wave-specialised mode uses 4 MFMA waves (2 x 2 over 256 x 128) and 4 loader
-// waves.  The k-step width follows the LDS budget (see BK below).  The
-// all-wave kernels with 64-wide stages use 16 x 16 MFMA blocks; the others
-// keep 32 x 32 blocks (a 32-wide stage holds a single 16 x 16 k-step, and the
-// loader/MFMA kernels' schedules are built around 32 x 32 blocks).
+// waves.  The k-step width follows the LDS budget (see BK below).  Configs
+// with 64-wide stages use 16 x 16 MFMA blocks; those with 32-wide stages keep
+// 32 x 32 blocks (such a stage holds a single 16 x 16 k-step, which the
+// fragment double buffering within a stage does not cover), and so does
+// ping-pong (a timing-only estimate showed no clear gain there).
 template <int SYNC, int S>
 struct Pick {
     // 64-wide k-steps (128-byte rows per DMA instruction) wherever the ring
     // fits: two stages of 256 x 256, three of the wave-specialised 256 x 128.
     static constexpr int BK = (S == 2 || (SYNC == SYNC_WAVESPEC && S == 3)) ? 64 : 32;
-    static constexpr int MF = (BK == 64 && SYNC != SYNC_WAVESPEC) ? 16 : 32;
+    static constexpr int MF = (BK == 64) ? 16 : 32;
     template <bool BT>
     using type = Cfg<256, (SYNC == SYNC_WAVESPEC) ? 128 : 256, BK, S, 2, (SYNC == SYNC_WAVESPEC) ? 2 : 4, SYNC, BT,
                      (SYNC == SYNC_WAVESPEC) ? 4 : 0, false, MF>;
