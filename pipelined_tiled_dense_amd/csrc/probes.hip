@@ -6,7 +6,8 @@
 // to the host, where a test compares it with the layout the kernels assume:
 //   - global_load_lds_dwordx4: which LDS bytes each lane's 16-byte load lands
 //     in, and that s_waitcnt vmcnt(0) covers the LDS write;
-//   - v_mfma_f32_32x32x16_bf16: the operand and accumulator lane layouts;
+//   - v_mfma_f32_32x32x16_bf16 and v_mfma_f32_16x16x32_bf16: the operand and
+//     accumulator lane layouts;
 //   - ds_read_b64_tr_b16: which lane receives which 16-bit element;
 //   - the fp32 -> bf16 conversion used by the epilogue (rounding mode);
 //   - buffer range checking, with and without a scalar offset.
@@ -19,6 +20,7 @@
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 
 namespace {
@@ -129,6 +131,22 @@ __global__ void __launch_bounds__(64) k_mfma(const uint16_t* __restrict__ a,
         d[16 * l + r] = acc[r];
 }
 
+// The same for v_mfma_f32_16x16x32_bf16: lane l supplies a[8l..8l+7] and
+// b[8l..8l+7] and writes its 4 accumulator values to d[4l..4l+3].
+__global__ void __launch_bounds__(64) k_mfma16(const uint16_t* __restrict__ a,
+                                               const uint16_t* __restrict__ b,
+                                               float* __restrict__ d)
+{
+    const int l = threadIdx.x;
+    bf16x8_t va, vb;
+    __builtin_memcpy(&va, a + 8 * l, 16);
+    __builtin_memcpy(&vb, b + 8 * l, 16);
+    f32x4_t acc = {};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, vb, acc, 0, 0, 0);
+    for (int r = 0; r < 4; ++r)
+        d[4 * l + r] = acc[r];
+}
+
 // LDS is filled with image[0..4095] (16-bit words); lane l then performs one
 // ds_read_b64_tr_b16 at byte address addr[l] and writes its four 16-bit
 // results to out[4l..4l+3].
@@ -211,6 +229,15 @@ int gemm_probe_mfma(const uint16_t* a, const uint16_t* b, float* d, void* stream
     if (!a || !b || !d)
         return -1;
     hipLaunchKernelGGL(k_mfma, dim3(1), dim3(64), 0, (hipStream_t)stream, a, b, d);
+    return launch_status();
+}
+
+// a, b: 512 bf16 each; d: 256 floats.
+int gemm_probe_mfma16(const uint16_t* a, const uint16_t* b, float* d, void* stream)
+{
+    if (!a || !b || !d)
+        return -1;
+    hipLaunchKernelGGL(k_mfma16, dim3(1), dim3(64), 0, (hipStream_t)stream, a, b, d);
     return launch_status();
 }
 

@@ -26,11 +26,12 @@ def probes():
     p = ctypes.c_void_p
     lib.gemm_probe_lds_dma.argtypes = [p, p, ctypes.c_int, p, p]
     lib.gemm_probe_mfma.argtypes = [p, p, p, p]
+    lib.gemm_probe_mfma16.argtypes = [p, p, p, p]
     lib.gemm_probe_ds_read_tr.argtypes = [p, p, p, p]
     lib.gemm_probe_cvt_bf16.argtypes = [p, p, ctypes.c_int64, p]
     lib.gemm_probe_buffer_oob.argtypes = [p, ctypes.c_int, p, p, p, ctypes.c_int, p]
     lib.gemm_probe_buffer_soffset.argtypes = [p, ctypes.c_int, p, ctypes.c_uint32, p, p]
-    for f in (lib.gemm_probe_lds_dma, lib.gemm_probe_mfma, lib.gemm_probe_ds_read_tr,
+    for f in (lib.gemm_probe_lds_dma, lib.gemm_probe_mfma, lib.gemm_probe_mfma16, lib.gemm_probe_ds_read_tr,
               lib.gemm_probe_cvt_bf16, lib.gemm_probe_buffer_oob, lib.gemm_probe_buffer_soffset):
         f.restype = ctypes.c_int
     return lib
@@ -133,6 +134,33 @@ def test_mfma_32x32x16_bf16_layout(probes):
     for l in range(64):
         for r in range(16):
             want[l, r] = D[8 * (r // 4) + 4 * (l // 32) + r % 4, l % 32]
+    np.testing.assert_array_equal(got, want)
+
+
+def test_mfma_16x16x32_bf16_layout(probes):
+    """v_mfma_f32_16x16x32_bf16 operand and result layouts:
+    A lane l holds A[l%16][8*(l//16) + i], B lane l holds B[8*(l//16) + i][l%16]
+    (i = 0..7), and accumulator register r of lane l is D[4*(l//16) + r][l%16]."""
+    print("probe mfma16", flush=True)
+    rng = np.random.default_rng(2)
+    A = rng.integers(-4, 5, size=(16, 32)).astype(np.float32)
+    B = rng.integers(-4, 5, size=(32, 16)).astype(np.float32)
+    D = A.astype(np.float64) @ B.astype(np.float64)
+    a = np.zeros((64, 8), np.float32)
+    b = np.zeros((64, 8), np.float32)
+    for l in range(64):
+        a[l] = A[l % 16, 8 * (l // 16):8 * (l // 16) + 8]
+        b[l] = B[8 * (l // 16):8 * (l // 16) + 8, l % 16]
+    da = torch.from_numpy(a.reshape(-1)).to(torch.bfloat16).cuda()
+    db = torch.from_numpy(b.reshape(-1)).to(torch.bfloat16).cuda()
+    dd = torch.zeros(64 * 4, dtype=torch.float32, device="cuda")
+    assert probes.gemm_probe_mfma16(da.data_ptr(), db.data_ptr(), dd.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    got = dd.cpu().numpy().reshape(64, 4)
+    want = np.zeros((64, 4))
+    for l in range(64):
+        for r in range(4):
+            want[l, r] = D[4 * (l // 16) + r, l % 16]
     np.testing.assert_array_equal(got, want)
 
 
