@@ -229,8 +229,8 @@ struct Cfg {
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(KK % 2 == 0, "fragment double buffering assumes an even number of MFMA k-steps");
     static_assert(FM >= 1 && FN >= 2 && FN % 2 == 0, "wave tile");
-    static_assert(MF == 32 || (MF == 16 && BK == 64 && FM % 2 == 0 && SYNC != SYNC_PINGPONG),
-                  "16 x 16 blocks: 64-wide stages (two 32-wide k-steps), not ping-pong");
+    static_assert(MF == 32 || (MF == 16 && BK == 64 && FM % 2 == 0),
+                  "16 x 16 blocks: 64-wide stages (two 32-wide k-steps)");
     static_assert(A_BYTES % (1024 * NLW) == 0 && B_BYTES % (1024 * NLW) == 0, "DMA split");
     static_assert(64 % CPR_K == 0, "a DMA window covers whole K-contiguous rows");
     static_assert(CPR_N == 16 || CPR_N == 32, "a DMA window covers whole K x N rows of B");
@@ -1857,20 +1857,24 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_pp(Params p)
         int32_t c = it * KT;
         wait_counter_long(full + c % C::S, (uint32_t)(c / C::S + 1) * C::NP, failed);
         read_frags<C>(fr[0], stage_of(c), wm, wn, lane, 0);
-        f32x16_t acc[C::FM][C::FN];
+        typename C::Acc acc[C::FM][C::FN];
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
             for (int j = 0; j < C::FN; ++j)
-                acc[i][j] = f32x16_t{};
+                acc[i][j] = typename C::Acc{};
         for (int32_t kt = 0; kt < KT; ++kt, ++c) {
             const lds_char* stage = stage_of(c);
+            auto region = [&]<int kk>() {
+                constexpr int M = region_mfmas<C>();
+                if constexpr (kk + 1 < C::KK) {
+                    constexpr RegionReads rr = region_reads<C, kk>();
+                    const FragReader<C> rdr(wm, wn, lane, rr.ks);
 #pragma unroll
-            for (int kk = 0; kk < C::KK; ++kk) {
-                if (kk + 1 < C::KK) {
-                    read_frags<C>(fr[(kk + 1) & 1], stage, wm, wn, lane, kk + 1);
-                    mfma_step<C>(acc, fr[kk & 1]);
-                    sched_slots<C::FM * C::FN, frag_reads<C>(), 0>();
+                    for (int d = 0; d < rr.d; ++d)
+                        rdr.read(fr[rr.buf], stage, wn, d + rr.off);
+                    region_mfma<C, kk, 0, M>(acc, fr);
+                    sched_slots<M, rr.d, 0>();
                 } else {
                     // The group's next position within this tile; the next
                     // tile's first position is waited for after the epilogue.
@@ -1879,7 +1883,10 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_pp(Params p)
                                            wm, wn, lane, failed);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-            }
+            };
+            [&]<int... KS>(std::integer_sequence<int, KS...>) {
+                (region.template operator()<KS>(), ...);
+            }(std::make_integer_sequence<int, C::KK>{});
         }
         if (p.splits > 1)
             store_partial<C>(p, acc, sp * p.span + u, wm, wn, lane);
@@ -1949,8 +1956,7 @@ __global__ void __launch_bounds__(256) k_pad_copy(const uint16_t* src, int64_t s
 // waves.  The k-step width follows the LDS budget (see BK below).  Configs
 // with 64-wide stages use 16 x 16 MFMA blocks; those with 32-wide stages keep
 // 32 x 32 blocks (such a stage holds a single 16 x 16 k-step, which the
-// fragment double buffering within a stage does not cover), and so does
-// ping-pong (a timing-only estimate showed no clear gain there).
+// fragment double buffering within a stage does not cover).
 template <int SYNC, int S>
 struct Pick {
     // 64-wide k-steps (128-byte rows per DMA instruction) wherever the ring
@@ -1969,7 +1975,7 @@ struct Pick {
 template <int S>
 struct Pick<SYNC_PINGPONG, S> {
     template <bool BT>
-    using type = Cfg<128, 128, 64, S, 2, 2, SYNC_PINGPONG, BT, 4>;
+    using type = Cfg<128, 128, 64, S, 2, 2, SYNC_PINGPONG, BT, 4, false, 16>;
 };
 
 // The split-window ring: the two-stage barrier instance's tile, waves and
