@@ -229,8 +229,8 @@ struct Cfg {
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(KK % 2 == 0, "fragment double buffering assumes an even number of MFMA k-steps");
     static_assert(FM >= 1 && FN >= 2 && FN % 2 == 0, "wave tile");
-    static_assert(MF == 32 || (MF == 16 && BK == 64 && FM % 2 == 0),
-                  "16 x 16 blocks: 64-wide stages (two 32-wide k-steps)");
+    static_assert(MF == 32 || (MF == 16 && FM % 2 == 0 && (BK == 64 || !PRODUCERS)),
+                  "16 x 16 blocks: 64-wide stages, or 32-wide stages in the all-wave kernels");
     static_assert(A_BYTES % (1024 * NLW) == 0 && B_BYTES % (1024 * NLW) == 0, "DMA split");
     static_assert(64 % CPR_K == 0, "a DMA window covers whole K-contiguous rows");
     static_assert(CPR_N == 16 || CPR_N == 32, "a DMA window covers whole K x N rows of B");
@@ -1011,11 +1011,50 @@ struct RegionReads {
     int ks, d, off, buf;
 };
 
+// Reads the last region of a stage issues for the next stage's first k-step,
+// after the synchronisation.  Normally all of them, into buffer 0.  With one
+// 16 x 16 k-step per stage (32-wide stages) buffer 0 is still in use by the
+// last region's MFMAs: the reads for the first half (A blocks 0 .. FM/2 - 1
+// and the B blocks) go to buffer 1 and are copied into buffer 0 at the end of
+// the stage (take_next_stage); the compiler needs real moves only for the B
+// blocks, whose registers the last region still reads.
+template <class C>
+constexpr int next_stage_reads()
+{
+    constexpr int NB = (C::BT ? 1 : 2) * C::FN;
+    return (C::MF == 16 && C::KK == 2) ? NB + C::FM / 2 : frag_reads<C>();
+}
+
+template <class C>
+__device__ __forceinline__ void take_next_stage(Frags<C> (&fr)[2])
+{
+    if constexpr (C::MF == 16 && C::KK == 2) {
+#pragma unroll
+        for (int i = 0; i < C::FM / 2; ++i)
+            fr[0].a[i] = fr[1].a[i];
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            if constexpr (C::BT) {
+                fr[0].b[j] = fr[1].b[j];
+            } else {
+                fr[0].bh[j][0] = fr[1].bh[j][0];
+                fr[0].bh[j][1] = fr[1].bh[j][1];
+            }
+        }
+    }
+}
+
 template <class C, int KKI>
 constexpr RegionReads region_reads()
 {
     constexpr int D = frag_reads<C>();
-    if constexpr (C::MF == 16) {
+    if constexpr (C::MF == 16 && C::KK == 2) {
+        // A 32-wide stage is one 16 x 16 k-step: its first region reads the
+        // A blocks of the second half (the last region of the previous stage
+        // read the rest, see next_stage_reads).
+        constexpr int NB = (C::BT ? 1 : 2) * C::FN;
+        return RegionReads{0, C::FM / 2, NB + C::FM / 2, 0};
+    } else if constexpr (C::MF == 16) {
         static_assert(D % 2 == 0, "two halves of a k-step's reads");
         constexpr int ks = (KKI >> 1) + 1;
         if constexpr (ks < C::KK / 2)
@@ -1494,11 +1533,14 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
                         sync_next(s_nxt, g_nxt);
                     }
                     constexpr int V = part_begin(1, NPARTS, C::LOADS);
+                    constexpr int DN = next_stage_reads<C>();
+                    constexpr int NBUF = (C::MF == 16 && C::KK == 2) ? 1 : 0;
                     const FragReader<C> rdr(wm, wn, lane, 0);
-                    region_memops<M - PRE, D, V>(rdr, fr[0], stage_at(s_nxt), wn, ld, next_prep, 0, stage_at(s_cur), w,
-                                                 lane);
+                    region_memops<M - PRE, DN, V>(rdr, fr[NBUF], stage_at(s_nxt), wn, ld, next_prep, 0,
+                                                  stage_at(s_cur), w, lane);
                     region_mfma<C, kk, PRE, M>(acc, fr);
-                    sched_slots<M - PRE, D, V>();
+                    sched_slots<M - PRE, DN, V>();
+                    take_next_stage<C>(fr);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             };
@@ -1953,16 +1995,17 @@ __global__ void __launch_bounds__(256) k_pad_copy(const uint16_t* src, int64_t s
 // use a 256 x 256 tile over 8 waves (2 x 4, each 128 x 64, two waves per SIMD
 // so that one can issue MFMAs while the other waits on a load); the
 // wave-specialised mode uses 4 MFMA waves (2 x 2 over 256 x 128) and 4 loader
-// waves.  The k-step width follows the LDS budget (see BK below).  Configs
-// with 64-wide stages use 16 x 16 MFMA blocks; those with 32-wide stages keep
-// 32 x 32 blocks (such a stage holds a single 16 x 16 k-step, which the
-// fragment double buffering within a stage does not cover).
+// waves.  The k-step width follows the LDS budget (see BK below).  Every
+// config uses 16 x 16 MFMA blocks except the wave-specialised 4-stage ring:
+// its 32-wide stages hold a single 16 x 16 k-step, which the all-wave kernel
+// covers by handing the next stage's fragments over at the end of each stage
+// (take_next_stage) and the loader/MFMA schedule does not.
 template <int SYNC, int S>
 struct Pick {
     // 64-wide k-steps (128-byte rows per DMA instruction) wherever the ring
     // fits: two stages of 256 x 256, three of the wave-specialised 256 x 128.
     static constexpr int BK = (S == 2 || (SYNC == SYNC_WAVESPEC && S == 3)) ? 64 : 32;
-    static constexpr int MF = (BK == 64) ? 16 : 32;
+    static constexpr int MF = (BK == 64 || SYNC != SYNC_WAVESPEC) ? 16 : 32;
     template <bool BT>
     using type = Cfg<256, (SYNC == SYNC_WAVESPEC) ? 128 : 256, BK, S, 2, (SYNC == SYNC_WAVESPEC) ? 2 : 4, SYNC, BT,
                      (SYNC == SYNC_WAVESPEC) ? 4 : 0, false, MF>;

@@ -28,9 +28,9 @@ SHAPES = {("barrier", 2): (256, 256, 64, 8, 0), ("barrier", 3): (256, 256, 32, 8
           ("pingpong", 4): (128, 128, 64, 8, 4)}
 
 
-# MFMA block edge: 16 x 16 x 32 MFMAs for 64-wide stages, 32 x 32 x 16 for
-# 32-wide ones.
-MFMA_BLOCK = {mode: (16 if SHAPES[mode][2] == 64 else 32) for mode in SHAPES}
+# MFMA block edge: 16 x 16 x 32 MFMAs everywhere but the wave-specialised
+# ring of 32-wide stages, which keeps 32 x 32 x 16.
+MFMA_BLOCK = {mode: (32 if mode[0] == "wavespec" and SHAPES[mode][2] == 32 else 16) for mode in SHAPES}
 
 
 def plan(M, N, K, bt, sync, stages, cus=CUS):
