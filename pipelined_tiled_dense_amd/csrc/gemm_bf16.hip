@@ -442,7 +442,7 @@ __device__ __forceinline__ uint32_t counter_read_issue(const lds_u32* ctr)
 __device__ __forceinline__ void wait_counter_issued(uint32_t v, const lds_u32* ctr, uint32_t target, bool& failed)
 {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v) : : "memory");
-    if (__builtin_amdgcn_readfirstlane(v) < target)
+    if ((uint32_t)__builtin_amdgcn_readfirstlane(v) < target)
         wait_counter(ctr, target, failed);
     COMPILER_FENCE();
 }
@@ -798,8 +798,14 @@ struct FragReader {
                 const uint32_t krow0 = (uint32_t)(32 * kk + 8 * h + rr);
                 b_off = opaque(krow0 * (C::BN * 2) + (uint32_t)((q >> 1) * 16 + (q & 1) * 8));
             }
-            return;
+        } else {
+            init32(wm, wn, lane, kk);
         }
+    }
+
+    // Offsets for 32 x 32 blocks (16-wide k-step kk).
+    __device__ __forceinline__ void init32(int wm, int wn, int lane, int kk)
+    {
         const int h = lane >> 5;
         const int r32 = lane & 31;
         const uint32_t xk = (uint32_t)(((2 * kk + h) ^ swz_k<C::BK>(r32)) << 4);
@@ -816,8 +822,9 @@ struct FragReader {
         }
     }
 
-    // Read instruction d: A blocks first (from the A tile at a_tile), then B
-    // (from the B tile at b_tile).
+    // Read instruction d, from the A tile at a_tile and the B tile at b_tile:
+    // with 16 x 16 blocks A block 0, the B reads, then the other A blocks;
+    // with 32 x 32 blocks the A blocks, then the B reads (read32).
     __device__ __forceinline__ void read(Frags<C>& f, const lds_char* a_tile, const lds_char* b_tile, int wn,
                                          int d) const
     {
@@ -835,8 +842,14 @@ struct FragReader {
                 const lds_char* addr = b_tile + b_off + (uint32_t)(4 * hh * (C::BN * 2)) + jchunk;
                 f.bh[j][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)addr);
             }
-            return;
+        } else {
+            read32(f, a_tile, b_tile, wn, d);
         }
+    }
+
+    __device__ __forceinline__ void read32(Frags<C>& f, const lds_char* a_tile, const lds_char* b_tile, int wn,
+                                           int d) const
+    {
         if (d < C::FM) {
             f.a[d] = *(const LDS_AS bf16x8_t*)(a_tile + a_off + d * (32 * C::BK * 2));
         } else if constexpr (C::BT) {
@@ -965,16 +978,6 @@ __device__ __forceinline__ void mfma_range(f32x16_t (&acc)[C::FM][C::FN], const 
     for (int x = LO; x < HI; ++x)
         acc[x / C::FN][x % C::FN] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(b_frag<C>(f, x % C::FN), f.a[x / C::FN], acc[x / C::FN][x % C::FN], 0, 0, 0);
-}
-
-template <class C>
-__device__ __forceinline__ void mfma_step(f32x16_t (&acc)[C::FM][C::FN], const Frags<C>& f)
-{
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b_frag<C>(f, j), f.a[i], acc[i][j], 0, 0, 0);
 }
 
 // MFMA region kk of a stage in the all-wave kernels.  32 x 32 blocks: the
@@ -1476,7 +1479,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
                 fire_prep = next_prep;
             // MFMA k-step region kk of this stage (kk is a constant).
             auto region = [&]<int kk>() {
-                constexpr int M = region_mfmas<C>(), D = frag_reads<C>();
+                constexpr int M = region_mfmas<C>();
                 constexpr int SALU = (PIR && kk == 1) ? 6 : 0;
                 if constexpr (PIR && kk == 1)
                     next_prep = ld.prepare_and_advance(p);
@@ -2197,7 +2200,7 @@ struct PadSet {
     bool a, b, c;
 };
 
-PadSet pad_set(int64_t N, int64_t K, bool bt, bool a_ok, bool b_ok, bool c_ok)
+PadSet pad_set(int64_t N, int64_t K, bool a_ok, bool b_ok, bool c_ok)
 {
     const bool k_off = K % 8 != 0, n_off = N % 8 != 0;
     return PadSet{k_off || !a_ok, k_off || n_off || !b_ok, n_off || !c_ok};
@@ -2205,7 +2208,7 @@ PadSet pad_set(int64_t N, int64_t K, bool bt, bool a_ok, bool b_ok, bool c_ok)
 
 // Bytes of those copies (256-byte aligned parts): A as M x K8, B as N8 x K8
 // (stored N x K) or K8 x N8, C as M x N8.
-int64_t pad_bytes(int64_t M, int64_t N, int64_t K, bool bt, PadSet ps)
+int64_t pad_bytes(int64_t M, int64_t N, int64_t K, PadSet ps)
 {
     auto up = [](int64_t b) { return (b + 255) & ~(int64_t)255; };
     const int64_t N8 = round8(N), K8 = round8(K);
@@ -2297,7 +2300,7 @@ int fill_plan(int64_t M, int64_t N_in, int64_t K_in, int b_transposed, int stage
     if (items > ((int64_t)1 << 30) || items * pl.k_steps > ((int64_t)1 << 30))
         return GEMM_ERR_UNSUPPORTED_SHAPE;
     pl.pad_bytes = (N != N_in || K != K_in)
-                       ? pad_bytes(M, N_in, K_in, b_transposed != 0, pad_set(N_in, K_in, b_transposed != 0, true, true, true))
+                       ? pad_bytes(M, N_in, K_in, pad_set(N_in, K_in, true, true, true))
                        : 0;
     *out = pl;
     return GEMM_OK;
@@ -2335,7 +2338,7 @@ int gemm_padded(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
     const int64_t b_rows = bt ? N8 : K8, b_cols = bt ? K8 : N8;
     const int64_t a_bytes = (ps.a && K > 0) ? M * K8 * 2 : 0;
     const int64_t b_bytes = (ps.b && K > 0) ? b_rows * b_cols * 2 : 0;
-    const int64_t bytes = pad_bytes(M, N, K, bt, ps);
+    const int64_t bytes = pad_bytes(M, N, K, ps);
     void* ws = nullptr;
     const hipError_t ae = pool ? hipMallocFromPoolAsync(&ws, (size_t)bytes, pool, s) : hipMallocAsync(&ws, (size_t)bytes, s);
     if (ae != hipSuccess || !ws)
@@ -2398,7 +2401,7 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
     // a 16-byte boundary, and a row stride must fit the loads' offsets.
     // Anything else runs on zero-padded copies of the operands that need them.
     auto fits = [](const void* ptr, int64_t ld) { return ld % 8 == 0 && ld <= kMaxLd && ((uintptr_t)ptr & 15) == 0; };
-    const PadSet ps = pad_set(N, K, bt, !reads || fits(A, lda), !reads || fits(B, ldb), fits(C, ldc));
+    const PadSet ps = pad_set(N, K, !reads || fits(A, lda), !reads || fits(B, ldb), fits(C, ldc));
     if (ps.a || ps.b || ps.c)
         return gemm_padded(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, s, bt, pool, ps);
     if (!reads) {
