@@ -42,13 +42,15 @@
  * allocates, frees or retains them.  A and B are only read.  C must not
  * overlap A or B.
  *
- * Split k range: a shape with fewer output tiles than half the compute units
- * (counted in 256 x 256 tiles) and a long k range -- K a multiple of 64 * s
+ * Split k range: a shape with at most half as many output tiles as compute
+ * units (in the chosen configuration's tile, see gemm_bf16_plan) and a long
+ * k range -- K a multiple of 64 * s
  * and K / s >= 512 for some s >= 2 -- is computed as s chunks of k (s <= 16)
  * so that the GPU fills.  Each output tile's chunks are summed in fp32, in
  * chunk order, after one fp32 chain per chunk; the result differs from the
  * unsplit sum only by fp32 rounding, is the same for every sync mode and
- * stage count with the same MFMA block, and is deterministic.  The fp32 partial tiles
+ * stage count with the same tile, MFMA block and split (plan.bm, plan.bn,
+ * plan.mfma_block, plan.k_splits), and is deterministic.  The fp32 partial tiles
  * (plan.workspace_bytes) are allocated stream-ordered on `stream` and
  * released (hipFreeAsync) by the same call, from a memory pool the library
  * creates once per device (hipMallocFromPoolAsync; hipMallocAsync if the pool

@@ -2218,17 +2218,16 @@ int64_t pad_bytes(int64_t M, int64_t N, int64_t K, PadSet ps)
     return up(a) + up(b) + up(c);
 }
 
-// Number of k chunks.  Shapes with fewer output tiles than half the compute
-// units (counted at 256 x 256, so that every sync mode splits alike and the
-// results stay bit-identical across modes) and a long k range are split into
-// equal chunks of a multiple of 64 elements, each at least 512 long, so that
-// tiles x chunks work items can fill the GPU.
-int64_t choose_splits(int64_t M, int64_t N, int64_t K, int cus)
+// Number of k chunks.  Shapes with at most half as many output tiles (in
+// the configuration's tile) as compute units and a long k range are split
+// into equal chunks of a multiple of 64 elements, each at least 512 long, so
+// that tiles x chunks work items can fill the GPU.  Configurations with
+// different tiles may therefore split a shape differently.
+int64_t choose_splits(int64_t tiles, int64_t K, int cus)
 {
-    const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
-    if (tiles256 <= 0 || 2 * tiles256 >= cus)
+    if (tiles <= 0 || 2 * tiles > cus)
         return 1;
-    int64_t s = cus / tiles256;
+    int64_t s = cus / tiles;
     if (s > kMaxSplits)
         s = kMaxSplits;
     for (; s >= 2; --s)
@@ -2290,7 +2289,7 @@ int fill_plan(int64_t M, int64_t N_in, int64_t K_in, int b_transposed, int stage
     pl.mfma_block = v.mfma_block;
     const int64_t tm = (M + v.bm - 1) / v.bm, tn = (N + v.bn - 1) / v.bn;
     pl.tiles = tm * tn;
-    pl.k_splits = choose_splits(M, N, K, cus);
+    pl.k_splits = choose_splits(pl.tiles, K, cus);
     pl.k_steps = (K / pl.k_splits + v.bk - 1) / v.bk;
     if (pl.k_splits == 1)
         pl.tail_splits = choose_tail_splits(pl.tiles, K, cus, pl.tail_tiles);

@@ -56,14 +56,14 @@ def block_of(M, N, K, bt, sync, stages):
 
 
 def assert_same_bits_per_block(outs, what="modes disagree bitwise"):
-    """outs: (mfma block, result) pairs; results of one block shape agree bit for bit."""
+    """outs: (key, result) pairs, the key an MFMA block edge or a split
+    signature; results with one key agree bit for bit."""
     first = {}
     for blk, got in outs:
         if blk in first:
-            np.testing.assert_array_equal(got, first[blk], err_msg="%s (%dx%d blocks)" % (what, blk, blk))
+            np.testing.assert_array_equal(got, first[blk], err_msg="%s (%s)" % (what, blk))
         else:
             first[blk] = got
-    assert set(first) == {16, 32}, sorted(first)
     return first
 
 
@@ -160,30 +160,59 @@ def test_many_tiles_per_workgroup(K, bt):
 def test_split_k(bt):
     """Few output tiles and a long k range: the k range is cut into chunks whose
     fp32 partial tiles are summed in chunk order.  1000 x 1032 has 20 tiles of
-    256 x 256, so K = 8192 splits into 8 chunks of 1024 (ragged M and N).  The
-    chunking depends on the shape only, so every mode with the same MFMA block
-    gives the same bits, run after run and on any stream; a K with no valid
-    chunking stays unsplit."""
+    256 x 256, so K = 8192 splits into 8 chunks of 1024 (ragged M and N); the
+    256 x 128 and 128 x 128 tiles of the loader/MFMA modes split it into 4 and
+    2.  Modes with the same split signature (tile, chunks, MFMA block) give the
+    same bits, run after run and on any stream; a K with no valid chunking
+    stays unsplit."""
     M, N, K = 1000, 1032, 8192
     for sync, stages in MODES:
         plan = bd.gemm_bf16_plan(M, N, K, bt, stages, bd.SYNC_MODES[sync])
-        assert plan["k_splits"] == 8, (sync, stages, plan)
-        assert plan["workspace_bytes"] == plan["tiles"] * 8 * plan["bm"] * plan["bn"] * 4
+        s = {256: 8, 128: 4}[plan["bn"]] if plan["bm"] == 256 else 2
+        assert plan["k_splits"] == s, (sync, stages, plan)
+        assert plan["workspace_bytes"] == plan["tiles"] * s * plan["bm"] * plan["bn"] * 4
     assert bd.gemm_bf16_plan(M, N, K + 8, bt, 0, 0)["k_splits"] == 1
     A, B = make_operands(M, N, K, b_transposed=bt, seed=4242 + bt)
     ref = oracle.load().gemm_bf16(bits(A), bits(B), bt)
     dA, dB = A.cuda(), B.cuda()
-    outs = []
+    by_sig = {}
     for sync, stages in MODES:
+        sig = split_signature(M, N, K, bt, sync, stages)
         got = run(dA, dB, bt, sync, stages)
         assert_within_tol(got, ref, "split %s/%d" % (sync, stages))
-        outs.append((block_of(M, N, K, bt, sync, stages), got))
-    first = assert_same_bits_per_block(outs)
+        if sig in by_sig:
+            np.testing.assert_array_equal(got, by_sig[sig], err_msg="same split, different bits")
+        else:
+            by_sig[sig] = got
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         C = bd.gemm(dA, dB, b_transposed=bt)
     side.synchronize()
-    np.testing.assert_array_equal(bits(C.cpu()), first[block_of(M, N, K, bt, "barrier", 0)])
+    np.testing.assert_array_equal(bits(C.cpu()), by_sig[split_signature(M, N, K, bt, "barrier", 0)])
+
+
+@pytest.mark.parametrize("bt", [False, True], ids=["kn", "nk"])
+def test_split_at_half_the_compute_units(bt):
+    """Exactly half as many 256 x 256 tiles as compute units (4096 x 2048, 128
+    tiles on 256 CUs) and K = 1024: two chunks of 512 for the 256 x 256 tile
+    (the loader/MFMA modes' smaller tiles fill the GPU unsplit).  Compared in
+    full with the oracle; modes with the same split signature agree bit for
+    bit."""
+    M, N, K = 4096, 2048, 1024
+    cus = bd.gemm_bf16_plan(8192, 8192, 8192, True, 0, 0)["grid"]
+    A, B = make_operands(M, N, K, b_transposed=bt, seed=6060 + bt)
+    ref = oracle.load().gemm_bf16(bits(A), bits(B), bt)
+    dA, dB = A.cuda(), B.cuda()
+    outs = []
+    for sync, stages in (("barrier", 2), ("barrier", bd.STAGES_WINDOWS), ("flags", 2), ("wavespec", 3),
+                         ("pingpong", 3)):
+        plan = bd.gemm_bf16_plan(M, N, K, bt, stages, bd.SYNC_MODES[sync])
+        if cus == 256:
+            assert plan["k_splits"] == (2 if plan["bn"] == 256 else 1), (sync, stages, plan)
+        got = run(dA, dB, bt, sync, stages)
+        assert_within_tol(got, ref, "half %s/%d" % (sync, stages))
+        outs.append((split_signature(M, N, K, bt, sync, stages), got))
+    assert_same_bits_per_block(outs, "same split, different bits")
 
 
 def test_plans():
@@ -505,15 +534,13 @@ def test_workload_full_size_sampled(name):
     ref = oracle.load().gemm_bf16(np.ascontiguousarray(Ab[rows]), Bb, w.b_transposed)
     dA, dB = A.cuda(), B.cuda()
     C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
-    first = None
+    outs = []
     for sync, stages in FULL[name]:
         C.fill_(7.0)
         got = run(dA, dB, w.b_transposed, sync, stages, out=C)
         assert_within_tol(got[rows], ref, "%s %s/%d (sampled %d rows)" % (name, sync, stages, len(rows)))
-        if first is None:
-            first = got
-        else:
-            np.testing.assert_array_equal(got, first, err_msg="modes disagree bitwise")
+        outs.append((split_signature(w.M, w.N, w.K, w.b_transposed, sync, stages), got))
+    assert_same_bits_per_block(outs, "same split, different bits")
 
 
 @pytest.mark.parametrize("name", ["gemm8192_nk", "tall32768x1024_k4096_kn", "longk1024_k32768_kn"])
@@ -547,16 +574,14 @@ def test_operand_over_2gib(which):
     rows = sample_rows(M)
     ref = oracle.load().gemm_bf16(bits(A[torch.from_numpy(rows).cuda()].cpu()), bits(B.cpu()), bt)
     C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    first = None
+    outs = []
     for sync, stages in [("barrier", 2), ("barrier", bd.STAGES_WINDOWS), ("flags", 2), ("wavespec", 3),
                          ("pingpong", 3)]:
         C.fill_(7.0)
         got = run(A, B, bt, sync, stages, out=C)
         assert_within_tol(got[rows], ref, "%s %s/%d (sampled %d rows)" % (which, sync, stages, len(rows)))
-        if first is None:
-            first = got
-        else:
-            np.testing.assert_array_equal(got, first, err_msg="modes disagree bitwise")
+        outs.append((split_signature(M, N, K, bt, sync, stages), got))
+    assert_same_bits_per_block(outs, "same split, different bits")
     del A, B, C
     torch.cuda.empty_cache()
 
@@ -578,15 +603,13 @@ def test_max_leading_dimensions_with_poisoned_padding(bt):
     dB[:, :cols_b] = B.cuda()
     ref = oracle.load().gemm_bf16(bits(A), bits(B), bt)
     Cbuf = torch.empty((M, LD), dtype=torch.bfloat16, device="cuda")
-    first = None
+    outs = []
     for sync, stages in MODES:
         Cbuf[:, :N + 4096].fill_(3.0)
         got = run(dA[:, :K], dB[:, :cols_b], bt, sync, stages, out=Cbuf[:, :N])
         assert_within_tol(got, ref, "ld 2^22 %s/%d" % (sync, stages))
         assert bool(torch.all(Cbuf[:, N:N + 4096] == 3.0)), (sync, stages)
-        if first is None:
-            first = got
-        else:
-            np.testing.assert_array_equal(got, first, err_msg="modes disagree bitwise")
+        outs.append((split_signature(M, N, K, bt, sync, stages), got))
+    assert_same_bits_per_block(outs, "same split, different bits")
     del dA, dB, Cbuf
     torch.cuda.empty_cache()

@@ -41,11 +41,11 @@ def cdiv(a, b):
     return -(-a // b)
 
 
-def want_splits(M, N, K, cus):
-    """Fewer 256 x 256 tiles than half the compute units: the largest s <= 16,
-    s <= cus / tiles, with 64 * s dividing K and K / s >= 512."""
-    t = cdiv(M, 256) * cdiv(N, 256)
-    if t == 0 or 2 * t >= cus:
+def want_splits(t, K, cus):
+    """At most half as many output tiles (in the configuration's tile) as compute
+    units: the largest s <= 16, s <= cus / tiles, with 64 * s dividing K and
+    K / s >= 512."""
+    if t == 0 or 2 * t > cus:
         return 1
     for s in range(min(cus // t, 16), 1, -1):
         if K % (64 * s) == 0 and K // s >= 512:
@@ -104,15 +104,29 @@ def test_benchmark_configurations():
     assert (pl["tiles"], pl["grid"], pl["tail_tiles"]) == (1024, 256, 0)
 
 
-def test_split_k_counts_256_tiles_for_every_mode():
-    """The split decision counts 256 x 256 tiles, so every mode splits a shape
-    alike (which keeps their results bit-identical)."""
+def test_split_k_counts_each_configurations_tiles():
+    """The split decision counts the configuration's own tiles: 1000 x 1032 is 20
+    tiles of 256 x 256 (8 chunks of 1024), 36 of 256 x 128 (4 chunks) and 72 of
+    128 x 128 (2 chunks); a K with no chunking of 64s stays unsplit."""
+    want = {(256, 256): 8, (256, 128): 4, (128, 128): 2}
     for sync, stages in MODES:
         pl = plan(1000, 1032, 8192, 1, sync, stages)
-        assert pl["k_splits"] == 8, (sync, stages)
-        assert pl["workspace_bytes"] == pl["tiles"] * 8 * pl["bm"] * pl["bn"] * 4
-        assert pl["k_steps"] == 1024 // pl["bk"]
+        s = want[(pl["bm"], pl["bn"])]
+        assert pl["k_splits"] == s == want_splits(pl["tiles"], 8192, CUS), (sync, stages)
+        assert pl["workspace_bytes"] == pl["tiles"] * s * pl["bm"] * pl["bn"] * 4
+        assert pl["k_steps"] == 8192 // s // pl["bk"]
         assert plan(1000, 1032, 8200, 1, sync, stages)["k_splits"] == 1
+
+
+def test_split_k_at_exactly_half_the_compute_units():
+    """128 tiles of 256 x 256 on 256 compute units (8192 x 1024): two chunks fill
+    the GPU; one more tile row or column of tiles and the shape stays unsplit."""
+    pl = plan(8192, 1024, 8192, 1, "barrier", 2)
+    assert (pl["tiles"], pl["k_splits"], pl["grid"], pl["k_steps"]) == (128, 2, 256, 64)
+    assert plan(8192 + 256, 1024, 8192, 1, "barrier", 2)["k_splits"] == 1      # 132 tiles
+    assert plan(4096, 2048, 1024, 0, "flags", 2)["k_splits"] == 2              # chunks of 512
+    assert plan(4096, 2048, 1000, 0, "flags", 2)["k_splits"] == 1              # no chunking of 64s
+    assert plan(8192, 1024, 8192, 1, "wavespec", 3)["k_splits"] == 1          # 256 tiles of 256 x 128
 
 
 def test_split_tail_named_shapes():
@@ -148,7 +162,7 @@ def test_random_shapes_follow_the_rules():
         bm, bn, bk = pl["bm"], pl["bn"], pl["bk"]
         tiles = cdiv(M, bm) * cdiv(N, bn)
         assert pl["tiles"] == tiles
-        s = want_splits(M, N, K, cus)
+        s = want_splits(tiles, K, cus)
         assert pl["k_splits"] == s, (M, N, K, sync, stages, cus, pl)
         r, ts = want_tail(tiles, K, cus) if s == 1 else (0, 0)
         assert (pl["tail_tiles"], pl["tail_splits"]) == (r, ts), (M, N, K, sync, stages, cus, pl)
