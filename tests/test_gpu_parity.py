@@ -435,6 +435,46 @@ def test_concurrent_split_calls_on_two_streams():
         np.testing.assert_array_equal(bits(C.cpu()), want[i], err_msg="case %d" % i)
 
 
+def random_shapes(seed, n):
+    """Seeded shapes on the fast path's 8-element grid: ragged M, N and K, and
+    every other shape few-tiled with a long k range (multiples of 512), which
+    the k split takes in some configurations' tiles and not in others."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        if i % 2:
+            M = int(rng.integers(1, 1200))
+            N = 8 * int(rng.integers(1, 150))
+            K = 512 * int(rng.integers(1, 9))
+        else:
+            M = int(rng.integers(1, 1600))
+            N = 8 * int(rng.integers(1, 200))
+            K = 8 * int(rng.integers(1, 300))
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("bt", [False, True], ids=["kn", "nk"])
+def test_random_shapes_all_modes(bt):
+    """Eight seeded random shapes (some split along k in some tiles, see
+    random_shapes), every mode, compared in full with the oracle; modes with
+    the same split signature agree bit for bit."""
+    splits = set()
+    for M, N, K in random_shapes(9000 + bt, 8):
+        A, B = make_operands(M, N, K, b_transposed=bt, seed=M + 7 * N + 13 * K)
+        ref = oracle.load().gemm_bf16(bits(A), bits(B), bt)
+        dA, dB = A.cuda(), B.cuda()
+        outs = []
+        for sync, stages in MODES:
+            sig = split_signature(M, N, K, bt, sync, stages)
+            splits.add(sig[2] > 1)
+            got = run(dA, dB, bt, sync, stages)
+            assert_within_tol(got, ref, "%dx%dx%d %s/%d" % (M, N, K, sync, stages))
+            outs.append((sig, got))
+        assert_same_bits_per_block(outs, "%dx%dx%d: same split, different bits" % (M, N, K))
+    assert splits == {False, True}
+
+
 def test_layouts_and_modes_bit_identical():
     M, N, K = 520, 776, 392
     A, B = make_operands(M, N, K, b_transposed=False, seed=99)
