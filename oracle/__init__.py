@@ -48,6 +48,8 @@ class Oracle:
         lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
         lib.oracle_round_array.argtypes = [i64, p, p]
         lib.oracle_round_array.restype = None
+        lib.oracle_decode_array.argtypes = [i64, p, p]
+        lib.oracle_decode_array.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -113,26 +115,42 @@ class Oracle:
         self.lib.oracle_round_array(x.size, x.ctypes.data, out.ctypes.data)
         return out
 
+    def decode(self, bits) -> np.ndarray:
+        """Exact fp64 values of bf16 bit patterns, by the C oracle's own decoder."""
+        b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+        out = np.empty(b.shape, dtype=np.float64)
+        self.lib.oracle_decode_array(b.size, b.ctypes.data, out.ctypes.data)
+        return out
+
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
-    """Exact decode of bf16 bit patterns: the upper half of a binary32 word."""
+    """Exact decode of bf16 bit patterns: the upper half of a binary32 word.
+    This is the decoder every tolerance comparison of GPU results uses."""
     bits = np.asarray(bits, dtype=np.uint16)
-    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):       # signalling NaN patterns widen to quiet NaNs
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 _default: Oracle | None = None
 
 
+def _stale(library: str = LIBRARY, source: str = SOURCE) -> bool:
+    """True when no library exists or the source was changed after it was built."""
+    return not os.path.exists(library) or os.path.getmtime(source) > os.path.getmtime(library)
+
+
 def load(path: str | None = None) -> Oracle:
-    """Load the built oracle, building it first only if no library exists."""
+    """Load the built oracle.  The default library is (re)built first when it
+    is missing or older than ``oracle_gemm.c``, so a stale build of an edited
+    source is never used."""
     global _default
     if path is not None:
         return Oracle(path)
     if _default is None:
-        if not os.path.exists(LIBRARY):
+        if _stale():
             build()
         _default = Oracle(LIBRARY)
     return _default

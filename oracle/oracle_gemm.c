@@ -94,7 +94,13 @@ uint16_t oracle_f64_to_bf16(double x)
     return (uint16_t)(sign | ((w >> 16) & 0x7FFF));
 }
 
-double oracle_bf16_to_f64(uint16_t h) { return decode_bf16(h); }
+/* Elementwise exact decoding of n bf16 bit patterns to fp64 (the decoder the
+ * sums use, exported so that it can be checked on every bit pattern). */
+void oracle_decode_array(int64_t n, const uint16_t *bits, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = decode_bf16(bits[i]);
+}
 
 /* Elementwise rounding of n fp64 values to bf16 bits. */
 void oracle_round_array(int64_t n, const double *x, uint16_t *out)

@@ -343,7 +343,43 @@ def pin_signed_zero_and_nan(o):
     assert int(o.gemm_bf16(A, B, False)[0, 0]) == 0x7FC0
 
 
+def _module_decoder(o):
+    """The Python bf16 decoder of the module that defines ``o``'s class: the
+    real oracle package, or a mutated copy of it."""
+    import sys
+    return sys.modules[type(o).__module__].bf16_bits_to_f64
+
+
+def pin_bf16_decoder(o):
+    """Both bf16 decoders -- the Python one that every GPU tolerance check
+    runs its operands through, and the C oracle's own -- against the format's
+    definition (``bf16_exact``) on all 65536 bit patterns: finite values
+    exactly, with the sign of zero; exponent field 255 with a zero fraction
+    gives +-Inf, with a nonzero fraction NaN."""
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    want = np.empty(pats.size, dtype=np.float64)
+    for b in range(1 << 16):
+        e, m = (b >> 7) & 0xFF, b & 0x7F
+        if e != 0xFF:
+            want[b] = float(bf16_exact(b))
+        elif m == 0:
+            want[b] = -math.inf if b & 0x8000 else math.inf
+        else:
+            want[b] = math.nan
+    neg = (pats & 0x8000) != 0
+    for name, got in (("python", _module_decoder(o)(pats)), ("c", o.decode(pats))):
+        assert got.shape == want.shape and got.dtype == np.float64, name
+        nan_w, nan_g = np.isnan(want), np.isnan(got)
+        assert np.array_equal(nan_w, nan_g), "%s decoder: NaN at %#06x" % (
+            name, int(pats[np.argmax(nan_w != nan_g)]))
+        ok = nan_w | (got == want)
+        assert ok.all(), "%s decoder: %#06x -> %r, want %r" % (
+            name, int(pats[np.argmin(ok)]), got[np.argmin(ok)], want[np.argmin(ok)])
+        sign_ok = nan_w | (np.signbit(got) == neg)
+        assert sign_ok.all(), "%s decoder: sign of %#06x" % (name, int(pats[np.argmin(sign_ok)]))
+
+
 ALL_PINS = [pin_rounding_golden, pin_rounding_exhaustive_exact, pin_brute_force,
             pin_identity_zero, pin_small_golden, pin_closed_forms, pin_linearity_exact,
             pin_linearity_bounded, pin_numpy_crosscheck, pin_layout_invariance,
-            pin_signed_zero_and_nan]
+            pin_signed_zero_and_nan, pin_bf16_decoder]

@@ -5,8 +5,10 @@ into a temporary directory; the pins of ``oracle_pins`` are run against it and
 at least one of them must fail.  This shows that the pins would notice a
 dropped term, a wrong sign, a wrong index or stride, a transposed operand, or
 a wrong rounding rule in the oracle."""
+import importlib.util
 import os
 import shutil
+import sys
 import tempfile
 
 import pytest
@@ -33,6 +35,17 @@ MUTANTS = {
     "noncanonical_nan": ("return 0x7FC0;", "return 0x7FFF;"),
     "overflow_saturates": ("return (uint16_t)(sign | 0x7F80);\n\n    float",
                            "return (uint16_t)(sign | 0x7F7F);\n\n    float"),
+    "c_decode_shift_15": ("uint32_t w = (uint32_t)h << 16;", "uint32_t w = (uint32_t)h << 15;"),
+}
+
+# Mistakes in the Python decoder (oracle.bf16_bits_to_f64), which every GPU
+# tolerance check uses: each is planted in a copy of the oracle package that
+# loads the real C library.
+PY_MUTANTS = {
+    "py_decode_no_shift": ("(bits.astype(np.uint32) << 16)", "(bits.astype(np.uint32))"),
+    "py_decode_shift_15": ("(bits.astype(np.uint32) << 16)", "(bits.astype(np.uint32) << 15)"),
+    "py_decode_drops_sign": ("bits = np.asarray(bits, dtype=np.uint16)\n",
+                             "bits = np.asarray(bits, dtype=np.uint16) & 0x7FFF\n"),
 }
 
 
@@ -64,3 +77,33 @@ def test_mutant_is_caught(name, workdir):
     so = oracle_pkg.build(path_c, os.path.join(workdir, "lib" + name + ".so"))
     caught = _first_failure(oracle_pkg.load(so))
     assert caught is not None, "mutant %s passed every pin" % name
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_python_decoder_mutant_is_caught(name, workdir):
+    old, new = PY_MUTANTS[name]
+    src = open(os.path.join(os.path.dirname(oracle_pkg.SOURCE), "__init__.py")).read()
+    assert src.count(old) == 1, "mutation site for %s not found" % name
+    pkg_dir = os.path.join(workdir, "oracle_" + name)
+    os.makedirs(pkg_dir, exist_ok=True)
+    path = os.path.join(pkg_dir, "__init__.py")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    mod_name = "oracle_mutant_" + name
+    spec = importlib.util.spec_from_file_location(mod_name, path)
+    mod = importlib.util.module_from_spec(spec)
+    sys.modules[mod_name] = mod
+    try:
+        spec.loader.exec_module(mod)
+        o = mod.load(oracle_pkg.load().path)          # the real C library, the mutated decoder
+        assert type(o).__module__ == mod_name
+        assert _first_failure(o) is not None, "mutant %s passed every pin" % name
+    finally:
+        del sys.modules[mod_name]
+
+
+def test_pins_use_the_decoder_gpu_checks_use():
+    """The Python decoder the pins check is the very function the GPU tests
+    and the smoke check decode with."""
+    import oracle_pins
+    assert oracle_pins._module_decoder(oracle_pkg.load()) is oracle_pkg.bf16_bits_to_f64
