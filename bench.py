@@ -3,25 +3,37 @@
 
 A step is one C = A * B over the whole throughput workload (8192 x 8192 x 8192,
 B stored N x K, seeded uniform[-1, 1) bf16 inputs already resident in HBM).
-Each sync mode (barrier, flags, wave-specialised) is timed at its default
-stage count, and barrier sync also over the split-window ring
-("barrier-windows"); ``value`` is the fastest and every one is listed under
-``modes``.  Prints one JSON line.
+Every (sync scheme, ring stages) configuration of the library is timed on it
+-- barrier sync at 2, 3 and 4 stages and over the split-window ring
+(stages 5), flag sync at 2, 3 and 4, the wave-specialised and the ping-pong
+kernels at 2, 3 and 4 -- and ``value`` is the fastest.  The other four
+workloads get the same matrix under ``workloads``.  Prints one JSON line.
 
 Also reports:
-  roofline      achieved matrix-core TFLOP/s of the GEMM kernel (2*M*N*K per
-                launch / mean launch time from HIP events on the launch
-                stream) against the dense bf16 peak, plus HBM traffic per
-                launch from the committed rocprofv3 counter summary when it
-                matches the current kernel source;
+  roofline      achieved matrix-core TFLOP/s of the fastest configuration's
+                GEMM kernel (2*M*N*K per launch / mean launch time from HIP
+                events on the launch stream) against the dense bf16 peak, plus
+                HBM traffic per launch from the committed rocprofv3 counter
+                summary when it matches the current kernel source;
+  clock         per configuration, the mean shader clock of its kernels in
+                the committed counter pass (GRBM_GUI_ACTIVE per XCD over the
+                dispatch's duration), and the fraction of the peak at that
+                clock (256 CU x 4096 FLOP/clk x clock);
+  ceiling       what the matrix cores sustain under the board's power limit
+                on the same kind of operand data with no memory traffic at
+                all (gemm_probe_mfma_ceiling, at the GEMM kernels' wave shape,
+                fragments in registers or re-read from LDS), beside the same
+                loop on all-zero operands;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same product
-                (a few rows of C), on the host cores it actually uses;
+                (a few rows of C), on the host cores it actually uses; each
+                other workload's oracle sample is under its entry;
   reference     torch.matmul (hipBLASLt) on the same operands in the same
-                process, as context: under the board's power limit the
-                attainable clock varies from one GPU to the next.
+                process, as context only.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sync all|barrier|flags|wavespec|barrier-windows]
-                       [--stages S] [--workload NAME] [--no-cpu-baseline] [--copy-calibration]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sync all|barrier|flags|wavespec|pingpong]
+                       [--stages S] [--workload NAME] [--no-cpu-baseline] [--no-workloads] ...
+       python bench.py --counter-run            (a short pass over every configuration, for rocprofv3 --pmc)
+       python bench.py --summarize-counters SQ_CSV FETCH_CSV WRITE_CSV MANIFEST_JSON   (no GPU)
 """
 import argparse
 import hashlib
@@ -34,127 +46,304 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
+PEAK_CLOCK_GHZ = 2.4
+FLOP_PER_CLK_GPU = 256 * 4096
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm8192_nk.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCE = os.path.join(ROOT, "pipelined_tiled_dense_amd", "csrc", "gemm_bf16.hip")
+HEADLINE = "gemm8192_nk"
+COPY_BYTES = 1 << 30
+
+SYNC_NAMES = {0: "barrier", 1: "flags", 2: "wavespec", 3: "pingpong"}
+# Every (sync mode, stages) configuration the library offers; stages 5 is the
+# split-window ring.  They run in this order on every workload: the first
+# launches of a process meet a cool chip whose clock then settles under the
+# power limit, so the slowest kernels go first.
+CONFIGS = [("pingpong", 2), ("pingpong", 3), ("pingpong", 4),
+           ("wavespec", 2), ("wavespec", 3), ("wavespec", 4),
+           ("flags", 2), ("flags", 3), ("flags", 4),
+           ("barrier", 3), ("barrier", 4), ("barrier", 5), ("barrier", 2)]
+DEFAULT_STAGES = {"barrier": 2, "flags": 2, "wavespec": 3, "pingpong": 3}
+
+
+def label(sync, stages):
+    return "%s/%d" % (sync, stages)
+
+
+def timed_configs(workload):
+    """The (sync, stages) runs bench.py times on a workload, in run order.
+    The full-size parity tests check exactly these."""
+    return list(CONFIGS)
 
 
 def kernel_sha():
     return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--sync", default="all",
-                    choices=["all", "barrier", "flags", "wavespec", "pingpong", "barrier-windows"])
-    ap.add_argument("--stages", type=int, default=0)
-    ap.add_argument("--workload", default="gemm8192_nk")
+    ap.add_argument("--sync", default="all", choices=["all", "barrier", "flags", "wavespec", "pingpong"])
+    ap.add_argument("--stages", type=int, default=0, help="with --sync: one stage count (0: the mode's default)")
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle sample")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a device-to-device copy of known size (counter calibration)")
-    ap.add_argument("--summarize-traffic", nargs=4, metavar=("GEMM_FETCH_CSV", "GEMM_WRITE_CSV",
-                                                            "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
-                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into the traffic "
-                         "summary read by the roofline line (no GPU needed)")
-    ap.add_argument("--traffic-kernel", default="Cfg<256, 256, 64, 2, 2, 4, 0, true, 0, false, 16>",
-                    help="kernel configuration the counter CSVs were taken for (a substring of "
-                         "the kernel name: Cfg<BM, BN, BK, S, WM, WN, SYNC, B_NxK, loader waves, windows, MFMA block>)")
+                    help="target CPU time of the headline workload's oracle sample")
+    ap.add_argument("--cpu-seconds-other", type=float, default=2.5,
+                    help="target CPU time of each other workload's oracle sample")
     ap.add_argument("--no-reference", action="store_true", help="skip the torch.matmul timing")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the matrix-core ceiling probe")
     ap.add_argument("--no-workloads", action="store_true",
-                    help="skip the per-workload summary of the other configurations")
-    return ap.parse_args()
+                    help="skip the other configurations")
+    ap.add_argument("--counter-run", action="store_true",
+                    help="a short, untimed pass over every workload and configuration (plus a 1 GiB "
+                         "device copy for the counter calibration), writing the dispatch manifest")
+    ap.add_argument("--manifest", default=None, help="where --counter-run writes its manifest")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_TRACE_CSV", "BENCH_JSON"),
+                    help="turn a rocprofv3 kernel trace of a bench.py run into the committed summary (no GPU)")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("SQ_CSV", "FETCH_CSV", "WRITE_CSV", "MANIFEST"),
+                    help="turn the rocprofv3 counter CSVs of --counter-run passes into the committed "
+                         "summary (no GPU needed)")
+    return ap.parse_args(argv)
 
 
-COPY_BYTES = 1 << 30
-
-
-def _counter_per_dispatch(path, counter, name_filter):
-    """Mean value of `counter` per dispatch of kernels whose name contains
-    name_filter, from a rocprofv3 counter_collection CSV (values summed over
-    counter instances within a dispatch)."""
+# -- counter summary (host only) --------------------------------------------------
+def _dispatches(path):
+    """rocprofv3 counter_collection CSV -> list of dispatches in order:
+    (kernel name, duration ns, {counter: value summed over instances})."""
     import csv
     per = {}
     for row in csv.DictReader(open(path)):
-        if row["Counter_Name"] != counter or name_filter not in row["Kernel_Name"]:
-            continue
-        per[row["Dispatch_Id"]] = per.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
-    if not per:
-        raise SystemExit("no %s samples for kernels matching %r in %s" % (counter, name_filter, path))
-    return sum(per.values()) / len(per), len(per)
+        d = per.setdefault(int(row["Dispatch_Id"]), {
+            "name": row["Kernel_Name"],
+            "ns": int(row["End_Timestamp"]) - int(row["Start_Timestamp"]),
+            "c": {}})
+        d["c"][row["Counter_Name"]] = d["c"].get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    return [per[k] for k in sorted(per)]
 
 
-SYNC_NAMES = {0: "barrier", 1: "flags", 2: "wavespec", 3: "pingpong"}
-# Timed configurations: label -> (sync mode, stages; 0 = the mode's default).
-# "barrier-windows" is barrier sync over the split-window ring.
-# They run in this order: the first launches of a process meet a cool chip
-# whose clock then settles under the power limit, so the slowest mode (never
-# the headline) goes first.
-MODE_RUNS = {"pingpong": ("pingpong", 0), "wavespec": ("wavespec", 0), "flags": ("flags", 0),
-             "barrier": ("barrier", 0), "barrier-windows": ("barrier", 5)}
-# Workloads whose configuration asks for a comparison of the two all-wave
-# synchronisation schemes over the ring depth: (sync, stages) runs, reported
-# as "sync/stages" -> TFLOP/s (stages 5 is the split-window ring).
-STAGE_SWEEPS = {"gemm4096_kn": (("flags", 2), ("flags", 3), ("flags", 4),
-                                ("barrier", 2), ("barrier", 3), ("barrier", 4), ("barrier", 5))}
+_FAMILY = None
 
 
-def cfg_fields(kname):
-    """(sync mode, stages) of a Cfg<BM, BN, BK, S, WM, WN, SYNC, B_NxK, NP,
-    windows, MFMA block> string; the split-window ring reports its stages value, 5."""
-    f = [x.strip() for x in kname[kname.index("<") + 1:].rstrip(">").split(",")]
-    if len(f) > 9 and f[9] == "true":
-        return SYNC_NAMES[int(f[6])], 5
-    return SYNC_NAMES[int(f[6])], int(f[3])
+def kernel_family(name):
+    """Which of the library's kernels a demangled name is ('k_gemm_ws', ...),
+    or None for kernels that are not the library's."""
+    global _FAMILY
+    if _FAMILY is None:
+        import re
+        _FAMILY = re.compile(r"(?:^|[^A-Za-z0-9_])(k_gemm_win|k_gemm_ws|k_gemm_pp|k_reduce_splits|k_gemm|"
+                             r"k_mfma_ceiling)<")
+    m = _FAMILY.search(name)
+    return m.group(1) if m else None
 
 
-def summarize_traffic(paths, kname):
-    """FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  Each is scaled by
-    the ratio of the known bytes a plain 1 GiB device copy moves to what the
-    same counter reads for that copy.  The result is stored in the traffic
-    summary under "<sync>/<stages>", next to the entries of other kernel
-    configurations profiled on the same kernel source."""
-    gf, gw, cf, cw = paths
-    sync, stages = cfg_fields(kname)
-    fetch_kib, n_f = _counter_per_dispatch(gf, "FETCH_SIZE", kname)
-    write_kib, n_w = _counter_per_dispatch(gw, "WRITE_SIZE", kname)
-    copy_f_kib, _ = _counter_per_dispatch(cf, "FETCH_SIZE", "copy")
-    copy_w_kib, _ = _counter_per_dispatch(cw, "WRITE_SIZE", "copy")
-    f_scale = COPY_BYTES / (copy_f_kib * 1024.0)
-    w_scale = COPY_BYTES / (copy_w_kib * 1024.0)
-    fetch = fetch_kib * 1024.0 * f_scale
-    write = write_kib * 1024.0 * w_scale
-    try:
-        with open(TRAFFIC_FILE) as f:
-            out = json.load(f)
-        if out.get("kernel_source_sha256") != kernel_sha() or "entries" not in out:
-            out = None
-    except (OSError, ValueError):
-        out = None
-    if out is None:
-        out = {"workload": "gemm8192_nk", "kernel_source_sha256": kernel_sha(),
-               "compulsory_bytes_per_launch": 2 * (3 * 8192 * 8192), "entries": {}}
-    out["entries"]["%s/%d" % (sync, stages)] = {
-        "kernel": kname,
-        "sync_mode": sync,
-        "stages": stages,
-        "fetch_bytes_per_launch": round(fetch),
-        "write_bytes_per_launch": round(write),
-        "hbm_bytes_per_launch": round(fetch + write),
-        "raw_fetch_kib": fetch_kib, "raw_write_kib": write_kib,
-        "copy_fetch_kib": copy_f_kib, "copy_write_kib": copy_w_kib,
-        "fetch_scale": f_scale, "write_scale": w_scale,
-        "dispatches": {"fetch": n_f, "write": n_w},
-    }
-    with open(TRAFFIC_FILE, "w") as f:
+def kernel_config(name):
+    """("sync/stages", B stored N x K) of a GEMM kernel name, read from its
+    Cfg<BM, BN, BK, S, WM, WN, SYNC, B_NxK, loader waves, windows, MFMA block>
+    (the split-window ring reports stages 5), or None."""
+    i = name.find("Cfg<")
+    if i < 0 or kernel_family(name) not in ("k_gemm", "k_gemm_win", "k_gemm_ws", "k_gemm_pp"):
+        return None
+    f = [x.strip() for x in name[i + 4:name.index(">", i)].split(",")]
+    stages = 5 if f[9] == "true" else int(f[3])
+    return label(SYNC_NAMES[int(f[6])], stages), f[7] == "true"
+
+
+def _assign(dispatches, manifest):
+    """Walk the library's dispatches in order against the manifest of calls.
+    Returns {(workload, label): [dispatch lists, one per call]} and the other
+    kernels dispatched before the first GEMM (the copy calibration's)."""
+    lib = [d for d in dispatches if kernel_family(d["name"])]
+    first = next((i for i, d in enumerate(dispatches) if kernel_family(d["name"])), len(dispatches))
+    other = dispatches[:first]
+    out = {}
+    i = 0
+    for e in manifest["calls"]:
+        key = (e["workload"], e["config"])
+        for _ in range(e["calls"]):
+            grp = lib[i:i + len(e["kernels"])]
+            fams = [kernel_family(d["name"]) for d in grp]
+            if fams != e["kernels"]:
+                raise SystemExit("dispatch %d: expected %s for %s, found %s" % (i, e["kernels"], key, fams))
+            out.setdefault(key, []).append(grp)
+            i += len(grp)
+    if i != len(lib):
+        raise SystemExit("%d library dispatches left over after the manifest" % (len(lib) - i))
+    return out, other
+
+
+def summarize_counters(paths, out_path=COUNTERS_FILE):
+    sq_csv, fetch_csv, write_csv, manifest_path = paths
+    manifest = json.load(open(manifest_path))
+    sq, _ = _assign(_dispatches(sq_csv), manifest)
+    fe, fe_other = _assign(_dispatches(fetch_csv), manifest)
+    wr, wr_other = _assign(_dispatches(write_csv), manifest)
+    # The 1 GiB device copy is the largest copy kernel ahead of the first GEMM
+    # (the first workload's small host-to-device copies may follow it).
+    copy_f = max((d["c"]["FETCH_SIZE"] for d in fe_other if "FETCH_SIZE" in d["c"] and "copy" in d["name"].lower()),
+                 default=0.0)
+    copy_w = max((d["c"]["WRITE_SIZE"] for d in wr_other if "WRITE_SIZE" in d["c"] and "copy" in d["name"].lower()),
+                 default=0.0)
+    if copy_f <= 0 or copy_w <= 0:
+        raise SystemExit("no copy-kernel dispatches for the calibration")
+    # FETCH_SIZE and WRITE_SIZE are in KiB; scale each by the ratio of the
+    # bytes a 1 GiB device copy moves to what the counter reads for it.
+    f_scale = COPY_BYTES / (copy_f * 1024.0)
+    w_scale = COPY_BYTES / (copy_w * 1024.0)
+    entries = {}
+    for (wl, cfg), calls in sq.items():
+        main = [c[0] for c in calls]                       # the GEMM kernel of each call
+        n = len(main)
+        mean = lambda f: sum(f(d) for d in main) / n
+        dur_ns = mean(lambda d: d["ns"])
+        grbm = mean(lambda d: d["c"].get("GRBM_GUI_ACTIVE", 0.0)) / 8.0      # per XCD
+        clock = grbm / dur_ns if dur_ns else 0.0
+        busy = mean(lambda d: d["c"].get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0))
+        lds_act = mean(lambda d: d["c"].get("SQ_LDS_IDX_ACTIVE", 0.0))
+        bank = mean(lambda d: d["c"].get("SQ_LDS_BANK_CONFLICT", 0.0))
+        call_bytes = lambda groups, ctr, scale: sum(sum(d["c"].get(ctr, 0.0) for d in g) for g in groups) \
+            / len(groups) * 1024.0 * scale
+        fetch = call_bytes(fe[(wl, cfg)], "FETCH_SIZE", f_scale)
+        write = call_bytes(wr[(wl, cfg)], "WRITE_SIZE", w_scale)
+        entries.setdefault(wl, {})[cfg] = {
+            "kernel": main[0]["name"],
+            "kernels_per_call": [kernel_family(d["name"]) for d in calls[0]],
+            "dispatches": n,
+            "duration_us": round(dur_ns / 1e3, 2),
+            "clock_ghz": round(clock, 4),
+            "mfma_busy": round(busy / (grbm * 1024.0), 4) if grbm else None,
+            "mfma_insts": mean(lambda d: d["c"].get("SQ_INSTS_MFMA", 0.0)),
+            "lds_insts": mean(lambda d: d["c"].get("SQ_INSTS_LDS", 0.0)),
+            "salu_insts": mean(lambda d: d["c"].get("SQ_INSTS_SALU", 0.0)),
+            "vmem_rd_insts": mean(lambda d: d["c"].get("SQ_INSTS_VMEM_RD", 0.0)),
+            "lds_bank_conflict_of_active": round(bank / lds_act, 5) if lds_act else None,
+            "lds_active_of_cycles": round(lds_act / (grbm * 256.0), 4) if grbm else None,
+            "fetch_bytes_per_call": round(fetch),
+            "write_bytes_per_call": round(write),
+            "hbm_bytes_per_call": round(fetch + write),
+        }
+    out = {"kernel_source_sha256": kernel_sha(),
+           "calibration": {"copy_bytes": COPY_BYTES, "fetch_scale": f_scale, "write_scale": w_scale,
+                           "copy_fetch_kib": copy_f, "copy_write_kib": copy_w},
+           "entries": entries}
+    with open(out_path, "w") as f:
         json.dump(out, f, indent=1)
-    print(json.dumps(out))
+    if out_path == COUNTERS_FILE:
+        write_counter_reports(out)
+    print(json.dumps({"written": out_path, "workloads": sorted(entries)}))
+    return out
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+COUNTER_COMMANDS = [
+    "cd /tmp && export TMPDIR=/tmp   # then, from the repository root:",
+    "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_INSTS_VMEM_RD "
+    "SQ_INSTS_VALU SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE --output-format csv -d <out>/sq -o sq "
+    "-- python3 bench.py --counter-run --manifest <out>/manifest.json",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/fetch -o fetch -- python3 bench.py --counter-run "
+    "--manifest <out>/manifest.json",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/write -o write -- python3 bench.py --counter-run "
+    "--manifest <out>/manifest.json",
+    "python3 bench.py --summarize-counters <out>/sq/sq_counter_collection.csv "
+    "<out>/fetch/fetch_counter_collection.csv <out>/write/write_counter_collection.csv <out>/manifest.json",
+]
+
+
+def write_counter_reports(info, out_dir=PROFILES):
+    """One markdown table per workload from the counter summary, with the
+    kernels' names exactly as rocprofv3 reports them."""
+    from pipelined_tiled_dense_amd.inputs import WORKLOADS
+    cal = info["calibration"]
+    paths = []
+    for wl, cfgs in info["entries"].items():
+        w = WORKLOADS.get(wl)
+        title = ("%s (%d x %d x %d, B stored %s)" % (wl, w.M, w.N, w.K, "N x K" if w.b_transposed else "K x N")
+                 if w else "matrix-core ceiling probe (gemm_probe_mfma_ceiling, 256 workgroups, 1024 iterations)")
+        lines = ["# Counters: %s, every sync mode and stage count" % title, "",
+                 "Kernel source sha256 `%s`.  Commands (one counter group per pass; each pass runs the same "
+                 "short, untimed sequence of calls, 4 per configuration, and the summary attributes every "
+                 "dispatch through the manifest that sequence writes):" % info["kernel_source_sha256"], "", "```"]
+        lines += COUNTER_COMMANDS + ["```", "",
+                 "Per call, mean over the 4 calls: duration of the GEMM kernel (or the probe); clock = "
+                 "GRBM_GUI_ACTIVE / 8 XCDs / duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (clock cycles x "
+                 "1024 SIMDs); bank conflicts = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; instruction counts are "
+                 "per call, whole GPU; HBM bytes = FETCH_SIZE x %.4f + WRITE_SIZE x %.4f (KiB), the factors that "
+                 "make a 1 GiB device copy read and write 1 GiB, summed over every kernel of the call (a split "
+                 "call's reduction included).  Calls shorter than a few microseconds give meaningless clocks."
+                 % (cal["fetch_scale"], cal["write_scale"]), "",
+                 "| config | kernel (as rocprofv3 names it) | duration (us) | clock (GHz) | MFMA busy | SALU instr | "
+                 "LDS instr | VMEM read instr | LDS bank conflicts | HBM read (GB) | HBM write (GB) |",
+                 "|---|---|---|---|---|---|---|---|---|---|---|"]
+        fmt = lambda v, f: "-" if v is None else f % v
+        for cfg, e in cfgs.items():
+            lines.append("| %s | `%s` | %.1f | %.3f | %s | %.3g | %.3g | %.3g | %s | %.3f | %.3f |" % (
+                cfg, e["kernel"], e["duration_us"], e["clock_ghz"], fmt(e["mfma_busy"], "%.3f"), e["salu_insts"],
+                e["lds_insts"], e["vmem_rd_insts"], fmt(e["lds_bank_conflict_of_active"], "%.4f"),
+                e["fetch_bytes_per_call"] / 1e9, e["write_bytes_per_call"] / 1e9))
+        path = os.path.join(out_dir, "%s_counters.md" % wl)
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        paths.append(path)
+    return paths
+
+
+def summarize_trace(trace_csv, bench_json, out_path=None, workload=HEADLINE):
+    """Kernel-trace summary of a bench.py run: per configuration of the
+    headline workload, the GEMM kernel's dispatches (warm-up included) and
+    their mean duration, beside the mean per-call time the same run measured
+    with HIP events.  The headline workload is the only one with B stored
+    N x K, so its kernels are told apart by name."""
+    import csv
+    line = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    per = {}
+    order = []
+    for row in csv.DictReader(open(trace_csv)):
+        name = row["Kernel_Name"]
+        ns = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+        if name not in per:
+            per[name] = []
+            order.append(name)
+        per[name].append(ns)
+    out_path = out_path or os.path.join(PROFILES, "%s_kernel_trace.md" % workload)
+    lines = ["# Kernel trace: %s, every sync mode and stage count" % workload, "",
+             "Command (from the repository root, with TMPDIR=/tmp):", "", "```",
+             "rocprofv3 --kernel-trace --stats --output-format csv -d <out>/kt -o kt -- python3 bench.py "
+             "--steps %d --warmup %d --no-cpu-baseline > <out>/kt_bench.json" % (line["steps"], line["warmup"]),
+             "python3 bench.py --summarize-trace <out>/kt/kt_kernel_trace.csv <out>/kt_bench.json", "```", "",
+             "Kernel source sha256 `%s`.  Per configuration: the dispatches of its kernel in the trace "
+             "(%d warm-up and %d timed calls), their mean and minimum duration, and the mean per-call time "
+             "bench.py measured in the same run with HIP events on the launch stream (the roofline's "
+             "`achieved` uses the latter)." % (kernel_sha(), line["warmup"], line["steps"]), "",
+             "| config | kernel (as rocprofv3 names it) | dispatches | trace mean (us) | trace min (us) | "
+             "HIP events mean (us) | TFLOP/s (events) |", "|---|---|---|---|---|---|---|"]
+    for cfg, e in line["modes"].items():
+        cands = [n for n in order if kernel_config(n) == (cfg, True)]
+        for n in cands:
+            d = per[n]
+            lines.append("| %s | `%s` | %d | %.1f | %.1f | %.1f | %.1f |" % (
+                cfg, n, len(d), sum(d) / len(d) / 1e3, min(d) / 1e3, e["kernel_ms_mean"] * 1e3, e["tflops"]))
+    lines += ["", "The run's line: value %.2f TFLOP/s (%s), roofline achieved %.2f TFLOP/s, frac %.4f."
+              % (line["value"], line["roofline"]["kernel"], line["roofline"]["achieved"], line["roofline"]["frac"])]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out_path
+
+
+def counters_for(workload, cfg, path=COUNTERS_FILE):
+    """The committed counter entry of a workload's configuration, or None when
+    there is none or it was taken on another kernel source."""
+    try:
+        info = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if info.get("kernel_source_sha256") != kernel_sha():
+        return None
+    return info.get("entries", {}).get(workload, {}).get(cfg)
+
+
+# -- GPU legs ---------------------------------------------------------------------
 def time_mode(bd, dA, dB, C, w, sync, stages, steps, warmup, torch):
     for _ in range(warmup):
         bd.gemm(dA, dB, b_transposed=w.b_transposed, sync=sync, stages=stages, out=C)
@@ -173,42 +362,37 @@ def time_mode(bd, dA, dB, C, w, sync, stages, steps, warmup, torch):
     return wall, per_launch_ms
 
 
-def cpu_baseline(w, A, B, target_s):
-    import numpy as np
-
-    import oracle
-    from pipelined_tiled_dense_amd.inputs import bits
-    o = oracle.load()
-    Ab, Bb = bits(A), bits(B)
-    threads = o.num_threads()
-    # calibrate on a few rows, then run a sample sized for ~target_s seconds
-    cal_rows = max(1, threads)
-    t0 = time.perf_counter()
-    o.gemm_bf16(np.ascontiguousarray(Ab[:cal_rows]), Bb, w.b_transposed)
-    t_cal = time.perf_counter() - t0
-    rows = int(max(cal_rows, min(w.M, cal_rows * target_s / max(t_cal, 1e-6))))
-    rows = max(threads, (rows // threads) * threads)
-    t0 = time.perf_counter()
-    o.gemm_bf16(np.ascontiguousarray(Ab[:rows]), Bb, w.b_transposed)
-    t = time.perf_counter() - t0
-    flops = 2.0 * rows * w.N * w.K
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "rows 0..%d of C (%d x %d x %d, %.3g GFLOP) in %.2f s; fp64 triple loop, "
-                      "one bf16 rounding" % (rows - 1, rows, w.N, w.K, flops / 1e9, t)}
-
-
-def traffic_per_launch(workload, sync, stages):
-    """HBM bytes per launch from the committed counter summary, or None when
-    it holds no entry for this kernel configuration or was taken on an older
-    kernel source."""
-    try:
-        info = json.load(open(TRAFFIC_FILE))
-    except (OSError, ValueError):
-        return None
-    if info.get("kernel_source_sha256") != kernel_sha() or info.get("workload") != workload:
-        return None
-    entry = info.get("entries", {}).get("%s/%d" % (sync, stages))
-    return entry.get("hbm_bytes_per_launch") if entry else None
+def measure_workload(bd, w, configs, args, torch, A=None, B=None):
+    """Every configuration on one workload: per-call time from HIP events on
+    the launch stream (mean, median, min), wall-clock throughput, % of peak,
+    and the counter pass's clock where the committed summary has it."""
+    from pipelined_tiled_dense_amd.inputs import workload_operands
+    if A is None:
+        A, B = workload_operands(w)
+    dA, dB = A.cuda(), B.cuda()
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    flops = 2.0 * w.M * w.N * w.K
+    res = {}
+    for sync, stages in configs:
+        plan = bd.gemm_bf16_plan(w.M, w.N, w.K, w.b_transposed, stages, bd.SYNC_MODES[sync])
+        wall, per = time_mode(bd, dA, dB, C, w, sync, stages, args.steps, args.warmup, torch)
+        mean_ms = sum(per) / len(per)
+        tf = flops / (mean_ms * 1e-3) / 1e12
+        e = {"tflops": round(tf, 2), "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+             "wall_tflops": round(flops / (wall / args.steps) / 1e12, 2),
+             "ms_per_step": round(wall * 1e3 / args.steps, 4),
+             "kernel_ms_mean": round(mean_ms, 4), "kernel_ms_median": round(sorted(per)[len(per) // 2], 4),
+             "kernel_ms_min": round(min(per), 4),
+             "tile": "%dx%dx%d" % (plan["bm"], plan["bn"], plan["bk"]), "grid": plan["grid"],
+             "k_splits": plan["k_splits"], "tail_tiles": plan["tail_tiles"], "mfma_block": plan["mfma_block"]}
+        cnt = counters_for(w.name, label(sync, stages))
+        if cnt and cnt.get("clock_ghz"):
+            e["counter_clock_ghz"] = cnt["clock_ghz"]
+            e["frac_of_peak_at_counter_clock"] = round(tf * 1e12 / (FLOP_PER_CLK_GPU * cnt["clock_ghz"] * 1e9), 4)
+            e["counter_mfma_busy"] = cnt.get("mfma_busy")
+        res[label(sync, stages)] = e
+        print("# %s %s: %s" % (w.name, label(sync, stages), json.dumps(e)), file=sys.stderr, flush=True)
+    return res, (A, B, dA, dB, C)
 
 
 def reference_matmul(dA, dB, C, w, steps, warmup, torch):
@@ -228,47 +412,145 @@ def reference_matmul(dA, dB, C, w, steps, warmup, torch):
             "ms_per_step": round(ms, 4)}
 
 
-def other_workloads(bd, skip, args, torch):
-    """The other configurations, each at every sync mode's default stage count:
-    best mode's TFLOP/s (HIP events around all launches) and torch.matmul on
-    the same operands."""
-    from pipelined_tiled_dense_amd.inputs import WORKLOADS, workload_operands
+# Variants of the matrix-core ceiling probe: name -> (waves, fragments from
+# LDS, all-zero data).  8 waves of 128 x 64 is the all-wave kernels' layout,
+# 4 waves of 128 x 128 the layout with a third fewer LDS reads per MFMA.
+CEILING_VARIANTS = {"w8_registers_zero_data": (8, 0, True), "w8_registers": (8, 0, False),
+                    "w8_lds_reads": (8, 1, False), "w4_registers": (4, 0, False), "w4_lds_reads": (4, 1, False)}
+CEILING_ITERS = 1024
+CEILING_BLOCKS = 256
+
+
+def _ceiling_lib():
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "pipelined_tiled_dense_amd", "libgemm_probes.so"))
+    lib.gemm_probe_mfma_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.gemm_probe_mfma_ceiling.restype = ctypes.c_int
+    return lib
+
+
+def _ceiling_call(torch, lib, variant, data, sink):
+    waves, from_lds, _ = CEILING_VARIANTS[variant]
+    rc = lib.gemm_probe_mfma_ceiling(data.data_ptr(), data.numel(), from_lds, waves, CEILING_ITERS, CEILING_BLOCKS,
+                                     sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError("gemm_probe_mfma_ceiling failed: %d" % rc)
+
+
+def _ceiling_data(torch):
+    g = torch.Generator(device="cpu").manual_seed(12345)
+    rand = (torch.rand(1 << 22, generator=g) * 2 - 1).to(torch.bfloat16).cuda()
+    zero = torch.zeros(1 << 22, dtype=torch.bfloat16, device="cuda")
+    sink = torch.empty(CEILING_BLOCKS * 512, dtype=torch.float32, device="cuda")
+    return rand, zero, sink
+
+
+def mfma_ceiling(torch, steps=20):
+    """gemm_probe_mfma_ceiling on 256 workgroups in every variant: TFLOP/s
+    from HIP events (2^23 FLOP per workgroup-iteration), with the counter
+    pass's clock and MFMA busy where the committed summary has them."""
+    lib = _ceiling_lib()
+    rand, zero, sink = _ceiling_data(torch)
+    flop = float(CEILING_BLOCKS) * (1 << 23) * CEILING_ITERS
+    stream = torch.cuda.current_stream()
     out = {}
+    for name, (_, _, zero_data) in CEILING_VARIANTS.items():
+        data = zero if zero_data else rand
+        for _ in range(3):
+            _ceiling_call(torch, lib, name, data, sink)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+        for i in range(steps):
+            ev[2 * i].record(stream)
+            _ceiling_call(torch, lib, name, data, sink)
+            ev[2 * i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / steps
+        tf = flop / (ms * 1e-3) / 1e12
+        e = {"tflops": round(tf, 1), "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "ms": round(ms, 4)}
+        cnt = counters_for("ceiling", name)
+        if cnt and cnt.get("clock_ghz"):
+            e["counter_clock_ghz"] = cnt["clock_ghz"]
+            e["counter_mfma_busy"] = cnt.get("mfma_busy")
+        out[name] = e
+    out["note"] = ("MFMA-only loop of 16x16x32 bf16 at the GEMM kernels' wave shapes, 256 workgroups, no global "
+                   "memory traffic; random uniform[-1,1) bf16 operands unless named zero_data")
+    return out
+
+
+def cpu_baseline(w, A, B, target_s):
+    import numpy as np
+
+    import oracle
+    from pipelined_tiled_dense_amd.inputs import bits
+    o = oracle.load()
+    Ab, Bb = bits(A), bits(B)
+    threads = o.num_threads()
+    # calibrate on a few rows, then run a sample sized for ~target_s seconds
+    cal_rows = max(1, min(w.M, threads))
+    t0 = time.perf_counter()
+    o.gemm_bf16(np.ascontiguousarray(Ab[:cal_rows]), Bb, w.b_transposed)
+    t_cal = time.perf_counter() - t0
+    rows = int(max(cal_rows, min(w.M, cal_rows * target_s / max(t_cal, 1e-6))))
+    rows = min(w.M, max(cal_rows, (rows // threads) * threads))
+    t0 = time.perf_counter()
+    o.gemm_bf16(np.ascontiguousarray(Ab[:rows]), Bb, w.b_transposed)
+    t = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": round(flops / t / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "rows 0..%d of C (%d x %d x %d, %.3g GFLOP) in %.2f s; fp64 triple loop, "
+                      "one bf16 rounding" % (rows - 1, rows, w.N, w.K, flops / 1e9, t)}
+
+
+def counter_run(bd, args, torch):
+    """Every configuration on every workload, 1 warm-up call and 3 counted
+    calls each, after a 1 GiB device copy: the command the rocprofv3 --pmc
+    passes profile.  The manifest lists the calls in order with the library
+    kernels each launches, so the summary can attribute every dispatch."""
+    from pipelined_tiled_dense_amd.inputs import WORKLOADS, workload_operands
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    calls = []
     for name, w in WORKLOADS.items():
-        if name == skip:
-            continue
         A, B = workload_operands(w)
         dA, dB = A.cuda(), B.cuda()
         C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
-        flops = 2.0 * w.M * w.N * w.K
-        per_mode = {}
-        for m in ("pingpong", "wavespec", "flags", "barrier"):
-            _, per = time_mode(bd, dA, dB, C, w, m, 0, args.steps, args.warmup, torch)
-            per_mode[m] = flops / (sum(per) / len(per) * 1e-3) / 1e12
-        best = max(per_mode, key=per_mode.get)
-        plan = bd.gemm_bf16_plan(w.M, w.N, w.K, w.b_transposed, 0, bd.SYNC_MODES[best])
-        entry = {"M": w.M, "N": w.N, "K": w.K, "b_layout": "N x K" if w.b_transposed else "K x N",
-                 "best_mode": best, "tflops": round(per_mode[best], 2),
-                 "modes_tflops": {m: round(v, 2) for m, v in per_mode.items()},
-                 "k_splits": plan["k_splits"]}
-        if name in STAGE_SWEEPS:
-            sweep = {}
-            for sync, stages in STAGE_SWEEPS[name]:
-                _, per = time_mode(bd, dA, dB, C, w, sync, stages, args.steps, args.warmup, torch)
-                sweep["%s/%d" % (sync, stages)] = round(flops / (sum(per) / len(per) * 1e-3) / 1e12, 2)
-            entry["sync_stages_tflops"] = sweep
-        if not args.no_reference:
-            entry["reference_tflops"] = reference_matmul(dA, dB, C, w, args.steps, args.warmup, torch)["tflops"]
-        out[name] = entry
-        print("# workload %s: %s" % (name, json.dumps(entry)), file=sys.stderr, flush=True)
+        for sync, stages in timed_configs(name):
+            pl = bd.gemm_bf16_plan(w.M, w.N, w.K, w.b_transposed, stages, bd.SYNC_MODES[sync])
+            fam = {"barrier": "k_gemm_win" if stages == 5 else "k_gemm", "flags": "k_gemm",
+                   "wavespec": "k_gemm_ws", "pingpong": "k_gemm_pp"}[sync]
+            kernels = [fam] + ([fam] if pl["tail_tiles"] > 0 else []) + \
+                      (["k_reduce_splits"] if pl["k_splits"] > 1 or pl["tail_tiles"] > 0 else [])
+            for _ in range(4):
+                bd.gemm(dA, dB, b_transposed=w.b_transposed, sync=sync, stages=stages, out=C)
+            torch.cuda.synchronize()
+            calls.append({"workload": name, "config": label(sync, stages), "calls": 4, "kernels": kernels})
         del dA, dB, C
-    return out
+    lib = _ceiling_lib()
+    rand, zero, sink = _ceiling_data(torch)
+    for name, (_, _, zero_data) in CEILING_VARIANTS.items():
+        for _ in range(4):
+            _ceiling_call(torch, lib, name, zero if zero_data else rand, sink)
+        torch.cuda.synchronize()
+        calls.append({"workload": "ceiling", "config": name, "calls": 4, "kernels": ["k_mfma_ceiling"]})
+    path = args.manifest or os.path.join(ROOT, "gpurun_out", "counter_manifest.json")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump({"calls": calls}, f, indent=1)
+    print(json.dumps({"manifest": path, "calls": len(calls)}), flush=True)
 
 
 def main():
     args = parse()
-    if args.summarize_traffic:
-        summarize_traffic(args.summarize_traffic, args.traffic_kernel)
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
+    if args.summarize_trace:
+        print(summarize_trace(*args.summarize_trace))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the GEMM has no multi-GPU path in this build "
@@ -278,58 +560,38 @@ def main():
     import torch
 
     from pipelined_tiled_dense_amd import binding as bd
-    from pipelined_tiled_dense_amd.inputs import WORKLOADS, workload_operands
+    from pipelined_tiled_dense_amd.inputs import WORKLOADS
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
     bd.library()
-
-    if args.copy_calibration:
-        nbytes = COPY_BYTES
-        src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": nbytes}))
+    if args.counter_run:
+        counter_run(bd, args, torch)
         return
 
     w = WORKLOADS[args.workload]
-    A, B = workload_operands(w)
-    dA, dB = A.cuda(), B.cuda()
-    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
-    modes = list(MODE_RUNS) if args.sync == "all" else [args.sync]
-    if args.stages != 0 and args.sync == "all":
-        modes = ["pingpong", "wavespec", "flags", "barrier"]
-    flops = 2.0 * w.M * w.N * w.K
-    results = {}
-    for m in modes:
-        sync, stages = MODE_RUNS[m]
-        stages = stages or args.stages
-        plan = bd.gemm_bf16_plan(w.M, w.N, w.K, w.b_transposed, stages, bd.SYNC_MODES[sync])
-        wall, per = time_mode(bd, dA, dB, C, w, sync, stages, args.steps, args.warmup, torch)
-        mean_ms = sum(per) / len(per)
-        results[m] = {"sync": sync, "stages": plan["stages"], "tile": "%dx%dx%d" % (plan["bm"], plan["bn"], plan["bk"]),
-                      "grid": plan["grid"], "ms_per_step": wall * 1e3 / args.steps,
-                      "kernel_ms_mean": mean_ms, "kernel_ms_median": sorted(per)[len(per) // 2],
-                      "kernel_ms_min": min(per),
-                      "tflops": flops / (wall / args.steps) / 1e12,
-                      "kernel_tflops": flops / (mean_ms * 1e-3) / 1e12}
-        print("# %s: %s" % (m, json.dumps(results[m])), file=sys.stderr, flush=True)
+    if args.sync == "all":
+        configs = timed_configs(w.name)
+    else:
+        configs = [(args.sync, args.stages or DEFAULT_STAGES[args.sync])]
+    results, (A, B, dA, dB, C) = measure_workload(bd, w, configs, args, torch)
     timeouts = bd.gemm_bf16_sync_timeouts()
-    best = max(results, key=lambda k: results[k]["tflops"])
+    best = max(results, key=lambda k: results[k]["wall_tflops"])
     r = results[best]
-    achieved = r["kernel_tflops"]
+    sync, stages = best.split("/")[0], int(best.split("/")[1])
+    achieved = r["tflops"]
+    cnt = counters_for(w.name, best)
+    kernel = {"wavespec": "k_gemm_ws", "pingpong": "k_gemm_pp"}.get(sync, "k_gemm_win" if stages == 5 else "k_gemm")
     line = {
         "metric": "bf16 GEMM TFLOP/s and % of MFMA peak at 1 GPU (8192^3, per sync mode)",
-        "value": round(r["tflops"], 2),
+        "value": r["wall_tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(r["ms_per_step"], 4),
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -338,28 +600,45 @@ def main():
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
                    "b_layout": "N x K (K contiguous)" if w.b_transposed else "K x N",
                    "inputs": "seeded uniform[-1,1) rounded to bf16, seed %d" % w.seed,
-                   "sync_mode": r["sync"], "stages": r["stages"], "tile": r["tile"], "grid": r["grid"],
+                   "sync_mode": sync, "stages": stages, "tile": r["tile"], "grid": r["grid"],
                    "accumulate": "fp32", "output": "bf16 (RNE)"},
-        "pct_of_peak": round(100.0 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
-        "modes": {m: {"tflops": round(v["tflops"], 2), "pct_of_peak": round(100 * v["tflops"] / PEAK_BF16_TFLOPS, 2),
-                      "stages": v["stages"], "tile": v["tile"], "kernel_ms_mean": round(v["kernel_ms_mean"], 4),
-                      "kernel_ms_median": round(v["kernel_ms_median"], 4), "kernel_ms_min": round(v["kernel_ms_min"], 4)}
-                  for m, v in results.items()},
+        "pct_of_peak": round(100.0 * r["wall_tflops"] / PEAK_BF16_TFLOPS, 2),
+        "modes": results,
         "sync_timeouts": timeouts,
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_per_launch(w.name, r["sync"], r["stages"]),
-                     "kernel": ("k_gemm_ws (%d stages)" % r["stages"] if r["sync"] == "wavespec"
-                                else "k_gemm_pp (%d stages)" % r["stages"] if r["sync"] == "pingpong"
-                                else "k_gemm_win (split-window ring)" if r["stages"] == 5
-                                else "k_gemm (%s, %d stages)" % (r["sync"], r["stages"]))},
+                     "traffic": cnt["hbm_bytes_per_call"] if cnt else None,
+                     "kernel": "%s (%s)" % (kernel, best),
+                     "clock_ghz_counter_pass": cnt["clock_ghz"] if cnt else None,
+                     "frac_at_counter_clock": r.get("frac_of_peak_at_counter_clock")},
     }
     if not args.no_reference:
         line["reference"] = reference_matmul(dA, dB, C, w, args.steps, args.warmup, torch)
+    del dA, dB, C
+    if not args.no_ceiling:
+        line["ceiling"] = mfma_ceiling(torch)
+        print("# ceiling: %s" % json.dumps(line["ceiling"]), file=sys.stderr, flush=True)
+    others = {}
     if not args.no_workloads:
-        line["workloads"] = other_workloads(bd, w.name, args, torch)
+        for name, ow in WORKLOADS.items():
+            if name == w.name:
+                continue
+            res, (oA, oB, odA, odB, oC) = measure_workload(bd, ow, timed_configs(name), args, torch)
+            b = max(res, key=lambda k: res[k]["tflops"])
+            entry = {"M": ow.M, "N": ow.N, "K": ow.K, "b_layout": "N x K" if ow.b_transposed else "K x N",
+                     "best": b, "tflops": res[b]["tflops"], "pct_of_peak": res[b]["pct_of_peak"],
+                     "configs": res}
+            if not args.no_reference:
+                entry["reference_tflops"] = reference_matmul(odA, odB, oC, ow, args.steps, args.warmup,
+                                                             torch)["tflops"]
+            del odA, odB, oC
+            others[name] = (entry, oA, oB)
+        line["workloads"] = {k: v[0] for k, v in others.items()}
+        line["sync_timeouts"] = bd.gemm_bf16_sync_timeouts()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_seconds)
+        for name, (entry, oA, oB) in others.items():
+            entry["cpu_baseline"] = cpu_baseline(WORKLOADS[name], oA, oB, args.cpu_seconds_other)
     print(json.dumps(line), flush=True)
 
 

@@ -14,12 +14,14 @@
  * sum is accumulated in fp32 by the matrix cores; the order of the fp32
  * additions is the library's, so results may differ from an exactly rounded
  * product by the fp32 rounding of the partial sums (well under one bf16 ulp
- * for K up to ~10^5 at unit-size inputs).  Calls whose plans report the
- * same MFMA block (plan.mfma_block: 16 x 16 x 32 or 32 x 32 x 16 MFMAs) run
- * the same chain of MFMA accumulations for every element and give the same
- * bits, whatever the sync mode, stage count or B layout; across block shapes
- * results may differ by fp32 rounding.  There is no alpha/beta: C is
- * overwritten.
+ * for K up to ~10^5 at unit-size inputs).  Bit identity: calls whose plans
+ * agree on the MFMA block (plan.mfma_block: 16 x 16 x 32 or 32 x 32 x 16
+ * MFMAs) and on the k split (plan.k_splits, plan.tail_tiles,
+ * plan.tail_splits, and the tile plan.bm x plan.bn whenever a split is
+ * present) run the same chain of MFMA accumulations for every element and
+ * give the same bits, whatever the sync mode, stage count or B layout.
+ * Calls whose plans differ in any of these may differ by fp32 rounding.
+ * There is no alpha/beta: C is overwritten.
  *
  * How the work is done (none of this changes the result):
  *   - a persistent grid walks the output tiles grid-stride ("Allow separate
@@ -108,7 +110,8 @@ enum {
  * backward kernel: exploratory shared-memory reduction" (section
  * "Shared-memory reduction strategies": buffer aliasing, and a producer that
  * streams one half of an operand while the consumer computes on the other).
- * Results are bit-identical to every other mode with 16 x 16 MFMA blocks.
+ * Results follow the bit-identity rule above (its plan has 16 x 16 MFMA
+ * blocks and the 256 x 256 tile).
  */
 enum { GEMM_STAGES_WINDOWS = 5 };
 

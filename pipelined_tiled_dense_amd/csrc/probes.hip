@@ -11,6 +11,9 @@
 //   - ds_read_b64_tr_b16: which lane receives which 16-bit element;
 //   - the fp32 -> bf16 conversion used by the epilogue (rounding mode);
 //   - buffer range checking, with and without a scalar offset.
+// One more entry point is a measurement rather than a semantics probe: the
+// matrix-core throughput the board sustains under its power limit on given
+// operand data, with no global memory traffic (gemm_probe_mfma_ceiling).
 // All accesses stay inside the buffers whose sizes are stated per entry
 // point; the host wrapper checks pointer arguments before launching.
 #include <hip/hip_runtime.h>
@@ -182,6 +185,92 @@ __global__ void __launch_bounds__(256) k_cvt(const float* __restrict__ in,
     out[2 * i + 1] = uhi;
 }
 
+// Matrix-core ceiling.  Each workgroup has the shape of the GEMM kernels'
+// MFMA waves: NW waves, each accumulating a 128 x (16 FN) fp32 tile as 8 x FN
+// blocks of v_mfma_f32_16x16x32_bf16, so a 32-wide k-step is 8 FN MFMAs over
+// 8 A and FN B fragments.  NW = 8, FN = 4 is the all-wave kernels' layout (two
+// waves per SIMD, 128 x 64 per wave); NW = 4, FN = 8 gives one wave per SIMD a
+// 128 x 128 tile (its 256 accumulator registers then need the accumulation
+// register file).  The fragments come from `data` (bf16x8 vectors, taken
+// modulo n_vec): two fragment sets alternate, so consecutive MFMAs see
+// different operands, as in a GEMM.  FROM_LDS: 128 KiB of LDS are filled
+// from `data` once, and every k-step re-reads its 8 + FN fragments per wave
+// from LDS (1 KiB per read instruction, contiguous across lanes, at a base
+// that moves every k-step within the first 64 KiB); otherwise
+// the fragments stay in registers.  No global memory is touched after the
+// start, and no synchronisation runs inside the loop.  Each thread writes one
+// float of the accumulators to sink[blockIdx.x * 64 NW + threadIdx.x].
+// Every workgroup-iteration is 2^23 FLOP whatever the shape.
+constexpr int kCeilVecs = 8192;   // 128 KiB of 16-byte fragments
+
+template <bool FROM_LDS, int NW, int FN>
+__global__ void __launch_bounds__(NW * 64) k_mfma_ceiling(const bf16x8_t* __restrict__ data, int n_vec, int iters,
+                                                          float* __restrict__ sink)
+{
+    static_assert(NW * FN == 32, "2^23 FLOP per workgroup-iteration");
+    constexpr int NF = 8 + FN;                 // fragments per k-step
+    __shared__ bf16x8_t lds[kCeilVecs];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    if constexpr (FROM_LDS) {
+        for (int i = t; i < kCeilVecs; i += NW * 64)
+            lds[i] = data[(int)(((int64_t)blockIdx.x * 1031 + i) % n_vec)];
+        __syncthreads();
+    }
+    bf16x8_t fa[2][8], fb[2][FN];
+    const int64_t base = ((int64_t)blockIdx.x * NW * 64 + t) * 2 * NF;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            fa[s][i] = data[(int)((base + s * NF + i) % n_vec)];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            fb[s][j] = data[(int)((base + s * NF + 8 + j) % n_vec)];
+    }
+    f32x4_t acc[8][FN];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+        if constexpr (FN == 8) {
+            // 256 accumulator registers: keep them in the accumulation
+            // register file for the whole loop.
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    asm volatile("" : "+a"(acc[i][j]));
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if constexpr (FROM_LDS) {
+                // The other set's fragments, for the next k-step.
+                const int v0 = ((((it * 2 + s) * NF + w * 7) * 64) & (kCeilVecs / 2 - 1)) + lane;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    fa[s ^ 1][i] = lds[v0 + i * 64];
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    fb[s ^ 1][j] = lds[v0 + (8 + j) * 64];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[s][j], fa[s][i], acc[i][j], 0, 0, 0);
+        }
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            sum += acc[i][j][0] + acc[i][j][1] + acc[i][j][2] + acc[i][j][3];
+    sink[(int64_t)blockIdx.x * NW * 64 + t] = sum;
+}
+
 int launch_status()
 {
     hipError_t e = hipGetLastError();
@@ -258,6 +347,31 @@ int gemm_probe_cvt_bf16(const float* in, uint16_t* out, int64_t n, void* stream)
         return 0;
     hipLaunchKernelGGL(k_cvt, dim3((pairs + 255) / 256), dim3(256), 0, (hipStream_t)stream,
                        in, out, pairs);
+    return launch_status();
+}
+
+// data: n_elems bf16 values (n_elems a positive multiple of 8, below 2^34);
+// sink: blocks * 512 floats.  Launches `blocks` workgroups, each running
+// `iters` iterations of two 32-wide k-steps: 2^23 * iters FLOP per workgroup.
+// waves = 8: 8 waves of 128 x 64 (the all-wave kernels' layout); waves = 4:
+// 4 waves of 128 x 128.
+int gemm_probe_mfma_ceiling(const uint16_t* data, int64_t n_elems, int from_lds, int waves, int iters, int blocks,
+                            float* sink, void* stream)
+{
+    if (!data || !sink || n_elems < 8 || n_elems % 8 != 0 || n_elems / 8 > ((int64_t)1 << 31) - 1 ||
+        iters < 1 || iters > (1 << 20) || blocks < 1 || blocks > 65536 || (waves != 4 && waves != 8))
+        return -1;
+    const int n_vec = (int)(n_elems / 8);
+    const hipStream_t s = (hipStream_t)stream;
+    const bf16x8_t* d = (const bf16x8_t*)data;
+    if (waves == 8 && from_lds)
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<true, 8, 4>), dim3(blocks), dim3(512), 0, s, d, n_vec, iters, sink);
+    else if (waves == 8)
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<false, 8, 4>), dim3(blocks), dim3(512), 0, s, d, n_vec, iters, sink);
+    else if (from_lds)
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<true, 4, 8>), dim3(blocks), dim3(256), 0, s, d, n_vec, iters, sink);
+    else
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<false, 4, 8>), dim3(blocks), dim3(256), 0, s, d, n_vec, iters, sink);
     return launch_status();
 }
 

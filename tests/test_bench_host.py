@@ -1,44 +1,131 @@
-"""Host-side logic of bench.py that needs no GPU: kernel-name parsing for the
-traffic summary, the traffic guard against a changed kernel source, and the
-one-GPU rule."""
+"""Host-side logic of bench.py that needs no GPU: the configuration matrix,
+kernel-name parsing and dispatch attribution for the counter summary, the
+summary's guard against a changed kernel source, and the one-GPU rule."""
+import csv
 import json
 import os
 import subprocess
 import sys
+
+import pytest
 
 import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def test_cfg_fields():
-    assert bench.cfg_fields("Cfg<256, 256, 64, 2, 2, 4, 0, true, 0, false, 16>") == ("barrier", 2)
-    assert bench.cfg_fields("Cfg<256, 256, 32, 4, 2, 4, 1, false, 0, false, 32>") == ("flags", 4)
-    assert bench.cfg_fields("Cfg<256, 128, 64, 3, 2, 2, 2, true, 4, false, 32>") == ("wavespec", 3)
-    # the split-window ring reports the stages value that selects it
-    assert bench.cfg_fields("Cfg<256, 256, 64, 2, 2, 4, 0, true, 0, true, 16>") == ("barrier", 5)
+def test_kernel_family():
+    ns = "void (anonymous namespace)::"
+    assert bench.kernel_family(ns + "k_gemm<(anonymous namespace)::Cfg<256, 256, 64, 2, 2, 4, 0, true, 0, "
+                                    "false, 16>, true, false>((anonymous namespace)::Params)") == "k_gemm"
+    assert bench.kernel_family(ns + "k_gemm_ws<Cfg<256, 128, 64, 3>>(Params)") == "k_gemm_ws"
+    assert bench.kernel_family(ns + "k_gemm_pp<Cfg<128>>(Params)") == "k_gemm_pp"
+    assert bench.kernel_family(ns + "k_gemm_win<Cfg<256>, true, false>(Params)") == "k_gemm_win"
+    assert bench.kernel_family(ns + "k_reduce_splits<Cfg<256>>(Params)") == "k_reduce_splits"
+    assert bench.kernel_family("__amd_rocclr_copyBuffer") is None
+    assert bench.kernel_family("Custom_Cijk_Alik_Bljk_BBS_BH_MT256x256x64_MI16x16x1") is None
 
 
-def test_mode_runs_cover_every_sync_mode():
-    assert set(s for s, _ in bench.MODE_RUNS.values()) == set(bench.SYNC_NAMES.values())
-    assert bench.MODE_RUNS["barrier-windows"] == ("barrier", 5)
+def test_every_configuration_is_timed_on_every_workload():
+    """Each sync scheme at 2, 3 and 4 stages, plus the split-window ring
+    (barrier sync, stages 5), on every workload; the slowest kernels first."""
+    from pipelined_tiled_dense_amd.inputs import WORKLOADS
+    want = {(s, st) for s in ("barrier", "flags", "wavespec", "pingpong") for st in (2, 3, 4)} | {("barrier", 5)}
+    for name in WORKLOADS:
+        got = bench.timed_configs(name)
+        assert set(got) == want and len(got) == len(want), name
+    assert bench.timed_configs("gemm8192_nk")[0][0] == "pingpong"
+    assert bench.timed_configs("gemm8192_nk")[-1] == ("barrier", 2)
 
 
-def test_traffic_only_for_the_profiled_kernel():
-    """Traffic is reported only for a workload and (sync mode, stages) that the
-    committed summary holds, and only while the kernel source is unchanged."""
-    with open(bench.TRAFFIC_FILE) as f:
-        info = json.load(f)
-    assert info["entries"], "the summary holds at least one kernel configuration"
-    for key, e in info["entries"].items():
-        assert key == "%s/%d" % (e["sync_mode"], e["stages"])
-        got = bench.traffic_per_launch(info["workload"], e["sync_mode"], e["stages"])
-        if info["kernel_source_sha256"] == bench.kernel_sha():
-            assert got == e["hbm_bytes_per_launch"] == e["fetch_bytes_per_launch"] + e["write_bytes_per_launch"]
-        else:
-            assert got is None
-        assert bench.traffic_per_launch("gemm4096_kn", e["sync_mode"], e["stages"]) is None
-    assert bench.traffic_per_launch(info["workload"], "flags", 3) is None
+def _write_csv(path, rows):
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=cols)
+        wr.writeheader()
+        for r in rows:
+            wr.writerow(dict(zip(cols, r)))
+
+
+def _synthetic_pass(path, counters):
+    """A copy kernel, a small host copy, then two calls of a plain GEMM and one
+    split call (GEMM + reduction), with per-instance counter values."""
+    ns = "void (anonymous namespace)::"
+    disp = [("__amd_rocclr_copyBuffer", 1000), ("__amd_rocclr_copyBuffer", 10),
+            (ns + "k_gemm<Cfg<256>, true, false>(Params)", 700_000),
+            (ns + "k_gemm<Cfg<256>, true, false>(Params)", 700_000),
+            (ns + "k_gemm_ws<Cfg<256>>(Params)", 100_000),
+            (ns + "k_reduce_splits<Cfg<256>>(Params)", 10_000)]
+    rows = []
+    for i, (name, ns_) in enumerate(disp):
+        for cname, val in counters(name).items():
+            for inst in range(2):                     # values are summed over instances
+                rows.append((i + 1, name, cname, val / 2, 1000, 1000 + ns_))
+    _write_csv(path, rows)
+
+
+def test_summarize_counters_end_to_end(tmp_path):
+    def sq(name):
+        if "copy" in name:
+            return {"GRBM_GUI_ACTIVE": 8.0}
+        return {"GRBM_GUI_ACTIVE": 8 * 1.7 * 700_000, "SQ_VALU_MFMA_BUSY_CYCLES": 0.8 * 1.7 * 700_000 * 1024,
+                "SQ_LDS_IDX_ACTIVE": 1000.0, "SQ_LDS_BANK_CONFLICT": 5.0, "SQ_INSTS_SALU": 3e7}
+
+    def fetch(name):
+        return {"FETCH_SIZE": 524288.0 if "copy" in name and "rocclr" in name else 1000.0}
+
+    def write(name):
+        return {"WRITE_SIZE": 1048576.0 if "copy" in name else 2000.0}
+
+    _synthetic_pass(tmp_path / "sq.csv", sq)
+    _synthetic_pass(tmp_path / "f.csv", fetch)
+    _synthetic_pass(tmp_path / "w.csv", write)
+    manifest = {"calls": [{"workload": "gemm8192_nk", "config": "barrier/2", "calls": 2, "kernels": ["k_gemm"]},
+                          {"workload": "longk1024_k32768_kn", "config": "wavespec/3", "calls": 1,
+                           "kernels": ["k_gemm_ws", "k_reduce_splits"]}]}
+    (tmp_path / "m.json").write_text(json.dumps(manifest))
+    out = tmp_path / "counters.json"
+    info = bench.summarize_counters([str(tmp_path / n) for n in ("sq.csv", "f.csv", "w.csv", "m.json")],
+                                    out_path=str(out))
+    cal = info["calibration"]
+    assert cal["fetch_scale"] == pytest.approx(2.0) and cal["write_scale"] == pytest.approx(1.0)
+    e = info["entries"]["gemm8192_nk"]["barrier/2"]
+    assert e["dispatches"] == 2 and e["clock_ghz"] == pytest.approx(1.7) and e["mfma_busy"] == pytest.approx(0.8)
+    assert e["duration_us"] == pytest.approx(700.0)
+    assert e["lds_bank_conflict_of_active"] == pytest.approx(0.005)
+    assert e["fetch_bytes_per_call"] == round(1000 * 1024 * 2.0)
+    assert e["write_bytes_per_call"] == round(2000 * 1024 * 1.0)
+    s = info["entries"]["longk1024_k32768_kn"]["wavespec/3"]
+    assert s["kernels_per_call"] == ["k_gemm_ws", "k_reduce_splits"]
+    assert s["fetch_bytes_per_call"] == round(2 * 1000 * 1024 * 2.0)      # both kernels of the call
+    assert bench.counters_for("gemm8192_nk", "barrier/2", path=str(out)) == e
+    assert bench.counters_for("gemm8192_nk", "flags/2", path=str(out)) is None
+    # taken on another kernel source: not used
+    stale = json.loads(out.read_text())
+    stale["kernel_source_sha256"] = "0" * 64
+    out.write_text(json.dumps(stale))
+    assert bench.counters_for("gemm8192_nk", "barrier/2", path=str(out)) is None
+
+
+def test_dispatches_that_do_not_match_the_manifest_are_rejected(tmp_path):
+    _synthetic_pass(tmp_path / "sq.csv", lambda name: {"GRBM_GUI_ACTIVE": 1.0})
+    wrong = {"calls": [{"workload": "x", "config": "barrier/2", "calls": 3, "kernels": ["k_gemm"]}]}
+    with pytest.raises(SystemExit):
+        bench._assign(bench._dispatches(tmp_path / "sq.csv"), wrong)
+    short = {"calls": [{"workload": "x", "config": "barrier/2", "calls": 1, "kernels": ["k_gemm"]}]}
+    with pytest.raises(SystemExit):
+        bench._assign(bench._dispatches(tmp_path / "sq.csv"), short)
+
+
+def test_committed_counters_match_their_source_or_are_ignored():
+    if not os.path.exists(bench.COUNTERS_FILE):
+        pytest.skip("no committed counter summary")
+    info = json.load(open(bench.COUNTERS_FILE))
+    for wl, cfgs in info["entries"].items():
+        for cfg, e in cfgs.items():
+            got = bench.counters_for(wl, cfg)
+            assert got == (e if info["kernel_source_sha256"] == bench.kernel_sha() else None)
+            assert e["hbm_bytes_per_call"] == e["fetch_bytes_per_call"] + e["write_bytes_per_call"]
 
 
 def test_more_than_one_gpu_is_refused():
@@ -50,8 +137,8 @@ def test_more_than_one_gpu_is_refused():
 
 def test_helpers_present():
     """Everything main() calls on the GPU path exists (a CPU run never reaches it)."""
-    for name in ("time_mode", "cpu_baseline", "traffic_per_launch", "summarize_traffic",
-                 "reference_matmul", "other_workloads", "kernel_sha", "parse"):
+    for name in ("time_mode", "measure_workload", "cpu_baseline", "counters_for", "summarize_counters",
+                 "reference_matmul", "mfma_ceiling", "counter_run", "kernel_sha", "parse"):
         assert callable(getattr(bench, name)), name
     import ast
     import builtins
@@ -62,18 +149,8 @@ def test_helpers_present():
             defined |= {(a.asname or a.name).split(".")[0] for a in n.names}
         elif isinstance(n, ast.Name) and isinstance(n.ctx, ast.Store):
             defined.add(n.id)
+        elif isinstance(n, (ast.FunctionDef, ast.arg)):
+            defined.add(n.name if isinstance(n, ast.FunctionDef) else n.arg)
     called = {n.func.id for n in ast.walk(tree) if isinstance(n, ast.Call) and isinstance(n.func, ast.Name)}
     missing = {c for c in called if c not in defined and not hasattr(builtins, c) and c not in dir(bench)}
     assert not missing, missing
-
-
-def test_stage_sweep_compares_both_all_wave_schemes_at_2_3_4_stages():
-    """The 4096^3 configuration compares barrier and flag synchronisation at
-    2, 3 and 4 ring stages; every sweep entry must be a valid (sync, stages)
-    pair of the library."""
-    sweep = bench.STAGE_SWEEPS["gemm4096_kn"]
-    for sync in ("barrier", "flags"):
-        assert {st for s, st in sweep if s == sync} >= {2, 3, 4}
-    for sync, stages in sweep:
-        assert sync in ("barrier", "flags")
-        assert stages in (2, 3, 4) or (sync, stages) == ("barrier", 5)
