@@ -128,8 +128,13 @@ enum {
     GEMM_ERR_SYNC_MODE = -5,         /* sync_mode not one of GEMM_SYNC_* */
     GEMM_ERR_DEVICE = -6,            /* no HIP device, or the current device is not gfx950 */
     GEMM_ERR_LAUNCH = -7,            /* the kernel launch was rejected by the runtime */
-    GEMM_ERR_ALIAS = -8              /* C overlaps A or B */
+    GEMM_ERR_ALIAS = -8,             /* C overlaps A or B */
+    GEMM_ERR_SCRATCH = -9            /* gemm_bf16_noalloc only: the call needs more temporary
+                                        memory than its scratch region holds */
 };
+
+/* Size of gemm_bf16_noalloc's per-device scratch region, in bytes. */
+enum { GEMM_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024 };
 
 /* The tiling and launch shape chosen for a problem (see gemm_bf16_plan). */
 typedef struct gemm_bf16_plan {
@@ -202,6 +207,37 @@ int gemm_bf16_bt(int64_t M, int64_t N, int64_t K,
                  const void* B, int64_t ldb,
                  void* C, int64_t ldc,
                  int stages, int sync_mode, void* stream);
+
+/*
+ * gemm_bf16_noalloc: gemm_bf16 for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, results and bits as gemm_bf16 (B stored
+ * K x N); it calls no hipMalloc, hipFree or allocating library routine.
+ *
+ * Where gemm_bf16 takes temporary memory from the library's pool -- the fp32
+ * partial tiles of a split k range or split tail (plan.workspace_bytes) and
+ * the zero-padded operand copies of a call off the 8-element grid
+ * (plan.pad_bytes, or less when only some operands need copying) -- this entry
+ * point uses a fixed scratch region of GEMM_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * per device instead: a static device array the library's code object
+ * carries, present on every GPU the library runs on until the process ends.
+ * 64 MiB holds every split workspace on a device with up to 256 compute units
+ * (one 256 x 256 fp32 partial tile per compute unit at most); padded copies
+ * must fit beside it.  A call whose needs exceed the region returns
+ * GEMM_ERR_SCRATCH before anything is enqueued.
+ *
+ * The region is shared by every call on one GPU and keeps the last call's
+ * contents (nothing in it needs to start at zero: every byte a call reads
+ * from it was written earlier in the same call).  Calls that overlap in time
+ * on one GPU -- on different streams, or from different host threads --
+ * race on it and give undefined results; order them on one stream, or use
+ * gemm_bf16.  Nothing here records a hipMemsetAsync.
+ */
+int gemm_bf16_noalloc(int64_t M, int64_t N, int64_t K,
+                      const void* A, int64_t lda,
+                      const void* B, int64_t ldb,
+                      void* C, int64_t ldc,
+                      int stages, int sync_mode, void* stream);
 
 /*
  * gemm_bf16_plan: the plan gemm_bf16 (b_transposed == 0) or gemm_bf16_bt

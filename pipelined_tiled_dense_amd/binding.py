@@ -21,6 +21,8 @@ GEMM_ERR_SYNC_MODE = -5
 GEMM_ERR_DEVICE = -6
 GEMM_ERR_LAUNCH = -7
 GEMM_ERR_ALIAS = -8
+GEMM_ERR_SCRATCH = -9
+GEMM_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 SYNC_MODES = {"barrier": 0, "flags": 1, "wavespec": 2, "pingpong": 3}
 STAGES_WINDOWS = 5          # GEMM_STAGES_WINDOWS: the split-window ring (barrier sync)
@@ -64,6 +66,8 @@ def library() -> ctypes.CDLL:
         lib.gemm_bf16.restype = i32
         lib.gemm_bf16_bt.argtypes = sig
         lib.gemm_bf16_bt.restype = i32
+        lib.gemm_bf16_noalloc.argtypes = sig
+        lib.gemm_bf16_noalloc.restype = i32
         lib.gemm_bf16_plan.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(Plan)]
         lib.gemm_bf16_plan.restype = i32
         lib.gemm_bf16_plan_cus.argtypes = [i64, i64, i64, i32, i32, i32, i32, ctypes.POINTER(Plan)]
@@ -83,6 +87,10 @@ def gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, stream) -> int
 
 def gemm_bf16_bt(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, stream) -> int:
     return library().gemm_bf16_bt(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, stream)
+
+
+def gemm_bf16_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, stream) -> int:
+    return library().gemm_bf16_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, stream)
 
 
 def gemm_bf16_plan(M, N, K, b_transposed, stages, sync_mode) -> dict:

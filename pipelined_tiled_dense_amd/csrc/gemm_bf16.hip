@@ -2100,6 +2100,16 @@ int default_stages(int sync_mode)
     return (sync_mode == GEMM_SYNC_WAVESPEC || sync_mode == GEMM_SYNC_PINGPONG) ? 3 : 2;
 }
 
+// The allocation-free entry point's temporary memory: one region per GPU the
+// library runs on, held until the process ends.  Its size covers every split
+// workspace on a device of up to 256 compute units (a split has at most one
+// 256 x 256 fp32 partial tile per compute unit); padded operand copies must
+// fit beside it.  In host code `scratch` names a host-side stand-in: the
+// device address is taken once per device with hipGetSymbolAddress (with
+// that device current) and only that address is ever passed to a kernel.
+constexpr int64_t kScratchBytes = GEMM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
 struct DeviceInfo {
     bool probed = false;
     int status = GEMM_OK;
@@ -2109,13 +2119,16 @@ struct DeviceInfo {
     // every synchronisation (the default pool's behaviour), so a split call
     // does not pay for a fresh allocation.  Null if it could not be created.
     hipMemPool_t pool = nullptr;
+    // This device's copy of `scratch` (null if its address could not be
+    // taken: the allocation-free entry point then returns GEMM_ERR_DEVICE).
+    char* scratch_ptr = nullptr;
 };
 
 constexpr int kMaxDevices = 64;
 std::mutex g_dev_mutex;
 DeviceInfo g_dev[kMaxDevices];
 
-int device_info(int* cus, hipMemPool_t* pool = nullptr)
+int device_info(int* cus, hipMemPool_t* pool = nullptr, char** scratch_ptr = nullptr)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
@@ -2145,13 +2158,59 @@ int device_info(int* cus, hipMemPool_t* pool = nullptr)
                 else
                     (void)hipMemPoolDestroy(pl);
             }
+            void* sp = nullptr;
+            if (hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch)) == hipSuccess && sp)
+                d.scratch_ptr = (char*)sp;
+            else
+                (void)hipGetLastError();   // leave no sticky error behind for the caller's next call
         }
         d.probed = true;
     }
     *cus = d.cus;
     if (pool)
         *pool = d.pool;
+    if (scratch_ptr)
+        *scratch_ptr = d.scratch_ptr;
     return d.status;
+}
+
+// Where a call's temporary device memory (split workspaces, padded operand
+// copies) comes from.  Pooled (fixed == nullptr): stream-ordered allocations
+// from the library's per-device pool, each released by the same call.
+// Fixed: consecutive pieces of this device's scratch region, taken in order
+// and never released; nothing is allocated or freed.
+struct TempMem {
+    hipMemPool_t pool = nullptr;
+    char* fixed = nullptr;
+    int64_t fixed_left = 0;
+};
+
+int64_t align256(int64_t b)
+{
+    return (b + 255) & ~(int64_t)255;
+}
+
+int temp_take(TempMem& t, int64_t bytes, hipStream_t s, void** p)
+{
+    *p = nullptr;
+    if (t.fixed) {
+        const int64_t need = align256(bytes);
+        if (need > t.fixed_left)
+            return GEMM_ERR_SCRATCH;
+        *p = t.fixed;
+        t.fixed += need;
+        t.fixed_left -= need;
+        return GEMM_OK;
+    }
+    const hipError_t e = t.pool ? hipMallocFromPoolAsync(p, (size_t)bytes, t.pool, s) : hipMallocAsync(p, (size_t)bytes, s);
+    return (e == hipSuccess && *p) ? GEMM_OK : GEMM_ERR_DEVICE;
+}
+
+int temp_give(const TempMem& t, void* p, hipStream_t s)
+{
+    if (t.fixed)
+        return GEMM_OK;
+    return hipFreeAsync(p, s) == hipSuccess ? GEMM_OK : GEMM_ERR_DEVICE;
 }
 
 bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes)
@@ -2305,8 +2364,8 @@ int fill_plan(int64_t M, int64_t N_in, int64_t K_in, int b_transposed, int stage
     return GEMM_OK;
 }
 
-int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-                void* C, int64_t ldc, int stages, int sync_mode, void* stream, bool bt);
+int gemm_direct(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                int64_t ldc, int stages, int sync_mode, hipStream_t s, bool bt, int cus, TempMem& tm);
 
 int launch_pad_copy(const void* src, int64_t src_rows, int64_t src_cols, int64_t ld_src, void* dst, int64_t dst_rows,
                     int64_t dst_cols, int64_t ld_dst, hipStream_t s)
@@ -2328,28 +2387,26 @@ int launch_pad_copy(const void* src, int64_t src_rows, int64_t src_cols, int64_t
 // runs on those (and on the operands used in place), and the valid N columns
 // of a padded result are copied into C.  Zero k-columns add only zero
 // products, so the result is that of the unpadded problem.  The copies live
-// in stream-ordered memory from the library's pool for this call only.
+// in temporary memory taken for this call (see TempMem).
 int gemm_padded(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
-                int64_t ldc, int stages, int sync_mode, hipStream_t s, bool bt, hipMemPool_t pool, PadSet ps)
+                int64_t ldc, int stages, int sync_mode, hipStream_t s, bool bt, int cus, TempMem& tm, PadSet ps)
 {
-    auto up = [](int64_t b) { return (b + 255) & ~(int64_t)255; };
     const int64_t N8 = round8(N), K8 = round8(K);
     const int64_t b_rows = bt ? N8 : K8, b_cols = bt ? K8 : N8;
     const int64_t a_bytes = (ps.a && K > 0) ? M * K8 * 2 : 0;
     const int64_t b_bytes = (ps.b && K > 0) ? b_rows * b_cols * 2 : 0;
     const int64_t bytes = pad_bytes(M, N, K, ps);
     void* ws = nullptr;
-    const hipError_t ae = pool ? hipMallocFromPoolAsync(&ws, (size_t)bytes, pool, s) : hipMallocAsync(&ws, (size_t)bytes, s);
-    if (ae != hipSuccess || !ws)
-        return GEMM_ERR_DEVICE;
+    int rc = temp_take(tm, bytes, s, &ws);
+    if (rc != GEMM_OK)
+        return rc;
     char* a2 = (char*)ws;
-    char* b2 = a2 + up(a_bytes);
-    char* c2 = b2 + up(b_bytes);
+    char* b2 = a2 + align256(a_bytes);
+    char* c2 = b2 + align256(b_bytes);
     const void* a_use = A;
     const void* b_use = B;
     void* c_use = ps.c ? (void*)c2 : C;
     int64_t lda_use = lda, ldb_use = ldb, ldc_use = ps.c ? N8 : ldc;
-    int rc = GEMM_OK;
     if (K > 0 && ps.a) {
         rc = launch_pad_copy(A, M, K, lda, a2, M, K8, K8, s);
         a_use = a2;
@@ -2361,17 +2418,20 @@ int gemm_padded(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
         ldb_use = b_cols;
     }
     if (rc == GEMM_OK)
-        rc = gemm_common(M, N8, K8, K > 0 ? a_use : nullptr, lda_use, K > 0 ? b_use : nullptr, ldb_use, c_use, ldc_use,
-                         stages, sync_mode, s, bt);
+        rc = gemm_direct(M, N8, K8, K > 0 ? a_use : nullptr, lda_use, K > 0 ? b_use : nullptr, ldb_use, c_use, ldc_use,
+                         stages, sync_mode, s, bt, cus, tm);
     if (rc == GEMM_OK && ps.c)
         rc = launch_pad_copy(c2, M, N8, N8, C, M, N, ldc, s);
-    if (hipFreeAsync(ws, s) != hipSuccess && rc == GEMM_OK)
-        rc = GEMM_ERR_DEVICE;
-    return rc;
+    const int frc = temp_give(tm, ws, s);
+    return rc != GEMM_OK ? rc : frc;
 }
 
-int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-                void* C, int64_t ldc, int stages, int sync_mode, void* stream, bool bt)
+// Every GEMM entry point: validation, device, then the padded or the direct
+// path.  noalloc: temporary memory comes from the device's scratch region
+// (checked up front, so a call that does not fit enqueues nothing) instead
+// of the pool.
+int gemm_entry(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+               void* C, int64_t ldc, int stages, int sync_mode, void* stream, bool bt, bool noalloc)
 {
     int rc = validate_shape(M, N, K, stages, sync_mode);
     if (rc != GEMM_OK)
@@ -2391,8 +2451,9 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
         return GEMM_ERR_ALIAS;
 
     int cus = 0;
-    hipMemPool_t pool = nullptr;
-    rc = device_info(&cus, &pool);
+    TempMem tm;
+    char* scratch_ptr = nullptr;
+    rc = device_info(&cus, &tm.pool, &scratch_ptr);
     if (rc != GEMM_OK)
         return rc;
     hipStream_t s = (hipStream_t)stream;
@@ -2401,8 +2462,37 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
     // Anything else runs on zero-padded copies of the operands that need them.
     auto fits = [](const void* ptr, int64_t ld) { return ld % 8 == 0 && ld <= kMaxLd && ((uintptr_t)ptr & 15) == 0; };
     const PadSet ps = pad_set(N, K, !reads || fits(A, lda), !reads || fits(B, ldb), fits(C, ldc));
-    if (ps.a || ps.b || ps.c)
-        return gemm_padded(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, s, bt, pool, ps);
+    const bool padded = ps.a || ps.b || ps.c;
+    if (noalloc) {
+        if (!scratch_ptr)
+            return GEMM_ERR_DEVICE;
+        tm.pool = nullptr;
+        tm.fixed = scratch_ptr;
+        tm.fixed_left = kScratchBytes;
+        // Everything the call takes: the padded copies, then the split
+        // workspace of the (padded) problem.
+        int64_t need = padded ? align256(pad_bytes(M, N, K, ps)) : 0;
+        if (reads) {
+            gemm_bf16_plan_t pl;
+            rc = fill_plan(M, N, K, bt, stages, sync_mode, cus, &pl);
+            if (rc != GEMM_OK)
+                return rc;
+            need += align256(pl.workspace_bytes);
+        }
+        if (need > kScratchBytes)
+            return GEMM_ERR_SCRATCH;
+    }
+    if (padded)
+        return gemm_padded(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, s, bt, cus, tm, ps);
+    return gemm_direct(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, s, bt, cus, tm);
+}
+
+// The fast path: N and K multiples of 8, operands addressable directly.
+int gemm_direct(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                int64_t ldc, int stages, int sync_mode, hipStream_t s, bool bt, int cus, TempMem& tm)
+{
+    int rc = GEMM_OK;
+    const bool reads = K > 0;
     if (!reads) {
         const int64_t chunks = M * (N / 8);
         int64_t blocks = (chunks + 255) / 256;
@@ -2445,13 +2535,13 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
         return with_cfg(sync_mode, pl.stages, bt, [&]<class C>() { return launch<C>(p, grid, s); });
 
     // Split k range (all tiles, or the tail): fp32 partial tiles in
-    // stream-ordered memory that lives for this call only, so calls on
-    // different streams never share it.
+    // temporary memory taken for this call (pooled: stream-ordered memory
+    // that lives for this call only, so calls on different streams never
+    // share it).
     void* ws = nullptr;
-    const hipError_t ae = pool ? hipMallocFromPoolAsync(&ws, (size_t)pl.workspace_bytes, pool, s)
-                               : hipMallocAsync(&ws, (size_t)pl.workspace_bytes, s);
-    if (ae != hipSuccess || !ws)
-        return GEMM_ERR_DEVICE;
+    rc = temp_take(tm, pl.workspace_bytes, s, &ws);
+    if (rc != GEMM_OK)
+        return rc;
     Params q = p;   // the launch whose partial tiles are reduced
     if (pl.tail_tiles > 0) {
         rc = with_cfg(sync_mode, pl.stages, bt, [&]<class C>() { return launch<C>(p, grid, s); });
@@ -2478,9 +2568,8 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
             return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
         });
     }
-    if (hipFreeAsync(ws, s) != hipSuccess && rc == GEMM_OK)
-        rc = GEMM_ERR_DEVICE;
-    return rc;
+    const int frc = temp_give(tm, ws, s);
+    return rc != GEMM_OK ? rc : frc;
 }
 
 }  // namespace
@@ -2490,13 +2579,19 @@ extern "C" {
 int gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
               void* C, int64_t ldc, int stages, int sync_mode, void* stream)
 {
-    return gemm_common(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, stream, false);
+    return gemm_entry(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, stream, false, false);
 }
 
 int gemm_bf16_bt(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
                  void* C, int64_t ldc, int stages, int sync_mode, void* stream)
 {
-    return gemm_common(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, stream, true);
+    return gemm_entry(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, stream, true, false);
+}
+
+int gemm_bf16_noalloc(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                      void* C, int64_t ldc, int stages, int sync_mode, void* stream)
+{
+    return gemm_entry(M, N, K, A, lda, B, ldb, C, ldc, stages, sync_mode, stream, false, true);
 }
 
 int gemm_bf16_plan(int64_t M, int64_t N, int64_t K, int b_transposed, int stages, int sync_mode,
@@ -2538,6 +2633,9 @@ const char* gemm_bf16_strerror(int status)
     case GEMM_ERR_DEVICE: return "no usable device (the current HIP device must be gfx950)";
     case GEMM_ERR_LAUNCH: return "kernel launch failed";
     case GEMM_ERR_ALIAS: return "C overlaps A or B";
+    case GEMM_ERR_SCRATCH:
+        return "the call needs more temporary memory than gemm_bf16_noalloc's scratch region "
+               "(GEMM_NOALLOC_SCRATCH_BYTES) holds";
     default: return "unknown status";
     }
 }

@@ -40,7 +40,7 @@ def test_library_exports_declared_symbols(header):
     lib = os.path.join(PKG, HEADER_LIB[header])
     assert os.path.exists(lib), "build the package first"
     names = declared_functions(os.path.join(ROOT, "include", header))
-    assert {"gemm_bf16", "gemm_bf16_bt", "gemm_bf16_plan", "gemm_bf16_strerror"} <= set(names)
+    assert {"gemm_bf16", "gemm_bf16_bt", "gemm_bf16_noalloc", "gemm_bf16_plan", "gemm_bf16_strerror"} <= set(names)
     syms = exported(lib)
     missing = [n for n in names if n not in syms]
     assert not missing, missing
@@ -72,7 +72,7 @@ def call(fn, M=64, N=64, K=64, A=ALIGNED, lda=64, B=2 * ALIGNED, ldb=64, C=4 * A
     return fn(M, N, K, A, lda, B, ldb, C, ldc, stages, sync, None)
 
 
-@pytest.mark.parametrize("fn", [bd.gemm_bf16, bd.gemm_bf16_bt], ids=["kn", "nk"])
+@pytest.mark.parametrize("fn", [bd.gemm_bf16, bd.gemm_bf16_bt, bd.gemm_bf16_noalloc], ids=["kn", "nk", "noalloc"])
 def test_validation_errors(fn):
     assert call(fn, sync=4) == bd.GEMM_ERR_SYNC_MODE
     assert call(fn, sync=-1) == bd.GEMM_ERR_SYNC_MODE
@@ -138,7 +138,7 @@ def test_plan_validation():
 
 
 def test_strerror():
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         s = bd.gemm_bf16_strerror(code)
         assert s and s != "unknown status"
     assert bd.gemm_bf16_strerror(-99) == "unknown status"
@@ -150,3 +150,17 @@ def test_no_gpu_gives_device_error():
     if torch.cuda.is_available():
         pytest.skip("a GPU is visible")
     assert call(bd.gemm_bf16) == bd.GEMM_ERR_DEVICE
+    assert call(bd.gemm_bf16_noalloc) == bd.GEMM_ERR_DEVICE
+
+
+def test_noalloc_scratch_limit_is_declared():
+    """The allocation-free entry point's scratch size in the header matches
+    the binding, and covers the largest split workspace on 256 compute units
+    (one 256 x 256 fp32 partial tile per compute unit)."""
+    text = open(os.path.join(ROOT, "include", "gemm_bf16.h")).read()
+    m = re.search(r"GEMM_NOALLOC_SCRATCH_BYTES\s*=\s*([0-9 *]+)\s*}", text)
+    assert m and eval(m.group(1)) == bd.GEMM_NOALLOC_SCRATCH_BYTES
+    worst = max(bd.gemm_bf16_plan_cus(M, N, K, bt, st, sy, 256)["workspace_bytes"]
+                for (M, N, K) in ((256, 256, 1 << 16), (1024, 1024, 32768), (4352, 4352, 4096), (256, 4096, 1 << 15))
+                for bt in (0, 1) for sy in (0, 1, 2, 3) for st in (0, 2, 3, 4))
+    assert 0 < worst <= bd.GEMM_NOALLOC_SCRATCH_BYTES == 256 * 256 * 256 * 4
