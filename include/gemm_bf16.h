@@ -267,13 +267,39 @@ int gemm_bf16_plan_cus(int64_t M, int64_t N, int64_t K, int b_transposed,
 const char* gemm_bf16_strerror(int status);
 
 /*
+ * Failed synchronisation.  The counter-synchronised modes (GEMM_SYNC_FLAGS,
+ * GEMM_SYNC_WAVESPEC, GEMM_SYNC_PINGPONG) wait on LDS counters with bounded
+ * polls, so a protocol failure -- a counter that never reaches its target --
+ * cannot hang the GPU: the wave gives up and runs its finite loops to the
+ * end.  Such a call still returns GEMM_OK (the failure happens after it
+ * returned).  The caller learns of it in two ways:
+ *   - C: every output tile whose computation may have used data the failure
+ *     let through is written as NaN (bf16 quiet NaN) in full.  Tiles of other
+ *     workgroups, and tiles a workgroup stored before its failure, hold
+ *     correct values.  A result without NaN where the inputs have none is
+ *     therefore trustworthy.
+ *   - gemm_bf16_sync_timeouts below counts the waits that gave up.
+ * GEMM_SYNC_BARRIER uses the hardware barrier only and cannot fail this way.
+ */
+
+/*
  * gemm_bf16_sync_timeouts: the number of bounded waits on ring counters that
- * gave up since the library was loaded on the current device (a protocol
- * failure: the kernel abandons the tile instead of hanging).  Zero in correct
- * operation.  Synchronises the device.  If reset != 0 the counter is cleared
- * after reading.  Returns the count (>= 0) or a negative status.
+ * gave up since the library was loaded on the current device.  Zero in
+ * correct operation.  Synchronises the device.  If reset != 0 the counter is
+ * cleared after reading.  Returns the count (>= 0) or a negative status.
  */
 int64_t gemm_bf16_sync_timeouts(int reset);
+
+/*
+ * gemm_bf16_set_sync_spin_limit: the number of unsuccessful polls after which
+ * a ring counter wait gives up, for calls made from now on (process-wide).
+ * polls == 0 restores the default (2^22 polls, about 0.3 s of waiting);
+ * polls must be at most 2^32 - 1.  Returns the previous limit, or
+ * GEMM_ERR_INVALID_VALUE.  A tiny limit makes waits give up while the data is
+ * merely late, which exercises the failure handling above on purpose; the
+ * kernels still terminate normally.
+ */
+int64_t gemm_bf16_set_sync_spin_limit(int64_t polls);
 
 #ifdef __cplusplus
 }

@@ -76,6 +76,8 @@ def library() -> ctypes.CDLL:
         lib.gemm_bf16_strerror.restype = ctypes.c_char_p
         lib.gemm_bf16_sync_timeouts.argtypes = [i32]
         lib.gemm_bf16_sync_timeouts.restype = i64
+        lib.gemm_bf16_set_sync_spin_limit.argtypes = [i64]
+        lib.gemm_bf16_set_sync_spin_limit.restype = i64
         _lib = lib
     return _lib
 
@@ -119,6 +121,13 @@ def gemm_bf16_sync_timeouts(reset: bool = False) -> int:
     n = library().gemm_bf16_sync_timeouts(int(bool(reset)))
     if n < 0:
         raise GemmError(int(n), "gemm_bf16_sync_timeouts")
+    return int(n)
+
+
+def gemm_bf16_set_sync_spin_limit(polls: int) -> int:
+    n = library().gemm_bf16_set_sync_spin_limit(int(polls))
+    if n < 0:
+        raise GemmError(int(n), "gemm_bf16_set_sync_spin_limit")
     return int(n)
 
 

@@ -84,6 +84,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 #include <utility>
@@ -110,7 +111,8 @@ constexpr uint32_t kOOB = 0x80000000u;
 constexpr uint32_t kMaxRecords = 0x7FFFFFF0u;
 // Raw buffer resource, 32-bit data format (third descriptor word for gfx9).
 constexpr int kRsrcWord3 = 0x00020000;
-// Bounded spin on ring counters: ~0.3 s at s_sleep(1) per poll.
+// Bounded spin on ring counters: ~0.3 s at s_sleep(1) per poll (the default;
+// gemm_bf16_set_sync_spin_limit changes it for later launches).
 constexpr uint32_t kSpinLimit = 1u << 22;
 
 __device__ unsigned long long g_sync_timeouts;
@@ -209,7 +211,9 @@ struct Cfg {
     static constexpr int CPR_K = BK / 8;                             // 16-byte chunks per K-contiguous row
     static constexpr int CPR_N = BN / 8;                             // chunks per row of a K x N B tile
     static constexpr int RING_BYTES = WIN ? NWIN * A_BYTES : S * STAGE_BYTES;
-    static constexpr int FLAG_BYTES = (SYNC != SYNC_BARRIER) ? 2 * S * 4 : 0;
+    // Ring counters (2 x S 32-bit words, or S 64-bit signal words) and the
+    // workgroup's poison word (SyncState), padded to 8 bytes.
+    static constexpr int FLAG_BYTES = (SYNC != SYNC_BARRIER) ? 2 * S * 4 + 8 : 0;
     // Epilogue strip per MFMA wave: 32 rows x 64 columns of bf16 when that
     // fits next to the ring (or, with windows, inside one window), else 32
     // rows x 32 columns.
@@ -258,6 +262,7 @@ struct Params {
     int32_t k_steps;                  // k-steps per work item
     int32_t group_m;
     int32_t small_span;               // A and B each span fewer than kMaxRecords bytes
+    uint32_t spin_limit;              // polls before a ring counter wait gives up
 };
 
 // Swizzles.  The LDS has 64 four-byte banks (256 bytes per cycle); a 16-byte
@@ -337,19 +342,40 @@ __device__ __forceinline__ uint32_t load_counter(const lds_u32* ctr)
     return __builtin_amdgcn_readfirstlane(v);
 }
 
-// Bounded wait until *ctr >= target.  A wait that gives up is counted and
-// sets the wave's sticky `failed` flag; once set, later waits return at once,
-// so the wave runs its (finite) loops to the end without blocking and the
-// kernel always terminates.  Results of such a launch are not meaningful.
-__device__ __forceinline__ void wait_counter(const lds_u32* ctr, uint32_t target, bool& failed)
+// A wave's state for the bounded waits on ring counters.  A wait that gives
+// up (after `limit` unsuccessful polls) is counted in g_sync_timeouts, sets
+// the wave's sticky `failed` flag -- once set, later waits return at once, so
+// the wave runs its finite loops to the end without blocking and the kernel
+// always terminates -- and sets the workgroup's poison word in LDS, waiting
+// until that write has landed.  Only after that can the wave go on to refill
+// a stage early or read one before its data landed, so any wave of the
+// workgroup that reads data corrupted by the failure reads it after the
+// poison word was set; every wave checks the word before it stores a tile
+// (poison_tile) and then writes NaN instead of values.  A workgroup's tiles
+// stored before the failure are correct; other workgroups are unaffected.
+struct SyncState {
+    bool failed = false;
+    lds_u32* poison = nullptr;   // one 32-bit LDS word per workgroup, zeroed before the first wait
+    uint32_t limit = kSpinLimit;
+};
+
+__device__ __forceinline__ void give_up(SyncState& st)
+{
+    if ((threadIdx.x & 63) == 0) {
+        atomicAdd(&g_sync_timeouts, 1ull);
+        asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(st.poison)), "v"(1u) : "memory");
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    st.failed = true;
+}
+
+// Bounded wait until *ctr >= target.
+__device__ __forceinline__ void wait_counter(const lds_u32* ctr, uint32_t target, SyncState& st)
 {
     uint32_t spins = 0;
-    while (!failed && load_counter(ctr) < target) {
-        if (++spins > kSpinLimit) {
-            if ((threadIdx.x & 63) == 0)
-                atomicAdd(&g_sync_timeouts, 1ull);
-            failed = true;
-        }
+    while (!st.failed && load_counter(ctr) < target) {
+        if (++spins > st.limit)
+            give_up(st);
         // The first polls go back to back (one LDS round trip each); a wait
         // that lasts longer sleeps between polls.
         if (spins > 8)
@@ -400,19 +426,16 @@ __device__ __forceinline__ bool pair_reached(uint64_t v, uint32_t full_target, u
 
 // Bounded like wait_counter.
 __device__ __forceinline__ void wait_pair(const lds_u64* word, uint32_t full_target, uint32_t empty_target,
-                                          bool& failed)
+                                          SyncState& st)
 {
     uint32_t spins = 0;
     for (;;) {
         uint64_t v;
         asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(word)) : "memory");
-        if (failed || pair_reached(v, full_target, empty_target))
+        if (st.failed || pair_reached(v, full_target, empty_target))
             break;
-        if (++spins > kSpinLimit) {
-            if ((threadIdx.x & 63) == 0)
-                atomicAdd(&g_sync_timeouts, 1ull);
-            failed = true;
-        }
+        if (++spins > st.limit)
+            give_up(st);
         if (spins > 8)
             __builtin_amdgcn_s_sleep(1);
     }
@@ -421,11 +444,11 @@ __device__ __forceinline__ void wait_pair(const lds_u64* word, uint32_t full_tar
 
 // Completes a read from pair_read_issue; polls on only if it came back short.
 __device__ __forceinline__ void wait_pair_issued(uint64_t v, const lds_u64* word, uint32_t full_target,
-                                                 uint32_t empty_target, bool& failed)
+                                                 uint32_t empty_target, SyncState& st)
 {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v) : : "memory");
     if (!pair_reached(v, full_target, empty_target))
-        wait_pair(word, full_target, empty_target, failed);
+        wait_pair(word, full_target, empty_target, st);
     COMPILER_FENCE();
 }
 
@@ -439,27 +462,24 @@ __device__ __forceinline__ uint32_t counter_read_issue(const lds_u32* ctr)
     return v;
 }
 
-__device__ __forceinline__ void wait_counter_issued(uint32_t v, const lds_u32* ctr, uint32_t target, bool& failed)
+__device__ __forceinline__ void wait_counter_issued(uint32_t v, const lds_u32* ctr, uint32_t target, SyncState& st)
 {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v) : : "memory");
     if ((uint32_t)__builtin_amdgcn_readfirstlane(v) < target)
-        wait_counter(ctr, target, failed);
+        wait_counter(ctr, target, st);
     COMPILER_FENCE();
 }
 
 // wait_counter for a wait that usually lasts long (a ping-pong group waiting
 // through the other group's tile): after the first polls it sleeps longer,
 // so a waiting wave takes fewer issue slots from the waves computing on its
-// SIMD.  Still bounded: kSpinLimit polls of at most 512 cycles' sleep.
-__device__ __forceinline__ void wait_counter_long(const lds_u32* ctr, uint32_t target, bool& failed)
+// SIMD.  Still bounded: st.limit polls of at most 512 cycles' sleep.
+__device__ __forceinline__ void wait_counter_long(const lds_u32* ctr, uint32_t target, SyncState& st)
 {
     uint32_t spins = 0;
-    while (!failed && load_counter(ctr) < target) {
-        if (++spins > kSpinLimit) {
-            if ((threadIdx.x & 63) == 0)
-                atomicAdd(&g_sync_timeouts, 1ull);
-            failed = true;
-        }
+    while (!st.failed && load_counter(ctr) < target) {
+        if (++spins > st.limit)
+            give_up(st);
         if (spins > 64)
             __builtin_amdgcn_s_sleep(8);
         else if (spins > 8)
@@ -1360,6 +1380,25 @@ __global__ void __launch_bounds__(256) k_reduce_splits(Params p)
     }
 }
 
+// Before a tile is stored: if this wave gave up a ring wait, or another wave
+// of the workgroup did (the poison word, see SyncState), every element of the
+// wave's part of the tile becomes NaN, so the output shows where it cannot be
+// trusted.  A uniform branch; the LDS read costs one round trip per tile.
+template <class C>
+__device__ __forceinline__ void poison_tile(typename C::Acc (&acc)[C::FM][C::FN], const SyncState& st)
+{
+    if (st.failed || load_counter(st.poison) != 0u) {
+        const float nan = __builtin_nanf("");
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                for (int r = 0; r < (int)(sizeof(typename C::Acc) / sizeof(float)); ++r)
+                    acc[i][j][r] = nan;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Kernel: every wave loads and computes (GEMM_SYNC_BARRIER, GEMM_SYNC_FLAGS).
 // ---------------------------------------------------------------------------
@@ -1375,9 +1414,12 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
     static_assert(C::FLAG_OFFSET % 8 == 0, "64-bit signal words");
     lds_u64* sig = (lds_u64*)(smem + C::FLAG_OFFSET);
 
+    lds_u32* poison = (lds_u32*)(sig + C::S);
     if constexpr (C::SYNC == SYNC_FLAGS) {
         if (threadIdx.x < C::S)
             sig[threadIdx.x] = 0ull;
+        if (threadIdx.x == 0)
+            *poison = 0u;
     }
     __syncthreads();   // counters are initialised before any wave can arrive
 
@@ -1403,7 +1445,9 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
     // c + S - 1 refills), and its generation gen = c / S.
     int s_cur = 0, s_prev = C::S - 1;
     uint32_t gen = 0;
-    bool failed = false;
+    SyncState st;
+    st.poison = poison;
+    st.limit = p.spin_limit;
 
     // Make position c + 1 (stage s_nxt, generation g_nxt) readable.  This
     // wave's DMA groups for positions c+1 .. c+S-1 are outstanding (S-1
@@ -1420,7 +1464,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
             block_barrier();
         } else {
             arrive_pair(sig + s_nxt, kAnnounce);
-            wait_pair_issued(pair_read_issue(sig + s_nxt), sig + s_nxt, (g_nxt + 1) * C::NW, 0u, failed);
+            wait_pair_issued(pair_read_issue(sig + s_nxt), sig + s_nxt, (g_nxt + 1) * C::NW, 0u, st);
         }
     };
 
@@ -1528,7 +1572,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
                         __builtin_amdgcn_sched_barrier(0);
                         region_mfma<C, kk, 1, PRE>(acc, fr);
                         __builtin_amdgcn_sched_barrier(0);
-                        wait_pair_issued(v, sig + s_nxt, (g_nxt + 1) * C::NW, (gen + 1) * C::NW, failed);
+                        wait_pair_issued(v, sig + s_nxt, (g_nxt + 1) * C::NW, (gen + 1) * C::NW, st);
                     } else {
                         region_mfma<C, kk, 0, PRE>(acc, fr);
                         __builtin_amdgcn_sched_barrier(0);
@@ -1558,6 +1602,8 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
             s_cur = s_nxt;
             gen = g_nxt;
         }
+        if constexpr (C::SYNC == SYNC_FLAGS)
+            poison_tile<C>(acc, st);
         if (p.splits > 1)
             store_partial<C>(p, acc, sp * p.span + u, wm, wn, lane);
         else
@@ -1706,7 +1752,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_win(Params p)
 // ---------------------------------------------------------------------------
 template <class C>
 __device__ __forceinline__ void producer_loop(const Params& p, lds_char* smem, lds_u32* full, lds_u32* empty,
-                                              int32_t n_tiles, int lw, int lane)
+                                              int32_t n_tiles, int lw, int lane, SyncState& st)
 {
     const int32_t total = n_tiles * p.k_steps;
     // Loader wave: one flat loop over (tile, k-step) positions.  The data
@@ -1719,13 +1765,12 @@ __device__ __forceinline__ void producer_loop(const Params& p, lds_char* smem, l
     constexpr int D = (C::S - 2 < 2) ? C::S - 2 : 2;
     Loader<C, false> ld;
     ld.init(p, n_tiles, lw, lane);
-    bool failed = false;
     for (int32_t q = 0; q < total; ++q) {
         const int s = q % C::S;
         // Each use of a stage is released by the NCWG MFMA waves of the one
         // group that computes the position.
         if (q >= C::S)
-            wait_counter(empty + s, (uint32_t)(q / C::S) * C::NCWG, failed);
+            wait_counter(empty + s, (uint32_t)(q / C::S) * C::NCWG, st);
         ld.issue_next(p, smem + s * C::STAGE_BYTES, lw, lane);
         if (q >= D) {
             wait_vmcnt<C::LOADS * D>();
@@ -1752,7 +1797,7 @@ template <class C>
 __device__ __forceinline__ void consumer_last_kstep(typename C::Acc (&acc)[C::FM][C::FN], Frags<C> (&fr)[2],
                                                     lds_u32* empty_cur, const lds_u32* full_next,
                                                     uint32_t next_target, bool has_next, const lds_char* next_stage,
-                                                    int wm, int wn, int lane, bool& failed)
+                                                    int wm, int wn, int lane, SyncState& st)
 {
     constexpr int M = region_mfmas<C>();
     constexpr int PRE = (C::MF == 16) ? M / 2 : (M > 4) ? M - 3 : M / 2;
@@ -1762,7 +1807,7 @@ __device__ __forceinline__ void consumer_last_kstep(typename C::Acc (&acc)[C::FM
     __builtin_amdgcn_sched_barrier(0);
     region_mfma<C, C::KK - 1, 0, PRE>(acc, fr);
     __builtin_amdgcn_sched_barrier(0);
-    wait_counter_issued(v, full_next, has_next ? next_target : 0u, failed);
+    wait_counter_issued(v, full_next, has_next ? next_target : 0u, st);
     if (has_next)
         read_frags<C>(fr[0], next_stage, wm, wn, lane, 0);
     region_mfma<C, C::KK - 1, PRE, M>(acc, fr);
@@ -1782,9 +1827,12 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     lds_u32* full = (lds_u32*)(smem + C::FLAG_OFFSET);
     lds_u32* empty = full + C::S;
-    if (threadIdx.x < 2 * C::S)
-        full[threadIdx.x] = 0u;
+    if (threadIdx.x < 2 * C::S + 1)
+        full[threadIdx.x] = 0u;   // full[], empty[] and the poison word
     __syncthreads();   // counters are initialised before the roles split
+    SyncState st;
+    st.poison = full + 2 * C::S;
+    st.limit = p.spin_limit;
 
     const int32_t G = gridDim.x, b = blockIdx.x;
     const int32_t n_tiles = (b < p.tiles) ? (p.tiles - 1 - b) / G + 1 : 0;
@@ -1792,7 +1840,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
     const int32_t total = n_tiles * KT;
 
     if (w >= C::NCW) {
-        producer_loop<C>(p, smem, full, empty, n_tiles, w - C::NCW, lane);
+        producer_loop<C>(p, smem, full, empty, n_tiles, w - C::NCW, lane, st);
         return;
     }
 
@@ -1802,8 +1850,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
     Frags<C> fr[2];
     if (total == 0)
         return;
-    bool failed = false;
-    wait_counter(full, (uint32_t)C::NP, failed);
+    wait_counter(full, (uint32_t)C::NP, st);
     read_frags<C>(fr[0], smem, wm, wn, lane, 0);
 
     int32_t c = 0;
@@ -1836,7 +1883,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
                     const int s1 = (c + 1) % C::S;
                     consumer_last_kstep<C>(acc, fr, empty + c % C::S, full + s1,
                                            (uint32_t)((c + 1) / C::S + 1) * C::NP, c + 1 < total,
-                                           smem + s1 * C::STAGE_BYTES, wm, wn, lane, failed);
+                                           smem + s1 * C::STAGE_BYTES, wm, wn, lane, st);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             };
@@ -1844,6 +1891,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
                 (region.template operator()<KS>(), ...);
             }(std::make_integer_sequence<int, C::KK>{});
         }
+        poison_tile<C>(acc, st);
         if (p.splits > 1)
             store_partial<C>(p, acc, sp * p.span + u, wm, wn, lane);
         else
@@ -1875,16 +1923,19 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_pp(Params p)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     lds_u32* full = (lds_u32*)(smem + C::FLAG_OFFSET);
     lds_u32* empty = full + C::S;
-    if (threadIdx.x < 2 * C::S)
-        full[threadIdx.x] = 0u;
+    if (threadIdx.x < 2 * C::S + 1)
+        full[threadIdx.x] = 0u;   // full[], empty[] and the poison word
     __syncthreads();   // counters are initialised before the roles split
+    SyncState st;
+    st.poison = full + 2 * C::S;
+    st.limit = p.spin_limit;
 
     const int32_t G = gridDim.x, b = blockIdx.x;
     const int32_t n_tiles = (b < p.tiles) ? (p.tiles - 1 - b) / G + 1 : 0;
     const int32_t KT = p.k_steps;
 
     if (w >= C::NCW) {
-        producer_loop<C>(p, smem, full, empty, n_tiles, w - C::NCW, lane);
+        producer_loop<C>(p, smem, full, empty, n_tiles, w - C::NCW, lane, st);
         return;
     }
 
@@ -1894,13 +1945,12 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_pp(Params p)
     lds_char* strip = smem + C::EPI_OFFSET + w * C::EPI_WAVE_BYTES;
     auto stage_of = [&](int32_t q) { return smem + (q % C::S) * C::STAGE_BYTES; };
     Frags<C> fr[2];
-    bool failed = false;
     for (int32_t it = g; it < n_tiles; it += 2) {
         int32_t tm, tn;
         int32_t sp, u;
         tile_coords(p, b + it * G, G, tm, tn, sp, u);
         int32_t c = it * KT;
-        wait_counter_long(full + c % C::S, (uint32_t)(c / C::S + 1) * C::NP, failed);
+        wait_counter_long(full + c % C::S, (uint32_t)(c / C::S + 1) * C::NP, st);
         read_frags<C>(fr[0], stage_of(c), wm, wn, lane, 0);
         typename C::Acc acc[C::FM][C::FN];
 #pragma unroll
@@ -1925,7 +1975,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_pp(Params p)
                     // tile's first position is waited for after the epilogue.
                     consumer_last_kstep<C>(acc, fr, empty + c % C::S, full + (c + 1) % C::S,
                                            (uint32_t)((c + 1) / C::S + 1) * C::NP, kt + 1 < KT, stage_of(c + 1),
-                                           wm, wn, lane, failed);
+                                           wm, wn, lane, st);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             };
@@ -1933,6 +1983,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_pp(Params p)
                 (region.template operator()<KS>(), ...);
             }(std::make_integer_sequence<int, C::KK>{});
         }
+        poison_tile<C>(acc, st);
         if (p.splits > 1)
             store_partial<C>(p, acc, sp * p.span + u, wm, wn, lane);
         else
@@ -2123,6 +2174,9 @@ struct DeviceInfo {
     // taken: the allocation-free entry point then returns GEMM_ERR_DEVICE).
     char* scratch_ptr = nullptr;
 };
+
+// Polls before a ring counter wait gives up, for every launch from now on.
+std::atomic<uint32_t> g_spin_limit{kSpinLimit};
 
 constexpr int kMaxDevices = 64;
 std::mutex g_dev_mutex;
@@ -2530,6 +2584,7 @@ int gemm_direct(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
     p.small_span = span_bytes(M, K, lda) < (int64_t)kMaxRecords &&
                    (bt ? span_bytes(N, K, ldb) : span_bytes(K, N, ldb)) < (int64_t)kMaxRecords;
     p.partial = nullptr;
+    p.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     const int64_t grid = pl.grid;
     if (p.splits == 1 && pl.tail_tiles == 0)
         return with_cfg(sync_mode, pl.stages, bt, [&]<class C>() { return launch<C>(p, grid, s); });
@@ -2638,6 +2693,13 @@ const char* gemm_bf16_strerror(int status)
                "(GEMM_NOALLOC_SCRATCH_BYTES) holds";
     default: return "unknown status";
     }
+}
+
+int64_t gemm_bf16_set_sync_spin_limit(int64_t polls)
+{
+    if (polls < 0 || polls > (int64_t)UINT32_MAX)
+        return GEMM_ERR_INVALID_VALUE;
+    return (int64_t)g_spin_limit.exchange(polls == 0 ? kSpinLimit : (uint32_t)polls);
 }
 
 int64_t gemm_bf16_sync_timeouts(int reset)

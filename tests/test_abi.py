@@ -164,3 +164,17 @@ def test_noalloc_scratch_limit_is_declared():
                 for (M, N, K) in ((256, 256, 1 << 16), (1024, 1024, 32768), (4352, 4352, 4096), (256, 4096, 1 << 15))
                 for bt in (0, 1) for sy in (0, 1, 2, 3) for st in (0, 2, 3, 4))
     assert 0 < worst <= bd.GEMM_NOALLOC_SCRATCH_BYTES == 256 * 256 * 256 * 4
+
+
+def test_sync_spin_limit_setting_needs_no_device():
+    prev = bd.gemm_bf16_set_sync_spin_limit(1000)
+    try:
+        assert bd.gemm_bf16_set_sync_spin_limit(7) == 1000
+        assert bd.gemm_bf16_set_sync_spin_limit(0) == 7           # 0 restores the default
+        assert bd.gemm_bf16_set_sync_spin_limit(0) == 1 << 22
+        for bad in (-1, 1 << 32):
+            with pytest.raises(bd.GemmError) as e:
+                bd.gemm_bf16_set_sync_spin_limit(bad)
+            assert e.value.code == bd.GEMM_ERR_INVALID_VALUE
+    finally:
+        bd.gemm_bf16_set_sync_spin_limit(prev if prev != 1000 else 0)

@@ -82,7 +82,10 @@ class Wave:
         self.done = False
 
 
-def run(ring, waves, seed, max_steps=200000):
+def run(ring, waves, seed, max_steps=200000, idle_polls=0):
+    """idle_polls: when no wave can move, re-evaluate the waits up to this many
+    times before declaring a deadlock (time passes for waits that poll with a
+    budget; unbounded waits never change their answer)."""
     rng = random.Random(seed)
     for w in waves:
         w.cond = None
@@ -96,6 +99,10 @@ def run(ring, waves, seed, max_steps=200000):
         if not live and not landable:
             return
         runnable = [w for w in live if w.cond is None or w.cond()]
+        for _ in range(idle_polls):
+            if runnable or landable:
+                break
+            runnable = [w for w in live if w.cond is None or w.cond()]
         choices = [("run", w) for w in runnable] + [("land", w) for w in landable]
         if not choices:
             raise Deadlock("no wave can move: %s" % [(w.wid, w.done) for w in waves])
@@ -495,3 +502,195 @@ def test_fault_window_load_wait_misses_next_b():
 
 def test_fault_window_refill_before_barrier():
     assert caught(lambda sd: run_windows(4, 3, 3, sd, early_refill=True))
+
+
+# --- bounded waits: a failure terminates and is visible -------------------------
+# The kernels' waits on ring counters give up after a bounded number of polls.
+# A wave that gives up sets the workgroup's poison word before its next step,
+# then runs its loops to the end; before storing a tile, every wave checks the
+# word (and its own failure) and writes NaN instead of values.  The model below
+# gives waits a budget of scheduler evaluations; with a fault that makes a
+# counter fall short for good, it checks that every wave finishes and that
+# every tile whose reads saw data the failure let through -- a stage read
+# before all of its loads landed, or a load landing in a stage being read -- is
+# stored flagged.  Without a failure nothing is flagged.
+class BoundedRing(Ring):
+    def __init__(self, S, parts):
+        super().__init__(S, parts)
+        self.poison = False
+        self.timeouts = 0
+        self.tile_of = {}               # wave -> tile it is computing
+        self.corrupt = set()            # (wave, tile) whose reads saw bad data
+        self.stores = []                # (wave, tile, flagged)
+
+    def _taint(self, s):
+        if not self.poison:
+            return False
+        for r in self.readers[s]:
+            self.corrupt.add((r, self.tile_of.get(r)))
+        return True
+
+    def issue(self, s, q):
+        if self.readers[s] and self._taint(s):
+            return
+        super().issue(s, q)
+
+    def land(self, s, part, q):
+        if self.readers[s] and self._taint(s):
+            self.landed[s][part] = q
+            return
+        super().land(s, part, q)
+
+    def begin_read(self, w, s, q):
+        have = self.landed[s]
+        if self.poison and (len(have) != self.parts or any(v != q for v in have.values())):
+            self.corrupt.add((w, self.tile_of.get(w)))
+            self.readers[s].add(w)
+            self.reads.setdefault(q, set()).add(w)
+            return
+        super().begin_read(w, s, q)
+
+
+def bounded(ring, wave, cond, limit):
+    """A wait that gives up after `limit` evaluations: the wave's failure
+    flag and the workgroup's poison word are set before it continues; a wave
+    that has failed does not wait any more."""
+    state = {"polls": 0}
+
+    def check():
+        if wave.failed or cond():
+            return True
+        state["polls"] += 1
+        if state["polls"] > limit:
+            wave.failed = True
+            ring.poison = True
+            ring.timeouts += 1
+            return True
+        return False
+    return check
+
+
+def bounded_loader(ring, wave, part, total, S, D, releasers, limit, lose=None):
+    """The loader of `loader` with bounded waits.  lose = position whose
+    announcement this loader never makes (the injected fault)."""
+    for q in range(total):
+        s = q % S
+        if q >= S:
+            yield bounded(ring, wave, at_least(ring.empty, s, (q // S) * releasers), limit)
+        ring.issue(s, q)
+        wave.inflight.append((s, part, q))
+        yield None
+        if q >= D:
+            yield vm_wait(wave, D)
+            if q - D != lose:
+                ring.full[(q - D) % S] += 1
+            yield None
+    yield vm_wait(wave, 0)
+    for q in range(max(total - D, 0), total):
+        if q != lose:
+            ring.full[q % S] += 1
+        yield None
+
+
+def bounded_consumer(ring, wave, tiles, KT, S, NP, limit, use_poison=True):
+    for t in tiles:
+        ring.tile_of[wave.wid] = t
+        for q in range(t * KT, (t + 1) * KT):
+            s = q % S
+            yield bounded(ring, wave, at_least(ring.full, s, (q // S + 1) * NP), limit)
+            ring.begin_read(wave.wid, s, q)
+            yield None
+            yield None
+            ring.end_read(wave.wid, s)
+            ring.empty[s] += 1
+            yield None
+        # the store: poison_tile checks the wave's flag and the poison word
+        ring.stores.append((wave.wid, t, wave.failed or (use_poison and ring.poison)))
+        yield None
+
+
+def run_bounded(S, NP, NCWG, groups, n_tiles, KT, seed, limit=30, lose=None, lose_part=0, use_poison=True,
+                loader_limit=None):
+    total = n_tiles * KT
+    ring = BoundedRing(S, NP)
+    D = min(S - 2, 2)
+    waves = []
+    for g in range(groups):
+        for i in range(NCWG):
+            wv = Wave(len(waves), None)
+            wv.failed = False
+            wv.gen = bounded_consumer(ring, wv, list(range(g, n_tiles, groups)), KT, S, NP, limit, use_poison)
+            waves.append(wv)
+    for part in range(NP):
+        wv = Wave(len(waves), None)
+        wv.failed = False
+        wv.gen = bounded_loader(ring, wv, part, total, S, D, NCWG, limit if loader_limit is None else loader_limit,
+                                lose if part == lose_part else None)
+        waves.append(wv)
+    run(ring, waves, seed, idle_polls=min(max(limit, loader_limit or 0) + 2, 10 ** 4))   # Deadlock if stuck
+    for w, t in ring.corrupt:
+        assert (w, t, True) in ring.stores, ("tile computed from bad data stored unflagged", w, t)
+    assert len(ring.stores) == NCWG * n_tiles
+    return ring
+
+
+@pytest.mark.parametrize("S", [2, 3, 4])
+@pytest.mark.parametrize("groups", [1, 2], ids=["wavespec", "pingpong"])
+def test_bounded_waits_without_failure_flag_nothing(S, groups):
+    """Generous budgets: no wait gives up, nothing is flagged, and the run
+    is the unbounded protocol's."""
+    for seed in SEEDS:
+        ring = run_bounded(S, 4, 4, groups, 4, 5, seed, limit=10 ** 6)
+        assert ring.timeouts == 0 and not ring.poison
+        assert not ring.corrupt and not any(f for _, _, f in ring.stores)
+
+
+@pytest.mark.parametrize("S", [2, 3, 4])
+@pytest.mark.parametrize("groups", [1, 2], ids=["wavespec", "pingpong"])
+def test_lost_announcement_terminates_and_is_flagged(S, groups):
+    """One loader never announces position 6: the consumers' waits for it
+    give up instead of hanging, every wave finishes, the failure is counted
+    and poisoned, and every tile whose reads saw bad data is stored flagged."""
+    for seed in SEEDS:
+        ring = run_bounded(S, 4, 4, groups, 4, 5, seed, limit=30, lose=6)
+        assert ring.timeouts > 0 and ring.poison
+        # the tile that needed position 6 is flagged by every one of its waves
+        t6 = 6 // 5
+        owners = [w for w in range(4 * groups) if (w // 4) == t6 % groups]
+        for w in owners:
+            assert (w, t6, True) in ring.stores
+
+
+def test_lost_announcement_without_bounds_hangs():
+    """The same fault with unbounded waits: no wave can move (what the bound
+    turns into a flagged result)."""
+    assert caught(lambda sd: run_bounded(3, 4, 4, 1, 4, 5, sd, limit=10 ** 9, lose=6))
+
+
+def test_tight_budget_flags_every_tile_it_corrupts():
+    """Budgets so small that waits give up while data is merely late (what the
+    library's spin-limit setting forces on the GPU): whatever is read too
+    early or overwritten while read, the tiles it feeds are stored flagged."""
+    seen = 0
+    for seed in range(40):
+        ring = run_bounded(3, 4, 4, 2, 4, 5, seed, limit=1)
+        seen += len(ring.corrupt) > 0
+    assert seen > 0
+
+
+def test_fault_flagging_by_own_failure_only():
+    """Without the shared poison word a wave flags only what it computed after
+    its own failure; a loader's failure then corrupts MFMA waves that never
+    failed themselves, and their tiles go out unflagged."""
+    assert caught(lambda sd: run_bounded(3, 4, 4, 2, 4, 5, sd, limit=10 ** 3, loader_limit=1, use_poison=False),
+                  seeds=range(60))
+
+
+def test_loader_failure_is_flagged_through_the_poison_word():
+    """The same loader-only failures with the poison word in place: every
+    corrupted tile is stored flagged."""
+    seen = 0
+    for seed in range(60):
+        ring = run_bounded(3, 4, 4, 2, 4, 5, seed, limit=10 ** 3, loader_limit=1)
+        seen += len(ring.corrupt) > 0
+    assert seen > 0
