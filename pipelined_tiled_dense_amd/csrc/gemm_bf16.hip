@@ -278,6 +278,40 @@ __device__ __forceinline__ int swz_k(int row)
 {
     return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
 }
+
+// K-contiguous tiles with 32-wide k-steps read by 16 x 16 x 32 MFMAs.  A
+// fragment read then covers one 16-row x 64-byte block (1 KiB, the span of one
+// DMA instruction): lane l (bits l5..l0) takes row r = l % 16 and chunk
+// h = l / 16.  With 64-byte rows the bank window of a row is set by the row's
+// place in the block, so XORing the chunk alone left 2-way conflicts under
+// the LDS's grouping of lanes into cycles (measured: half of all LDS cycles
+// were conflict stalls, with or without the DMA running; the 64-wide swizzle
+// above measures conflict-free).  So the rows of each block are permuted as
+// well: row r (bits r3..r0) goes to the 64-byte segment
+//     seg(r) = (r2, r1, r3, r0)
+// and its chunk h to position h ^ (r2, r1) in the segment.  The bank slot of
+// a read is then (r3, r0, h1 ^ r2, h0 ^ r1), which spreads the lanes of every
+// cycle over distinct slots for every grouping of lanes under which the
+// 64-wide swizzle is conflict-free.  A row keeps its 4 chunks in one 64-byte
+// segment, so each DMA instruction still fetches whole 64-byte row pieces.
+__device__ __forceinline__ int kperm_seg(int r)
+{
+    return (r & 1) | (((r >> 3) & 1) << 1) | (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 3);
+}
+
+// Inverse of kperm_seg: the row held in segment k.
+__device__ __forceinline__ int kperm_row(int k)
+{
+    return (k & 1) | (((k >> 2) & 1) << 1) | (((k >> 3) & 1) << 2) | (((k >> 1) & 1) << 3);
+}
+
+// The 16-byte slot, within its block, of reading lane l's (row, chunk).
+__device__ __forceinline__ int kperm_slot(int l)
+{
+    const int r = l & 15;
+    return kperm_seg(r) * 4 + ((l >> 4) ^ ((r >> 1) & 3));
+}
+
 // K x N tiles of B hold rows of BN elements (512 or 256 bytes, so every row
 // starts on the same bank).  With 32 x 32 blocks a transposing read has lanes
 // 0..31 on 4 consecutive k-rows x 4 chunks; XORing chunk bits 2-3 with
@@ -572,11 +606,25 @@ struct Loader {
     const char* b_end;
 
     __device__ __forceinline__ static int slot(int t, int lw, int lane) { return (t * C::NLW + lw) * 64 + lane; }
+    // K-contiguous tiles with 32-wide k-steps and 16 x 16 blocks permute the
+    // rows of each 1 KiB block as well as their chunks (kperm_seg); otherwise
+    // rows stay in place and only the chunk is swizzled.
+    static constexpr bool KPERM = C::MF == 16 && C::BK == 32;
+    // Logical row (within the tile) of a K-contiguous slot.
+    __device__ __forceinline__ static int krow(int s)
+    {
+        if constexpr (KPERM)
+            return (s >> 6) * 16 + kperm_row((s & 63) >> 2);
+        else
+            return s / C::CPR_K;
+    }
     // Logical k offset (elements) of a K-contiguous slot.
     __device__ __forceinline__ static int kofs_k(int s)
     {
-        const int row = s / C::CPR_K;
-        return ((s % C::CPR_K) ^ swz_k<C::BK>(row)) * 8;
+        if constexpr (KPERM)
+            return ((s & 3) ^ (((s & 63) >> 4) & 3)) * 8;
+        else
+            return ((s % C::CPR_K) ^ swz_k<C::BK>(s / C::CPR_K)) * 8;
     }
     // Logical column offset (elements) of a slot in a K x N tile of B.
     __device__ __forceinline__ static int nofs_n(int s)
@@ -591,13 +639,13 @@ struct Loader {
 #pragma unroll
         for (int t = 0; t < C::A_LOADS; ++t) {
             const int s = slot(t, lw, lane);
-            voffA[t] = (uint32_t)(s / C::CPR_K) * lda2 + (uint32_t)kofs_k(s) * 2u;
+            voffA[t] = (uint32_t)krow(s) * lda2 + (uint32_t)kofs_k(s) * 2u;
         }
 #pragma unroll
         for (int t = 0; t < C::B_LOADS; ++t) {
             const int s = slot(t, lw, lane);
             if constexpr (C::BT)
-                voffB[t] = (uint32_t)(s / C::CPR_K) * ldb2 + (uint32_t)kofs_k(s) * 2u;
+                voffB[t] = (uint32_t)krow(s) * ldb2 + (uint32_t)kofs_k(s) * 2u;
             else
                 voffB[t] = (uint32_t)(s / C::CPR_N) * ldb2 + (uint32_t)nofs_n(s) * 2u;
         }
@@ -807,10 +855,14 @@ struct FragReader {
     {
         if constexpr (C::MF == 16) {
             const int h = lane >> 4, r16 = lane & 15;
-            const uint32_t xk = (uint32_t)(((4 * kk + h) ^ swz_k<C::BK>(r16)) << 4);
-            a_off = opaque((uint32_t)((wm * C::TM + r16) * (C::BK * 2)) + xk);
+            // 64-wide k-steps: row r16 in place, chunk swizzled; 32-wide: the
+            // lane's (row, chunk) at kperm_slot(lane) of the 1 KiB block.
+            const uint32_t in_block = (C::BK == 32) ? (uint32_t)kperm_slot(lane) << 4
+                                                     : (uint32_t)(r16 * (C::BK * 2)) +
+                                                           (uint32_t)(((4 * kk + h) ^ swz_k<C::BK>(r16)) << 4);
+            a_off = opaque((uint32_t)(wm * C::TM * (C::BK * 2)) + in_block);
             if constexpr (C::BT) {
-                b_off = opaque((uint32_t)((wn * C::TN + r16) * (C::BK * 2)) + xk);
+                b_off = opaque((uint32_t)(wn * C::TN * (C::BK * 2)) + in_block);
                 r = 0;
             } else {
                 const int q = r16 & 3, rr = r16 >> 2;
