@@ -425,15 +425,17 @@ def _ceiling_lib():
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "pipelined_tiled_dense_amd", "libgemm_probes.so"))
     lib.gemm_probe_mfma_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
-                                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p]
     lib.gemm_probe_mfma_ceiling.restype = ctypes.c_int
     return lib
 
 
-def _ceiling_call(torch, lib, variant, data, sink):
+def _ceiling_call(torch, lib, variant, data, sink, stamps=None):
     waves, from_lds, _ = CEILING_VARIANTS[variant]
     rc = lib.gemm_probe_mfma_ceiling(data.data_ptr(), data.numel(), from_lds, waves, CEILING_ITERS, CEILING_BLOCKS,
-                                     sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+                                     sink.data_ptr(), stamps.data_ptr() if stamps is not None else None,
+                                     torch.cuda.current_stream().cuda_stream)
     if rc != 0:
         raise RuntimeError("gemm_probe_mfma_ceiling failed: %d" % rc)
 
@@ -454,6 +456,8 @@ def mfma_ceiling(torch, steps=20):
     rand, zero, sink = _ceiling_data(torch)
     flop = float(CEILING_BLOCKS) * (1 << 23) * CEILING_ITERS
     stream = torch.cuda.current_stream()
+    stamps = torch.zeros((steps, CEILING_BLOCKS, 2), dtype=torch.int64, device="cuda")
+    rt_hz = wall_clock_hz(torch)
     out = {}
     for name, (_, _, zero_data) in CEILING_VARIANTS.items():
         data = zero if zero_data else rand
@@ -463,12 +467,16 @@ def mfma_ceiling(torch, steps=20):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
         for i in range(steps):
             ev[2 * i].record(stream)
-            _ceiling_call(torch, lib, name, data, sink)
+            _ceiling_call(torch, lib, name, data, sink, stamps[i])
             ev[2 * i + 1].record(stream)
         torch.cuda.synchronize()
         ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / steps
         tf = flop / (ms * 1e-3) / 1e12
-        e = {"tflops": round(tf, 1), "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "ms": round(ms, 4)}
+        st = stamps.double().sum(dim=(0, 1))
+        clock = float(st[0] / st[1]) * rt_hz / 1e9 if float(st[1]) > 0 else None
+        e = {"tflops": round(tf, 1), "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "ms": round(ms, 4),
+             "clock_ghz_memtime": round(clock, 3) if clock else None,
+             "mfma_busy_at_that_clock": round(tf * 1e12 / (FLOP_PER_CLK_GPU * clock * 1e9), 3) if clock else None}
         cnt = counters_for("ceiling", name)
         if cnt and cnt.get("clock_ghz"):
             e["counter_clock_ghz"] = cnt["clock_ghz"]
@@ -477,6 +485,16 @@ def mfma_ceiling(torch, steps=20):
     out["note"] = ("MFMA-only loop of 16x16x32 bf16 at the GEMM kernels' wave shapes, 256 workgroups, no global "
                    "memory traffic; random uniform[-1,1) bf16 operands unless named zero_data")
     return out
+
+
+def wall_clock_hz(torch):
+    """Tick rate of s_memrealtime (the device's constant-rate wall clock)."""
+    import ctypes
+    lib = _ceiling_lib()
+    lib.gemm_probe_wall_clock_hz.argtypes = []
+    lib.gemm_probe_wall_clock_hz.restype = ctypes.c_int64
+    hz = lib.gemm_probe_wall_clock_hz()
+    return float(hz) if hz > 0 else 100e6
 
 
 def cpu_baseline(w, A, B, target_s):

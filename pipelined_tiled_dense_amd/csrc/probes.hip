@@ -205,8 +205,12 @@ constexpr int kCeilVecs = 8192;   // 128 KiB of 16-byte fragments
 
 template <bool FROM_LDS, int NW, int FN>
 __global__ void __launch_bounds__(NW * 64) k_mfma_ceiling(const bf16x8_t* __restrict__ data, int n_vec, int iters,
-                                                          float* __restrict__ sink)
+                                                          float* __restrict__ sink, uint64_t* __restrict__ stamps)
 {
+    // Shader-clock and constant-rate timestamps at the start and the end of
+    // the workgroup (s_memtime, s_memrealtime): their ratio over many
+    // workgroups gives the clock the loop ran at, without a profiler.
+    const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
     static_assert(NW * FN == 32, "2^23 FLOP per workgroup-iteration");
     constexpr int NF = 8 + FN;                 // fragments per k-step
     __shared__ bf16x8_t lds[kCeilVecs];
@@ -269,6 +273,11 @@ __global__ void __launch_bounds__(NW * 64) k_mfma_ceiling(const bf16x8_t* __rest
         for (int j = 0; j < FN; ++j)
             sum += acc[i][j][0] + acc[i][j][1] + acc[i][j][2] + acc[i][j][3];
     sink[(int64_t)blockIdx.x * NW * 64 + t] = sum;
+    if (stamps && t == 0) {
+        const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+        stamps[2 * blockIdx.x] = c1 - c0;
+        stamps[2 * blockIdx.x + 1] = r1 - r0;
+    }
 }
 
 int launch_status()
@@ -351,12 +360,13 @@ int gemm_probe_cvt_bf16(const float* in, uint16_t* out, int64_t n, void* stream)
 }
 
 // data: n_elems bf16 values (n_elems a positive multiple of 8, below 2^34);
-// sink: blocks * 512 floats.  Launches `blocks` workgroups, each running
-// `iters` iterations of two 32-wide k-steps: 2^23 * iters FLOP per workgroup.
-// waves = 8: 8 waves of 128 x 64 (the all-wave kernels' layout); waves = 4:
-// 4 waves of 128 x 128.
+// sink: blocks * 512 floats; stamps: null, or 2 * blocks 64-bit words that
+// receive each workgroup's elapsed s_memtime and s_memrealtime ticks.
+// Launches `blocks` workgroups, each running `iters` iterations of two
+// 32-wide k-steps: 2^23 * iters FLOP per workgroup.  waves = 8: 8 waves of
+// 128 x 64 (the all-wave kernels' layout); waves = 4: 4 waves of 128 x 128.
 int gemm_probe_mfma_ceiling(const uint16_t* data, int64_t n_elems, int from_lds, int waves, int iters, int blocks,
-                            float* sink, void* stream)
+                            float* sink, uint64_t* stamps, void* stream)
 {
     if (!data || !sink || n_elems < 8 || n_elems % 8 != 0 || n_elems / 8 > ((int64_t)1 << 31) - 1 ||
         iters < 1 || iters > (1 << 20) || blocks < 1 || blocks > 65536 || (waves != 4 && waves != 8))
@@ -365,14 +375,24 @@ int gemm_probe_mfma_ceiling(const uint16_t* data, int64_t n_elems, int from_lds,
     const hipStream_t s = (hipStream_t)stream;
     const bf16x8_t* d = (const bf16x8_t*)data;
     if (waves == 8 && from_lds)
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<true, 8, 4>), dim3(blocks), dim3(512), 0, s, d, n_vec, iters, sink);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<true, 8, 4>), dim3(blocks), dim3(512), 0, s, d, n_vec, iters, sink, stamps);
     else if (waves == 8)
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<false, 8, 4>), dim3(blocks), dim3(512), 0, s, d, n_vec, iters, sink);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<false, 8, 4>), dim3(blocks), dim3(512), 0, s, d, n_vec, iters, sink, stamps);
     else if (from_lds)
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<true, 4, 8>), dim3(blocks), dim3(256), 0, s, d, n_vec, iters, sink);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<true, 4, 8>), dim3(blocks), dim3(256), 0, s, d, n_vec, iters, sink, stamps);
     else
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<false, 4, 8>), dim3(blocks), dim3(256), 0, s, d, n_vec, iters, sink);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<false, 4, 8>), dim3(blocks), dim3(256), 0, s, d, n_vec, iters, sink, stamps);
     return launch_status();
+}
+
+// Tick rate of s_memrealtime on the current device, in Hz (0 on error).
+int64_t gemm_probe_wall_clock_hz(void)
+{
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+        return 0;
+    return (int64_t)khz * 1000;
 }
 
 }  // extern "C"

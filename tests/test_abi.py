@@ -60,7 +60,8 @@ def test_library_has_no_oracle_dependency():
 def test_probe_library_exports():
     syms = exported(os.path.join(PKG, "libgemm_probes.so"))
     for n in ("gemm_probe_lds_dma", "gemm_probe_buffer_oob", "gemm_probe_mfma", "gemm_probe_mfma16",
-              "gemm_probe_ds_read_tr", "gemm_probe_cvt_bf16", "gemm_probe_buffer_soffset"):
+              "gemm_probe_ds_read_tr", "gemm_probe_cvt_bf16", "gemm_probe_buffer_soffset",
+              "gemm_probe_mfma_ceiling", "gemm_probe_wall_clock_hz"):
         assert n in syms
 
 
