@@ -126,3 +126,36 @@ def test_noalloc_zero_k():
     torch.cuda.synchronize()
     assert (bits(out.cpu()) == 0).all()
     assert (Cbuf[:, 0] == 3.0).all() and (Cbuf[:, 12:] == 3.0).all()
+
+
+def test_noalloc_under_graph_capture():
+    """The use gemm_bf16_noalloc exists for: a split call (fp32 partial tiles
+    in the scratch region, then the reduction) captured in a HIP graph and
+    replayed several times, with eager work and synchronisations between the
+    replays, each replay checked against the eager result.  The library is
+    used eagerly first, so its one-time device setup happens outside the
+    capture."""
+    M, N, K = 1000, 1032, 8192
+    A, B = make_operands(M, N, K, b_transposed=False, seed=77)
+    dA, dB = A.cuda(), B.cuda()
+    assert bd.gemm_bf16_plan(M, N, K, False, 2, 0)["k_splits"] > 1
+    want = both(dA, dB, "barrier", 2)[0]
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            rc = bd.gemm_bf16_noalloc(M, N, K, dA.data_ptr(), dA.stride(0), dB.data_ptr(), dB.stride(0),
+                                      C.data_ptr(), C.stride(0), 2, 0, side.cuda_stream)
+    assert rc == bd.GEMM_OK
+    torch.cuda.synchronize()
+    other = torch.empty_like(C)
+    for rep in range(4):
+        C.fill_(7.0)
+        # eager work between replays: another call that uses the same scratch region
+        assert call(bd.gemm_bf16_noalloc, dA[:512], dB, other, "barrier", 2) == bd.GEMM_OK
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(C.cpu()), want, err_msg="replay %d" % rep)
