@@ -313,17 +313,21 @@ def summarize_trace(trace_csv, bench_json, out_path=None, workload=HEADLINE):
              "--steps %d --warmup %d --no-cpu-baseline > <out>/kt_bench.json" % (line["steps"], line["warmup"]),
              "python3 bench.py --summarize-trace <out>/kt/kt_kernel_trace.csv <out>/kt_bench.json", "```", "",
              "Kernel source sha256 `%s`.  Per configuration: the dispatches of its kernel in the trace "
-             "(%d warm-up and %d timed calls), their mean and minimum duration, and the mean per-call time "
-             "bench.py measured in the same run with HIP events on the launch stream (the roofline's "
-             "`achieved` uses the latter)." % (kernel_sha(), line["warmup"], line["steps"]), "",
+             "(%d warm-up, %d timed and %d clock-sampled calls), their mean and minimum duration, the mean "
+             "per-call time bench.py measured in the same run with HIP events on the launch stream (the "
+             "roofline's `achieved` uses it), and the clock sampled inside the kernels in the calls right "
+             "after the timed ones, with the MFMA-busy fraction it implies (TFLOP/s over 1,048,576 FLOP per "
+             "clock)." % (kernel_sha(), line["warmup"], line["steps"], CLOCK_SAMPLE_CALLS), "",
              "| config | kernel (as rocprofv3 names it) | dispatches | trace mean (us) | trace min (us) | "
-             "HIP events mean (us) | TFLOP/s (events) |", "|---|---|---|---|---|---|---|"]
+             "HIP events mean (us) | TFLOP/s (events) | clock (GHz) | MFMA busy |",
+             "|---|---|---|---|---|---|---|---|---|"]
     for cfg, e in line["modes"].items():
         cands = [n for n in order if kernel_config(n) == (cfg, True)]
         for n in cands:
             d = per[n]
-            lines.append("| %s | `%s` | %d | %.1f | %.1f | %.1f | %.1f |" % (
-                cfg, n, len(d), sum(d) / len(d) / 1e3, min(d) / 1e3, e["kernel_ms_mean"] * 1e3, e["tflops"]))
+            lines.append("| %s | `%s` | %d | %.1f | %.1f | %.1f | %.1f | %s | %s |" % (
+                cfg, n, len(d), sum(d) / len(d) / 1e3, min(d) / 1e3, e["kernel_ms_mean"] * 1e3, e["tflops"],
+                e.get("clock_ghz", "-"), e.get("mfma_busy", "-")))
     lines += ["", "The run's line: value %.2f TFLOP/s (%s), roofline achieved %.2f TFLOP/s, frac %.4f."
               % (line["value"], line["roofline"]["kernel"], line["roofline"]["achieved"], line["roofline"]["frac"])]
     with open(out_path, "w") as f:
@@ -362,10 +366,32 @@ def time_mode(bd, dA, dB, C, w, sync, stages, steps, warmup, torch):
     return wall, per_launch_ms
 
 
+CLOCK_SAMPLE_CALLS = 10
+
+
+def sampled_clock(bd, dA, dB, C, w, sync, stages, calls=CLOCK_SAMPLE_CALLS):
+    """The clock the GEMM kernels ran at over `calls` further calls, from the
+    library's in-kernel samples (elapsed s_memtime over elapsed s_memrealtime
+    per workgroup), in GHz; None without samples.  Run right after a timed
+    loop, so the board is in the same power state."""
+    bd.gemm_bf16_clock_samples(reset=True)
+    prev = bd.gemm_bf16_set_clock_sampling(True)
+    try:
+        for _ in range(calls):
+            bd.gemm(dA, dB, b_transposed=w.b_transposed, sync=sync, stages=stages, out=C)
+        got = bd.gemm_bf16_clock_samples(reset=True)
+    finally:
+        bd.gemm_bf16_set_clock_sampling(prev)
+    return got["clock_ghz"]
+
+
 def measure_workload(bd, w, configs, args, torch, A=None, B=None):
     """Every configuration on one workload: per-call time from HIP events on
     the launch stream (mean, median, min), wall-clock throughput, % of peak,
-    and the counter pass's clock where the committed summary has it."""
+    the clock sampled inside the kernels right after the timed loop and the
+    MFMA-busy fraction it implies (FLOP rate over 1,048,576 FLOP per clock;
+    for split calls the reduction kernel's time counts as not busy), and the
+    counter pass's clock where the committed summary has it."""
     from pipelined_tiled_dense_amd.inputs import workload_operands
     if A is None:
         A, B = workload_operands(w)
@@ -385,6 +411,10 @@ def measure_workload(bd, w, configs, args, torch, A=None, B=None):
              "kernel_ms_min": round(min(per), 4),
              "tile": "%dx%dx%d" % (plan["bm"], plan["bn"], plan["bk"]), "grid": plan["grid"],
              "k_splits": plan["k_splits"], "tail_tiles": plan["tail_tiles"], "mfma_block": plan["mfma_block"]}
+        ghz = sampled_clock(bd, dA, dB, C, w, sync, stages)
+        if ghz:
+            e["clock_ghz"] = round(ghz, 3)
+            e["mfma_busy"] = round(tf * 1e12 / (FLOP_PER_CLK_GPU * ghz * 1e9), 4)
         cnt = counters_for(w.name, label(sync, stages))
         if cnt and cnt.get("clock_ghz"):
             e["counter_clock_ghz"] = cnt["clock_ghz"]
@@ -414,11 +444,22 @@ def reference_matmul(dA, dB, C, w, steps, warmup, torch):
 
 # Variants of the matrix-core ceiling probe: name -> (waves, fragments from
 # LDS, all-zero data).  8 waves of 128 x 64 is the all-wave kernels' layout,
-# 4 waves of 128 x 128 the layout with a third fewer LDS reads per MFMA.
+# 4 waves of 128 x 128 the layout with a third fewer LDS reads per MFMA, and
+# 4 waves of 128 x 64 (waves = -4) the wave-specialised kernel's MFMA waves,
+# one per SIMD.
 CEILING_VARIANTS = {"w8_registers_zero_data": (8, 0, True), "w8_registers": (8, 0, False),
-                    "w8_lds_reads": (8, 1, False), "w4_registers": (4, 0, False), "w4_lds_reads": (4, 1, False)}
+                    "w8_lds_reads": (8, 1, False), "w4_registers": (4, 0, False), "w4_lds_reads": (4, 1, False),
+                    "w4x64_registers": (-4, 0, False), "w4x64_lds_reads": (-4, 1, False)}
+
+
+def ceiling_flop_per_block_iter(variant):
+    waves = CEILING_VARIANTS[variant][0]
+    return 1 << (22 if waves == -4 else 23)
 CEILING_ITERS = 1024
 CEILING_BLOCKS = 256
+# Untimed calls before each variant (about 1 ms each): the clock settles tens
+# of milliseconds after the load changes, and the variants draw different power.
+CEILING_WARMUP = 30
 
 
 def _ceiling_lib():
@@ -454,14 +495,13 @@ def mfma_ceiling(torch, steps=20):
     pass's clock and MFMA busy where the committed summary has them."""
     lib = _ceiling_lib()
     rand, zero, sink = _ceiling_data(torch)
-    flop = float(CEILING_BLOCKS) * (1 << 23) * CEILING_ITERS
     stream = torch.cuda.current_stream()
     stamps = torch.zeros((steps, CEILING_BLOCKS, 2), dtype=torch.int64, device="cuda")
     rt_hz = wall_clock_hz(torch)
     out = {}
     for name, (_, _, zero_data) in CEILING_VARIANTS.items():
         data = zero if zero_data else rand
-        for _ in range(3):
+        for _ in range(CEILING_WARMUP):
             _ceiling_call(torch, lib, name, data, sink)
         torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
@@ -471,6 +511,7 @@ def mfma_ceiling(torch, steps=20):
             ev[2 * i + 1].record(stream)
         torch.cuda.synchronize()
         ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / steps
+        flop = float(CEILING_BLOCKS) * ceiling_flop_per_block_iter(name) * CEILING_ITERS
         tf = flop / (ms * 1e-3) / 1e12
         st = stamps.double().sum(dim=(0, 1))
         clock = float(st[0] / st[1]) * rt_hz / 1e9 if float(st[1]) > 0 else None
@@ -627,6 +668,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": cnt["hbm_bytes_per_call"] if cnt else None,
                      "kernel": "%s (%s)" % (kernel, best),
+                     "clock_ghz_in_kernel": r.get("clock_ghz"), "mfma_busy_in_kernel": r.get("mfma_busy"),
                      "clock_ghz_counter_pass": cnt["clock_ghz"] if cnt else None,
                      "frac_at_counter_clock": r.get("frac_of_peak_at_counter_clock")},
     }

@@ -301,6 +301,34 @@ int64_t gemm_bf16_sync_timeouts(int reset);
  */
 int64_t gemm_bf16_set_sync_spin_limit(int64_t polls);
 
+/*
+ * Clock sampling, for measurement.  Under load the clock of these boards is
+ * set by the power limit and depends on the kernel and the data, so a
+ * throughput alone does not say how busy the matrix cores were; profiler
+ * counter passes change the power state themselves.  While sampling is on,
+ * thread 0 of every GEMM workgroup that has work adds its elapsed shader-clock
+ * ticks (s_memtime), its elapsed constant-rate ticks (s_memrealtime) and a
+ * count of one to per-device sums when it finishes.  Sampling costs a few
+ * scalar instructions and three atomic adds per workgroup and leaves results
+ * unchanged bit for bit.  The split reduction, zero-fill and padding kernels
+ * take no samples.
+ *
+ * gemm_bf16_set_clock_sampling: on (enable != 0) or off for calls made from
+ * now on (process-wide, default off).  Returns the previous setting (0 or 1).
+ */
+int gemm_bf16_set_clock_sampling(int enable);
+
+/*
+ * gemm_bf16_clock_samples: the current device's sums since the library was
+ * loaded or last reset: out[0] shader-clock ticks, out[1] constant-rate
+ * ticks, out[2] samples (workgroups), and out[3] the constant rate in Hz.
+ * The mean clock in Hz is out[0] / out[1] * out[3].  `out` is host memory of
+ * four uint64_t.  Synchronises the device (not for use under graph capture);
+ * if reset != 0 the sums are cleared after reading.  Returns GEMM_OK,
+ * GEMM_ERR_INVALID_VALUE for a null `out`, or GEMM_ERR_DEVICE.
+ */
+int gemm_bf16_clock_samples(uint64_t* out, int reset);
+
 #ifdef __cplusplus
 }
 #endif

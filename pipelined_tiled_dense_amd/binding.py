@@ -78,6 +78,10 @@ def library() -> ctypes.CDLL:
         lib.gemm_bf16_sync_timeouts.restype = i64
         lib.gemm_bf16_set_sync_spin_limit.argtypes = [i64]
         lib.gemm_bf16_set_sync_spin_limit.restype = i64
+        lib.gemm_bf16_set_clock_sampling.argtypes = [i32]
+        lib.gemm_bf16_set_clock_sampling.restype = i32
+        lib.gemm_bf16_clock_samples.argtypes = [ctypes.POINTER(ctypes.c_uint64), i32]
+        lib.gemm_bf16_clock_samples.restype = i32
         _lib = lib
     return _lib
 
@@ -129,6 +133,24 @@ def gemm_bf16_set_sync_spin_limit(polls: int) -> int:
     if n < 0:
         raise GemmError(int(n), "gemm_bf16_set_sync_spin_limit")
     return int(n)
+
+
+def gemm_bf16_set_clock_sampling(enable: bool) -> bool:
+    """Turns the kernels' clock sampling on or off; returns the previous setting."""
+    return bool(library().gemm_bf16_set_clock_sampling(int(bool(enable))))
+
+
+def gemm_bf16_clock_samples(reset: bool = False) -> dict:
+    """The current device's clock sums: shader-clock ticks, constant-rate ticks,
+    samples, the constant rate in Hz, and the mean clock in GHz they give
+    (None without samples)."""
+    out = (ctypes.c_uint64 * 4)()
+    rc = library().gemm_bf16_clock_samples(out, int(bool(reset)))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_bf16_clock_samples")
+    shader, wall, n, hz = (int(v) for v in out)
+    return {"shader_ticks": shader, "wall_ticks": wall, "samples": n, "wall_hz": hz,
+            "clock_ghz": shader / wall * hz / 1e9 if wall > 0 else None}
 
 
 strerror = gemm_bf16_strerror

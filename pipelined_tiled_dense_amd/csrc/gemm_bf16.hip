@@ -117,6 +117,14 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 
 __device__ unsigned long long g_sync_timeouts;
 
+// Sums of the kernels' clock samples (clock_begin / clock_end): per slot,
+// shader-clock ticks, constant-rate ticks, samples.  Workgroup b adds to slot
+// b mod kClockSlots; each slot has a 128-byte line of its own, so the atomics
+// of one launch's workgroups do not queue on one address (same-address
+// device-wide atomics from all XCDs cost several percent of a 100 us call).
+constexpr int kClockSlots = 256;
+__device__ __align__(128) unsigned long long g_clock_sums[kClockSlots][16];
+
 // s_waitcnt immediates (gfx9 layout: vmcnt[3:0] + [15:14], expcnt[6:4],
 // lgkmcnt[11:8]); counters not named are left at their maximum.
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
@@ -263,7 +271,39 @@ struct Params {
     int32_t group_m;
     int32_t small_span;               // A and B each span fewer than kMaxRecords bytes
     uint32_t spin_limit;              // polls before a ring counter wait gives up
+    uint32_t clock_on;                // nonzero: workgroups add clock samples to g_clock_sums
 };
+
+// Optional clock sampling.  With p.clock_on set, thread 0 of every workgroup
+// that has work adds its elapsed shader-clock ticks (s_memtime), its elapsed
+// constant-rate ticks (s_memrealtime) and a count of one to its slot of
+// g_clock_sums.
+// The ratio of the two sums times the constant rate is the clock the kernels
+// ran at, measured without a profiler (whose counter passes change the power
+// state).  Nothing stays live in between: the start subtracts its stamps from
+// the sums and the end adds its own (unsigned sums wrap, so they hold the sum
+// of the elapsed ticks once every workgroup has ended).  Wave 0, which takes
+// the samples, is an MFMA wave in every kernel.
+__device__ __forceinline__ void clock_begin(const Params& p)
+{
+    if (p.clock_on && threadIdx.x == 0) {
+        const uint64_t c = __builtin_amdgcn_s_memtime(), r = __builtin_amdgcn_s_memrealtime();
+        unsigned long long* slot = g_clock_sums[blockIdx.x % kClockSlots];
+        atomicAdd(&slot[0], (unsigned long long)(0 - c));
+        atomicAdd(&slot[1], (unsigned long long)(0 - r));
+    }
+}
+
+__device__ __forceinline__ void clock_end(const Params& p)
+{
+    if (p.clock_on && threadIdx.x == 0) {
+        const uint64_t c = __builtin_amdgcn_s_memtime(), r = __builtin_amdgcn_s_memrealtime();
+        unsigned long long* slot = g_clock_sums[blockIdx.x % kClockSlots];
+        atomicAdd(&slot[0], (unsigned long long)c);
+        atomicAdd(&slot[1], (unsigned long long)r);
+        atomicAdd(&slot[2], 1ull);
+    }
+}
 
 // Swizzles.  The LDS has 64 four-byte banks (256 bytes per cycle); a 16-byte
 // read is served 16 lanes at a time, an 8-byte read 32 lanes at a time.
@@ -1482,6 +1522,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
 
     if (total == 0)
         return;
+    clock_begin(p);
     Loader<C, LONGK, EDGE> ld;
     ld.init(p, n_tiles, w, lane);
 #pragma unroll
@@ -1661,6 +1702,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm(Params p)
         else
             store_tile<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
     }
+    clock_end(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -1700,6 +1742,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_win(Params p)
     const int32_t KT = p.k_steps;
     if (n_tiles == 0 || KT == 0)
         return;
+    clock_begin(p);
 
     constexpr int AH = C::A_LOADS / 2, BH = C::B_LOADS / 2;   // DMA instructions per half tile
     auto win = [&](int i) { return smem + i * C::A_BYTES; };
@@ -1797,6 +1840,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_win(Params p)
             block_barrier();
         }
     }
+    clock_end(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -1902,6 +1946,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
     Frags<C> fr[2];
     if (total == 0)
         return;
+    clock_begin(p);
     wait_counter(full, (uint32_t)C::NP, st);
     read_frags<C>(fr[0], smem, wm, wn, lane, 0);
 
@@ -1949,6 +1994,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
         else
             store_tile<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
     }
+    clock_end(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -1997,6 +2043,8 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_pp(Params p)
     lds_char* strip = smem + C::EPI_OFFSET + w * C::EPI_WAVE_BYTES;
     auto stage_of = [&](int32_t q) { return smem + (q % C::S) * C::STAGE_BYTES; };
     Frags<C> fr[2];
+    if (n_tiles > 0)
+        clock_begin(p);
     for (int32_t it = g; it < n_tiles; it += 2) {
         int32_t tm, tn;
         int32_t sp, u;
@@ -2041,6 +2089,8 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_pp(Params p)
         else
             store_tile<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
     }
+    if (n_tiles > 0)
+        clock_end(p);
 }
 
 // C = 0 for K == 0 (16-byte stores, range-checked like the epilogue).
@@ -2229,6 +2279,9 @@ struct DeviceInfo {
 
 // Polls before a ring counter wait gives up, for every launch from now on.
 std::atomic<uint32_t> g_spin_limit{kSpinLimit};
+
+// Clock sampling (ClockSample) for every launch from now on.
+std::atomic<bool> g_clock_on{false};
 
 constexpr int kMaxDevices = 64;
 std::mutex g_dev_mutex;
@@ -2637,6 +2690,7 @@ int gemm_direct(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
                    (bt ? span_bytes(N, K, ldb) : span_bytes(K, N, ldb)) < (int64_t)kMaxRecords;
     p.partial = nullptr;
     p.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+    p.clock_on = g_clock_on.load(std::memory_order_relaxed) ? 1u : 0u;
     const int64_t grid = pl.grid;
     if (p.splits == 1 && pl.tail_tiles == 0)
         return with_cfg(sync_mode, pl.stages, bt, [&]<class C>() { return launch<C>(p, grid, s); });
@@ -2771,6 +2825,45 @@ int64_t gemm_bf16_sync_timeouts(int reset)
             return GEMM_ERR_DEVICE;
     }
     return (int64_t)v;
+}
+
+int gemm_bf16_set_clock_sampling(int enable)
+{
+    return g_clock_on.exchange(enable != 0) ? 1 : 0;
+}
+
+int gemm_bf16_clock_samples(uint64_t* out, int reset)
+{
+    if (!out)
+        return GEMM_ERR_INVALID_VALUE;
+    int cus = 0;
+    int rc = device_info(&cus);
+    if (rc != GEMM_OK)
+        return rc;
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+        return GEMM_ERR_DEVICE;
+    if (hipDeviceSynchronize() != hipSuccess)
+        return GEMM_ERR_DEVICE;
+    static unsigned long long v[kClockSlots][16];   // guarded by g_dev_mutex
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (hipMemcpyFromSymbol(v, HIP_SYMBOL(g_clock_sums), sizeof v, 0, hipMemcpyDeviceToHost) != hipSuccess)
+        return GEMM_ERR_DEVICE;
+    uint64_t sum[3] = {0, 0, 0};
+    for (int i = 0; i < kClockSlots; ++i)
+        for (int j = 0; j < 3; ++j)
+            sum[j] += v[i][j];
+    if (reset) {
+        memset(v, 0, sizeof v);
+        if (hipMemcpyToSymbol(HIP_SYMBOL(g_clock_sums), v, sizeof v, 0, hipMemcpyHostToDevice) != hipSuccess)
+            return GEMM_ERR_DEVICE;
+    }
+    out[0] = sum[0];
+    out[1] = sum[1];
+    out[2] = sum[2];
+    out[3] = (uint64_t)khz * 1000u;
+    return GEMM_OK;
 }
 
 }  // extern "C"

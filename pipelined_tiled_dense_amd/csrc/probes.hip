@@ -200,26 +200,35 @@ __global__ void __launch_bounds__(256) k_cvt(const float* __restrict__ in,
 // the fragments stay in registers.  No global memory is touched after the
 // start, and no synchronisation runs inside the loop.  Each thread writes one
 // float of the accumulators to sink[blockIdx.x * 64 NW + threadIdx.x].
-// Every workgroup-iteration is 2^23 FLOP whatever the shape.
+// A workgroup-iteration is NW * FN * 2^18 FLOP (2^23 for 8 x 4 and 4 x 8, 2^22
+// for 4 x 4: the wave-specialised kernel's MFMA waves, one per SIMD).
 constexpr int kCeilVecs = 8192;   // 128 KiB of 16-byte fragments
 
-template <bool FROM_LDS, int NW, int FN>
-__global__ void __launch_bounds__(NW * 64) k_mfma_ceiling(const bf16x8_t* __restrict__ data, int n_vec, int iters,
+// NT threads per workgroup, of which the first NW waves run the loop.  The
+// 4 x 4 shape is launched as the wave-specialised kernel is, 8 waves with 4
+// of them doing MFMAs: the other 4 leave after the LDS fill, and the
+// compiler gets the same budget of 256 registers per wave (given 512, it moves
+// accumulators between register files inside the loop).
+template <bool FROM_LDS, int NW, int FN, int NT>
+__global__ void __launch_bounds__(NT) k_mfma_ceiling(const bf16x8_t* __restrict__ data, int n_vec, int iters,
                                                           float* __restrict__ sink, uint64_t* __restrict__ stamps)
 {
     // Shader-clock and constant-rate timestamps at the start and the end of
     // the workgroup (s_memtime, s_memrealtime): their ratio over many
     // workgroups gives the clock the loop ran at, without a profiler.
     const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
-    static_assert(NW * FN == 32, "2^23 FLOP per workgroup-iteration");
+    static_assert((NW == 8 && FN == 4 && NT == 512) || (NW == 4 && FN == 8 && NT == 256) ||
+                  (NW == 4 && FN == 4 && NT == 512), "wave shapes");
     constexpr int NF = 8 + FN;                 // fragments per k-step
     __shared__ bf16x8_t lds[kCeilVecs];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     if constexpr (FROM_LDS) {
-        for (int i = t; i < kCeilVecs; i += NW * 64)
+        for (int i = t; i < kCeilVecs; i += NT)
             lds[i] = data[(int)(((int64_t)blockIdx.x * 1031 + i) % n_vec)];
         __syncthreads();
     }
+    if (w >= NW)
+        return;
     bf16x8_t fa[2][8], fb[2][FN];
     const int64_t base = ((int64_t)blockIdx.x * NW * 64 + t) * 2 * NF;
 #pragma unroll
@@ -237,16 +246,17 @@ __global__ void __launch_bounds__(NW * 64) k_mfma_ceiling(const bf16x8_t* __rest
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (FN == 8) {
+        // 256 accumulator registers: placed in the accumulation register file
+        // once, before the loop (a placement inside the loop makes the
+        // compiler move them between register files every iteration).
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                asm volatile("" : "+a"(acc[i][j]));
+    }
     for (int it = 0; it < iters; ++it) {
-        if constexpr (FN == 8) {
-            // 256 accumulator registers: keep them in the accumulation
-            // register file for the whole loop.
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    asm volatile("" : "+a"(acc[i][j]));
-        }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             if constexpr (FROM_LDS) {
@@ -363,25 +373,32 @@ int gemm_probe_cvt_bf16(const float* in, uint16_t* out, int64_t n, void* stream)
 // sink: blocks * 512 floats; stamps: null, or 2 * blocks 64-bit words that
 // receive each workgroup's elapsed s_memtime and s_memrealtime ticks.
 // Launches `blocks` workgroups, each running `iters` iterations of two
-// 32-wide k-steps: 2^23 * iters FLOP per workgroup.  waves = 8: 8 waves of
-// 128 x 64 (the all-wave kernels' layout); waves = 4: 4 waves of 128 x 128.
+// 32-wide k-steps.  waves = 8: 8 waves of 128 x 64 (the all-wave kernels'
+// layout, 2^23 FLOP per workgroup-iteration); waves = 4: 4 waves of 128 x 128
+// (2^23); waves = -4: 4 waves of 128 x 64, one per SIMD, in a workgroup of 8
+// whose other 4 waves exit at once (the wave-specialised kernel's MFMA waves,
+// 2^22).
 int gemm_probe_mfma_ceiling(const uint16_t* data, int64_t n_elems, int from_lds, int waves, int iters, int blocks,
                             float* sink, uint64_t* stamps, void* stream)
 {
     if (!data || !sink || n_elems < 8 || n_elems % 8 != 0 || n_elems / 8 > ((int64_t)1 << 31) - 1 ||
-        iters < 1 || iters > (1 << 20) || blocks < 1 || blocks > 65536 || (waves != 4 && waves != 8))
+        iters < 1 || iters > (1 << 20) || blocks < 1 || blocks > 65536 || (waves != 4 && waves != 8 && waves != -4))
         return -1;
     const int n_vec = (int)(n_elems / 8);
     const hipStream_t s = (hipStream_t)stream;
     const bf16x8_t* d = (const bf16x8_t*)data;
     if (waves == 8 && from_lds)
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<true, 8, 4>), dim3(blocks), dim3(512), 0, s, d, n_vec, iters, sink, stamps);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<true, 8, 4, 512>), dim3(blocks), dim3(512), 0, s, d, n_vec, iters, sink, stamps);
     else if (waves == 8)
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<false, 8, 4>), dim3(blocks), dim3(512), 0, s, d, n_vec, iters, sink, stamps);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<false, 8, 4, 512>), dim3(blocks), dim3(512), 0, s, d, n_vec, iters, sink, stamps);
+    else if (waves == -4 && from_lds)
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<true, 4, 4, 512>), dim3(blocks), dim3(512), 0, s, d, n_vec, iters, sink, stamps);
+    else if (waves == -4)
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<false, 4, 4, 512>), dim3(blocks), dim3(512), 0, s, d, n_vec, iters, sink, stamps);
     else if (from_lds)
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<true, 4, 8>), dim3(blocks), dim3(256), 0, s, d, n_vec, iters, sink, stamps);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<true, 4, 8, 256>), dim3(blocks), dim3(256), 0, s, d, n_vec, iters, sink, stamps);
     else
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<false, 4, 8>), dim3(blocks), dim3(256), 0, s, d, n_vec, iters, sink, stamps);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<false, 4, 8, 256>), dim3(blocks), dim3(256), 0, s, d, n_vec, iters, sink, stamps);
     return launch_status();
 }
 

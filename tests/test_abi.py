@@ -179,3 +179,20 @@ def test_sync_spin_limit_setting_needs_no_device():
             assert e.value.code == bd.GEMM_ERR_INVALID_VALUE
     finally:
         bd.gemm_bf16_set_sync_spin_limit(prev if prev != 1000 else 0)
+
+
+def test_clock_sampling_setting_needs_no_device():
+    """The sampling switch is host state; reading the sums needs a device."""
+    prev = bd.gemm_bf16_set_clock_sampling(True)
+    try:
+        assert bd.gemm_bf16_set_clock_sampling(False) is True
+        assert bd.gemm_bf16_set_clock_sampling(False) is False
+    finally:
+        bd.gemm_bf16_set_clock_sampling(prev)
+    assert bd.library().gemm_bf16_clock_samples(None, 0) == bd.GEMM_ERR_INVALID_VALUE
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    with pytest.raises(bd.GemmError) as e:
+        bd.gemm_bf16_clock_samples()
+    assert e.value.code == bd.GEMM_ERR_DEVICE

@@ -154,3 +154,30 @@ def test_helpers_present():
     called = {n.func.id for n in ast.walk(tree) if isinstance(n, ast.Call) and isinstance(n.func, ast.Name)}
     missing = {c for c in called if c not in defined and not hasattr(builtins, c) and c not in dir(bench)}
     assert not missing, missing
+
+
+def test_summarize_trace_end_to_end(tmp_path):
+    """Dispatches of the headline workload's kernels are matched to their
+    configuration by name; the table carries the run's events and clocks."""
+    ns = "void (anonymous namespace)::"
+    k2 = ns + "k_gemm<(anonymous namespace)::Cfg<256, 256, 64, 2, 2, 4, 0, true, 0, false, 16>, true, false>(P)"
+    kw = ns + "k_gemm_ws<(anonymous namespace)::Cfg<256, 128, 64, 3, 2, 2, 2, true, 4, false, 16> >(P)"
+    kn = ns + "k_gemm<(anonymous namespace)::Cfg<256, 256, 64, 2, 2, 4, 0, false, 0, false, 16>, true, false>(P)"
+    rows = [(k2, 700_000), (k2, 710_000), (kw, 900_000), (kn, 5_000)]
+    with open(tmp_path / "kt.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        wr.writeheader()
+        for name, dur in rows:
+            wr.writerow({"Kernel_Name": name, "Start_Timestamp": 1000, "End_Timestamp": 1000 + dur})
+    line = {"steps": 20, "warmup": 5, "value": 1500.0,
+            "roofline": {"kernel": "k_gemm (barrier/2)", "achieved": 1510.0, "frac": 0.6},
+            "modes": {"barrier/2": {"kernel_ms_mean": 0.705, "tflops": 1510.0, "clock_ghz": 1.72, "mfma_busy": 0.84},
+                      "wavespec/3": {"kernel_ms_mean": 0.9, "tflops": 1200.0}}}
+    (tmp_path / "b.json").write_text("# noise\n" + json.dumps(line) + "\n")
+    out = bench.summarize_trace(str(tmp_path / "kt.csv"), str(tmp_path / "b.json"), out_path=str(tmp_path / "t.md"))
+    text = open(out).read()
+    table = [r for r in text.splitlines() if r.startswith("| barrier/2") or r.startswith("| wavespec/3")]
+    assert len(table) == 2                                   # the K x N kernel belongs to no headline config
+    assert "| 2 | 705.0 | 700.0 | 705.0 | 1510.0 | 1.72 | 0.84 |" in table[0]
+    assert "| 1 | 900.0 | 900.0 | 900.0 | 1200.0 | - | - |" in table[1]
+    assert "%d clock-sampled calls" % bench.CLOCK_SAMPLE_CALLS in text
