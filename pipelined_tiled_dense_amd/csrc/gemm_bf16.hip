@@ -34,7 +34,10 @@
 //   talking only through the full/empty counters.  The empty counters start at
 //   zero and are read as "free" for a stage's first use, which is what the
 //   consumer's initial arrive on every empty barrier achieves there.  gfx950
-//   cannot move registers between roles, so all waves get one register budget.
+//   cannot move registers between roles, so all waves get one register budget:
+//   either one MFMA wave per SIMD next to the loaders (256 x 128 tiles,
+//   double-buffered fragments) or two (256 x 256 tiles, one fragment set per
+//   wave, the other wave covering its reads).
 //
 // * Ping-pong (same page, section "Why?", which names ping-pong matmul
 //   kernels as a goal).  GEMM_SYNC_PINGPONG keeps the loader waves and splits
@@ -1943,6 +1946,50 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
     // MFMA wave: tile { k-step { wait full; read; release; MFMA } epilogue }.
     const int wm = w / C::WN, wn = w % C::WN;
     lds_char* strip = smem + C::EPI_OFFSET + w * C::EPI_WAVE_BYTES;
+    if constexpr (C::NCW == 8) {
+        // Two MFMA waves per SIMD and one fragment set each (Pick above):
+        // per 16-wide k-step read, wait, MFMAs; while one wave waits for its
+        // reads the other wave's MFMAs keep the SIMD's matrix core busy.  The
+        // stage is handed back once the reads of its last 16-wide k-step
+        // have landed, before that k-step's MFMAs, which read registers only.
+        static_assert(C::MF == 32, "one fragment set of 32 x 32 blocks per 16-wide k-step");
+        if (total == 0)
+            return;
+        clock_begin(p);
+        int32_t c = 0;
+        for (int32_t it = 0; it < n_tiles; ++it) {
+            int32_t tm, tn;
+            int32_t sp, u;
+            tile_coords(p, b + it * G, G, tm, tn, sp, u);
+            typename C::Acc acc[C::FM][C::FN];
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j)
+                    acc[i][j] = typename C::Acc{};
+            for (int32_t kt = 0; kt < KT; ++kt, ++c) {
+                const int s = c % C::S;
+                const lds_char* stage = smem + s * C::STAGE_BYTES;
+                wait_counter(full + s, (uint32_t)(c / C::S + 1) * C::NP, st);
+#pragma unroll
+                for (int kk = 0; kk < C::KK; ++kk) {
+                    Frags<C> f;
+                    read_frags<C>(f, stage, wm, wn, lane, kk);
+                    wait_lgkm0();
+                    if (kk == C::KK - 1)
+                        arrive(empty + s);
+                    mfma_range<C, 0, C::FM * C::FN>(acc, f);
+                }
+            }
+            poison_tile<C>(acc, st);
+            if (p.splits > 1)
+                store_partial<C>(p, acc, sp * p.span + u, wm, wn, lane);
+            else
+                store_tile<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
+        }
+        clock_end(p);
+        return;
+    }
     Frags<C> fr[2];
     if (total == 0)
         return;
@@ -2149,22 +2196,40 @@ __global__ void __launch_bounds__(256) k_pad_copy(const uint16_t* src, int64_t s
 // ---------------------------------------------------------------------------
 // The kernel instance used for each (sync mode, stage count).  All-wave modes
 // use a 256 x 256 tile over 8 waves (2 x 4, each 128 x 64, two waves per SIMD
-// so that one can issue MFMAs while the other waits on a load); the
-// wave-specialised mode uses 4 MFMA waves (2 x 2 over 256 x 128) and 4 loader
-// waves.  The k-step width follows the LDS budget (see BK below).  Every
-// config uses 16 x 16 MFMA blocks except the wave-specialised 4-stage ring:
-// its 32-wide stages hold a single 16 x 16 k-step, which the all-wave kernel
-// covers by handing the next stage's fragments over at the end of each stage
-// (take_next_stage) and the loader/MFMA schedule does not.
+// so that one can issue MFMAs while the other waits on a load) with 16 x 16
+// MFMA blocks.  The wave-specialised 3-stage ring uses 4 MFMA waves (2 x 2
+// over 256 x 128, one per SIMD, double-buffered fragments, 16 x 16 blocks)
+// and 4 loader waves; the 2- and 4-stage rings are specialised below.  The
+// k-step width follows the LDS budget (see BK below).
 template <int SYNC, int S>
 struct Pick {
     // 64-wide k-steps (128-byte rows per DMA instruction) wherever the ring
     // fits: two stages of 256 x 256, three of the wave-specialised 256 x 128.
     static constexpr int BK = (S == 2 || (SYNC == SYNC_WAVESPEC && S == 3)) ? 64 : 32;
-    static constexpr int MF = (BK == 64 || SYNC != SYNC_WAVESPEC) ? 16 : 32;
+    static_assert(SYNC != SYNC_WAVESPEC || S == 3, "the other wave-specialised rings are specialised below");
     template <bool BT>
     using type = Cfg<256, (SYNC == SYNC_WAVESPEC) ? 128 : 256, BK, S, 2, (SYNC == SYNC_WAVESPEC) ? 2 : 4, SYNC, BT,
-                     (SYNC == SYNC_WAVESPEC) ? 4 : 0, false, MF>;
+                     (SYNC == SYNC_WAVESPEC) ? 4 : 0, false, 16>;
+};
+
+// The wave-specialised 2- and 4-stage rings: 8 MFMA waves (two per SIMD,
+// 128 x 64 each) over a 256 x 256 tile next to 4 loader waves.  Three waves
+// per SIMD leave each 168 registers: 128 accumulators and one fragment set of
+// 32 x 32 blocks (24 registers) fit, two sets do not, so these MFMA waves run
+// k_gemm_ws's single-buffered loop and rely on the other MFMA wave of their
+// SIMD to cover their fragment reads.  Two 64-wide stages or four 32-wide
+// ones fill 128 KiB.  The 3-stage ring keeps the 256 x 128 tile with one
+// MFMA wave per SIMD and double-buffered fragments.
+template <>
+struct Pick<SYNC_WAVESPEC, 2> {
+    template <bool BT>
+    using type = Cfg<256, 256, 64, 2, 2, 4, SYNC_WAVESPEC, BT, 4, false, 32>;
+};
+
+template <>
+struct Pick<SYNC_WAVESPEC, 4> {
+    template <bool BT>
+    using type = Cfg<256, 256, 32, 4, 2, 4, SYNC_WAVESPEC, BT, 4, false, 32>;
 };
 
 // Ping-pong: each of the two MFMA groups needs a wave on every SIMD, so
@@ -2246,8 +2311,8 @@ auto with_cfg(int sync_mode, int stages, bool bt, F&& f)
 
 // 64-wide k-steps: each DMA instruction then covers 8 rows of 128 bytes
 // instead of 16 rows of 64, which the texture path serves markedly faster.
-// The LDS holds two such stages of the all-wave modes' 256 x 256 tile and
-// three of the wave-specialised mode's 256 x 128.
+// The LDS holds two such stages of a 256 x 256 tile and three of the
+// wave-specialised mode's 256 x 128.
 int default_stages(int sync_mode)
 {
     return (sync_mode == GEMM_SYNC_WAVESPEC || sync_mode == GEMM_SYNC_PINGPONG) ? 3 : 2;
@@ -2280,7 +2345,7 @@ struct DeviceInfo {
 // Polls before a ring counter wait gives up, for every launch from now on.
 std::atomic<uint32_t> g_spin_limit{kSpinLimit};
 
-// Clock sampling (ClockSample) for every launch from now on.
+// Clock sampling (clock_begin / clock_end) for every launch from now on.
 std::atomic<bool> g_clock_on{false};
 
 constexpr int kMaxDevices = 64;

@@ -165,8 +165,8 @@ def test_split_k(bt):
     """Few output tiles and a long k range: the k range is cut into chunks whose
     fp32 partial tiles are summed in chunk order.  1000 x 1032 has 20 tiles of
     256 x 256, so K = 8192 splits into 8 chunks of 1024 (ragged M and N); the
-    256 x 128 and 128 x 128 tiles of the loader/MFMA modes split it into 4 and
-    2.  Modes with the same split signature (tile, chunks, MFMA block) give the
+    256 x 128 tiles of the wave-specialised 3-stage ring and the 128 x 128
+    tiles of ping-pong split it into 4 and 2.  Modes with the same split signature (tile, chunks, MFMA block) give the
     same bits, run after run and on any stream; a K with no valid chunking
     stays unsplit."""
     M, N, K = 1000, 1032, 8192
@@ -222,13 +222,14 @@ def test_split_at_half_the_compute_units(bt):
 def test_plans():
     """The launch shape each (sync mode, stages) resolves to: 256 x 256 tiles over
     8 waves for the all-wave modes (64-wide k-steps with 2 stages or the split
-    window ring, 32-wide with 3 and 4), 256 x 128 over 4 + 4 waves for the
-    wave-specialised mode; the LDS never exceeds 160 KiB, and the split-window
-    ring (five 32 KiB windows, epilogue staged inside one) uses all of it."""
+    window ring, 32-wide with 3 and 4); for the wave-specialised mode 256 x 256
+    over 8 MFMA + 4 loader waves with 2 and 4 stages and 256 x 128 over 4 + 4
+    with 3; the LDS never exceeds 160 KiB, and the split-window ring (five
+    32 KiB windows, epilogue staged inside one) uses all of it."""
     want = {("barrier", 2): (256, 64, 8, 0), ("barrier", 3): (256, 32, 8, 0), ("barrier", 4): (256, 32, 8, 0),
             ("barrier", bd.STAGES_WINDOWS): (256, 64, 8, 0),
             ("flags", 2): (256, 64, 8, 0), ("flags", 3): (256, 32, 8, 0), ("flags", 4): (256, 32, 8, 0),
-            ("wavespec", 2): (128, 64, 4, 4), ("wavespec", 3): (128, 64, 4, 4), ("wavespec", 4): (128, 32, 4, 4),
+            ("wavespec", 2): (256, 64, 8, 4), ("wavespec", 3): (128, 64, 4, 4), ("wavespec", 4): (256, 32, 8, 4),
             ("pingpong", 2): (128, 64, 8, 4), ("pingpong", 3): (128, 64, 8, 4), ("pingpong", 4): (128, 64, 8, 4)}
     for (sync, stages), (bn, bk, mw, pw) in want.items():
         bm = 128 if sync == "pingpong" else 256

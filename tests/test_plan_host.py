@@ -22,15 +22,16 @@ MODES = [("barrier", 2), ("barrier", 3), ("barrier", 4), ("barrier", bd.STAGES_W
 SHAPES = {("barrier", 2): (256, 256, 64, 8, 0), ("barrier", 3): (256, 256, 32, 8, 0),
           ("barrier", 4): (256, 256, 32, 8, 0), ("barrier", bd.STAGES_WINDOWS): (256, 256, 64, 8, 0),
           ("flags", 2): (256, 256, 64, 8, 0), ("flags", 3): (256, 256, 32, 8, 0), ("flags", 4): (256, 256, 32, 8, 0),
-          ("wavespec", 2): (256, 128, 64, 4, 4), ("wavespec", 3): (256, 128, 64, 4, 4),
-          ("wavespec", 4): (256, 128, 32, 4, 4),
+          ("wavespec", 2): (256, 256, 64, 8, 4), ("wavespec", 3): (256, 128, 64, 4, 4),
+          ("wavespec", 4): (256, 256, 32, 8, 4),
           ("pingpong", 2): (128, 128, 64, 8, 4), ("pingpong", 3): (128, 128, 64, 8, 4),
           ("pingpong", 4): (128, 128, 64, 8, 4)}
 
 
 # MFMA block edge: 16 x 16 x 32 MFMAs everywhere but the wave-specialised
-# ring of 32-wide stages, which keeps 32 x 32 x 16.
-MFMA_BLOCK = {mode: (32 if mode[0] == "wavespec" and SHAPES[mode][2] == 32 else 16) for mode in SHAPES}
+# rings with two MFMA waves per SIMD (256 x 256 tiles), whose one fragment
+# set per wave holds 32 x 32 x 16 blocks.
+MFMA_BLOCK = {mode: (32 if mode[0] == "wavespec" and SHAPES[mode][3] == 8 else 16) for mode in SHAPES}
 
 
 def plan(M, N, K, bt, sync, stages, cus=CUS):
