@@ -1948,11 +1948,10 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
     lds_char* strip = smem + C::EPI_OFFSET + w * C::EPI_WAVE_BYTES;
     if constexpr (C::NCW == 8) {
         // Two MFMA waves per SIMD and one fragment set each (Pick above):
-        // per 16-wide k-step read, wait, MFMAs; while one wave waits for its
-        // reads the other wave's MFMAs keep the SIMD's matrix core busy.  The
-        // stage is handed back once the reads of its last 16-wide k-step
-        // have landed, before that k-step's MFMAs, which read registers only.
-        static_assert(C::MF == 32, "one fragment set of 32 x 32 blocks per 16-wide k-step");
+        // read, wait, MFMAs; while one wave waits for its reads the other
+        // wave's MFMAs keep the SIMD's matrix core busy.  The stage is handed
+        // back once its last fragment reads have landed, before the MFMAs on
+        // them, which read registers only.
         if (total == 0)
             return;
         clock_begin(p);
@@ -1971,14 +1970,50 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
                 const int s = c % C::S;
                 const lds_char* stage = smem + s * C::STAGE_BYTES;
                 wait_counter(full + s, (uint32_t)(c / C::S + 1) * C::NP, st);
+                if constexpr (C::MF == 32) {
+                    // Per 16-wide k-step: all fragments, then its MFMAs.
 #pragma unroll
-                for (int kk = 0; kk < C::KK; ++kk) {
-                    Frags<C> f;
-                    read_frags<C>(f, stage, wm, wn, lane, kk);
-                    wait_lgkm0();
-                    if (kk == C::KK - 1)
-                        arrive(empty + s);
-                    mfma_range<C, 0, C::FM * C::FN>(acc, f);
+                    for (int kk = 0; kk < C::KK; ++kk) {
+                        Frags<C> f;
+                        read_frags<C>(f, stage, wm, wn, lane, kk);
+                        wait_lgkm0();
+                        if (kk == C::KK - 1)
+                            arrive(empty + s);
+                        mfma_range<C, 0, C::FM * C::FN>(acc, f);
+                    }
+                } else {
+                    // Per 32-wide k-step: the B blocks and A blocks
+                    // 0 .. FM/2 - 1 (read order of FragReader), their MFMAs,
+                    // then A blocks FM/2 .. FM - 1 into the same A registers
+                    // and theirs.
+                    constexpr int H = (C::BT ? 1 : 2) * C::FN + C::FM / 2;
+#pragma unroll
+                    for (int ks = 0; ks < C::BK / 32; ++ks) {
+                        const FragReader<C> rd(wm, wn, lane, ks);
+                        Frags<C> f;
+#pragma unroll
+                        for (int d = 0; d < H; ++d)
+                            rd.read(f, stage, wn, d);
+                        wait_lgkm0();
+#pragma unroll
+                        for (int i = 0; i < C::FM / 2; ++i)
+#pragma unroll
+                            for (int j = 0; j < C::FN; ++j)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b_frag<C>(f, j), f.a[i],
+                                                                                   acc[i][j], 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < C::FM / 2; ++i)
+                            f.a[i] = *(const LDS_AS bf16x8_t*)(stage + rd.a_off + (C::FM / 2 + i) * (16 * C::BK * 2));
+                        wait_lgkm0();
+                        if (ks == C::BK / 32 - 1)
+                            arrive(empty + s);
+#pragma unroll
+                        for (int i = 0; i < C::FM / 2; ++i)
+#pragma unroll
+                            for (int j = 0; j < C::FN; ++j)
+                                acc[C::FM / 2 + i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    b_frag<C>(f, j), f.a[i], acc[C::FM / 2 + i][j], 0, 0, 0);
+                    }
                 }
             }
             poison_tile<C>(acc, st);
@@ -2218,12 +2253,16 @@ struct Pick {
 // 32 x 32 blocks (24 registers) fit, two sets do not, so these MFMA waves run
 // k_gemm_ws's single-buffered loop and rely on the other MFMA wave of their
 // SIMD to cover their fragment reads.  Two 64-wide stages or four 32-wide
-// ones fill 128 KiB.  The 3-stage ring keeps the 256 x 128 tile with one
-// MFMA wave per SIMD and double-buffered fragments.
+// ones fill 128 KiB.  With B stored N x K the 2-stage ring uses 16 x 16
+// blocks instead, half a 32-wide k-step of fragments at a time (32
+// registers); with a K x N B their transposing reads need more registers
+// than that leaves, and the 32 x 32 form runs faster.  The 3-stage ring
+// keeps the 256 x 128 tile with one MFMA wave per SIMD and double-buffered
+// fragments.
 template <>
 struct Pick<SYNC_WAVESPEC, 2> {
     template <bool BT>
-    using type = Cfg<256, 256, 64, 2, 2, 4, SYNC_WAVESPEC, BT, 4, false, 32>;
+    using type = Cfg<256, 256, 64, 2, 2, 4, SYNC_WAVESPEC, BT, 4, false, BT ? 16 : 32>;
 };
 
 template <>

@@ -30,8 +30,12 @@ SHAPES = {("barrier", 2): (256, 256, 64, 8, 0), ("barrier", 3): (256, 256, 32, 8
 
 # MFMA block edge: 16 x 16 x 32 MFMAs everywhere but the wave-specialised
 # rings with two MFMA waves per SIMD (256 x 256 tiles), whose one fragment
-# set per wave holds 32 x 32 x 16 blocks.
-MFMA_BLOCK = {mode: (32 if mode[0] == "wavespec" and SHAPES[mode][3] == 8 else 16) for mode in SHAPES}
+# set per wave holds 32 x 32 x 16 blocks -- except the 2-stage ring with B
+# stored N x K, which reads half a 16 x 16 k-step at a time.
+def mfma_block(sync, stages, bt):
+    if sync == "wavespec" and SHAPES[(sync, stages)][3] == 8:
+        return 16 if (stages == 2 and bt) else 32
+    return 16
 
 
 def plan(M, N, K, bt, sync, stages, cus=CUS):
@@ -74,7 +78,7 @@ def test_tile_configuration(sync, stages, bt):
     assert (pl["bm"], pl["bn"], pl["bk"], pl["mfma_waves"], pl["producer_waves"]) == (bm, bn, bk, mw, pw)
     assert pl["stages"] == stages and pl["sync_mode"] == bd.SYNC_MODES[sync] and pl["b_transposed"] == bt
     assert pl["threads"] == 64 * (mw + pw)
-    assert pl["mfma_block"] == MFMA_BLOCK[(sync, stages)]
+    assert pl["mfma_block"] == mfma_block(sync, stages, bt)
     assert 0 < pl["lds_bytes"] <= 160 * 1024
     assert pl["tiles"] == (8192 // bm) * (8192 // bn)
     assert pl["k_steps"] == 8192 // bk
