@@ -382,6 +382,15 @@ def test_wavespec_protocol(S, seed):
     run_producer_consumer(S, NP=4, NCWG=4, groups=1, n_tiles=3, KT=5, seed=seed)
 
 
+@pytest.mark.parametrize("S", [2, 4])
+@pytest.mark.parametrize("seed", SEEDS)
+def test_wavespec_two_mfma_waves_per_simd_protocol(S, seed):
+    """The 2- and 4-stage rings of the wave-specialised kernel: 8 MFMA waves
+    (each releases a stage once all its reads of it have landed) beside 4
+    loader waves, whose refill of a stage waits for all 8 releases."""
+    run_producer_consumer(S, NP=4, NCWG=8, groups=1, n_tiles=3, KT=5, seed=seed)
+
+
 @pytest.mark.parametrize("S", [2, 3, 4])
 @pytest.mark.parametrize("seed", SEEDS)
 def test_pingpong_protocol(S, seed):
@@ -425,6 +434,13 @@ def test_fault_pingpong_release_count_of_all_mfma_waves():
     """Loaders waiting for releases by all 8 MFMA waves, when one group of 4
     releases each position, never see the stage freed."""
     assert caught(lambda sd: run_producer_consumer(3, 4, 4, 2, 4, 4, sd, releasers=8))
+
+
+def test_fault_two_wave_ring_release_count_of_one_wave_per_simd():
+    """Loaders of the 8-MFMA-wave ring that refill a stage after 4 releases
+    (the 4-MFMA-wave layout's count) overwrite data still being read."""
+    for S in (2, 4):
+        assert caught(lambda sd: run_producer_consumer(S, 4, 8, 1, 3, 5, sd, releasers=4))
 
 
 def test_fault_loader_skips_war_wait():
