@@ -984,6 +984,13 @@ struct FragReader {
     {
         read(f, stage, stage + C::A_BYTES, wn, d);
     }
+
+    // With 16 x 16 blocks: A block i of a whole stage into f.a[slot].
+    __device__ __forceinline__ void read_a_into(Frags<C>& f, const lds_char* stage, int i, int slot) const
+    {
+        static_assert(C::MF == 16, "16 x 16 blocks");
+        f.a[slot] = *(const LDS_AS bf16x8_t*)(stage + a_off + i * (16 * C::BK * 2));
+    }
 };
 
 template <class C>
@@ -2003,7 +2010,7 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
                                                                                    acc[i][j], 0, 0, 0);
 #pragma unroll
                         for (int i = 0; i < C::FM / 2; ++i)
-                            f.a[i] = *(const LDS_AS bf16x8_t*)(stage + rd.a_off + (C::FM / 2 + i) * (16 * C::BK * 2));
+                            rd.read_a_into(f, stage, C::FM / 2 + i, i);
                         wait_lgkm0();
                         if (ks == C::BK / 32 - 1)
                             arrive(empty + s);
