@@ -181,3 +181,39 @@ def test_summarize_trace_end_to_end(tmp_path):
     assert "| 2 | 705.0 | 700.0 | 705.0 | 1510.0 | 1.72 | 0.84 |" in table[0]
     assert "| 1 | 900.0 | 900.0 | 900.0 | 1200.0 | - | - |" in table[1]
     assert "%d clock-sampled calls" % bench.CLOCK_SAMPLE_CALLS in text
+
+
+def test_sampled_clock_turns_sampling_on_only_for_its_calls():
+    """sampled_clock resets the sums, samples exactly its calls with sampling on,
+    and restores the previous setting even when a call raises."""
+    class FakeBinding:
+        def __init__(self, fail_at=None):
+            self.on, self.log, self.calls, self.fail_at = False, [], 0, fail_at
+
+        def gemm_bf16_set_clock_sampling(self, enable):
+            prev, self.on = self.on, bool(enable)
+            self.log.append(("set", bool(enable)))
+            return prev
+
+        def gemm_bf16_clock_samples(self, reset=False):
+            self.log.append(("read", reset, self.on))
+            return {"clock_ghz": 1.75 if self.calls else None}
+
+        def gemm(self, *a, **k):
+            self.calls += 1
+            self.log.append(("call", self.on))
+            if self.fail_at == self.calls:
+                raise RuntimeError("launch failed")
+
+    class W:
+        b_transposed = True
+
+    fb = FakeBinding()
+    assert bench.sampled_clock(fb, None, None, None, W, "barrier", 2, calls=3) == 1.75
+    assert fb.log[0] == ("read", True, False)                      # stale sums cleared first
+    assert [e for e in fb.log if e[0] == "call"] == [("call", True)] * 3
+    assert fb.log[-1] == ("set", False) and fb.on is False         # previous setting restored
+    fb = FakeBinding(fail_at=2)
+    with pytest.raises(RuntimeError):
+        bench.sampled_clock(fb, None, None, None, W, "barrier", 2, calls=3)
+    assert fb.on is False
