@@ -390,8 +390,9 @@ def measure_workload(bd, w, configs, args, torch, A=None, B=None):
     the launch stream (mean, median, min), wall-clock throughput, % of peak,
     the clock sampled inside the kernels right after the timed loop and the
     MFMA-busy fraction it implies (FLOP rate over 1,048,576 FLOP per clock;
-    for split calls the reduction kernel's time counts as not busy), and the
-    counter pass's clock where the committed summary has it."""
+    for split calls the reduction kernel's time counts as not busy), and, where
+    the committed counter summary has them, the counter pass's clock and the
+    call's HBM traffic with the rate it gives at this run's time."""
     from pipelined_tiled_dense_amd.inputs import workload_operands
     if A is None:
         A, B = workload_operands(w)
@@ -420,6 +421,11 @@ def measure_workload(bd, w, configs, args, torch, A=None, B=None):
             e["counter_clock_ghz"] = cnt["clock_ghz"]
             e["frac_of_peak_at_counter_clock"] = round(tf * 1e12 / (FLOP_PER_CLK_GPU * cnt["clock_ghz"] * 1e9), 4)
             e["counter_mfma_busy"] = cnt.get("mfma_busy")
+        if cnt and cnt.get("hbm_bytes_per_call"):
+            # HBM bytes of the counter pass per call, and the rate they give at
+            # this run's per-call time
+            e["hbm_gb_per_call"] = round(cnt["hbm_bytes_per_call"] / 1e9, 4)
+            e["hbm_gbps"] = round(cnt["hbm_bytes_per_call"] / (mean_ms * 1e-3) / 1e9, 1)
         res[label(sync, stages)] = e
         print("# %s %s: %s" % (w.name, label(sync, stages), json.dumps(e)), file=sys.stderr, flush=True)
     return res, (A, B, dA, dB, C)
