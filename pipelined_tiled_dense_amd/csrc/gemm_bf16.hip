@@ -43,7 +43,10 @@
 //   kernels as a goal).  GEMM_SYNC_PINGPONG keeps the loader waves and splits
 //   the MFMA waves into two groups that take the workgroup's output tiles in
 //   turn; each position is released by the group that computes it, so one
-//   group's epilogue overlaps the other's main loop.
+//   group's epilogue overlaps the other's main loop.  With 3 and 4 stages the
+//   groups share one ring and their main loops alternate; with 2 stages each
+//   group has a pipeline of its own (ring, counters, two loader waves), and
+//   the groups compute side by side, two MFMA waves per SIMD.
 //
 // * Split windows ("[WIP] SM120 fused backward kernel: exploratory
 //   shared-memory reduction", section "Shared-memory reduction strategies":
@@ -184,7 +187,7 @@ enum {
 // Compile-time configuration of one kernel instance.
 // ---------------------------------------------------------------------------
 template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, int SYNC_, bool BT_, int NP_, bool WIN_ = false,
-          int MF_ = 32>
+          int MF_ = 32, bool DUAL_ = false>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_;
     static constexpr int SYNC = SYNC_;
@@ -200,7 +203,11 @@ struct Cfg {
     static constexpr int NCWG = WM * WN;            // MFMA waves per group: one output tile
     static constexpr int NCW = GROUPS * NCWG;       // MFMA waves
     static constexpr int NP = PRODUCERS ? NP_ : 0;  // dedicated loader waves
-    static constexpr int NLW = PRODUCERS ? NP : NCW; // waves that load
+    // Ping-pong with one pipeline per MFMA group: each group has its own
+    // ring of S stages, its own counters and NP / GROUPS loader waves.
+    static constexpr bool DUAL = DUAL_;
+    static constexpr int PIPES = DUAL ? GROUPS : 1;
+    static constexpr int NLW = PRODUCERS ? NP / PIPES : NCW; // waves that load one position
     static constexpr int NW = NCW + NP;
     static constexpr int THREADS = NW * 64;
     static constexpr int TM = BM / WM, TN = BN / WN;                 // wave tile
@@ -221,10 +228,10 @@ struct Cfg {
     static constexpr int LOADS = A_LOADS + B_LOADS;
     static constexpr int CPR_K = BK / 8;                             // 16-byte chunks per K-contiguous row
     static constexpr int CPR_N = BN / 8;                             // chunks per row of a K x N B tile
-    static constexpr int RING_BYTES = WIN ? NWIN * A_BYTES : S * STAGE_BYTES;
+    static constexpr int RING_BYTES = WIN ? NWIN * A_BYTES : PIPES * S * STAGE_BYTES;
     // Ring counters (2 x S 32-bit words, or S 64-bit signal words) and the
     // workgroup's poison word (SyncState), padded to 8 bytes.
-    static constexpr int FLAG_BYTES = (SYNC != SYNC_BARRIER) ? 2 * S * 4 + 8 : 0;
+    static constexpr int FLAG_BYTES = (SYNC != SYNC_BARRIER) ? PIPES * 2 * S * 4 + 8 : 0;
     // Epilogue strip per MFMA wave: 32 rows x 64 columns of bf16 when that
     // fits next to the ring (or, with windows, inside one window), else 32
     // rows x 32 columns.
@@ -251,6 +258,7 @@ struct Cfg {
     static_assert(CPR_N == 16 || CPR_N == 32, "a DMA window covers whole K x N rows of B");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(S >= 2 && S <= 4, "stages");
+    static_assert(!DUAL || (SYNC == SYNC_PINGPONG && NP % GROUPS == 0), "one pipeline per ping-pong group");
     static_assert(!WIN || (SYNC == SYNC_BARRIER && S == 2 && KK == 4 && A_BYTES == B_BYTES &&
                            NCW * EPI_WAVE_BYTES <= A_BYTES),
                   "the window ring runs the barrier kernel on equal A and B tiles");
@@ -640,6 +648,7 @@ template <class C, bool LONGK, bool EDGE = true>
 struct Loader {
     int32_t total;                // positions in this workgroup's stream
     int32_t n_tiles;
+    int32_t t_first = 0, t_stride = 1;   // the stream's tiles: t_first + t * t_stride
     uint32_t voffA[C::A_LOADS];
     uint32_t voffB[C::B_LOADS];
     // One past the last byte of A and of B.  Each operand's resource runs from
@@ -676,8 +685,11 @@ struct Loader {
         return ((s % C::CPR_N) ^ swz_n<C::MF>(row)) * 8;
     }
 
-    __device__ __forceinline__ void init(const Params& p, int32_t ntiles, int lw, int lane)
+    __device__ __forceinline__ void init(const Params& p, int32_t ntiles, int lw, int lane, int32_t first = 0,
+                                         int32_t stride = 1)
     {
+        t_first = first;
+        t_stride = stride;
         const uint32_t lda2 = (uint32_t)p.lda * 2u, ldb2 = (uint32_t)p.ldb * 2u;
 #pragma unroll
         for (int t = 0; t < C::A_LOADS; ++t) {
@@ -715,8 +727,8 @@ struct Loader {
                                                 int32_t& n_left, int32_t& k_left) const
     {
         int32_t tm = 0, tn = 0, sp = 0, u = 0;
-        tile_coords(p, (int32_t)blockIdx.x + min(t, n_tiles - 1) * (int32_t)gridDim.x, (int32_t)gridDim.x, tm, tn,
-                    sp, u);
+        tile_coords(p, (int32_t)blockIdx.x + (t_first + min(t, n_tiles - 1) * t_stride) * (int32_t)gridDim.x,
+                    (int32_t)gridDim.x, tm, tn, sp, u);
         const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN, k0 = (int64_t)sp * p.ksplit;
         a = p.A + (m0 * p.lda + k0) * 2;
         b = C::BT ? p.B + (n0 * p.ldb + k0) * 2 : p.B + (k0 * p.ldb + n0) * 2;
@@ -1858,7 +1870,8 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_win(Params p)
 // ---------------------------------------------------------------------------
 template <class C>
 __device__ __forceinline__ void producer_loop(const Params& p, lds_char* smem, lds_u32* full, lds_u32* empty,
-                                              int32_t n_tiles, int lw, int lane, SyncState& st)
+                                              int32_t n_tiles, int lw, int lane, SyncState& st, int32_t first = 0,
+                                              int32_t stride = 1)
 {
     const int32_t total = n_tiles * p.k_steps;
     // Loader wave: one flat loop over (tile, k-step) positions.  The data
@@ -1870,7 +1883,7 @@ __device__ __forceinline__ void producer_loop(const Params& p, lds_char* smem, l
     // every stage wait for that release-issue-announce chain).
     constexpr int D = (C::S - 2 < 2) ? C::S - 2 : 2;
     Loader<C, false> ld;
-    ld.init(p, n_tiles, lw, lane);
+    ld.init(p, n_tiles, lw, lane, first, stride);
     for (int32_t q = 0; q < total; ++q) {
         const int s = q % C::S;
         // Each use of a stage is released by the NCWG MFMA waves of the one
@@ -2090,7 +2103,8 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
 // Kernel: loader waves and two MFMA wave groups that take the output tiles in
 // turn (GEMM_SYNC_PINGPONG).
 //
-// The loader waves stream the workgroup's (tile, k-step) positions in order,
+// One shared ring (3 and 4 stages).  The loader waves stream the
+// workgroup's (tile, k-step) positions in order,
 // exactly as in the wave-specialised kernel.  MFMA group g computes the
 // workgroup's tiles g, g + 2, ...: it waits for and releases only the
 // positions of its own tiles, and each position is released by the one
@@ -2099,6 +2113,12 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
 // loaders keep streaming, so the epilogue overlaps MFMA work; the two
 // groups' main loops alternate.  A group's first wait for a tile lasts about
 // one tile of the other group (far inside the bounded wait).
+//
+// One pipeline per group (C::DUAL, 2 stages).  Only one group computing at a
+// time leaves one MFMA wave per SIMD issuing.  Here group g has a ring, full
+// and empty counters and two loader waves of its own and streams its tiles
+// g, g + 2, ... with the wave-specialised MFMA loop, so both groups compute
+// at once; each group's epilogue overlaps the other group's main loop.
 // ---------------------------------------------------------------------------
 template <class C>
 __global__ void __launch_bounds__(C::THREADS) k_gemm_pp(Params p)
@@ -2108,14 +2128,88 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_pp(Params p)
     lds_char* smem = (lds_char*)smem_raw;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    constexpr int NCTR = C::PIPES * 2 * C::S;     // full[] and empty[] of every pipeline
     lds_u32* full = (lds_u32*)(smem + C::FLAG_OFFSET);
     lds_u32* empty = full + C::S;
-    if (threadIdx.x < 2 * C::S + 1)
-        full[threadIdx.x] = 0u;   // full[], empty[] and the poison word
+    if (threadIdx.x < NCTR + 1)
+        full[threadIdx.x] = 0u;   // the counters and the poison word
     __syncthreads();   // counters are initialised before the roles split
     SyncState st;
-    st.poison = full + 2 * C::S;
+    st.poison = full + NCTR;
     st.limit = p.spin_limit;
+
+    if constexpr (C::DUAL) {
+        // One pipeline per group: group g owns ring g, counters g, loader
+        // waves g * NLG .. + NLG - 1 and the workgroup's tiles g, g + 2, ...
+        // The groups run side by side, each on its own tiles; the stagger
+        // of their epilogues comes from the other group's work.
+        constexpr int NLG = C::NP / C::GROUPS;
+        const int32_t G = gridDim.x, b = blockIdx.x;
+        const int32_t n_tiles = (b < p.tiles) ? (p.tiles - 1 - b) / G + 1 : 0;
+        const int32_t KT = p.k_steps;
+        const int g = (w < C::NCW) ? w / C::NCWG : (w - C::NCW) / NLG;
+        const int32_t n_g = n_tiles > g ? (n_tiles - g + C::GROUPS - 1) / C::GROUPS : 0;
+        lds_char* ring = smem + g * C::S * C::STAGE_BYTES;
+        lds_u32* full_g = full + g * 2 * C::S;
+        lds_u32* empty_g = full_g + C::S;
+        if (w >= C::NCW) {
+            producer_loop<C>(p, ring, full_g, empty_g, n_g, (w - C::NCW) % NLG, lane, st, g, C::GROUPS);
+            return;
+        }
+        const int wg = w % C::NCWG;
+        const int wm = wg / C::WN, wn = wg % C::WN;
+        lds_char* strip = smem + C::EPI_OFFSET + w * C::EPI_WAVE_BYTES;
+        const int32_t total = n_g * KT;
+        if (total == 0)
+            return;
+        clock_begin(p);
+        Frags<C> fr[2];
+        wait_counter(full_g, (uint32_t)NLG, st);
+        read_frags<C>(fr[0], ring, wm, wn, lane, 0);
+        int32_t c = 0;
+        for (int32_t j = 0; j < n_g; ++j) {
+            int32_t tm, tn;
+            int32_t sp, u;
+            tile_coords(p, b + (g + C::GROUPS * j) * G, G, tm, tn, sp, u);
+            typename C::Acc acc[C::FM][C::FN];
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int jj = 0; jj < C::FN; ++jj)
+                    acc[i][jj] = typename C::Acc{};
+            for (int32_t kt = 0; kt < KT; ++kt, ++c) {
+                const lds_char* stage = ring + (c % C::S) * C::STAGE_BYTES;
+                auto region = [&]<int kk>() {
+                    constexpr int M = region_mfmas<C>();
+                    if constexpr (kk + 1 < C::KK) {
+                        constexpr RegionReads rr = region_reads<C, kk>();
+                        const FragReader<C> rdr(wm, wn, lane, rr.ks);
+#pragma unroll
+                        for (int d = 0; d < rr.d; ++d)
+                            rdr.read(fr[rr.buf], stage, wn, d + rr.off);
+                        region_mfma<C, kk, 0, M>(acc, fr);
+                        sched_slots<M, rr.d, 0>();
+                    } else {
+                        const int s1 = (c + 1) % C::S;
+                        consumer_last_kstep<C>(acc, fr, empty_g + c % C::S, full_g + s1,
+                                               (uint32_t)((c + 1) / C::S + 1) * NLG, c + 1 < total,
+                                               ring + s1 * C::STAGE_BYTES, wm, wn, lane, st);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                };
+                [&]<int... KS>(std::integer_sequence<int, KS...>) {
+                    (region.template operator()<KS>(), ...);
+                }(std::make_integer_sequence<int, C::KK>{});
+            }
+            poison_tile<C>(acc, st);
+            if (p.splits > 1)
+                store_partial<C>(p, acc, sp * p.span + u, wm, wn, lane);
+            else
+                store_tile<C>(p, acc, strip, tm * C::BM, tn * C::BN, wm, wn, lane);
+        }
+        clock_end(p);
+        return;
+    }
 
     const int32_t G = gridDim.x, b = blockIdx.x;
     const int32_t n_tiles = (b < p.tiles) ? (p.tiles - 1 - b) / G + 1 : 0;
@@ -2281,11 +2375,18 @@ struct Pick<SYNC_WAVESPEC, 4> {
 // Ping-pong: each of the two MFMA groups needs a wave on every SIMD, so
 // with the loader waves a SIMD holds three waves and each has about a third
 // of the register file: the groups' tiles are 128 x 128 (4 waves of 64 x 64).
-// A stage is 32 KiB at 64-wide k-steps, so up to 4 stages fit.
+// A stage is 32 KiB at 64-wide k-steps, so up to 4 stages fit in one shared
+// ring, or two per group in the 2-stage instance's per-group rings.
 template <int S>
 struct Pick<SYNC_PINGPONG, S> {
     template <bool BT>
     using type = Cfg<128, 128, 64, S, 2, 2, SYNC_PINGPONG, BT, 4, false, 16>;
+};
+
+template <>
+struct Pick<SYNC_PINGPONG, 2> {
+    template <bool BT>
+    using type = Cfg<128, 128, 64, 2, 2, 2, SYNC_PINGPONG, BT, 4, false, 16, true>;
 };
 
 // The split-window ring: the two-stage barrier instance's tile, waves and

@@ -36,7 +36,8 @@ def samples_per_call(M, N, K, bt, stages, sync):
 CASES = [((2048, 2048, 2048), True, "barrier", 2), ((2048, 2048, 2048), True, "barrier", 5),
          ((2048, 2048, 2048), False, "flags", 3), ((2048, 2048, 2048), False, "wavespec", 3),
          ((2048, 2048, 2048), True, "wavespec", 2), ((2048, 2048, 2048), False, "wavespec", 4),
-         ((2048, 2048, 2048), True, "pingpong", 4), ((4352, 4352, 4096), False, "barrier", 2),
+         ((2048, 2048, 2048), True, "pingpong", 4), ((2048, 2048, 2048), False, "pingpong", 2),
+         ((4352, 4352, 4096), False, "barrier", 2),
          ((1024, 1024, 32768), False, "wavespec", 3), ((300, 200, 4104), False, "barrier", 2)]
 
 

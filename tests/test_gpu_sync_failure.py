@@ -38,7 +38,8 @@ def run(dA, dB, bt, sync, stages):
 CASES = [((2048, 2048, 2048), False, "flags", 2), ((2048, 2048, 2048), True, "flags", 3),
          ((2048, 2048, 2048), False, "wavespec", 3), ((2048, 2048, 2048), True, "wavespec", 4),
          ((2048, 2048, 2048), True, "wavespec", 2), ((2048, 2048, 2048), False, "wavespec", 2),
-         ((2048, 2048, 2048), False, "pingpong", 3), ((1024, 1024, 32768), False, "flags", 2),
+         ((2048, 2048, 2048), False, "pingpong", 3), ((2048, 2048, 2048), True, "pingpong", 2),
+         ((2048, 2048, 2048), False, "pingpong", 2), ((1024, 1024, 32768), False, "flags", 2),
          ((1024, 1024, 32768), False, "wavespec", 3)]
 
 

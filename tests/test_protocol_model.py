@@ -391,6 +391,14 @@ def test_wavespec_two_mfma_waves_per_simd_protocol(S, seed):
     run_producer_consumer(S, NP=4, NCWG=8, groups=1, n_tiles=3, KT=5, seed=seed)
 
 
+@pytest.mark.parametrize("seed", SEEDS)
+def test_pingpong_per_group_pipeline_protocol(seed):
+    """Ping-pong with one pipeline per MFMA group (2 stages): each group's ring
+    is filled by 2 loader waves (two announcements per position) and read by
+    its 4 MFMA waves; the two pipelines share nothing but the workgroup."""
+    run_producer_consumer(2, NP=2, NCWG=4, groups=1, n_tiles=3, KT=5, seed=seed)
+
+
 @pytest.mark.parametrize("S", [2, 3, 4])
 @pytest.mark.parametrize("seed", SEEDS)
 def test_pingpong_protocol(S, seed):
