@@ -161,6 +161,9 @@ typedef struct gemm_bf16_plan {
                                  (v_mfma_f32_32x32x16_bf16, 16 k per instruction).  Calls whose plans agree
                                  on it and on the k split (k_splits, tail_tiles, tail_splits, bm, bn) run
                                  the same chain of MFMAs for every element and give the same bits. */
+    int64_t pipelines;        /* independent LDS rings per workgroup: 2 where each MFMA group has its own
+                                 ring and takes every other work item (GEMM_SYNC_PINGPONG, 2 stages), else 1.
+                                 The k split fills compute units x pipelines work items. */
 } gemm_bf16_plan_t;
 
 /*

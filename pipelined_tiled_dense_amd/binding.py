@@ -43,7 +43,8 @@ class Plan(ctypes.Structure):
                 ("k_steps", ctypes.c_int64), ("grid", ctypes.c_int64),
                 ("k_splits", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
                 ("tail_tiles", ctypes.c_int64), ("tail_splits", ctypes.c_int64),
-                ("pad_bytes", ctypes.c_int64), ("mfma_block", ctypes.c_int64)]
+                ("pad_bytes", ctypes.c_int64), ("mfma_block", ctypes.c_int64),
+                ("pipelines", ctypes.c_int64)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -2429,13 +2429,13 @@ int launch(const Params& p, int64_t grid, hipStream_t stream)
 }
 
 struct Shape {
-    int bm, bn, bk, mfma_waves, producer_waves, threads, lds_bytes, mfma_block;
+    int bm, bn, bk, mfma_waves, producer_waves, threads, lds_bytes, mfma_block, pipes;
 };
 
 template <class C>
 Shape shape_of()
 {
-    return Shape{C::BM, C::BN, C::BK, C::NCW, C::NP, C::THREADS, C::LDS_BYTES, C::MF};
+    return Shape{C::BM, C::BN, C::BK, C::NCW, C::NP, C::THREADS, C::LDS_BYTES, C::MF, C::PIPES};
 }
 
 // Calls f.template operator()<Cfg>() for the instance of (sync, stages, bt).
@@ -2649,10 +2649,13 @@ int64_t pad_bytes(int64_t M, int64_t N, int64_t K, PadSet ps)
 }
 
 // Number of k chunks.  Shapes with at most half as many output tiles (in
-// the configuration's tile) as compute units and a long k range are split
-// into equal chunks of a multiple of 64 elements, each at least 512 long, so
-// that tiles x chunks work items can fill the GPU.  Configurations with
-// different tiles may therefore split a shape differently.
+// the configuration's tile) as pipelines and a long k range are split into
+// equal chunks of a multiple of 64 elements, each at least 512 long, so that
+// tiles x chunks work items can fill the GPU.  `cus` counts pipelines: the
+// compute units times the independent pipelines one workgroup runs (two where
+// each MFMA group has its own ring and takes every other work item).
+// Configurations with different tiles or pipeline counts may therefore split
+// a shape differently.
 int64_t choose_splits(int64_t tiles, int64_t K, int cus)
 {
     if (tiles <= 0 || 2 * tiles > cus)
@@ -2717,9 +2720,10 @@ int fill_plan(int64_t M, int64_t N_in, int64_t K_in, int b_transposed, int stage
     pl.threads = v.threads;
     pl.lds_bytes = v.lds_bytes;
     pl.mfma_block = v.mfma_block;
+    pl.pipelines = v.pipes;
     const int64_t tm = (M + v.bm - 1) / v.bm, tn = (N + v.bn - 1) / v.bn;
     pl.tiles = tm * tn;
-    pl.k_splits = choose_splits(pl.tiles, K, cus);
+    pl.k_splits = choose_splits(pl.tiles, K, cus * v.pipes);
     pl.k_steps = (K / pl.k_splits + v.bk - 1) / v.bk;
     if (pl.k_splits == 1)
         pl.tail_splits = choose_tail_splits(pl.tiles, K, cus, pl.tail_tiles);

@@ -1,7 +1,7 @@
 /* A C99 caller of the library's host-only entry points (no GPU needed): the
  * plan of a few shapes for every sync mode and stage count, printed one per
  * line as "M N K bt stages sync rc bm bn bk stages grid tiles k_splits
- * tail_tiles tail_splits mfma_block workspace_bytes", and the text of every
+ * tail_tiles tail_splits mfma_block workspace_bytes pipelines", and the text of every
  * status code.  Built with -std=c99 -pedantic -Werror against include/ only. */
 #include <stdio.h>
 #include <stdint.h>
@@ -27,10 +27,11 @@ int main(void)
                 printf("%lld %lld %lld %d %d %d %d", (long long)shapes[s][0], (long long)shapes[s][1],
                        (long long)shapes[s][2], bt, modes[m][1], modes[m][0], rc);
                 if (rc == GEMM_OK)
-                    printf(" %lld %lld %lld %lld %lld %lld %lld %lld %lld %lld %lld", (long long)p.bm,
+                    printf(" %lld %lld %lld %lld %lld %lld %lld %lld %lld %lld %lld %lld", (long long)p.bm,
                            (long long)p.bn, (long long)p.bk, (long long)p.stages, (long long)p.grid,
                            (long long)p.tiles, (long long)p.k_splits, (long long)p.tail_tiles,
-                           (long long)p.tail_splits, (long long)p.mfma_block, (long long)p.workspace_bytes);
+                           (long long)p.tail_splits, (long long)p.mfma_block, (long long)p.workspace_bytes,
+                           (long long)p.pipelines);
                 printf("\n");
             }
     for (code = -9; code <= 0; ++code)

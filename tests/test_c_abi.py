@@ -34,7 +34,7 @@ def test_host_entry_points_from_c(tmp_path):
     exe = build(tmp_path, "plan_from_c", ["-pedantic", "-Werror"])
     out = subprocess.run([exe], capture_output=True, text=True, timeout=60, check=True).stdout.splitlines()
     keys = ("bm", "bn", "bk", "stages", "grid", "tiles", "k_splits", "tail_tiles", "tail_splits", "mfma_block",
-            "workspace_bytes")
+            "workspace_bytes", "pipelines")
     plans = statuses = 0
     for line in out:
         f = line.split()

@@ -165,14 +165,15 @@ def test_split_k(bt):
     """Few output tiles and a long k range: the k range is cut into chunks whose
     fp32 partial tiles are summed in chunk order.  1000 x 1032 has 20 tiles of
     256 x 256, so K = 8192 splits into 8 chunks of 1024 (ragged M and N); the
-    256 x 128 tiles of the wave-specialised 3-stage ring and the 128 x 128
-    tiles of ping-pong split it into 4 and 2.  Modes with the same split signature (tile, chunks, MFMA block) give the
-    same bits, run after run and on any stream; a K with no valid chunking
-    stays unsplit."""
+    256 x 128 tiles of the wave-specialised 3-stage ring split it into 4, the
+    128 x 128 tiles of ping-pong into 2, or into 4 where each MFMA group has a
+    ring of its own (two pipelines per workgroup).  Modes with the same split
+    signature (tile, chunks, MFMA block) give the same bits, run after run and
+    on any stream; a K with no valid chunking stays unsplit."""
     M, N, K = 1000, 1032, 8192
     for sync, stages in MODES:
         plan = bd.gemm_bf16_plan(M, N, K, bt, stages, bd.SYNC_MODES[sync])
-        s = {256: 8, 128: 4}[plan["bn"]] if plan["bm"] == 256 else 2
+        s = {256: 8, 128: 4}[plan["bn"]] if plan["bm"] == 256 else 2 * plan["pipelines"]
         assert plan["k_splits"] == s, (sync, stages, plan)
         assert plan["workspace_bytes"] == plan["tiles"] * s * plan["bm"] * plan["bn"] * 4
     assert bd.gemm_bf16_plan(M, N, K + 8, bt, 0, 0)["k_splits"] == 1

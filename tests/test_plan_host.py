@@ -46,10 +46,16 @@ def cdiv(a, b):
     return -(-a // b)
 
 
+# Independent LDS rings per workgroup: the 2-stage ping-pong gives each MFMA
+# group its own ring and every other work item.
+def pipelines(sync, stages):
+    return 2 if (sync, stages) == ("pingpong", 2) else 1
+
+
 def want_splits(t, K, cus):
-    """At most half as many output tiles (in the configuration's tile) as compute
-    units: the largest s <= 16, s <= cus / tiles, with 64 * s dividing K and
-    K / s >= 512."""
+    """At most half as many output tiles (in the configuration's tile) as
+    pipelines (cus: compute units x pipelines per workgroup): the largest
+    s <= 16, s <= cus / tiles, with 64 * s dividing K and K / s >= 512."""
     if t == 0 or 2 * t > cus:
         return 1
     for s in range(min(cus // t, 16), 1, -1):
@@ -107,17 +113,25 @@ def test_benchmark_configurations():
     assert pl["workspace_bytes"] == 16 * 16 * 256 * 256 * 4
     pl = plan(32768, 1024, 4096, 0, "wavespec", 3)
     assert (pl["tiles"], pl["grid"], pl["tail_tiles"]) == (1024, 256, 0)
+    # 64 tiles of 128 x 128: 4 chunks give one work item per workgroup; with a
+    # ring per MFMA group, 8 chunks give one per group.
+    assert plan(1024, 1024, 32768, 0, "pingpong", 3)["k_splits"] == 4
+    pl = plan(1024, 1024, 32768, 0, "pingpong", 2)
+    assert (pl["tiles"], pl["k_splits"], pl["grid"], pl["k_steps"], pl["pipelines"]) == (64, 8, 256, 64, 2)
 
 
 def test_split_k_counts_each_configurations_tiles():
-    """The split decision counts the configuration's own tiles: 1000 x 1032 is 20
-    tiles of 256 x 256 (8 chunks of 1024), 36 of 256 x 128 (4 chunks) and 72 of
-    128 x 128 (2 chunks); a K with no chunking of 64s stays unsplit."""
-    want = {(256, 256): 8, (256, 128): 4, (128, 128): 2}
+    """The split decision counts the configuration's own tiles and pipelines:
+    1000 x 1032 is 20 tiles of 256 x 256 (8 chunks of 1024), 36 of 256 x 128
+    (4 chunks) and 72 of 128 x 128 (2 chunks; 4 with two pipelines per
+    workgroup, 512 / 72 = 7 and 6 and 5 do not divide 8192 in 64s); a K with
+    no chunking of 64s stays unsplit."""
+    want = {(256, 256, 1): 8, (256, 128, 1): 4, (128, 128, 1): 2, (128, 128, 2): 4}
     for sync, stages in MODES:
         pl = plan(1000, 1032, 8192, 1, sync, stages)
-        s = want[(pl["bm"], pl["bn"])]
-        assert pl["k_splits"] == s == want_splits(pl["tiles"], 8192, CUS), (sync, stages)
+        assert pl["pipelines"] == pipelines(sync, stages), (sync, stages, pl)
+        s = want[(pl["bm"], pl["bn"], pl["pipelines"])]
+        assert pl["k_splits"] == s == want_splits(pl["tiles"], 8192, CUS * pl["pipelines"]), (sync, stages)
         assert pl["workspace_bytes"] == pl["tiles"] * s * pl["bm"] * pl["bn"] * 4
         assert pl["k_steps"] == 8192 // s // pl["bk"]
         assert plan(1000, 1032, 8200, 1, sync, stages)["k_splits"] == 1
@@ -167,7 +181,8 @@ def test_random_shapes_follow_the_rules():
         bm, bn, bk = pl["bm"], pl["bn"], pl["bk"]
         tiles = cdiv(M, bm) * cdiv(N, bn)
         assert pl["tiles"] == tiles
-        s = want_splits(tiles, K, cus)
+        assert pl["pipelines"] == pipelines(sync, stages)
+        s = want_splits(tiles, K, cus * pipelines(sync, stages))
         assert pl["k_splits"] == s, (M, N, K, sync, stages, cus, pl)
         r, ts = want_tail(tiles, K, cus) if s == 1 else (0, 0)
         assert (pl["tail_tiles"], pl["tail_splits"]) == (r, ts), (M, N, K, sync, stages, cus, pl)
