@@ -44,9 +44,9 @@
  * allocates, frees or retains them.  A and B are only read.  C must not
  * overlap A or B.
  *
- * Split k range: a shape with at most half as many output tiles as compute
- * units (in the chosen configuration's tile, see gemm_bf16_plan) and a long
- * k range -- K a multiple of 64 * s
+ * Split k range: a shape with at most half as many output tiles as pipelines
+ * (compute units x plan.pipelines, in the chosen configuration's tile, see
+ * gemm_bf16_plan) and a long k range -- K a multiple of 64 * s
  * and K / s >= 512 for some s >= 2 -- is computed as s chunks of k (s <= 16)
  * so that the GPU fills.  Each output tile's chunks are summed in fp32, in
  * chunk order, after one fp32 chain per chunk; the result differs from the
@@ -95,7 +95,9 @@ enum {
     GEMM_SYNC_FLAGS = 1,    /* per-stage full/empty LDS counters, every wave loads and computes */
     GEMM_SYNC_WAVESPEC = 2, /* per-stage counters between loader waves and MFMA waves */
     GEMM_SYNC_PINGPONG = 3  /* as GEMM_SYNC_WAVESPEC, with two MFMA wave groups taking output
-                               tiles in turn: one group's epilogue overlaps the other's MFMAs */
+                               tiles in turn: one group's epilogue overlaps the other's MFMAs.
+                               With 2 stages each group has a ring of its own and both
+                               groups compute at once (plan.pipelines = 2) */
 };
 
 /*
