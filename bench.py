@@ -11,8 +11,9 @@ workloads get the same matrix under ``workloads``.  Prints one JSON line.
 
 Also reports:
   roofline      achieved matrix-core TFLOP/s of the fastest configuration's
-                GEMM kernel (2*M*N*K per launch / mean launch time from HIP
-                events on the launch stream) against the dense bf16 peak, plus
+                GEMM kernel (2*M*N*K per call / mean time per call from HIP
+                events on the launch stream before the first and after the
+                last timed call) against the dense bf16 peak, plus
                 HBM traffic per launch from the committed rocprofv3 counter
                 summary when it matches the current kernel source;
   clock         per configuration, the mean shader clock of its kernels in
@@ -314,8 +315,8 @@ def summarize_trace(trace_csv, bench_json, out_path=None, workload=HEADLINE):
              "python3 bench.py --summarize-trace <out>/kt/kt_kernel_trace.csv <out>/kt_bench.json", "```", "",
              "Kernel source sha256 `%s`.  Per configuration: the dispatches of its kernel in the trace "
              "(%d warm-up, %d timed and %d clock-sampled calls), their mean and minimum duration, the mean "
-             "per-call time bench.py measured in the same run with HIP events on the launch stream (the "
-             "roofline's `achieved` uses it), and the clock sampled inside the kernels in the calls right "
+             "per-call time bench.py measured in the same run (HIP events on the launch stream before the first "
+             "and after the last timed call; the roofline's `achieved` uses it), and the clock sampled inside the kernels in the calls right "
              "after the timed ones, with the MFMA-busy fraction it implies (TFLOP/s over 1,048,576 FLOP per "
              "clock)." % (kernel_sha(), line["warmup"], line["steps"], CLOCK_SAMPLE_CALLS), "",
              "| config | kernel (as rocprofv3 names it) | dispatches | trace mean (us) | trace min (us) | "
@@ -349,21 +350,25 @@ def counters_for(workload, cfg, path=COUNTERS_FILE):
 
 # -- GPU legs ---------------------------------------------------------------------
 def time_mode(bd, dA, dB, C, w, sync, stages, steps, warmup, torch):
+    """`warmup` untimed calls, then exactly `steps` calls timed between two
+    synchronisations: the wall clock around them, and HIP events recorded on
+    the launch stream before the first and after the last.  No events go
+    between the calls: each would put a marker between two kernels, which
+    measured 2-4 us per call on the GPU.  Returns (wall seconds, mean ms per
+    call on the GPU)."""
     for _ in range(warmup):
         bd.gemm(dA, dB, b_transposed=w.b_transposed, sync=sync, stages=stages, out=C)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
+    e0.record(stream)
+    for _ in range(steps):
         bd.gemm(dA, dB, b_transposed=w.b_transposed, sync=sync, stages=stages, out=C)
-        ends[i].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return wall, per_launch_ms
+    return wall, e0.elapsed_time(e1) / steps
 
 
 CLOCK_SAMPLE_CALLS = 10
@@ -386,8 +391,8 @@ def sampled_clock(bd, dA, dB, C, w, sync, stages, calls=CLOCK_SAMPLE_CALLS):
 
 
 def measure_workload(bd, w, configs, args, torch, A=None, B=None):
-    """Every configuration on one workload: per-call time from HIP events on
-    the launch stream (mean, median, min), wall-clock throughput, % of peak,
+    """Every configuration on one workload: mean time per call from HIP events
+    on the launch stream around the timed calls, wall-clock throughput, % of peak,
     the clock sampled inside the kernels right after the timed loop and the
     MFMA-busy fraction it implies (FLOP rate over 1,048,576 FLOP per clock;
     for split calls the reduction kernel's time counts as not busy), and, where
@@ -402,14 +407,12 @@ def measure_workload(bd, w, configs, args, torch, A=None, B=None):
     res = {}
     for sync, stages in configs:
         plan = bd.gemm_bf16_plan(w.M, w.N, w.K, w.b_transposed, stages, bd.SYNC_MODES[sync])
-        wall, per = time_mode(bd, dA, dB, C, w, sync, stages, args.steps, args.warmup, torch)
-        mean_ms = sum(per) / len(per)
+        wall, mean_ms = time_mode(bd, dA, dB, C, w, sync, stages, args.steps, args.warmup, torch)
         tf = flops / (mean_ms * 1e-3) / 1e12
         e = {"tflops": round(tf, 2), "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
              "wall_tflops": round(flops / (wall / args.steps) / 1e12, 2),
              "ms_per_step": round(wall * 1e3 / args.steps, 4),
-             "kernel_ms_mean": round(mean_ms, 4), "kernel_ms_median": round(sorted(per)[len(per) // 2], 4),
-             "kernel_ms_min": round(min(per), 4),
+             "kernel_ms_mean": round(mean_ms, 4),
              "tile": "%dx%dx%d" % (plan["bm"], plan["bn"], plan["bk"]), "grid": plan["grid"],
              "k_splits": plan["k_splits"], "tail_tiles": plan["tail_tiles"], "mfma_block": plan["mfma_block"]}
         ghz = sampled_clock(bd, dA, dB, C, w, sync, stages)

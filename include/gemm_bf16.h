@@ -53,12 +53,8 @@
  * unsplit sum only by fp32 rounding, is the same for every sync mode and
  * stage count with the same tile, MFMA block and split (plan.bm, plan.bn,
  * plan.mfma_block, plan.k_splits), and is deterministic.  The fp32 partial tiles
- * (plan.workspace_bytes) are allocated stream-ordered on `stream` and
- * released (hipFreeAsync) by the same call, from a memory pool the library
- * creates once per device (hipMallocFromPoolAsync; hipMallocAsync if the pool
- * could not be created).  The pool keeps freed memory for later calls until
- * the process ends, so it holds as much as the largest workspaces in flight
- * at once.  A failed allocation returns GEMM_ERR_DEVICE.  Not a section of the pages: the
+ * (plan.workspace_bytes) live in temporary device memory the library keeps
+ * (see "Temporary memory" below).  Not a section of the pages: the
  * persistent schedule there assumes enough output tiles.
  *
  * Split tail: when the output tiles (in the chosen configuration's tile) do
@@ -179,14 +175,30 @@ typedef struct gemm_bf16_plan {
  *
  * Fast path: N and K multiples of 8, lda, ldb, ldc multiples of 8 and at most
  * 2^22, A, B, C 16-byte aligned.  Any other call copies A and B, zero-padded
- * to multiples of 8 elements, into compact buffers (plan.pad_bytes, from the
- * library's stream-ordered pool, released by the call), runs the fast path on
- * them and copies the N valid columns of the result into C.  The zero padding
+ * to multiples of 8 elements, into compact buffers (plan.pad_bytes, temporary
+ * memory as below), runs the fast path on them and copies the N valid columns
+ * of the result into C.  The zero padding
  * along K contributes only zero products, so results are those of the
  * unpadded problem.
  *
  * stages: 0 picks the default for the sync mode; otherwise 2, 3 or 4 whole
  * stages, or GEMM_STAGES_WINDOWS (barrier sync only).
+ *
+ * Temporary memory (split workspaces, padded copies): the library keeps
+ * blocks of device memory per device and reuses them; a call allocates only
+ * when no kept block fits, and nothing is freed until the process ends.  A
+ * block is reused by a later call on the stream of its last use (stream
+ * order makes that safe), or on any stream once the event it recorded after
+ * that use has completed.  So repeated calls on one stream reuse one block
+ * per size, and each stream that runs such calls concurrently with another
+ * holds its own.  New blocks are sized to a power of two of at least 1 MiB
+ * and allocated stream-ordered (hipMallocFromPoolAsync from a pool the
+ * library creates per device; hipMallocAsync if it could not be created).
+ * The calls never free memory and never wait for the GPU: a stream-ordered
+ * free (hipFreeAsync) returns only after the stream's queued work has
+ * finished.  Under graph capture the memory is allocated and freed inside
+ * the captured graph instead.  A failed allocation returns GEMM_ERR_DEVICE.
+ * gemm_bf16_workspace_info reports what is kept.
  * sync_mode: GEMM_SYNC_BARRIER, GEMM_SYNC_FLAGS, GEMM_SYNC_WAVESPEC or
  * GEMM_SYNC_PINGPONG.
  * stream: a hipStream_t (NULL for the null stream).
@@ -219,7 +231,7 @@ int gemm_bf16_bt(int64_t M, int64_t N, int64_t K,
  * allocation).  Same arguments, results and bits as gemm_bf16 (B stored
  * K x N); it calls no hipMalloc, hipFree or allocating library routine.
  *
- * Where gemm_bf16 takes temporary memory from the library's pool -- the fp32
+ * Where gemm_bf16 takes temporary memory the library keeps -- the fp32
  * partial tiles of a split k range or split tail (plan.workspace_bytes) and
  * the zero-padded operand copies of a call off the 8-element grid
  * (plan.pad_bytes, or less when only some operands need copying) -- this entry
@@ -305,6 +317,16 @@ int64_t gemm_bf16_sync_timeouts(int reset);
  * kernels still terminate normally.
  */
 int64_t gemm_bf16_set_sync_spin_limit(int64_t polls);
+
+/*
+ * gemm_bf16_workspace_info: the temporary memory the library keeps on the
+ * current device for split and padded calls ("Temporary memory" above):
+ * *blocks the number of blocks, *bytes their total size, *busy how many are
+ * taken by a call that is being enqueued right now (0 between calls).  Host
+ * memory, three int64_t; host-side only, does not synchronise.  Returns
+ * GEMM_OK, GEMM_ERR_INVALID_VALUE for a null pointer, or GEMM_ERR_DEVICE.
+ */
+int gemm_bf16_workspace_info(int64_t* blocks, int64_t* bytes, int64_t* busy);
 
 /*
  * Clock sampling, for measurement.  Under load the clock of these boards is

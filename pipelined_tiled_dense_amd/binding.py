@@ -83,6 +83,8 @@ def library() -> ctypes.CDLL:
         lib.gemm_bf16_set_clock_sampling.restype = i32
         lib.gemm_bf16_clock_samples.argtypes = [ctypes.POINTER(ctypes.c_uint64), i32]
         lib.gemm_bf16_clock_samples.restype = i32
+        lib.gemm_bf16_workspace_info.argtypes = [ctypes.POINTER(ctypes.c_int64)] * 3
+        lib.gemm_bf16_workspace_info.restype = i32
         _lib = lib
     return _lib
 
@@ -134,6 +136,16 @@ def gemm_bf16_set_sync_spin_limit(polls: int) -> int:
     if n < 0:
         raise GemmError(int(n), "gemm_bf16_set_sync_spin_limit")
     return int(n)
+
+
+def gemm_bf16_workspace_info() -> dict:
+    """The temporary memory the library keeps on the current device: blocks,
+    their total bytes, and how many are taken right now."""
+    blocks, nbytes, busy = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    rc = library().gemm_bf16_workspace_info(ctypes.byref(blocks), ctypes.byref(nbytes), ctypes.byref(busy))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_bf16_workspace_info")
+    return {"blocks": blocks.value, "bytes": nbytes.value, "busy": busy.value}
 
 
 def gemm_bf16_set_clock_sampling(enable: bool) -> bool:

@@ -85,6 +85,7 @@
 // Edges: buffer resources range-check every load and store.  Rows past M or
 // N, and the k tail of the last k-step, are read as zeros (the lane's offset is
 // pushed past the resource); stores past M or N are dropped the same way.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -94,6 +95,7 @@
 #include <mutex>
 #include <type_traits>
 #include <utility>
+#include <vector>
 
 #include "gemm_bf16.h"
 
@@ -2475,15 +2477,28 @@ int default_stages(int sync_mode)
 constexpr int64_t kScratchBytes = GEMM_NOALLOC_SCRATCH_BYTES;
 static __device__ __align__(256) char scratch[kScratchBytes];
 
+// A block of temporary device memory (split workspace, padded operand
+// copies) that the library keeps for later calls.
+struct WsBlock {
+    char* ptr = nullptr;
+    int64_t bytes = 0;
+    hipStream_t stream = nullptr;  // stream of the block's last use
+    hipEvent_t done = nullptr;     // recorded on `stream` right after that use
+    bool busy = false;             // taken by a call that has not handed it back
+};
+
 struct DeviceInfo {
     bool probed = false;
     int status = GEMM_OK;
     int cus = 0;
-    // Split workspaces come from this stream-ordered pool, which keeps freed
-    // memory for the next call instead of returning it to the device at
-    // every synchronisation (the default pool's behaviour), so a split call
-    // does not pay for a fresh allocation.  Null if it could not be created.
+    // New temporary blocks are allocated from this stream-ordered pool (the
+    // default pool if it could not be created).
     hipMemPool_t pool = nullptr;
+    // The blocks kept for reuse (guarded by g_dev_mutex).  None is ever
+    // freed: the runtime's stream-ordered free returns only once the
+    // stream's queued work has finished, which would stall the caller for
+    // the whole GPU time of every call that needs temporary memory.
+    std::vector<WsBlock> blocks;
     // This device's copy of `scratch` (null if its address could not be
     // taken: the allocation-free entry point then returns GEMM_ERR_DEVICE).
     char* scratch_ptr = nullptr;
@@ -2499,7 +2514,7 @@ constexpr int kMaxDevices = 64;
 std::mutex g_dev_mutex;
 DeviceInfo g_dev[kMaxDevices];
 
-int device_info(int* cus, hipMemPool_t* pool = nullptr, char** scratch_ptr = nullptr)
+int device_info(int* cus, hipMemPool_t* pool = nullptr, char** scratch_ptr = nullptr, DeviceInfo** info = nullptr)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
@@ -2538,6 +2553,8 @@ int device_info(int* cus, hipMemPool_t* pool = nullptr, char** scratch_ptr = nul
         d.probed = true;
     }
     *cus = d.cus;
+    if (info)
+        *info = &d;
     if (pool)
         *pool = d.pool;
     if (scratch_ptr)
@@ -2546,11 +2563,11 @@ int device_info(int* cus, hipMemPool_t* pool = nullptr, char** scratch_ptr = nul
 }
 
 // Where a call's temporary device memory (split workspaces, padded operand
-// copies) comes from.  Pooled (fixed == nullptr): stream-ordered allocations
-// from the library's per-device pool, each released by the same call.
-// Fixed: consecutive pieces of this device's scratch region, taken in order
-// and never released; nothing is allocated or freed.
+// copies) comes from.  Kept (fixed == nullptr): the device's reusable blocks
+// (temp_take).  Fixed: consecutive pieces of this device's scratch region,
+// taken in order and never released; nothing is allocated or freed.
 struct TempMem {
+    DeviceInfo* info = nullptr;
     hipMemPool_t pool = nullptr;
     char* fixed = nullptr;
     int64_t fixed_left = 0;
@@ -2561,9 +2578,30 @@ int64_t align256(int64_t b)
     return (b + 255) & ~(int64_t)255;
 }
 
-int temp_take(TempMem& t, int64_t bytes, hipStream_t s, void** p)
+hipError_t pool_alloc(const TempMem& t, void** p, int64_t bytes, hipStream_t s)
+{
+    return t.pool ? hipMallocFromPoolAsync(p, (size_t)bytes, t.pool, s) : hipMallocAsync(p, (size_t)bytes, s);
+}
+
+// Temporary memory of `bytes` for one call on stream s, handed back with
+// temp_give once the call's work on it is enqueued.
+//
+// Kept blocks: the smallest free block that is large enough and either was
+// last used on s (stream order puts that use before this one) or whose
+// completion event has fired.  Without one, a new block -- the size rounded
+// up to a power of two, at least 1 MiB, so that one block serves a range of
+// calls -- is allocated stream-ordered on s and kept.  Calls on one stream
+// therefore reuse one block per size they need at once, and each stream that
+// runs such calls at the same time as another holds its own.
+//
+// Under graph capture the memory is allocated and freed inside the graph
+// instead (nothing runs at capture, so the free does not stall), as each
+// replay's own allocation.
+int temp_take(TempMem& t, int64_t bytes, hipStream_t s, void** p, hipEvent_t* done = nullptr)
 {
     *p = nullptr;
+    if (done)
+        *done = nullptr;
     if (t.fixed) {
         const int64_t need = align256(bytes);
         if (need > t.fixed_left)
@@ -2573,14 +2611,78 @@ int temp_take(TempMem& t, int64_t bytes, hipStream_t s, void** p)
         t.fixed_left -= need;
         return GEMM_OK;
     }
-    const hipError_t e = t.pool ? hipMallocFromPoolAsync(p, (size_t)bytes, t.pool, s) : hipMallocAsync(p, (size_t)bytes, s);
-    return (e == hipSuccess && *p) ? GEMM_OK : GEMM_ERR_DEVICE;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_ERR_DEVICE;
+    }
+    if (cs != hipStreamCaptureStatusNone) {
+        const hipError_t e = pool_alloc(t, p, bytes, s);
+        return (e == hipSuccess && *p) ? GEMM_OK : GEMM_ERR_DEVICE;
+    }
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    std::vector<WsBlock>& v = t.info->blocks;
+    int best = -1;
+    for (int i = 0; i < (int)v.size(); ++i) {
+        const WsBlock& b = v[i];
+        if (b.busy || b.bytes < bytes || (best >= 0 && v[best].bytes <= b.bytes))
+            continue;
+        if (b.stream != s && hipEventQuery(b.done) != hipSuccess) {
+            (void)hipGetLastError();   // not finished yet: no error for the caller's next call
+            continue;
+        }
+        best = i;
+    }
+    if (best < 0) {
+        int64_t size = (int64_t)1 << 20;
+        while (size < bytes)
+            size <<= 1;
+        WsBlock b;
+        if (hipEventCreateWithFlags(&b.done, hipEventDisableTiming) != hipSuccess) {
+            (void)hipGetLastError();
+            return GEMM_ERR_DEVICE;
+        }
+        void* q = nullptr;
+        if (pool_alloc(t, &q, size, s) != hipSuccess || !q) {
+            (void)hipEventDestroy(b.done);
+            (void)hipGetLastError();
+            return GEMM_ERR_DEVICE;
+        }
+        b.ptr = (char*)q;
+        b.bytes = size;
+        v.push_back(b);
+        best = (int)v.size() - 1;
+    }
+    v[best].busy = true;
+    v[best].stream = s;
+    *p = v[best].ptr;
+    if (done)
+        *done = v[best].done;
+    return GEMM_OK;
 }
 
-int temp_give(const TempMem& t, void* p, hipStream_t s)
+// Hands back what temp_take gave: a kept block becomes free once its
+// completion event is recorded on s after the call's work on it -- here, or,
+// with `recorded`, already by the launch of the last kernel that uses it
+// (as that kernel's completion, with no separate marker on the stream);
+// memory taken under graph capture is freed in the graph.
+int temp_give(const TempMem& t, void* p, hipStream_t s, bool recorded = false)
 {
-    if (t.fixed)
+    if (t.fixed || !p)
         return GEMM_OK;
+    {
+        std::lock_guard<std::mutex> lock(g_dev_mutex);
+        for (WsBlock& b : t.info->blocks)
+            if (b.busy && b.ptr == (char*)p) {
+                if (!recorded && hipEventRecord(b.done, s) != hipSuccess) {
+                    // Its last use has no event to wait on: it stays taken.
+                    (void)hipGetLastError();
+                    return GEMM_ERR_DEVICE;
+                }
+                b.busy = false;
+                return GEMM_OK;
+            }
+    }
     return hipFreeAsync(p, s) == hipSuccess ? GEMM_OK : GEMM_ERR_DEVICE;
 }
 
@@ -2828,7 +2930,7 @@ int gemm_entry(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
     int cus = 0;
     TempMem tm;
     char* scratch_ptr = nullptr;
-    rc = device_info(&cus, &tm.pool, &scratch_ptr);
+    rc = device_info(&cus, &tm.pool, &scratch_ptr, &tm.info);
     if (rc != GEMM_OK)
         return rc;
     hipStream_t s = (hipStream_t)stream;
@@ -2916,7 +3018,8 @@ int gemm_direct(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
     // that lives for this call only, so calls on different streams never
     // share it).
     void* ws = nullptr;
-    rc = temp_take(tm, pl.workspace_bytes, s, &ws);
+    hipEvent_t ws_done = nullptr;   // the kept block's completion event (null: none to record)
+    rc = temp_take(tm, pl.workspace_bytes, s, &ws, &ws_done);
     if (rc != GEMM_OK)
         return rc;
     Params q = p;   // the launch whose partial tiles are reduced
@@ -2940,12 +3043,15 @@ int gemm_direct(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
         int64_t blocks = (units + 255) / 256;
         if (blocks > 65536)
             blocks = 65536;
+        // The reduction is the workspace's last use: its completion records
+        // the block's event.
         rc = with_cfg(sync_mode, pl.stages, bt, [&]<class C>() {
-            hipLaunchKernelGGL(k_reduce_splits<C>, dim3((unsigned)blocks), dim3(256), 0, s, q);
+            hipExtLaunchKernelGGL(k_reduce_splits<C>, dim3((unsigned)blocks), dim3(256), 0, s, nullptr, ws_done, 0,
+                                  q);
             return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
         });
     }
-    const int frc = temp_give(tm, ws, s);
+    const int frc = temp_give(tm, ws, s, rc == GEMM_OK && ws_done != nullptr);
     return rc != GEMM_OK ? rc : frc;
 }
 
@@ -3041,6 +3147,26 @@ int64_t gemm_bf16_sync_timeouts(int reset)
             return GEMM_ERR_DEVICE;
     }
     return (int64_t)v;
+}
+
+int gemm_bf16_workspace_info(int64_t* blocks, int64_t* bytes, int64_t* busy)
+{
+    if (!blocks || !bytes || !busy)
+        return GEMM_ERR_INVALID_VALUE;
+    int cus = 0;
+    DeviceInfo* info = nullptr;
+    int rc = device_info(&cus, nullptr, nullptr, &info);
+    if (rc != GEMM_OK)
+        return rc;
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    *blocks = (int64_t)info->blocks.size();
+    *bytes = 0;
+    *busy = 0;
+    for (const WsBlock& b : info->blocks) {
+        *bytes += b.bytes;
+        *busy += b.busy ? 1 : 0;
+    }
+    return GEMM_OK;
 }
 
 int gemm_bf16_set_clock_sampling(int enable)

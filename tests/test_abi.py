@@ -65,6 +65,11 @@ def test_probe_library_exports():
         assert n in syms
 
 
+def test_workspace_info_rejects_null_pointers():
+    """Checked before the device is touched."""
+    assert bd.library().gemm_bf16_workspace_info(None, None, None) == bd.GEMM_ERR_INVALID_VALUE
+
+
 ALIGNED = 1 << 20        # fake, 16-byte aligned addresses: never dereferenced by these cases
 
 

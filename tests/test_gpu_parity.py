@@ -417,8 +417,9 @@ def test_unaligned_zero_k():
 
 
 def test_concurrent_split_calls_on_two_streams():
-    """Split calls take their workspaces from one stream-ordered pool.  Calls
-    on two streams, interleaved with no synchronisation between them (a split
+    """Split and padded calls take their temporary memory from the blocks the
+    library keeps per device.  Calls on two streams, interleaved with no
+    synchronisation between them (a split
     k range on one, a split tail and an off-grid shape on the other), must
     each give the bits of the same call run alone."""
     cases = [((1000, 1032, 8192), True), ((4300, 4344, 4096), False), ((37, 45, 4100), True)]
