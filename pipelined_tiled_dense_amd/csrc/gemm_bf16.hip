@@ -924,6 +924,13 @@ struct FragReader {
             } else {
                 const int q = r16 & 3, rr = r16 >> 2;
                 r = 2 * rr + (h & 1);
+                // With one fragment set per wave (two MFMA waves per SIMD
+                // beside loader waves, 168 registers each) the four B block
+                // offsets derived from r would stay live through the k-step
+                // loop and push it into spills; an opaque r makes them be
+                // recomputed (two VALU operations per read) at every k-step.
+                if constexpr (C::PRODUCERS && C::NCW == 8)
+                    r = (int)opaque((uint32_t)r);
                 const uint32_t krow0 = (uint32_t)(32 * kk + 8 * h + rr);
                 b_off = opaque(krow0 * (C::BN * 2) + (uint32_t)((q >> 1) * 16 + (q & 1) * 8));
             }
@@ -2356,16 +2363,16 @@ struct Pick {
 // 32 x 32 blocks (24 registers) fit, two sets do not, so these MFMA waves run
 // k_gemm_ws's single-buffered loop and rely on the other MFMA wave of their
 // SIMD to cover their fragment reads.  Two 64-wide stages or four 32-wide
-// ones fill 128 KiB.  With B stored N x K the 2-stage ring uses 16 x 16
-// blocks instead, half a 32-wide k-step of fragments at a time (32
-// registers); with a K x N B their transposing reads need more registers
-// than that leaves, and the 32 x 32 form runs faster.  The 3-stage ring
-// keeps the 256 x 128 tile with one MFMA wave per SIMD and double-buffered
-// fragments.
+// ones fill 128 KiB.  The 2-stage ring uses 16 x 16 blocks instead, half a
+// 32-wide k-step of fragments at a time (32 registers); with a K x N B that
+// fits only because FragReader recomputes the lane-dependent offsets of the
+// transposing B reads at every k-step instead of keeping them live.  The
+// 3-stage ring keeps the 256 x 128 tile with one MFMA wave per SIMD and
+// double-buffered fragments.
 template <>
 struct Pick<SYNC_WAVESPEC, 2> {
     template <bool BT>
-    using type = Cfg<256, 256, 64, 2, 2, 4, SYNC_WAVESPEC, BT, 4, false, BT ? 16 : 32>;
+    using type = Cfg<256, 256, 64, 2, 2, 4, SYNC_WAVESPEC, BT, 4, false, 16>;
 };
 
 template <>
@@ -2462,9 +2469,11 @@ auto with_cfg(int sync_mode, int stages, bool bt, F&& f)
 // instead of 16 rows of 64, which the texture path serves markedly faster.
 // The LDS holds two such stages of a 256 x 256 tile and three of the
 // wave-specialised mode's 256 x 128.
+// stages == 0: two for every mode but ping-pong, whose 3-stage ring shares one
+// ring between its groups.
 int default_stages(int sync_mode)
 {
-    return (sync_mode == GEMM_SYNC_WAVESPEC || sync_mode == GEMM_SYNC_PINGPONG) ? 3 : 2;
+    return sync_mode == GEMM_SYNC_PINGPONG ? 3 : 2;
 }
 
 // The allocation-free entry point's temporary memory: one region per GPU the

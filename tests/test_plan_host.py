@@ -29,12 +29,13 @@ SHAPES = {("barrier", 2): (256, 256, 64, 8, 0), ("barrier", 3): (256, 256, 32, 8
 
 
 # MFMA block edge: 16 x 16 x 32 MFMAs everywhere but the wave-specialised
-# rings with two MFMA waves per SIMD (256 x 256 tiles), whose one fragment
-# set per wave holds 32 x 32 x 16 blocks -- except the 2-stage ring with B
-# stored N x K, which reads half a 16 x 16 k-step at a time.
+# 4-stage ring (two MFMA waves per SIMD over 256 x 256 tiles, 32-wide
+# stages), whose one fragment set per wave holds 32 x 32 x 16 blocks.  The
+# 2-stage ring of that layout reads half a 32-wide k-step of 16 x 16 blocks
+# at a time, with either B layout.
 def mfma_block(sync, stages, bt):
-    if sync == "wavespec" and SHAPES[(sync, stages)][3] == 8:
-        return 16 if (stages == 2 and bt) else 32
+    if sync == "wavespec" and stages == 4:
+        return 32
     return 16
 
 
@@ -95,7 +96,7 @@ def test_tile_configuration(sync, stages, bt):
 def test_default_stages():
     assert plan(512, 512, 512, 1, "barrier", 0)["stages"] == 2
     assert plan(512, 512, 512, 1, "flags", 0)["stages"] == 2
-    assert plan(512, 512, 512, 1, "wavespec", 0)["stages"] == 3
+    assert plan(512, 512, 512, 1, "wavespec", 0)["stages"] == 2
     assert plan(512, 512, 512, 1, "pingpong", 0)["stages"] == 3
     assert plan(512, 512, 512, 1, "barrier", bd.STAGES_WINDOWS)["lds_bytes"] == 5 * 256 * 64 * 2
 
