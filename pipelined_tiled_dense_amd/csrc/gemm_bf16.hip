@@ -116,6 +116,9 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 
 // A byte offset no resource covers: loads there return zeros, stores vanish.
 constexpr uint32_t kOOB = 0x80000000u;
+// Cache policies of buffer stores: the default, and non-temporal (the nt bit).
+constexpr int kStoreDefault = 0;
+constexpr int kStoreNonTemporal = 2;
 constexpr uint32_t kMaxRecords = 0x7FFFFFF0u;
 // Raw buffer resource, 32-bit data format (third descriptor word for gfx9).
 constexpr int kRsrcWord3 = 0x00020000;
@@ -212,6 +215,18 @@ struct Cfg {
     static constexpr int NLW = PRODUCERS ? NP / PIPES : NCW; // waves that load one position
     static constexpr int NW = NCW + NP;
     static constexpr int THREADS = NW * 64;
+    // Cache policy of the stores of C.  C is written once and never read back
+    // by the GEMM, and each XCD writes as much C per round of output tiles as
+    // its L2 holds; stored normally those lines displace operand lines that
+    // the XCD's other workgroups are still reading, so C goes out
+    // non-temporal (measured +1-6% on the barrier and flag kernels, level on
+    // the wave-specialised ones).  Ping-pong over one shared ring, where one
+    // group's epilogue runs beside the other group's main loop, measured
+    // 3-5% slower with it and keeps the default.  Operand loads keep the
+    // default policy (non-temporal loads lost 10-40%: their lines are reused
+    // across the XCD's workgroups within a few k-steps), and so do fp32
+    // partial tiles, which the reduction reads right back.
+    static constexpr int STORE_C = (SYNC == SYNC_PINGPONG && !DUAL) ? kStoreDefault : kStoreNonTemporal;
     static constexpr int TM = BM / WM, TN = BN / WN;                 // wave tile
     // MFMA block edge.  32: v_mfma_f32_32x32x16_bf16, one 16-wide k-step per
     // MFMA region.  16: v_mfma_f32_16x16x32_bf16, whose 32-wide k-step takes
@@ -1279,7 +1294,7 @@ __device__ __forceinline__ void epilogue(const Params& p, f32x16_t (&acc)[C::FM]
                 if (u >= 2)
                     v = u32x4_t{v.z, v.w, v.x, v.y};
                 const bool ok = (gr0 + 8 * u < mrem) && (gc < nrem);
-                __builtin_amdgcn_raw_buffer_store_b128(v, rc, ok ? obase + (uint32_t)(8 * u) * ldc2 : kOOB, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(v, rc, ok ? obase + (uint32_t)(8 * u) * ldc2 : kOOB, 0, C::STORE_C);
             }
             wait_lgkm0();
         }
@@ -1332,7 +1347,7 @@ __device__ __forceinline__ void epilogue_narrow(const Params& p, f32x16_t (&acc)
                 if (u == 1)
                     v = u32x4_t{v.z, v.w, v.x, v.y};
                 const bool ok = (gr0 + 16 * u < mrem) && (gc < nrem);
-                __builtin_amdgcn_raw_buffer_store_b128(v, rc, ok ? obase + (uint32_t)(16 * u) * ldc2 : kOOB, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(v, rc, ok ? obase + (uint32_t)(16 * u) * ldc2 : kOOB, 0, C::STORE_C);
             }
             wait_lgkm0();
         }
@@ -1392,7 +1407,7 @@ __device__ __forceinline__ void epilogue16(const Params& p, f32x4_t (&acc)[C::FM
                 const int row = rrow + RPI * u;
                 const u32x4_t v = *(const LDS_AS u32x4_t*)(strip + row * RB + ((rchunk ^ swz(row)) << 4));
                 const bool ok = (gr0 + RPI * u < mrem) && (gc < nrem);
-                __builtin_amdgcn_raw_buffer_store_b128(v, rc, ok ? obase + (uint32_t)(RPI * u) * ldc2 : kOOB, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(v, rc, ok ? obase + (uint32_t)(RPI * u) * ldc2 : kOOB, 0, C::STORE_C);
             }
             wait_lgkm0();
         }
