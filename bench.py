@@ -64,7 +64,7 @@ CONFIGS = [("pingpong", 2), ("pingpong", 3), ("pingpong", 4),
            ("wavespec", 2), ("wavespec", 3), ("wavespec", 4),
            ("flags", 2), ("flags", 3), ("flags", 4),
            ("barrier", 3), ("barrier", 4), ("barrier", 5), ("barrier", 2)]
-DEFAULT_STAGES = {"barrier": 2, "flags": 2, "wavespec": 2, "pingpong": 3}
+DEFAULT_STAGES = {"barrier": 5, "flags": 2, "wavespec": 2, "pingpong": 3}
 
 
 def label(sync, stages):

@@ -181,8 +181,9 @@ typedef struct gemm_bf16_plan {
  * along K contributes only zero products, so results are those of the
  * unpadded problem.
  *
- * stages: 0 picks the default for the sync mode (3 for GEMM_SYNC_PINGPONG,
- * 2 for the others); otherwise 2, 3 or 4 whole
+ * stages: 0 picks the default for the sync mode (GEMM_STAGES_WINDOWS for
+ * GEMM_SYNC_BARRIER, 3 for GEMM_SYNC_PINGPONG, 2 for the others); otherwise
+ * 2, 3 or 4 whole
  * stages, or GEMM_STAGES_WINDOWS (barrier sync only).
  *
  * Temporary memory (split workspaces, padded copies): the library keeps

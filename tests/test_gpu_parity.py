@@ -242,7 +242,7 @@ def test_plans():
             assert pl["lds_bytes"] <= 160 * 1024, (sync, stages, pl)
     pl = bd.gemm_bf16_plan(8192, 8192, 8192, True, bd.STAGES_WINDOWS, 0)
     assert pl["lds_bytes"] == 5 * 256 * 64 * 2
-    assert bd.gemm_bf16_plan(8192, 8192, 8192, True, 0, 0)["stages"] == 2
+    assert bd.gemm_bf16_plan(8192, 8192, 8192, True, 0, 0)["stages"] == bd.STAGES_WINDOWS
     assert bd.gemm_bf16_plan(8192, 8192, 8192, True, 0, 2)["stages"] == 2
     assert bd.gemm_bf16_plan(8192, 8192, 8192, True, 0, 3)["stages"] == 3
     assert bd.gemm_bf16_plan(8192, 8192, 8192, True, 0, 3)["tiles"] == 64 * 64

@@ -94,7 +94,7 @@ def test_tile_configuration(sync, stages, bt):
 
 
 def test_default_stages():
-    assert plan(512, 512, 512, 1, "barrier", 0)["stages"] == 2
+    assert plan(512, 512, 512, 1, "barrier", 0)["stages"] == bd.STAGES_WINDOWS
     assert plan(512, 512, 512, 1, "flags", 0)["stages"] == 2
     assert plan(512, 512, 512, 1, "wavespec", 0)["stages"] == 2
     assert plan(512, 512, 512, 1, "pingpong", 0)["stages"] == 3
