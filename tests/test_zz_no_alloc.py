@@ -59,7 +59,8 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("sync,stages", [("barrier", 2), ("wavespec", 3), ("pingpong", 3), ("flags", 2)])
+@pytest.mark.parametrize("sync,stages", [("barrier", 2), ("barrier", 0), ("wavespec", 0), ("wavespec", 3), ("pingpong", 2),
+                                         ("pingpong", 3), ("flags", 2)])
 def test_noalloc_equals_gemm_bf16(sync, stages):
     """Every case in order (larger temporary memory first), same bits as
     gemm_bf16; the largest and a padded one also against the oracle."""
