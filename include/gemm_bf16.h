@@ -183,27 +183,27 @@ typedef struct gemm_bf16_plan {
  *
  * stages: 0 picks the default for the sync mode (GEMM_STAGES_WINDOWS for
  * GEMM_SYNC_BARRIER, 3 for GEMM_SYNC_PINGPONG, 2 for the others); otherwise
- * 2, 3 or 4 whole
- * stages, or GEMM_STAGES_WINDOWS (barrier sync only).
- *
- * Temporary memory (split workspaces, padded copies): the library keeps
- * blocks of device memory per device and reuses them; a call allocates only
- * when no kept block fits, and nothing is freed until the process ends.  A
- * block is reused by a later call on the stream of its last use (stream
- * order makes that safe), or on any stream once the event it recorded after
- * that use has completed.  So repeated calls on one stream reuse one block
- * per size, and each stream that runs such calls concurrently with another
- * holds its own.  New blocks are sized to a power of two of at least 1 MiB
- * and allocated stream-ordered (hipMallocFromPoolAsync from a pool the
- * library creates per device; hipMallocAsync if it could not be created).
- * The calls never free memory and never wait for the GPU: a stream-ordered
- * free (hipFreeAsync) returns only after the stream's queued work has
- * finished.  Under graph capture the memory is allocated and freed inside
- * the captured graph instead.  A failed allocation returns GEMM_ERR_DEVICE.
- * gemm_bf16_workspace_info reports what is kept.
+ * 2, 3 or 4 whole stages, or GEMM_STAGES_WINDOWS (barrier sync only).
  * sync_mode: GEMM_SYNC_BARRIER, GEMM_SYNC_FLAGS, GEMM_SYNC_WAVESPEC or
  * GEMM_SYNC_PINGPONG.
  * stream: a hipStream_t (NULL for the null stream).
+ *
+ * Temporary memory (split workspaces, padded copies): the library keeps
+ * blocks of device memory per device and reuses them; a call allocates only
+ * when no kept block fits, and frees nothing (gemm_bf16_release_workspaces
+ * does, on request).  A block is reused by a later call on the stream of its
+ * last use (stream order makes that safe), or on any stream once the event
+ * it recorded after that use has completed.  So repeated calls on one stream
+ * reuse one block per size, and each stream that runs such calls
+ * concurrently with another holds its own.  New blocks are sized to a power
+ * of two of at least 1 MiB and allocated stream-ordered
+ * (hipMallocFromPoolAsync from a pool the library creates per device;
+ * hipMallocAsync if it could not be created).  The calls never wait for the
+ * GPU: a stream-ordered free (hipFreeAsync) returns only after the stream's
+ * queued work has finished, which is why they keep their blocks.  Under
+ * graph capture the memory is allocated and freed inside the captured graph
+ * instead.  A failed allocation returns GEMM_ERR_DEVICE.
+ * gemm_bf16_workspace_info reports what is kept.
  *
  * Returns GEMM_OK once the work is enqueued, else a negative status.
  * Validation that does not need the device happens before any HIP call; after
@@ -329,6 +329,17 @@ int64_t gemm_bf16_set_sync_spin_limit(int64_t polls);
  * GEMM_OK, GEMM_ERR_INVALID_VALUE for a null pointer, or GEMM_ERR_DEVICE.
  */
 int gemm_bf16_workspace_info(int64_t* blocks, int64_t* bytes, int64_t* busy);
+
+/*
+ * gemm_bf16_release_workspaces: frees the temporary memory the library keeps
+ * on the current device ("Temporary memory" above) and returns it from the
+ * library's pool to the device.  Synchronises the device first; calls made
+ * from other threads meanwhile wait for it.  A block that another thread's
+ * call holds at that moment stays kept.  Later split and padded calls
+ * allocate again as needed.  Not for use under graph capture.  Returns
+ * GEMM_OK or GEMM_ERR_DEVICE.
+ */
+int gemm_bf16_release_workspaces(void);
 
 /*
  * Clock sampling, for measurement.  Under load the clock of these boards is

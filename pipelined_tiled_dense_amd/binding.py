@@ -85,6 +85,8 @@ def library() -> ctypes.CDLL:
         lib.gemm_bf16_clock_samples.restype = i32
         lib.gemm_bf16_workspace_info.argtypes = [ctypes.POINTER(ctypes.c_int64)] * 3
         lib.gemm_bf16_workspace_info.restype = i32
+        lib.gemm_bf16_release_workspaces.argtypes = []
+        lib.gemm_bf16_release_workspaces.restype = i32
         _lib = lib
     return _lib
 
@@ -146,6 +148,14 @@ def gemm_bf16_workspace_info() -> dict:
     if rc != GEMM_OK:
         raise GemmError(rc, "gemm_bf16_workspace_info")
     return {"blocks": blocks.value, "bytes": nbytes.value, "busy": busy.value}
+
+
+def gemm_bf16_release_workspaces() -> None:
+    """Frees the temporary memory the library keeps on the current device
+    (synchronises the device)."""
+    rc = library().gemm_bf16_release_workspaces()
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_bf16_release_workspaces")
 
 
 def gemm_bf16_set_clock_sampling(enable: bool) -> bool:

@@ -3196,6 +3196,47 @@ int gemm_bf16_workspace_info(int64_t* blocks, int64_t* bytes, int64_t* busy)
     return GEMM_OK;
 }
 
+int gemm_bf16_release_workspaces(void)
+{
+    int cus = 0;
+    DeviceInfo* info = nullptr;
+    int rc = device_info(&cus, nullptr, nullptr, &info);
+    if (rc != GEMM_OK)
+        return rc;
+    // Under the lock no call can take a block; the device synchronisation
+    // then finishes every use already enqueued, so the free blocks are idle.
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (hipDeviceSynchronize() != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_ERR_DEVICE;
+    }
+    int status = GEMM_OK;
+    std::vector<WsBlock> keep;
+    for (WsBlock& b : info->blocks) {
+        // A block is busy only while a call on another thread enqueues its
+        // work; that call still owns it.
+        if (!b.busy && hipFreeAsync(b.ptr, nullptr) == hipSuccess) {
+            (void)hipEventDestroy(b.done);
+            continue;
+        }
+        if (!b.busy) {
+            (void)hipGetLastError();
+            status = GEMM_ERR_DEVICE;
+        }
+        keep.push_back(b);
+    }
+    info->blocks.swap(keep);
+    if (hipStreamSynchronize(nullptr) != hipSuccess) {
+        (void)hipGetLastError();
+        status = GEMM_ERR_DEVICE;
+    }
+    if (info->pool && hipMemPoolTrimTo(info->pool, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        status = GEMM_ERR_DEVICE;
+    }
+    return status;
+}
+
 int gemm_bf16_set_clock_sampling(int enable)
 {
     return g_clock_on.exchange(enable != 0) ? 1 : 0;

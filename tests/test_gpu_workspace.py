@@ -1,8 +1,8 @@
 """Temporary memory of split and padded calls on the GPU: the library keeps
 blocks and reuses them, so repeated calls on one stream allocate nothing after
 the first, the calling thread never waits for the GPU, results are those of
-the same call run alone, and a split call captured in a HIP graph gets its
-memory inside the graph."""
+the same call run alone, a split call captured in a HIP graph gets its memory
+inside the graph, and the kept blocks can be released on request."""
 import time
 
 import numpy as np
@@ -140,3 +140,20 @@ def test_split_call_under_graph_capture():
         torch.cuda.synchronize()
         np.testing.assert_array_equal(bits(C.cpu()), want, err_msg="replay %d" % rep)
         np.testing.assert_array_equal(bits(other.cpu()), want, err_msg="eager %d" % rep)
+
+
+def test_release_workspaces():
+    """After a split and a padded call the library keeps blocks; releasing
+    them leaves none, and the same calls then allocate again and give the
+    same bits."""
+    sA, sB = operands(SPLIT, True, 41)
+    pA, pB = operands(PADDED, False, 42)
+    want = (bits(bd.gemm(sA, sB, b_transposed=True).cpu()), bits(bd.gemm(pA, pB).cpu()))
+    assert bd.gemm_bf16_workspace_info()["blocks"] >= 1
+    bd.gemm_bf16_release_workspaces()
+    info = bd.gemm_bf16_workspace_info()
+    assert (info["blocks"], info["bytes"], info["busy"]) == (0, 0, 0), info
+    got = (bits(bd.gemm(sA, sB, b_transposed=True).cpu()), bits(bd.gemm(pA, pB).cpu()))
+    np.testing.assert_array_equal(got[0], want[0])
+    np.testing.assert_array_equal(got[1], want[1])
+    assert bd.gemm_bf16_workspace_info()["blocks"] >= 1
