@@ -463,11 +463,11 @@ def random_shapes(seed, n):
 
 @pytest.mark.parametrize("bt", [False, True], ids=["kn", "nk"])
 def test_random_shapes_all_modes(bt):
-    """Eight seeded random shapes (some split along k in some tiles, see
+    """Twenty-four seeded random shapes (some split along k in some tiles, see
     random_shapes), every mode, compared in full with the oracle; modes with
     the same split signature agree bit for bit."""
     splits = set()
-    for M, N, K in random_shapes(9000 + bt, 8):
+    for M, N, K in random_shapes(9000 + bt, 24):
         A, B = make_operands(M, N, K, b_transposed=bt, seed=M + 7 * N + 13 * K)
         ref = oracle.load().gemm_bf16(bits(A), bits(B), bt)
         dA, dB = A.cuda(), B.cuda()
