@@ -78,9 +78,10 @@
 // * Counter initialisation happens before any wave can arrive on a counter
 //   ("[Tutorial] Fix race condition in 2SM TMEM alloc ...", sections
 //   "Problem" and "Fix"): counters are zeroed, then one workgroup barrier,
-//   then the first arrive or poll.  Every counter wait is bounded; a wait that
-//   gives up is counted (gemm_bf16_sync_timeouts) and the wave leaves the
-//   kernel instead of hanging.
+//   then the first arrive or poll.  Every counter wait is bounded: a wait that
+//   gives up is counted (gemm_bf16_sync_timeouts), marks its workgroup, and
+//   the wave finishes its loops instead of hanging; the workgroup then writes
+//   every output tile its reads may have corrupted as NaN.
 //
 // Edges: buffer resources range-check every load and store.  Rows past M or
 // N, and the k tail of the last k-step, are read as zeros (the lane's offset is
@@ -192,7 +193,7 @@ enum {
 // Compile-time configuration of one kernel instance.
 // ---------------------------------------------------------------------------
 template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, int SYNC_, bool BT_, int NP_, bool WIN_ = false,
-          int MF_ = 32, bool DUAL_ = false>
+          int MF_ = 32, bool DUAL_ = false, int SPREAD_ = 0>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_;
     static constexpr int SYNC = SYNC_;
@@ -264,6 +265,14 @@ struct Cfg {
     // at least this many k-steps per tile.
     static constexpr bool PREP_IN_REGION = KK >= 3;
     static constexpr int LONGK_MIN_KT = WIN ? 3 : S + (PREP_IN_REGION ? 1 : 2);
+    // Loader waves: s_sleep argument (units of 64 cycles) between pairs of
+    // a position's DMA instructions, 0 for one burst.  When every workgroup
+    // of an XCD issues the same panel slice at the same moment, their
+    // requests for a line reach the L2 while its first miss is still
+    // outstanding, and each of them misses and fetches the line again;
+    // spread over part of the position's compute time, the later requests
+    // find it.  Chosen per configuration by measurement (Pick below).
+    static constexpr int SPREAD_SLEEP = PRODUCERS ? SPREAD_ : 0;
 
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(KK % 2 == 0, "fragment double buffering assumes an even number of MFMA k-steps");
@@ -275,6 +284,7 @@ struct Cfg {
     static_assert(CPR_N == 16 || CPR_N == 32, "a DMA window covers whole K x N rows of B");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(S >= 2 && S <= 4, "stages");
+    static_assert(SPREAD_ >= 0 && SPREAD_ <= 8 && (SPREAD_ == 0 || PRODUCERS), "loader spread");
     static_assert(!DUAL || (SYNC == SYNC_PINGPONG && NP % GROUPS == 0), "one pipeline per ping-pong group");
     static_assert(!WIN || (SYNC == SYNC_BARRIER && S == 2 && KK == 4 && A_BYTES == B_BYTES &&
                            NCW * EPI_WAVE_BYTES <= A_BYTES),
@@ -1914,7 +1924,17 @@ __device__ __forceinline__ void producer_loop(const Params& p, lds_char* smem, l
         // group that computes the position.
         if (q >= C::S)
             wait_counter(empty + s, (uint32_t)(q / C::S) * C::NCWG, st);
-        ld.issue_next(p, smem + s * C::STAGE_BYTES, lw, lane);
+        if constexpr (C::SPREAD_SLEEP > 0) {
+            const auto pr = ld.prepare_and_advance(p);
+#pragma unroll
+            for (int t = 0; t < C::LOADS; ++t) {
+                ld.fire_one(pr, t, smem + s * C::STAGE_BYTES, lw, lane);
+                if (t % 2 == 1 && t + 1 < C::LOADS)
+                    __builtin_amdgcn_s_sleep(C::SPREAD_SLEEP);
+            }
+        } else {
+            ld.issue_next(p, smem + s * C::STAGE_BYTES, lw, lane);
+        }
         if (q >= D) {
             wait_vmcnt<C::LOADS * D>();
             arrive(full + (q - D) % C::S);
@@ -2384,33 +2404,41 @@ struct Pick {
 // transposing B reads at every k-step instead of keeping them live.  The
 // 3-stage ring keeps the 256 x 128 tile with one MFMA wave per SIMD and
 // double-buffered fragments.
+//
+// The loaders' spread (the last Cfg argument, s_sleep units between pairs of
+// DMA instructions) was measured per configuration on the three large
+// workloads: 2 for the 2-stage ring (+1-8%; L2 misses per call 3.8 -> 2.1
+// GB at 8192^3), 3 for the 4-stage ring (+3-4%).  The 3-stage ring keeps
+// one burst (with a spread it measured up to 1% slower).
 template <>
 struct Pick<SYNC_WAVESPEC, 2> {
     template <bool BT>
-    using type = Cfg<256, 256, 64, 2, 2, 4, SYNC_WAVESPEC, BT, 4, false, 16>;
+    using type = Cfg<256, 256, 64, 2, 2, 4, SYNC_WAVESPEC, BT, 4, false, 16, false, 2>;
 };
 
 template <>
 struct Pick<SYNC_WAVESPEC, 4> {
     template <bool BT>
-    using type = Cfg<256, 256, 32, 4, 2, 4, SYNC_WAVESPEC, BT, 4, false, 32>;
+    using type = Cfg<256, 256, 32, 4, 2, 4, SYNC_WAVESPEC, BT, 4, false, 32, false, 3>;
 };
 
 // Ping-pong: each of the two MFMA groups needs a wave on every SIMD, so
 // with the loader waves a SIMD holds three waves and each has about a third
 // of the register file: the groups' tiles are 128 x 128 (4 waves of 64 x 64).
 // A stage is 32 KiB at 64-wide k-steps, so up to 4 stages fit in one shared
-// ring, or two per group in the 2-stage instance's per-group rings.
+// ring, or two per group in the 2-stage instance's per-group rings.  The
+// loaders sleep one unit between pairs of DMA instructions (measured 0-6%
+// faster than one burst; longer sleeps starve these smaller stages).
 template <int S>
 struct Pick<SYNC_PINGPONG, S> {
     template <bool BT>
-    using type = Cfg<128, 128, 64, S, 2, 2, SYNC_PINGPONG, BT, 4, false, 16>;
+    using type = Cfg<128, 128, 64, S, 2, 2, SYNC_PINGPONG, BT, 4, false, 16, false, 1>;
 };
 
 template <>
 struct Pick<SYNC_PINGPONG, 2> {
     template <bool BT>
-    using type = Cfg<128, 128, 64, 2, 2, 2, SYNC_PINGPONG, BT, 4, false, 16, true>;
+    using type = Cfg<128, 128, 64, 2, 2, 2, SYNC_PINGPONG, BT, 4, false, 16, true, 1>;
 };
 
 // The split-window ring: the two-stage barrier instance's tile, waves and
