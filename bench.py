@@ -34,7 +34,7 @@ Also reports:
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sync all|barrier|flags|wavespec|pingpong]
                        [--stages S] [--workload NAME] [--no-cpu-baseline] [--no-workloads] ...
        python bench.py --counter-run            (a short pass over every configuration, for rocprofv3 --pmc)
-       python bench.py --summarize-counters SQ_CSV FETCH_CSV WRITE_CSV MANIFEST_JSON   (no GPU)
+       python bench.py --summarize-counters SQ_CSV FETCH_CSV WRITE_CSV MANIFEST_JSON [TCC_CSV]   (no GPU)
 """
 import argparse
 import hashlib
@@ -104,7 +104,7 @@ def parse(argv=None):
     ap.add_argument("--manifest", default=None, help="where --counter-run writes its manifest")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_TRACE_CSV", "BENCH_JSON"),
                     help="turn a rocprofv3 kernel trace of a bench.py run into the committed summary (no GPU)")
-    ap.add_argument("--summarize-counters", nargs=4, metavar=("SQ_CSV", "FETCH_CSV", "WRITE_CSV", "MANIFEST"),
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                     help="turn the rocprofv3 counter CSVs of --counter-run passes into the committed "
                          "summary (no GPU needed)")
     return ap.parse_args(argv)
@@ -176,11 +176,17 @@ def _assign(dispatches, manifest):
 
 
 def summarize_counters(paths, out_path=COUNTERS_FILE):
-    sq_csv, fetch_csv, write_csv, manifest_path = paths
+    """paths: SQ_CSV FETCH_CSV WRITE_CSV MANIFEST [TCC_CSV] -- the CSVs of
+    the counter passes over --counter-run, its manifest, and optionally the
+    pass with the L2 request, hit and miss counts."""
+    if len(paths) not in (4, 5):
+        raise SystemExit("--summarize-counters SQ_CSV FETCH_CSV WRITE_CSV MANIFEST [TCC_CSV]")
+    sq_csv, fetch_csv, write_csv, manifest_path = paths[:4]
     manifest = json.load(open(manifest_path))
     sq, _ = _assign(_dispatches(sq_csv), manifest)
     fe, fe_other = _assign(_dispatches(fetch_csv), manifest)
     wr, wr_other = _assign(_dispatches(write_csv), manifest)
+    tcc = _assign(_dispatches(paths[4]), manifest)[0] if len(paths) == 5 else None
     # The 1 GiB device copy is the largest copy kernel ahead of the first GEMM
     # (the first workload's small host-to-device copies may follow it).
     copy_f = max((d["c"]["FETCH_SIZE"] for d in fe_other if "FETCH_SIZE" in d["c"] and "copy" in d["name"].lower()),
@@ -225,6 +231,14 @@ def summarize_counters(paths, out_path=COUNTERS_FILE):
             "write_bytes_per_call": round(write),
             "hbm_bytes_per_call": round(fetch + write),
         }
+        if tcc is not None:
+            # The GEMM kernel's own L2 traffic (a split call's reduction is
+            # not counted here), in 128-byte requests.
+            gemm = [c[0] for c in tcc[(wl, cfg)]]
+            req = sum(d["c"].get("TCC_REQ_sum", 0.0) for d in gemm) / len(gemm)
+            miss = sum(d["c"].get("TCC_MISS_sum", 0.0) for d in gemm) / len(gemm)
+            entries[wl][cfg].update({"l2_requests": req, "l2_misses": miss,
+                                     "l2_miss_rate": round(miss / req, 4) if req else None})
     out = {"kernel_source_sha256": kernel_sha(),
            "calibration": {"copy_bytes": COPY_BYTES, "fetch_scale": f_scale, "write_scale": w_scale,
                            "copy_fetch_kib": copy_f, "copy_write_kib": copy_w},
@@ -247,8 +261,11 @@ COUNTER_COMMANDS = [
     "--manifest <out>/manifest.json",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/write -o write -- python3 bench.py --counter-run "
     "--manifest <out>/manifest.json",
+    "rocprofv3 --pmc TCC_REQ_sum TCC_HIT_sum TCC_MISS_sum --output-format csv -d <out>/tcc -o tcc -- python3 "
+    "bench.py --counter-run --manifest <out>/manifest.json",
     "python3 bench.py --summarize-counters <out>/sq/sq_counter_collection.csv "
-    "<out>/fetch/fetch_counter_collection.csv <out>/write/write_counter_collection.csv <out>/manifest.json",
+    "<out>/fetch/fetch_counter_collection.csv <out>/write/write_counter_collection.csv <out>/manifest.json "
+    "<out>/tcc/tcc_counter_collection.csv",
 ]
 
 
@@ -272,17 +289,21 @@ def write_counter_reports(info, out_dir=PROFILES):
                  "1024 SIMDs); bank conflicts = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; instruction counts are "
                  "per call, whole GPU; HBM bytes = FETCH_SIZE x %.4f + WRITE_SIZE x %.4f (KiB), the factors that "
                  "make a 1 GiB device copy read and write 1 GiB, summed over every kernel of the call (a split "
-                 "call's reduction included).  Calls shorter than a few microseconds give meaningless clocks."
+                 "call's reduction included).  L2 requests (128 bytes each) and the fraction that missed are "
+                 "TCC_REQ_sum and TCC_MISS_sum of the GEMM kernel alone.  Calls shorter than a few microseconds "
+                 "give meaningless clocks."
                  % (cal["fetch_scale"], cal["write_scale"]), "",
                  "| config | kernel (as rocprofv3 names it) | duration (us) | clock (GHz) | MFMA busy | SALU instr | "
-                 "LDS instr | VMEM read instr | LDS bank conflicts | HBM read (GB) | HBM write (GB) |",
-                 "|---|---|---|---|---|---|---|---|---|---|---|"]
+                 "LDS instr | VMEM read instr | LDS bank conflicts | HBM read (GB) | HBM write (GB) | L2 requests | "
+                 "L2 miss rate |",
+                 "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
         fmt = lambda v, f: "-" if v is None else f % v
         for cfg, e in cfgs.items():
-            lines.append("| %s | `%s` | %.1f | %.3f | %s | %.3g | %.3g | %.3g | %s | %.3f | %.3f |" % (
+            lines.append("| %s | `%s` | %.1f | %.3f | %s | %.3g | %.3g | %.3g | %s | %.3f | %.3f | %s | %s |" % (
                 cfg, e["kernel"], e["duration_us"], e["clock_ghz"], fmt(e["mfma_busy"], "%.3f"), e["salu_insts"],
                 e["lds_insts"], e["vmem_rd_insts"], fmt(e["lds_bank_conflict_of_active"], "%.4f"),
-                e["fetch_bytes_per_call"] / 1e9, e["write_bytes_per_call"] / 1e9))
+                e["fetch_bytes_per_call"] / 1e9, e["write_bytes_per_call"] / 1e9,
+                fmt(e.get("l2_requests"), "%.3g"), fmt(e.get("l2_miss_rate"), "%.3f")))
         path = os.path.join(out_dir, "%s_counters.md" % wl)
         with open(path, "w") as f:
             f.write("\n".join(lines) + "\n")

@@ -107,6 +107,42 @@ def test_summarize_counters_end_to_end(tmp_path):
     assert bench.counters_for("gemm8192_nk", "barrier/2", path=str(out)) is None
 
 
+def test_summarize_counters_with_l2_pass(tmp_path):
+    """The optional fifth CSV (TCC_REQ_sum, TCC_HIT_sum, TCC_MISS_sum) adds
+    the GEMM kernel's own L2 requests and miss rate; the reduction of a split
+    call is left out."""
+    def sq(name):
+        return {"GRBM_GUI_ACTIVE": 8.0} if "copy" in name else {"GRBM_GUI_ACTIVE": 8 * 1.7 * 700_000}
+
+    def fetch(name):
+        return {"FETCH_SIZE": 524288.0 if "copy" in name and "rocclr" in name else 1000.0}
+
+    def write(name):
+        return {"WRITE_SIZE": 1048576.0 if "copy" in name else 2000.0}
+
+    def tcc(name):
+        if "k_reduce_splits" in name:
+            return {"TCC_REQ_sum": 1e9, "TCC_HIT_sum": 0.0, "TCC_MISS_sum": 1e9}
+        return {"TCC_REQ_sum": 6.9e7, "TCC_HIT_sum": 5.5e7, "TCC_MISS_sum": 1.4e7}
+
+    for n, f in (("sq.csv", sq), ("f.csv", fetch), ("w.csv", write), ("t.csv", tcc)):
+        _synthetic_pass(tmp_path / n, f)
+    manifest = {"calls": [{"workload": "gemm8192_nk", "config": "barrier/2", "calls": 2, "kernels": ["k_gemm"]},
+                          {"workload": "longk1024_k32768_kn", "config": "wavespec/3", "calls": 1,
+                           "kernels": ["k_gemm_ws", "k_reduce_splits"]}]}
+    (tmp_path / "m.json").write_text(json.dumps(manifest))
+    paths = [str(tmp_path / n) for n in ("sq.csv", "f.csv", "w.csv", "m.json")]
+    info = bench.summarize_counters(paths + [str(tmp_path / "t.csv")], out_path=str(tmp_path / "c.json"))
+    for wl, cfg in (("gemm8192_nk", "barrier/2"), ("longk1024_k32768_kn", "wavespec/3")):
+        e = info["entries"][wl][cfg]
+        assert e["l2_requests"] == pytest.approx(6.9e7) and e["l2_misses"] == pytest.approx(1.4e7)
+        assert e["l2_miss_rate"] == pytest.approx(1.4 / 6.9, abs=1e-4)
+    without = bench.summarize_counters(paths, out_path=str(tmp_path / "c4.json"))
+    assert "l2_requests" not in without["entries"]["gemm8192_nk"]["barrier/2"]
+    with pytest.raises(SystemExit):
+        bench.summarize_counters(paths[:3], out_path=str(tmp_path / "c3.json"))
+
+
 def test_dispatches_that_do_not_match_the_manifest_are_rejected(tmp_path):
     _synthetic_pass(tmp_path / "sq.csv", lambda name: {"GRBM_GUI_ACTIVE": 1.0})
     wrong = {"calls": [{"workload": "x", "config": "barrier/2", "calls": 3, "kernels": ["k_gemm"]}]}
