@@ -251,11 +251,17 @@ struct Cfg {
     // workgroup's poison word (SyncState), padded to 8 bytes.
     static constexpr int FLAG_BYTES = (SYNC != SYNC_BARRIER) ? PIPES * 2 * S * 4 + 8 : 0;
     // Epilogue strip per MFMA wave: 32 rows x 64 columns of bf16 when that
-    // fits next to the ring (or, with windows, inside one window), else 32
-    // rows x 32 columns.
-    static constexpr int EPI_W =
-        (WIN ? NCW * 32 * 64 * 2 <= A_BYTES : RING_BYTES + NCW * 32 * 64 * 2 + FLAG_BYTES <= 160 * 1024) ? 64 : 32;
-    static constexpr int EPI_WAVE_BYTES = 32 * EPI_W * 2;
+    // fits next to the ring (or, with windows, inside one window).  Else,
+    // with 16 x 16 blocks, 16 rows x 64 columns: the same bytes as 32 x 32,
+    // but every row the strip hands to the stores is a whole 128-byte line
+    // of C (64-byte rows wrote 35-40% more bytes to HBM than C holds, and
+    // slowed the epilogue where all workgroups store at once); with 32 x 32
+    // blocks, 32 rows x 32 columns.
+    static constexpr bool EPI_FULL =
+        WIN ? NCW * 32 * 64 * 2 <= A_BYTES : RING_BYTES + NCW * 32 * 64 * 2 + FLAG_BYTES <= 160 * 1024;
+    static constexpr int EPI_W = (EPI_FULL || MF_ == 16) ? 64 : 32;
+    static constexpr int EPI_H = (EPI_FULL || MF_ != 16) ? 32 : 16;
+    static constexpr int EPI_WAVE_BYTES = EPI_H * EPI_W * 2;
     static constexpr int EPI_OFFSET = RING_BYTES;
     static constexpr int FLAG_OFFSET = WIN ? RING_BYTES : EPI_OFFSET + NCW * EPI_WAVE_BYTES;
     static constexpr int LDS_BYTES = FLAG_OFFSET + FLAG_BYTES;
@@ -1378,8 +1384,9 @@ __device__ __forceinline__ void epilogue16(const Params& p, f32x4_t (&acc)[C::FM
                                            int32_t m0, int32_t n0, int wm, int wn, int lane_in)
 {
     constexpr int W = C::EPI_W, RB = 2 * W, JB = W / 16;   // columns, row bytes and blocks per pass
+    constexpr int EH = C::EPI_H, IB = EH / 16;              // rows and block rows per pass
     constexpr int LPR = RB / 16, RPI = 64 / LPR;           // lanes per strip row, rows per read
-    static_assert(C::FN % JB == 0, "whole passes");
+    static_assert(C::FN % JB == 0 && C::FM % IB == 0, "whole passes");
     const int lane = (int)opaque((uint32_t)lane_in);
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(p.C + ((int64_t)m0 * p.ldc + n0) * 2, ((p.M - m0 - 1) * p.ldc + (p.N - n0)) * 2);
@@ -1390,15 +1397,15 @@ __device__ __forceinline__ void epilogue16(const Params& p, f32x4_t (&acc)[C::FM
     const int wrow = lane & 15, wq = lane >> 4;
     const int rrow = lane / LPR, rchunk = lane % LPR;
 #pragma unroll
-    for (int i2 = 0; i2 < C::FM / 2; ++i2) {
+    for (int i2 = 0; i2 < C::FM / IB; ++i2) {
 #pragma unroll
         for (int jp = 0; jp < C::FN / JB; ++jp) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ii = 0; ii < 2; ++ii) {
+            for (int ii = 0; ii < IB; ++ii) {
 #pragma unroll
                 for (int jj = 0; jj < JB; ++jj) {
-                    const f32x4_t& a = acc[2 * i2 + ii][JB * jp + jj];
+                    const f32x4_t& a = acc[IB * i2 + ii][JB * jp + jj];
                     u32x2_t v;
                     v.x = pack_bf16x2(a[0], a[1]);
                     v.y = pack_bf16x2(a[2], a[3]);
@@ -1409,11 +1416,11 @@ __device__ __forceinline__ void epilogue16(const Params& p, f32x4_t (&acc)[C::FM
                 }
             }
             wait_lgkm0();
-            const int gr0 = wm * C::TM + 32 * i2 + rrow;         // tile row of read slot 0
+            const int gr0 = wm * C::TM + EH * i2 + rrow;         // tile row of read slot 0
             const int gc = wn * C::TN + W * jp + 8 * rchunk;     // tile column of this lane's chunk
             const uint32_t obase = opaque((uint32_t)gr0 * ldc2 + (uint32_t)gc * 2u);
 #pragma unroll
-            for (int u = 0; u < 32 / RPI; ++u) {
+            for (int u = 0; u < EH / RPI; ++u) {
                 const int row = rrow + RPI * u;
                 const u32x4_t v = *(const LDS_AS u32x4_t*)(strip + row * RB + ((rchunk ^ swz(row)) << 4));
                 const bool ok = (gr0 + RPI * u < mrem) && (gc < nrem);
