@@ -25,6 +25,10 @@ Also reports:
                 all (gemm_probe_mfma_ceiling, at the GEMM kernels' wave shape,
                 fragments in registers or re-read from LDS), beside the same
                 loop on all-zero operands;
+  sustained     the fastest configuration run back to back for several seconds
+                (--sustain-seconds) in batches timed with HIP events: the
+                throughput once the clock has settled for seconds, and the
+                spread between batches;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same product
                 (a few rows of C), on the host cores it actually uses; each
                 other workload's oracle sample is under its entry;
@@ -95,6 +99,9 @@ def parse(argv=None):
     ap.add_argument("--cpu-seconds-other", type=float, default=2.5,
                     help="target CPU time of each other workload's oracle sample")
     ap.add_argument("--no-reference", action="store_true", help="skip the torch.matmul timing")
+    ap.add_argument("--sustain-seconds", type=float, default=8.0,
+                    help="run the fastest configuration back to back for this long after the timed steps "
+                         "and report it as `sustained` (0: skip)")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the matrix-core ceiling probe")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the other configurations")
@@ -462,6 +469,30 @@ def measure_workload(bd, w, configs, args, torch, A=None, B=None):
 REFERENCE_WARMUP = 100
 
 
+def sustained(bd, w, sync, stages, dA, dB, C, seconds, torch, batch=100):
+    """The fastest configuration run back to back for about `seconds`, in
+    batches of `batch` calls, each batch between one pair of HIP events on the
+    launch stream: the throughput once the board's clock has settled under its
+    power limit for seconds rather than milliseconds, and how much it moves
+    from batch to batch.  Also keeps the GPU visibly busy for that long."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rates, total_ms, calls = [], 0.0, 0
+    while total_ms < 1000.0 * seconds:
+        e0.record()
+        for _ in range(batch):
+            bd.gemm(dA, dB, b_transposed=w.b_transposed, sync=sync, stages=stages, out=C)
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        total_ms += ms
+        calls += batch
+        rates.append(2.0 * w.M * w.N * w.K * batch / ms / 1e9)
+    return {"config": label(sync, stages), "seconds": round(total_ms / 1e3, 2), "calls": calls,
+            "tflops": round(2.0 * w.M * w.N * w.K * calls / total_ms / 1e9, 2),
+            "batch_tflops_min": round(min(rates), 2), "batch_tflops_max": round(max(rates), 2),
+            "pct_of_peak": round(100.0 * 2.0 * w.M * w.N * w.K * calls / total_ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+
+
 def reference_matmul(dA, dB, C, w, steps, warmup, torch):
     """torch.matmul on the same operands (B^T as a view when B is stored N x K),
     after max(warmup, REFERENCE_WARMUP) untimed calls."""
@@ -710,6 +741,9 @@ def main():
                      "clock_ghz_counter_pass": cnt["clock_ghz"] if cnt else None,
                      "frac_at_counter_clock": r.get("frac_of_peak_at_counter_clock")},
     }
+    if args.sustain_seconds > 0:
+        line["sustained"] = sustained(bd, w, sync, stages, dA, dB, C, args.sustain_seconds, torch)
+        print("# sustained: %s" % json.dumps(line["sustained"]), file=sys.stderr, flush=True)
     if not args.no_reference:
         line["reference"] = reference_matmul(dA, dB, C, w, args.steps, args.warmup, torch)
     del dA, dB, C

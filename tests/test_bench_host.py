@@ -174,7 +174,7 @@ def test_more_than_one_gpu_is_refused():
 def test_helpers_present():
     """Everything main() calls on the GPU path exists (a CPU run never reaches it)."""
     for name in ("time_mode", "measure_workload", "cpu_baseline", "counters_for", "summarize_counters",
-                 "reference_matmul", "mfma_ceiling", "counter_run", "kernel_sha", "parse"):
+                 "reference_matmul", "mfma_ceiling", "counter_run", "kernel_sha", "parse", "sustained"):
         assert callable(getattr(bench, name)), name
     import ast
     import builtins
@@ -253,3 +253,36 @@ def test_sampled_clock_turns_sampling_on_only_for_its_calls():
     with pytest.raises(RuntimeError):
         bench.sampled_clock(fb, None, None, None, W, "barrier", 2, calls=3)
     assert fb.on is False
+
+
+def test_sustained_runs_whole_batches_until_the_time_is_up():
+    """bench.sustained with a stand-in GPU: every batch takes 50 ms of event
+    time, so 0.12 s needs three batches; the rate is FLOPs over event time."""
+    from types import SimpleNamespace
+
+    class Event:
+        def __init__(self, enable_timing=False):
+            self.t = None
+
+        def record(self):
+            fake.clock += 0.0
+
+        def synchronize(self):
+            pass
+
+        def elapsed_time(self, other):
+            return 50.0
+
+    fake = SimpleNamespace(clock=0.0, calls=0)
+    torch_stub = SimpleNamespace(cuda=SimpleNamespace(Event=Event))
+
+    def gemm(A, B, *, b_transposed, sync, stages, out):
+        fake.calls += 1
+
+    bd = SimpleNamespace(gemm=gemm)
+    w = SimpleNamespace(M=1024, N=1024, K=1024, b_transposed=True)
+    r = bench.sustained(bd, w, "barrier", 2, None, None, None, 0.12, torch_stub, batch=10)
+    assert fake.calls == 30 and r["calls"] == 30 and r["seconds"] == pytest.approx(0.15)
+    flops = 2.0 * 1024 ** 3 * 30
+    assert r["tflops"] == pytest.approx(round(flops / 150.0 / 1e9, 2))
+    assert r["batch_tflops_min"] == r["batch_tflops_max"] and r["config"] == "barrier/2"
