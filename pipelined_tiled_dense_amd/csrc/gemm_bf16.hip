@@ -1371,14 +1371,14 @@ __device__ __forceinline__ void epilogue_narrow(const Params& p, f32x16_t (&acc)
 }
 
 // 16 x 16 blocks: lane l of block (i, j) holds row 16i + l%16 and columns
-// 16j + 4*(l/16) + 0..3.  A pass converts two block rows (32 rows) by W/16
-// blocks (W columns, the strip's width: 64, or 32 when LDS is short) into
-// the strip, then stores it.  Writes: the 32 lanes of a write cycle cover 16
-// rows at one chunk (both 8-byte halves); the chunk is XORed with
-// (row / 2) mod 8 (128-byte rows, two per 256-byte bank window) or with
-// (row / 4) mod 4 (64-byte rows, four per window), which puts them on 32
-// different 8-byte bank slots.  Reads: W/8 lanes cover one row segment of C,
-// 16 lanes (2 or 4 rows) per cycle on 16 different 16-byte slots.
+// 16j + 4*(l/16) + 0..3.  A pass converts EH/16 block rows (EH rows, the
+// strip's height: 32, or 16 when LDS is short) by 4 blocks (the strip's 64
+// columns, 128-byte rows) into the strip, then stores it.  Writes: the 32
+// lanes of a write cycle cover 16 rows at one chunk (both 8-byte halves);
+// the chunk is XORed with (row / 2) mod 8 (two rows per 256-byte bank
+// window), which puts them on 32 different 8-byte bank slots.  Reads: 8
+// lanes cover one 128-byte row segment of C, 16 lanes (2 rows) per cycle on
+// 16 different 16-byte slots.
 template <class C>
 __device__ __forceinline__ void epilogue16(const Params& p, f32x4_t (&acc)[C::FM][C::FN], lds_char* strip,
                                            int32_t m0, int32_t n0, int wm, int wn, int lane_in)
@@ -1386,14 +1386,14 @@ __device__ __forceinline__ void epilogue16(const Params& p, f32x4_t (&acc)[C::FM
     constexpr int W = C::EPI_W, RB = 2 * W, JB = W / 16;   // columns, row bytes and blocks per pass
     constexpr int EH = C::EPI_H, IB = EH / 16;              // rows and block rows per pass
     constexpr int LPR = RB / 16, RPI = 64 / LPR;           // lanes per strip row, rows per read
-    static_assert(C::FN % JB == 0 && C::FM % IB == 0, "whole passes");
+    static_assert(W == 64 && C::FN % JB == 0 && C::FM % IB == 0, "whole passes of 128-byte rows");
     const int lane = (int)opaque((uint32_t)lane_in);
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(p.C + ((int64_t)m0 * p.ldc + n0) * 2, ((p.M - m0 - 1) * p.ldc + (p.N - n0)) * 2);
     const int32_t mrem = (int32_t)min(p.M - m0, (int64_t)C::BM);
     const int32_t nrem = (int32_t)min(p.N - n0, (int64_t)C::BN);
     const uint32_t ldc2 = (uint32_t)p.ldc * 2u;
-    auto swz = [](int row) { return W == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3); };
+    auto swz = [](int row) { return (row >> 1) & 7; };
     const int wrow = lane & 15, wq = lane >> 4;
     const int rrow = lane / LPR, rchunk = lane % LPR;
 #pragma unroll
