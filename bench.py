@@ -594,7 +594,35 @@ def mfma_ceiling(torch, steps=20):
         out[name] = e
     out["note"] = ("MFMA-only loop of 16x16x32 bf16 at the GEMM kernels' wave shapes, 256 workgroups, no global "
                    "memory traffic; random uniform[-1,1) bf16 operands unless named zero_data")
+    out["lds_read_bandwidth"] = lds_read_bandwidth(torch)
     return out
+
+
+LDS_BW_ITERS = 4096
+
+
+def lds_read_bandwidth(torch):
+    """gemm_probe_lds_read_bw on 256 workgroups (one per compute unit): the
+    LDS read bandwidth of a CU in bytes per shader clock, from each
+    workgroup's own s_memtime stamps around its reads.  The swizzles and the
+    LDS budget of the kernels assume 64 four-byte banks, 256 bytes per clock."""
+    import ctypes
+    lib = _ceiling_lib()
+    lib.gemm_probe_lds_read_bw.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p]
+    lib.gemm_probe_lds_read_bw.restype = ctypes.c_int
+    blocks = 256
+    sink = torch.empty(blocks * 1024, dtype=torch.int32, device="cuda")
+    stamps = torch.zeros((blocks, 2), dtype=torch.int64, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        if lib.gemm_probe_lds_read_bw(LDS_BW_ITERS, blocks, sink.data_ptr(), stamps.data_ptr(), s) != 0:
+            raise RuntimeError("gemm_probe_lds_read_bw failed")
+    torch.cuda.synchronize()
+    ticks = stamps[:, 0].double().cpu()
+    bpc = (LDS_BW_ITERS + 1) * 128 * 1024 / ticks
+    return {"bytes_per_clk_per_cu": round(float(bpc.mean()), 1), "min": round(float(bpc.min()), 1),
+            "max": round(float(bpc.max()), 1), "of_256": round(float(bpc.mean()) / 256.0, 4)}
 
 
 def wall_clock_hz(torch):

@@ -11,9 +11,11 @@
 //   - ds_read_b64_tr_b16: which lane receives which 16-bit element;
 //   - the fp32 -> bf16 conversion used by the epilogue (rounding mode);
 //   - buffer range checking, with and without a scalar offset.
-// One more entry point is a measurement rather than a semantics probe: the
+// Two more entry points are measurements rather than semantics probes: the
 // matrix-core throughput the board sustains under its power limit on given
-// operand data, with no global memory traffic (gemm_probe_mfma_ceiling).
+// operand data, with no global memory traffic (gemm_probe_mfma_ceiling), and
+// the LDS read bandwidth of one compute unit in bytes per shader clock
+// (gemm_probe_lds_read_bw).
 // All accesses stay inside the buffers whose sizes are stated per entry
 // point; the host wrapper checks pointer arguments before launching.
 #include <hip/hip_runtime.h>
@@ -290,6 +292,58 @@ __global__ void __launch_bounds__(NT) k_mfma_ceiling(const bf16x8_t* __restrict_
     }
 }
 
+// LDS read bandwidth: one workgroup of 1024 threads per compute unit (96 KiB
+// of LDS each, so no two share a CU) fills 64 KiB of it, then each of its 16
+// waves issues `iters` x 8 ds_read_b128 loads of 1 KiB each -- 64 lanes on
+// 64 consecutive 16-byte slots, free of bank conflicts -- XOR-folding them
+// into registers so that none can be dropped.  The next iteration's 8 loads
+// are issued before the current ones are folded, so each wave keeps up to 16
+// loads in flight.  The shader clock is stamped (s_memtime) after the fill
+// and after a workgroup barrier at the end, so a stamp pair spans every
+// wave's reads.  Bytes per clock of one CU = iters * 8 reads * 16 waves *
+// 1024 bytes / elapsed ticks.
+constexpr int kBwAlloc = 96 * 1024 / 16;      // 16-byte units allocated
+constexpr int kBwThreads = 1024;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4v_t;
+
+__global__ void __launch_bounds__(kBwThreads) k_lds_read_bw(int iters, uint32_t* __restrict__ sink,
+                                                           uint64_t* __restrict__ stamps)
+{
+    __shared__ u32x4v_t lds[kBwAlloc];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    for (int i = t; i < kBwAlloc; i += kBwThreads)
+        lds[i] = u32x4v_t{(unsigned)i, (unsigned)i * 3u, (unsigned)i * 5u, (unsigned)i * 7u};
+    __syncthreads();
+    const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    // Iteration it of wave w reads the 8 KiB block (w + it) mod 8 of the 64
+    // KiB at one address plus immediate offsets.
+    auto block = [&](int it) { return lds + (((w + it) & 7) * 512 + lane); };
+    u32x4v_t cur[8], nxt[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        cur[r] = block(0)[r * 64];
+    uint32_t acc0 = 0u, acc1 = 0u;
+    for (int it = 1; it <= iters; ++it) {
+        const u32x4v_t* src = block(it);
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            nxt[r] = src[r * 64];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            acc0 ^= cur[r].x ^ cur[r].y;
+            acc1 ^= cur[r].z ^ cur[r].w;
+            cur[r] = nxt[r];
+        }
+    }
+    __syncthreads();
+    const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    sink[(int64_t)blockIdx.x * kBwThreads + t] = acc0 ^ acc1;
+    if (stamps && t == 0) {
+        stamps[2 * blockIdx.x] = c1 - c0;
+        stamps[2 * blockIdx.x + 1] = r1 - r0;
+    }
+}
+
 int launch_status()
 {
     hipError_t e = hipGetLastError();
@@ -399,6 +453,17 @@ int gemm_probe_mfma_ceiling(const uint16_t* data, int64_t n_elems, int from_lds,
         hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<true, 4, 8, 256>), dim3(blocks), dim3(256), 0, s, d, n_vec, iters, sink, stamps);
     else
         hipLaunchKernelGGL(HIP_KERNEL_NAME(k_mfma_ceiling<false, 4, 8, 256>), dim3(blocks), dim3(256), 0, s, d, n_vec, iters, sink, stamps);
+    return launch_status();
+}
+
+// sink: blocks * 1024 words; stamps: null, or 2 * blocks 64-bit words that
+// receive each workgroup's elapsed s_memtime and s_memrealtime ticks over its
+// reads.  Each workgroup reads (iters + 1) * 128 KiB.
+int gemm_probe_lds_read_bw(int iters, int blocks, uint32_t* sink, uint64_t* stamps, void* stream)
+{
+    if (!sink || iters < 1 || iters > (1 << 20) || blocks < 1 || blocks > 65536)
+        return -1;
+    hipLaunchKernelGGL(k_lds_read_bw, dim3(blocks), dim3(kBwThreads), 0, (hipStream_t)stream, iters, sink, stamps);
     return launch_status();
 }
 

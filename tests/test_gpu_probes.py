@@ -246,3 +246,28 @@ def test_buffer_range_check_counts_scalar_offset(probes):
     np.testing.assert_array_equal(got[:32], data[:32])
     np.testing.assert_array_equal(got[48:], zero[48:])
     np.testing.assert_array_equal(got[32:48], zero[32:48])
+
+
+def test_lds_read_bandwidth_is_64_banks_per_clock(probes):
+    """The kernels' LDS swizzles and their bank-conflict arithmetic assume 64
+    four-byte banks, 256 bytes per clock per compute unit.  Conflict-free
+    ds_read_b128 streams from 16 waves of one workgroup per CU, timed with
+    each workgroup's own shader-clock stamps, come within 15% of that and
+    never above it."""
+    print("probe lds_read_bw", flush=True)
+    probes.gemm_probe_lds_read_bw.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p]
+    probes.gemm_probe_lds_read_bw.restype = ctypes.c_int
+    blocks, iters = 256, 2048
+    sink = torch.empty(blocks * 1024, dtype=torch.int32, device="cuda")
+    stamps = torch.zeros((blocks, 2), dtype=torch.int64, device="cuda")
+    for _ in range(2):
+        assert probes.gemm_probe_lds_read_bw(iters, blocks, sink.data_ptr(), stamps.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    ticks = stamps[:, 0].double().cpu()
+    assert bool((ticks > 0).all())
+    bpc = (iters + 1) * 128 * 1024 / ticks
+    print("  bytes per clock per CU: mean %.1f, min %.1f, max %.1f" % (bpc.mean(), bpc.min(), bpc.max()), flush=True)
+    assert float(bpc.mean()) >= 0.85 * 256
+    assert float(bpc.max()) <= 256 * 1.01
+    assert probes.gemm_probe_lds_read_bw(0, blocks, sink.data_ptr(), None, _stream()) == -1
