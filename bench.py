@@ -656,7 +656,27 @@ def cpu_baseline(w, A, B, target_s):
     flops = 2.0 * rows * w.N * w.K
     return {"value": round(flops / t / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": "rows 0..%d of C (%d x %d x %d, %.3g GFLOP) in %.2f s; fp64 triple loop, "
-                      "one bf16 rounding" % (rows - 1, rows, w.N, w.K, flops / 1e9, t)}
+                      "one bf16 rounding" % (rows - 1, rows, w.N, w.K, flops / 1e9, t),
+            "host": host_cpu()}
+
+
+def host_cpu():
+    """The host CPU the oracle ran on: model name and the cores this process
+    may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = os.cpu_count()
+    return {"model": model, "cores_allowed": allowed}
 
 
 def counter_run(bd, args, torch):

@@ -174,7 +174,8 @@ def test_more_than_one_gpu_is_refused():
 def test_helpers_present():
     """Everything main() calls on the GPU path exists (a CPU run never reaches it)."""
     for name in ("time_mode", "measure_workload", "cpu_baseline", "counters_for", "summarize_counters",
-                 "reference_matmul", "mfma_ceiling", "counter_run", "kernel_sha", "parse", "sustained"):
+                 "reference_matmul", "mfma_ceiling", "counter_run", "kernel_sha", "parse", "sustained",
+                 "lds_read_bandwidth", "host_cpu"):
         assert callable(getattr(bench, name)), name
     import ast
     import builtins
@@ -286,3 +287,9 @@ def test_sustained_runs_whole_batches_until_the_time_is_up():
     flops = 2.0 * 1024 ** 3 * 30
     assert r["tflops"] == pytest.approx(round(flops / 150.0 / 1e9, 2))
     assert r["batch_tflops_min"] == r["batch_tflops_max"] and r["config"] == "barrier/2"
+
+
+def test_host_cpu_reports_model_and_allowed_cores():
+    h = bench.host_cpu()
+    assert set(h) == {"model", "cores_allowed"}
+    assert h["cores_allowed"] is None or h["cores_allowed"] >= 1
