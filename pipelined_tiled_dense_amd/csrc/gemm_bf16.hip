@@ -2056,7 +2056,11 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
                     // Per 32-wide k-step: the B blocks and A blocks
                     // 0 .. FM/2 - 1 (read order of FragReader), their MFMAs,
                     // then A blocks FM/2 .. FM - 1 into the same A registers
-                    // and theirs.
+                    // and theirs.  No wait for all of a batch's reads: each
+                    // MFMA waits (lgkmcnt) only for its own fragments, so the
+                    // first MFMAs start once A block 0 and B block 0 are in
+                    // (measured +0.4-2%); the stage is released after a wait
+                    // for every read of its last k-step.
                     constexpr int H = (C::BT ? 1 : 2) * C::FN + C::FM / 2;
 #pragma unroll
                     for (int ks = 0; ks < C::BK / 32; ++ks) {
@@ -2065,7 +2069,6 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
 #pragma unroll
                         for (int d = 0; d < H; ++d)
                             rd.read(f, stage, wn, d);
-                        wait_lgkm0();
 #pragma unroll
                         for (int i = 0; i < C::FM / 2; ++i)
 #pragma unroll
@@ -2075,9 +2078,10 @@ __global__ void __launch_bounds__(C::THREADS) k_gemm_ws(Params p)
 #pragma unroll
                         for (int i = 0; i < C::FM / 2; ++i)
                             rd.read_a_into(f, stage, C::FM / 2 + i, i);
-                        wait_lgkm0();
-                        if (ks == C::BK / 32 - 1)
+                        if (ks == C::BK / 32 - 1) {
+                            wait_lgkm0();
                             arrive(empty + s);
+                        }
 #pragma unroll
                         for (int i = 0; i < C::FM / 2; ++i)
 #pragma unroll
