@@ -713,7 +713,7 @@ def counter_run(bd, args, torch):
             _ceiling_call(torch, lib, name, zero if zero_data else rand, sink)
         torch.cuda.synchronize()
         calls.append({"workload": "ceiling", "config": name, "calls": 4, "kernels": ["k_mfma_ceiling"]})
-    path = args.manifest or os.path.join(ROOT, "gpurun_out", "counter_manifest.json")
+    path = args.manifest or os.path.join(ROOT, "counter_out", "counter_manifest.json")
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
         json.dump({"calls": calls}, f, indent=1)
